@@ -1,0 +1,245 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` takes an :class:`oracle.Oracle` and raises AssertionError when
+the oracle disagrees with something the mathematics or an independent library
+routine fixes: the IEEE binary16 definition (checked exhaustively against
+numpy's float16), exact rational arithmetic on tiny inputs, closed forms
+(all-ones, identity, K=1), exact integer arithmetic, an exact fixed-point sum
+with the fp64 recursive-summation error bound, and invariants (transpose,
+padding, thread count, sampled vs full).  The same pins run against
+deliberately broken builds of the oracle (tests/test_oracle_mutants.py) to
+show that a plausible mistake anywhere in it is caught.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+from shape_driven_tile_amd import inputs
+
+ALL_BITS = np.arange(65536, dtype=np.uint16)
+U = 2.0 ** -53  # unit roundoff of fp64
+
+
+def _np_dec(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+# ---- binary16 codec -------------------------------------------------------
+
+def pin_decode_exhaustive(o):
+    d = o.f16_decode(ALL_BITS)
+    ref = _np_dec(ALL_BITS)
+    same = (d == ref) | (np.isnan(d) & np.isnan(ref))
+    assert same.all(), f"decode differs at {np.flatnonzero(~same)[:8]}"
+    # sign of zero survives
+    assert np.signbit(d[0x8000]) and not np.signbit(d[0])
+
+
+def pin_encode_roundtrip(o):
+    d = _np_dec(ALL_BITS)
+    fin = ~np.isnan(d)
+    e = o.f16_encode_rne(d)
+    assert (e[fin] == ALL_BITS[fin]).all(), "encode(decode(h)) != h"
+    nan_out = e[~fin]
+    assert ((nan_out & 0x7C00) == 0x7C00).all() and ((nan_out & 0x3FF) != 0).all()
+
+
+def pin_encode_rne_ties(o):
+    """Every midpoint between neighbouring finite binary16 values rounds to the
+    neighbour with an even encoding; one fp64 ulp either side goes to the
+    nearer neighbour."""
+    h = np.arange(0, 0x7BFF, dtype=np.uint16)          # pairs (h, h+1), both finite
+    lo = _np_dec(h)
+    hi = _np_dec(h + 1)
+    mid = (lo + hi) / 2.0                               # exact in fp64
+    want = np.where(h % 2 == 0, h, h + 1).astype(np.uint16)
+    for sgn, sbit in ((1.0, 0), (-1.0, 0x8000)):
+        got = o.f16_encode_rne(sgn * mid)
+        assert (got == (want | sbit)).all(), "tie not rounded to even"
+        below = o.f16_encode_rne(sgn * np.nextafter(mid, 0.0))
+        above = o.f16_encode_rne(sgn * np.nextafter(mid, np.inf))
+        assert (below == (h | sbit)).all(), "value below a midpoint not rounded down"
+        assert (above == ((h + 1) | sbit)).all(), "value above a midpoint not rounded up"
+
+
+def pin_encode_vs_numpy(o):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal(400_000) * np.exp2(rng.uniform(-27.0, 17.0, 400_000))
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)
+    assert (o.f16_encode_rne(x) == ref).all()
+
+
+def pin_encode_special_values(o):
+    cases = [
+        (65504.0, 0x7BFF), (np.nextafter(65520.0, 0.0), 0x7BFF), (65520.0, 0x7C00),
+        (-65520.0, 0xFC00), (np.inf, 0x7C00), (-np.inf, 0xFC00), (0.0, 0x0000),
+        (-0.0, 0x8000), (2.0 ** -24, 0x0001), (2.0 ** -25, 0x0000),
+        (np.nextafter(2.0 ** -25, 1.0), 0x0001), (3 * 2.0 ** -25, 0x0002),
+        (2.0 ** -14, 0x0400), (1.0, 0x3C00), (-2.0, 0xC000), (1.0 + 2.0 ** -11, 0x3C00),
+        (1.0 + 3 * 2.0 ** -11, 0x3C02),
+    ]
+    xs = np.array([c[0] for c in cases], dtype=np.float64)
+    want = np.array([c[1] for c in cases], dtype=np.uint16)
+    got = o.f16_encode_rne(xs)
+    assert (got == want).all(), f"{xs[got != want]} -> {got[got != want]}"
+
+
+# ---- GEMM -----------------------------------------------------------------
+
+def pin_bruteforce_fraction(o):
+    """Tiny shapes: the oracle equals the exact rational sum up to the fp64
+    recursive-summation bound (K-1)*u*sum|ab|."""
+    for (M, N, K, seed) in [(1, 1, 1, 1), (2, 3, 5, 2), (3, 2, 8, 3), (5, 5, 3, 4),
+                            (8, 1, 2, 5), (1, 8, 7, 6)]:
+        A = inputs.uniform_f16((M, K), 100 + seed)
+        B = inputs.uniform_f16((N, K), 200 + seed)
+        C = o.gemm(A, B)
+        a = A.astype(np.float64)
+        b = B.astype(np.float64)
+        for m in range(M):
+            for n in range(N):
+                exact = sum((Fraction(a[m, k]) * Fraction(b[n, k]) for k in range(K)),
+                            Fraction(0))
+                mag = sum(abs(Fraction(a[m, k]) * Fraction(b[n, k])) for k in range(K))
+                err = abs(Fraction(C[m, n]) - exact)
+                assert err <= Fraction(max(K - 1, 0)) * Fraction(U) * mag, (M, N, K, m, n)
+
+
+def pin_all_ones(o):
+    """A = B = 1 gives K in every element, exactly."""
+    for K in (1, 7, 256, 1920, 1984, 2048, 2112, 2176, 2304, 4096, 8192, 16384):
+        A = np.ones((3, K), np.float16)
+        B = np.ones((5, K), np.float16)
+        C = o.gemm(A, B)
+        assert (C == K).all(), K
+
+
+def pin_identity(o):
+    """B = I gives C = A exactly (one non-zero product per sum), M != K."""
+    A = inputs.uniform_f16((40, 24), 11)
+    B = np.eye(24, dtype=np.float16)
+    C = o.gemm(A, B)
+    assert (C == A.astype(np.float64)).all()
+    assert (o.f16_encode_rne(C) == A.view(np.uint16)).all()
+
+
+def pin_k1_outer(o):
+    """K = 1: C(m, n) = a_m * b_n, exact in fp64; its fp16 rounding equals
+    numpy's correctly rounded cast of the same product."""
+    a = inputs.uniform_f16((17, 1), 12)
+    b = inputs.uniform_f16((9, 1), 13)
+    C = o.gemm(a, b)
+    ref = np.outer(a[:, 0].astype(np.float64), b[:, 0].astype(np.float64))
+    assert (C == ref).all()
+    assert (o.f16_encode_rne(C) == ref.astype(np.float16).view(np.uint16)).all()
+
+
+def pin_integer_exact(o):
+    """Small-integer inputs: every sum is an exact integer; compare with exact
+    int64 matrix products (rectangular shapes, so a transposed operand fails)."""
+    for (M, N, K, seed) in [(33, 17, 2304, 1), (5, 9, 1, 2), (64, 48, 130, 3)]:
+        A = inputs.integer_f16((M, K), 300 + seed)
+        B = inputs.integer_f16((N, K), 400 + seed)
+        ref = A.astype(np.int64) @ B.astype(np.int64).T
+        C = o.gemm(A, B)
+        assert (C == ref).all(), (M, N, K)
+
+
+def pin_fixed_point_bound(o):
+    """Inputs in [-1, 1] are integer multiples of 2^-24, so the exact sum is an
+    integer multiple of 2^-48 computed exactly in int64; the oracle must be
+    within the fp64 bound (K-1)*u*sum|ab| of it."""
+    for (M, N, K, seed) in [(24, 20, 300, 1), (6, 40, 1000, 2)]:
+        A = inputs.uniform_f16((M, K), 500 + seed)
+        B = inputs.uniform_f16((N, K), 600 + seed)
+        ia = (A.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+        ib = (B.astype(np.float64) * 2.0 ** 24).astype(np.int64)
+        assert (ia.astype(np.float64) == A.astype(np.float64) * 2.0 ** 24).all()
+        exact = (ia @ ib.T).astype(object)                    # units of 2^-48
+        mag = (np.abs(ia) @ np.abs(ib).T).astype(object)
+        C = o.gemm(A, B)
+        c48 = (C * 2.0 ** 48).astype(np.int64).astype(object)  # exact: C is a multiple of 2^-48
+        assert ((C * 2.0 ** 48) == np.floor(C * 2.0 ** 48)).all()
+        err = np.abs(c48 - exact)
+        bound = [(K - 1) * Fraction(int(s)) / 2 ** 53 for s in mag.ravel()]
+        for e, bnd in zip(err.ravel(), bound):
+            assert Fraction(int(e)) <= bnd
+
+
+def pin_transpose(o):
+    """gemm(B, A) is gemm(A, B) transposed, bit for bit (both K-contiguous)."""
+    A = inputs.uniform_f16((13, 40), 21)
+    B = inputs.uniform_f16((7, 40), 22)
+    assert (o.gemm(B, A) == o.gemm(A, B).T).all()
+
+
+def pin_numpy_crosscheck(o):
+    """Against numpy's fp64 matmul (a different summation order)."""
+    A = inputs.uniform_f16((50, 70), 31)
+    B = inputs.uniform_f16((60, 70), 32)
+    a = A.astype(np.float64)
+    b = B.astype(np.float64)
+    ref = a @ b.T
+    mag = np.abs(a) @ np.abs(b).T
+    assert (np.abs(o.gemm(A, B) - ref) <= 2 * 70 * U * mag).all()
+
+
+def pin_padding_ignored(o):
+    """Row padding past K (filled with NaN) never reaches the result."""
+    A = inputs.uniform_f16((19, 72), 41)
+    B = inputs.uniform_f16((23, 72), 42)
+    tight = o.gemm(A, B)
+    padded = o.gemm(inputs.padded(A, 80), inputs.padded(B, 96), K=72)
+    assert (tight == padded).all()
+
+
+def pin_k0(o):
+    """K = 0 is the empty sum."""
+    A = np.full((4, 8), np.nan, np.float16)
+    B = np.full((3, 8), np.nan, np.float16)
+    assert (o.gemm(A, B, K=0) == 0.0).all()
+
+
+def pin_sample(o):
+    A = inputs.uniform_f16((37, 90), 51)
+    B = inputs.uniform_f16((29, 90), 52)
+    full = o.gemm(A, B)
+    rng = np.random.default_rng(5)
+    r = rng.integers(0, 37, 200)
+    c = rng.integers(0, 29, 200)
+    assert (o.gemm_sample(A, B, r, c) == full[r, c]).all()
+
+
+def pin_threads(o):
+    A = inputs.uniform_f16((64, 257), 61)
+    B = inputs.uniform_f16((48, 257), 62)
+    assert (o.gemm(A, B, threads=1) == o.gemm(A, B, threads=max(2, o.max_threads()))).all()
+
+
+# ---- M=1 decode GEMV ------------------------------------------------------
+
+def pin_gemv(o):
+    K, N = 300, 50
+    x = inputs.uniform_f16((K,), 71)
+    W = inputs.normal_f16((N, K), 72)
+    Wp = inputs.padded(W, 304)
+    y = o.gemv_m1(x, Wp, K=K)
+    # the same definition as a one-row GEMM
+    assert (y == o.gemm(x[None, :], W)[0]).all()
+    # one-hot activations select one weight per column
+    for j in (0, 1, 150, K - 1):
+        e = np.zeros(K, np.float16)
+        e[j] = 1
+        assert (o.gemv_m1(e, Wp, K=K) == W[:, j].astype(np.float64)).all(), j
+    # all-ones
+    assert (o.gemv_m1(np.ones(K, np.float16), np.ones((N, K), np.float16)) == K).all()
+    # fp64 cross-check
+    ref = W.astype(np.float64) @ x.astype(np.float64)
+    mag = np.abs(W.astype(np.float64)) @ np.abs(x.astype(np.float64))
+    assert (np.abs(y - ref) <= 2 * K * U * mag).all()
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
