@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp16 GEMM / M=1 decode GEMV hot path on one MI355X.
+
+One step is one pass of the whole path over one batch of synthetic inputs
+resident in HBM: gemm_f16 (pick_tile + MFMA kernel) on every square size of
+the measured range, 256^3 through 8192^3, then gemm_f16 at M=1, K=4096,
+N=12288 (routed to the streaming GEMV) on the next of 8 rotating weight
+buffers.  The printed value is the step's algorithmic fp16 FLOP rate.
+
+Before any number is printed the outputs are checked against the CPU oracle
+(sampled elements of every square product, every element of all 8 decode
+products); a failure prints no throughput.  The dominant kernel (8192^3) and
+the GEMV are additionally timed launch by launch with HIP events inside the
+timed region, which feed the roofline object.  Per-size, K-sweep and
+cold-cache decode details follow the protocol of the pages: warm-up, then
+10 repeats, min/median/max.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("fp16 GEMM TFLOP/s (and % MFMA peak) 256³–8192³; "
+          "M=1 GEMV µs + HBM GB/s")
+# MI355X nominal peaks: 256 CUs x 4096 fp16 FLOP/clk/CU x 2.4 GHz; HBM3E 8 TB/s.
+PEAK_FP16_TFLOPS = 256 * 4096 * 2.4e9 / 1e12
+PEAK_HBM_GBS = 8000.0
+SIZES = (256, 512, 768, 1024, 1536, 2048, 4096, 8192)
+# seed index of each size's operands (matches the parity tests)
+SEED_INDEX = {256: 0, 512: 1, 768: 1, 1024: 1, 1536: 1, 2048: 1, 4096: 2, 8192: 2}
+DOMINANT = 8192
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=400)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-detail", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from shape_driven_tile_amd import binding as sdt
+    from shape_driven_tile_amd import inputs
+
+    sdt.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"device {props.name} CUs={props.multi_processor_count}")
+
+    def dev_tensor(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs, resident in HBM --------------------------------------------
+    host = {}
+    ops = {}
+    for n in SIZES:
+        A, B = inputs.square_operands(n, SEED_INDEX[n])
+        host[n] = (A, B)
+        ops[n] = (dev_tensor(A), dev_tensor(B), torch.empty((n, n), dtype=torch.float16, device=dev))
+    x_h = inputs.decode_activations()
+    W_h = [inputs.decode_weights(r) for r in range(inputs.DECODE_BUFFERS)]
+    x = dev_tensor(x_h)
+    Ws = [dev_tensor(w) for w in W_h]
+    y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
+    x2 = x.view(1, -1)
+    y2 = y.view(1, -1)
+    log("inputs resident")
+
+    flop_gemm = {n: 2.0 * n ** 3 for n in SIZES}
+    K_dec, N_dec = inputs.DECODE_K, inputs.DECODE_N
+    flop_gemv = 2.0 * K_dec * N_dec
+    bytes_gemv = 2.0 * K_dec * N_dec           # weight bytes per launch (the pages' GB/s)
+    bytes_gemv_all = 2.0 * (K_dec * N_dec + K_dec + N_dec)
+    flop_step = sum(flop_gemm.values()) + flop_gemv
+
+    def step(i, ev=None):
+        for n in SIZES:
+            A, B, C = ops[n]
+            if ev is not None and n == DOMINANT:
+                ev[0].record()
+                sdt.gemm_f16(A, B, C)
+                ev[1].record()
+            else:
+                sdt.gemm_f16(A, B, C)
+        if ev is not None:
+            ev[2].record()
+        sdt.gemm_f16(x2, Ws[i % inputs.DECODE_BUFFERS], y2)   # M=1 -> streaming GEMV
+        if ev is not None:
+            ev[3].record()
+
+    # ---- parity gate ----------------------------------------------------------
+    import oracle
+    step(0)
+    torch.cuda.synchronize()
+    gate = {}
+    for n in SIZES:
+        A, B = host[n]
+        C = ops[n][2].cpu().numpy().astype(np.float64)
+        rng = np.random.default_rng(n)
+        r = rng.integers(0, n, 2048)
+        c = rng.integers(0, n, 2048)
+        ref = oracle.gemm_sample(A, B, r, c)
+        bad = int((~(np.abs(C[r, c] - ref) <= oracle.tolerance(ref))).sum())
+        gate[f"gemm_{n}"] = bad
+    bad_dec = 0
+    for r in range(inputs.DECODE_BUFFERS):
+        sdt.gemm_f16(x2, Ws[r], y2)
+        torch.cuda.synchronize()
+        ref = oracle.gemv_m1(x_h, W_h[r])
+        got = y.cpu().numpy().astype(np.float64)
+        bad_dec += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+    gate["gemv_8_buffers"] = bad_dec
+    if any(gate.values()):
+        print(json.dumps({"metric": METRIC, "value": None, "error": "parity gate failed",
+                          "gate": gate}), flush=True)
+        sys.exit(1)
+    log(f"parity gate passed: {gate}")
+
+    # ---- warm-up and the timed region ---------------------------------------
+    t0 = time.time()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warm-up {args.warmup} steps in {time.time() - t0:.2f} s")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    dom_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    dom_avg_us = 1e3 * sum(dom_ms) / len(dom_ms)
+    dec_avg_us = 1e3 * sum(dec_ms) / len(dec_ms)
+    value = flop_step / (ms_per_step * 1e-3) / 1e12
+    achieved = flop_gemm[DOMINANT] / (dom_avg_us * 1e-6) / 1e12
+    log(f"step {ms_per_step:.3f} ms -> {value:.1f} TFLOP/s; {DOMINANT}^3 {dom_avg_us:.1f} us "
+        f"= {achieved:.1f} TFLOP/s; decode {dec_avg_us:.2f} us")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded uniform[-1,1] fp16 operands; N(0,0.02) fp16 decode weights)",
+        "config": {
+            "workload": ("square fp16 GEMM C=A.B (A row-major, B K-major, fp32 accumulate, "
+                         "fp16 out) at M=N=K in {256,512,768,1024,1536,2048,4096,8192}, then "
+                         "M=1 decode GEMV K=4096 N=12288 over 8 rotating weight buffers"),
+            "flop_per_step": flop_step,
+            "device": props.name,
+            "cus": props.multi_processor_count,
+            "tiles": {str(n): sdt.pick_tile(n, n, n, props.multi_processor_count)["id"]
+                      for n in SIZES},
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"gemm_f16_kernel at {DOMINANT}^3",
+            "achieved": round(achieved, 1),
+            "peak": round(PEAK_FP16_TFLOPS, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dom_avg_us, 2),
+        },
+        "decode": {
+            "avg_launch_us_in_step": round(dec_avg_us, 3),
+            "GBps_in_step": round(bytes_gemv / (dec_avg_us * 1e-6) / 1e9, 1),
+            "hbm_frac_in_step": round(bytes_gemv / (dec_avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        },
+        "gate": "pass",
+    }
+
+    if not args.no_detail:
+        result["detail"] = detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor,
+                                  flop_gemm, bytes_gemv, bytes_gemv_all)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+def _ranges(vals):
+    s = sorted(vals)
+    return {"min": round(s[0], 3), "median": round(s[len(s) // 2], 3), "max": round(s[-1], 3)}
+
+
+def time_launches(torch, fn, launches, repeats=10):
+    """Per-launch microseconds of `launches` back-to-back calls, `repeats` times."""
+    out = []
+    for _ in range(repeats):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for j in range(launches):
+            fn(j)
+        b.record()
+        b.synchronize()
+        out.append(1e3 * a.elapsed_time(b) / launches)
+    return out
+
+
+def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, bytes_gemv,
+           bytes_gemv_all):
+    det = {"square": {}, "k_sweep": {}, "decode_cold": {}}
+    for n, (A, B, C) in ops.items():
+        launches = 200 if n <= 2048 else (50 if n == 4096 else 20)
+        f = (lambda j, A=A, B=B, C=C: sdt.gemm_f16(A, B, C))
+        for j in range(max(20, launches)):
+            f(j)
+        us = time_launches(torch, f, launches)
+        med = sorted(us)[len(us) // 2]
+        det["square"][str(n)] = {
+            "us": _ranges(us),
+            "tflops_median": round(flop_gemm[n] / (med * 1e-6) / 1e12, 1),
+            "peak_frac_median": round(flop_gemm[n] / (med * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "tile": sdt.pick_tile(n, n, n, 0)["id"],
+        }
+        log(f"square {n}: median {med:.2f} us {det['square'][str(n)]['tflops_median']} TFLOP/s")
+    # K sweep at M=N=2048: automatic arm, plus the stagger-off arm at K=2048
+    for K in inputs.K_SWEEP_K:
+        A, B = inputs.square_operands(inputs.K_SWEEP_MN, 3, k=K)
+        dA, dB = dev_tensor(A), dev_tensor(B)
+        C = torch.empty((2048, 2048), dtype=torch.float16, device=dev)
+        arms = {"auto": (-1, -1)}
+        if K == 2048:
+            arms["stagger_off"] = (-1, 0)
+        for name, (tile, st) in arms.items():
+            f = (lambda j, tile=tile, st=st: sdt.gemm_f16_ex(dA, dB, C, tile_id=tile, stagger=st))
+            for j in range(50):
+                f(j)
+            us = time_launches(torch, f, 200)
+            med = sorted(us)[len(us) // 2]
+            det["k_sweep"][f"{K}_{name}"] = {
+                "us": _ranges(us),
+                "tflops_median": round(2.0 * 2048 * 2048 * K / (med * 1e-6) / 1e12, 1),
+                "stagger": bool(sdt.stagger_auto(K)) if st == -1 else bool(st),
+            }
+    # Cold-cache decode: 8 rotating 100.7 MB weight buffers (805 MB >> 256 MB
+    # Infinity Cache), ~1 s warm-up, 200 launches x 10 repeats.
+    x2, y2 = x.view(1, -1), y.view(1, -1)
+    g = (lambda j: sdt.gemm_f16(x2, Ws[j % len(Ws)], y2))
+    t0 = time.time()
+    j = 0
+    while time.time() - t0 < 1.0:
+        g(j)
+        j += 1
+        if j % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    us = time_launches(torch, g, 200)
+    med = sorted(us)[len(us) // 2]
+    det["decode_cold"] = {
+        "us": _ranges(us),
+        "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
+        "GBps_all_median": round(bytes_gemv_all / (med * 1e-6) / 1e9, 1),
+        "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "protocol": "8 rotating buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
+    }
+    log(f"decode cold: median {med:.2f} us = {det['decode_cold']['GBps_weights_median']} GB/s")
+    return det
+
+
+def cpu_baseline(oracle, AB, target_s):
+    """The oracle, untuned, on a bounded sample of the dominant product: whole
+    output rows of the 8192^3 GEMM, as many as take about target_s seconds."""
+    import numpy as np
+    A, B = AB
+    n = A.shape[0]
+    threads = oracle.max_threads()
+    t = time.time()
+    oracle.gemm(A[:4], B)
+    per_row = max((time.time() - t) / 4, 1e-6)
+    rows = int(min(n, max(4, target_s / per_row)))
+    t = time.time()
+    oracle.gemm(A[:rows], B)
+    dt = time.time() - t
+    flop = 2.0 * rows * n * n
+    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{rows} full output rows of the {n}^3 product ({flop:.3g} FLOP) in "
+                      f"{dt:.2f} s, fp64 accumulation, {threads} OpenMP threads"}
+
+
+if __name__ == "__main__":
+    main()

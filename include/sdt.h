@@ -1,0 +1,154 @@
+/*
+ * sdt.h -- C ABI of the MI355X (gfx950) fp16 GEMM and M=1 decode GEMV.
+ *
+ * The operation is the fp16 matrix product of "Beating hipBLASLt on a Gaming
+ * GPU" (section "The result": square fp16 GEMM) and of the mojo-baro project
+ * page (section "Four rounds on the decode shape": the M=1, K=4096, N=12288
+ * skinny product whose weights stream from HBM), in the transposed-B form
+ * C = A @ B_T.T benchmarked by the FlyDSL pull request "Speed up the RDNA3
+ * GEMM up to 1.85x by choosing the tile from the shape" (Performance).
+ *
+ * Layouts (all strides in elements, taken from the caller, never assumed
+ * tight -- FlyDSL PR, Changes: caller-supplied lda/ldb/ldc):
+ *   A(m,k) = A[m*lda + k]   (M x K, row-major)
+ *   B(k,n) = B[n*ldb + k]   ("K-major": K contiguous, N rows of length ldb)
+ *   C(m,n) = C[m*ldc + n]   (M x N, row-major)
+ * Elements are IEEE binary16 bit patterns.  Products are accumulated in fp32
+ * and the result is rounded to fp16 with round-to-nearest-even (overflow to
+ * +-inf).  C is overwritten (no alpha/beta).
+ *
+ * Ownership and execution: every pointer is a device pointer owned by the
+ * caller and must stay valid until the enqueued work completes; C must not
+ * alias A or B.  Calls enqueue on `stream` (a hipStream_t passed as void*;
+ * NULL is the default stream) of the calling thread's current HIP device and
+ * return without synchronising.  The library allocates no memory per call,
+ * never prints, aborts or exits, and is safe to call from several threads.
+ *
+ * Errors: every call returns an sdt_status.  On any error nothing is
+ * enqueued.  SDT_ERR_HIP keeps the HIP error code for sdt_last_hip_error().
+ */
+#ifndef SDT_H
+#define SDT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sdt_status {
+    SDT_OK = 0,
+    SDT_ERR_INVALID_ARG = 1,  /* negative size, null pointer with work to do,
+                                 leading dimension smaller than the row */
+    SDT_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels handle:
+                                 misaligned pointer or stride, size limits */
+    SDT_ERR_HIP = 3           /* the HIP runtime refused the launch */
+} sdt_status;
+
+/* One rung of the tile ladder: a compile-time instantiation of the GEMM
+ * kernel (bm x bn output block per workgroup, bk = k-tile depth, waves_m x
+ * waves_n wavefronts of 64 lanes), after "Beating hipBLASLt on a Gaming GPU",
+ * section "The part that actually mattered" (tile shape as a compile-time
+ * kernel parameter, each with its own warp layout). */
+typedef struct sdt_tile {
+    int id;          /* index in the ladder, 0 = largest tile */
+    int bm, bn, bk;
+    int waves_m, waves_n;
+    int threads;     /* 64 * waves_m * waves_n */
+    int lds_bytes;   /* two LDS stages of (bm + bn) x bk fp16 */
+} sdt_tile;
+
+/* ---- main entry points ---------------------------------------------------- */
+
+/* C = A.B for M x N x K.
+ * Requirements: M, N, K >= 0; lda >= K, ldb >= K, ldc >= N (else
+ * SDT_ERR_INVALID_ARG); A, B, C 16-byte aligned and lda, ldb, ldc multiples of
+ * 8 elements, lda and ldb below 2^22 (else SDT_ERR_UNSUPPORTED).  Any M, N, K
+ * within those limits is computed exactly as defined (ragged edges are
+ * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
+ * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
+ * definition).  The tile is chosen by sdt_pick_tile from the device's CU
+ * count; the k-tile stagger is enabled exactly when the k-tile count is a
+ * power of two (FlyDSL PR, Changes: stagger). */
+int gemm_f16(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda,
+             const void* B, int64_t ldb,
+             void* C, int64_t ldc, void* stream);
+
+/* y(n) = sum_k x(k) * B(k,n), n < N: the M=1 decode product (mojo-baro page,
+ * "Four rounds on the decode shape"), with B stored K-major as above (column n
+ * of the math B is the contiguous run B[n*ldb .. n*ldb+K-1]); x holds K fp16
+ * values, y receives N fp16 values.  Requirements as for gemm_f16 with M = 1
+ * (x, B 16-byte aligned, ldb % 8 == 0).  N == 0 is a no-op, K == 0 writes
+ * zeros. */
+int gemv_f16_m1(int64_t N, int64_t K, const void* x,
+                const void* B, int64_t ldb, void* y, void* stream);
+
+/* ---- test / benchmark extras ---------------------------------------------- */
+
+/* gemm_f16 with the launcher's choices forced.  tile_id: -1 = automatic,
+ * else a ladder index (SDT_ERR_INVALID_ARG if out of range).  stagger: -1 =
+ * automatic (on iff the k-tile count is a power of two), 0 = off, 1 = on
+ * (SDT_ERR_UNSUPPORTED when the k-tile count is not a power of two, since the
+ * wrap-around is a mask).  M == 1 is not rerouted to the GEMV here. */
+int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda,
+                const void* B, int64_t ldb,
+                void* C, int64_t ldc, void* stream,
+                int tile_id, int stagger);
+
+/* gemv_f16_m1 with the kernel instantiation forced: variant in
+ * [0, sdt_gemv_num_variants()) selects how many output columns one wave
+ * streams (variant 0 is what gemv_f16_m1 uses).  Same result definition. */
+int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x,
+                   const void* B, int64_t ldb, void* y, void* stream,
+                   int variant);
+int sdt_gemv_num_variants(void);
+
+/* Host-only: the tile the launcher would use for an M x N x K product on a
+ * device with num_cu compute units (num_cu <= 0 reads the current device).
+ * The rule compares the number of output blocks the grid produces with the
+ * CU count ("Beating hipBLASLt on a Gaming GPU", "The part that actually
+ * mattered"; ladder constants fitted on MI355X).  Touches no device when
+ * num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
+int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
+
+/* Host-only, the mechanism of the rule above: given `rungs` thresholds in
+ * units of ref_bm x ref_bn output blocks (largest tile first, non-increasing),
+ * returns the first rung r with ceil(M/ref_bm)*ceil(N/ref_bn) >=
+ * min_blocks[r], or rungs-1 if none qualifies; -1 on invalid input. */
+int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
+                  int rungs, const int64_t* min_blocks);
+
+/* Host-only: number of ladder rungs, and the description of rung tile_id. */
+int sdt_num_tiles(void);
+int sdt_tile_info(int tile_id, sdt_tile* out);
+
+/* Host-only: 1 if the k-loop stagger is used for K with k-tile depth bk
+ * (the k-tile count ceil(K/bk) is a power of two), else 0. */
+int sdt_stagger_auto(int64_t K, int bk);
+
+/* Host-only: the k-tile visited at step i by workgroup wg when staggered:
+ * (wg + i) & (nkt - 1); nkt must be a power of two (else -1). */
+int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt);
+
+/* Host-only argument check used by gemm_f16 before anything is enqueued.
+ * Returns the status gemm_f16 would return for these arguments (SDT_OK when
+ * the call would be launched). */
+int sdt_check_gemm_args(int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda,
+                        const void* B, int64_t ldb,
+                        const void* C, int64_t ldc);
+
+/* Human-readable name of a status code (static storage). */
+const char* sdt_status_string(int status);
+
+/* The hipError_t value recorded by the last SDT_ERR_HIP on this thread
+ * (0 if none). */
+int sdt_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDT_H */

@@ -1,0 +1,215 @@
+"""Thin ctypes binding over ``libsdt.so`` (C ABI in ``include/sdt.h``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of the library.  Tensors are torch tensors on a ROCm device, used for
+device memory and streams; the library is handed raw pointers, strides in
+elements, and the current stream.  A missing library raises immediately: there
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsdt.so")
+
+SDT_OK = 0
+SDT_ERR_INVALID_ARG = 1
+SDT_ERR_UNSUPPORTED = 2
+SDT_ERR_HIP = 3
+
+# Every function include/sdt.h declares.
+EXPORTS = (
+    "gemm_f16", "gemv_f16_m1", "gemm_f16_ex", "gemv_f16_m1_ex", "sdt_gemv_num_variants",
+    "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
+    "sdt_stagger_auto", "sdt_stagger_ktile", "sdt_check_gemm_args",
+    "sdt_status_string", "sdt_last_hip_error",
+)
+
+
+class SdtTile(ctypes.Structure):
+    _fields_ = [("id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
+                ("bk", ctypes.c_int), ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
+                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+
+    def as_dict(self) -> dict:
+        return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class SdtError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = status_string(status)
+        if status == SDT_ERR_HIP:
+            msg += f" (hipError {last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+
+
+_lib = None
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+_int = ctypes.c_int
+
+
+def lib():
+    """Load libsdt.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m shape_driven_tile_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    L.gemm_f16.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+    L.gemm_f16_ex.argtypes = L.gemm_f16.argtypes + [_int, _int]
+    L.gemv_f16_m1.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp, _vp]
+    L.gemv_f16_m1_ex.argtypes = L.gemv_f16_m1.argtypes + [_int]
+    L.sdt_gemv_num_variants.argtypes = []
+    L.sdt_pick_tile.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(SdtTile)]
+    L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
+    L.sdt_num_tiles.argtypes = []
+    L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
+    L.sdt_stagger_auto.argtypes = [_i64, _int]
+    L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
+    L.sdt_stagger_ktile.restype = _i64
+    L.sdt_check_gemm_args.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
+    L.sdt_status_string.argtypes = [_int]
+    L.sdt_status_string.restype = ctypes.c_char_p
+    L.sdt_last_hip_error.argtypes = []
+    for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
+                 "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
+                 "sdt_tile_info", "sdt_stagger_auto", "sdt_check_gemm_args",
+                 "sdt_last_hip_error"):
+        getattr(L, name).restype = _int
+    _lib = L
+    return L
+
+
+# ---- host-only helpers ------------------------------------------------------
+
+def status_string(status: int) -> str:
+    return lib().sdt_status_string(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return int(lib().sdt_last_hip_error())
+
+
+def num_tiles() -> int:
+    return int(lib().sdt_num_tiles())
+
+
+def tile_info(tile_id: int) -> dict:
+    t = SdtTile()
+    rc = lib().sdt_tile_info(int(tile_id), ctypes.byref(t))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_tile_info")
+    return t.as_dict()
+
+
+def pick_tile(M: int, N: int, K: int, num_cu: int) -> dict:
+    t = SdtTile()
+    rc = lib().sdt_pick_tile(int(M), int(N), int(K), int(num_cu), ctypes.byref(t))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_pick_tile")
+    return t.as_dict()
+
+
+def pick_rung(M: int, N: int, ref_bm: int, ref_bn: int, min_blocks) -> int:
+    arr = (_i64 * len(min_blocks))(*[int(v) for v in min_blocks])
+    return int(lib().sdt_pick_rung(int(M), int(N), int(ref_bm), int(ref_bn), len(min_blocks), arr))
+
+
+def stagger_auto(K: int, bk: int = 64) -> bool:
+    return bool(lib().sdt_stagger_auto(int(K), int(bk)))
+
+
+def stagger_ktile(wg: int, i: int, nkt: int) -> int:
+    return int(lib().sdt_stagger_ktile(int(wg), int(i), int(nkt)))
+
+
+def check_gemm_args(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc) -> int:
+    return int(lib().sdt_check_gemm_args(int(M), int(N), int(K), A_ptr, int(lda), B_ptr,
+                                         int(ldb), C_ptr, int(ldc)))
+
+
+def gemv_num_variants() -> int:
+    return int(lib().sdt_gemv_num_variants())
+
+
+# ---- compute entry points (torch tensors on a ROCm device) -------------------
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _rows(t, name):
+    import torch
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with unit stride along its rows")
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1]))
+
+
+def gemm_f16(A, B, C, stream=None) -> None:
+    """C[M, N] = A[M, K] . B[N, K]^T (B stored K-major), fp32 accumulate, fp16 out."""
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    pa, lda = _rows(A, "A")
+    pb, ldb = _rows(B, "B")
+    pc, ldc = _rows(C, "C")
+    rc = lib().gemm_f16(M, N, K, pa, lda, pb, ldb, pc, ldc, _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "gemm_f16")
+
+
+def gemm_f16_ex(A, B, C, tile_id: int = -1, stagger: int = -1, stream=None) -> None:
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    pa, lda = _rows(A, "A")
+    pb, ldb = _rows(B, "B")
+    pc, ldc = _rows(C, "C")
+    rc = lib().gemm_f16_ex(M, N, K, pa, lda, pb, ldb, pc, ldc, _stream_handle(stream),
+                           int(tile_id), int(stagger))
+    if rc != SDT_OK:
+        raise SdtError(rc, "gemm_f16_ex")
+
+
+def gemv_f16_m1(x, B, y, stream=None, variant: int | None = None) -> None:
+    """y[N] = x[K] . B[N, K]^T for the M=1 decode shape (B stored K-major)."""
+    import torch
+    if x.dtype != torch.float16 or y.dtype != torch.float16:
+        raise TypeError("x and y must be float16")
+    if x.dim() != 1 or y.dim() != 1 or x.stride(0) != 1 or y.stride(0) != 1:
+        raise ValueError("x and y must be contiguous vectors")
+    N, K = B.shape
+    if x.shape[0] != K or y.shape[0] != N:
+        raise ValueError(f"shape mismatch x{tuple(x.shape)} B{tuple(B.shape)} y{tuple(y.shape)}")
+    pb, ldb = _rows(B, "B")
+    h = _stream_handle(stream)
+    if variant is None:
+        rc = lib().gemv_f16_m1(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h)
+    else:
+        rc = lib().gemv_f16_m1_ex(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h, int(variant))
+    if rc != SDT_OK:
+        raise SdtError(rc, "gemv_f16_m1")
+
+
+def gemm_f16_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream_ptr=None) -> int:
+    """The C call with raw integers/pointers; returns the status."""
+    return int(lib().gemm_f16(int(M), int(N), int(K), A_ptr, int(lda), B_ptr, int(ldb),
+                              C_ptr, int(ldc), stream_ptr))
+
+
+def gemv_f16_m1_raw(N, K, x_ptr, B_ptr, ldb, y_ptr, stream_ptr=None) -> int:
+    return int(lib().gemv_f16_m1(int(N), int(K), x_ptr, B_ptr, int(ldb), y_ptr, stream_ptr))

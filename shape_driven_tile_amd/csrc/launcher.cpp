@@ -1,0 +1,122 @@
+// Host-side launch decisions (see launcher.hpp).  No HIP dependency.
+#include "launcher.hpp"
+
+#include <cstdint>
+
+namespace sdt {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+sdt_tile describe(int id) {
+    const TileDesc& d = kLadder[id];
+    sdt_tile t;
+    t.id = id;
+    t.bm = d.bm;
+    t.bn = d.bn;
+    t.bk = kBK;
+    t.waves_m = d.waves_m;
+    t.waves_n = d.waves_n;
+    t.threads = 64 * d.waves_m * d.waves_n;
+    t.lds_bytes = 2 * (d.bm + d.bn) * kBK * 2;
+    return t;
+}
+
+// "Beating hipBLASLt on a Gaming GPU", section "The part that actually
+// mattered": count how many reference-sized output blocks the grid produces
+// (ceil division on both sides) and take the first rung whose threshold that
+// count reaches; the last rung is the fallback.
+int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
+              const int64_t* min_blocks) {
+    if (M < 0 || N < 0 || ref_bm <= 0 || ref_bn <= 0 || rungs <= 0 || !min_blocks)
+        return -1;
+    const int64_t blocks = ceil_div(M, ref_bm) * ceil_div(N, ref_bn);
+    for (int r = 0; r < rungs; ++r)
+        if (blocks >= min_blocks[r]) return r;
+    return rungs - 1;
+}
+
+// MI355X rule.  Blocks are counted in units of the smallest rung (64x64), so
+// a rung of area a*64*64 produces blocks/a workgroups on a shape its tile
+// divides.  A rung qualifies when it still hands every CU at least
+// kFill[r] workgroups' worth of 64x64 blocks scaled by its area: the largest
+// tile that still fills the machine wins, as in the pages' ladder.
+int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
+    if (num_cu <= 0) num_cu = 256;
+    int64_t thresholds[kNumTiles];
+    for (int r = 0; r < kNumTiles; ++r) {
+        const int64_t area = int64_t(kLadder[r].bm / 64) * (kLadder[r].bn / 64);
+        thresholds[r] = area * num_cu;
+    }
+    thresholds[kNumTiles - 1] = 0;
+    return pick_rung(M, N, 64, 64, kNumTiles, thresholds);
+}
+
+static bool aligned16(const void* p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, const void* C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return SDT_ERR_INVALID_ARG;
+    if (lda < K || ldb < K || ldc < N) return SDT_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return SDT_OK;  // nothing to compute or write
+    if (!C) return SDT_ERR_INVALID_ARG;
+    if (K > 0 && (!A || !B)) return SDT_ERR_INVALID_ARG;
+    // 16-byte vector loads and stores: aligned rows.  A stride only matters
+    // when there is more than one row to step over.
+    if (!aligned16(C) || (M > 1 && ldc % 8 != 0)) return SDT_ERR_UNSUPPORTED;
+    if (K > 0) {
+        if (!aligned16(A) || !aligned16(B)) return SDT_ERR_UNSUPPORTED;
+        if ((M > 1 && lda % 8 != 0) || (N > 1 && ldb % 8 != 0)) return SDT_ERR_UNSUPPORTED;
+        if (lda > kMaxLd || ldb > kMaxLd) return SDT_ERR_UNSUPPORTED;
+    }
+    return SDT_OK;
+}
+
+}  // namespace sdt
+
+// ---- host-only C ABI --------------------------------------------------------
+
+extern "C" int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
+                             const int64_t* min_blocks) {
+    return sdt::pick_rung(M, N, ref_bm, ref_bn, rungs, min_blocks);
+}
+
+extern "C" int sdt_num_tiles(void) { return sdt::kNumTiles; }
+
+extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
+    if (tile_id < 0 || tile_id >= sdt::kNumTiles || !out) return SDT_ERR_INVALID_ARG;
+    *out = sdt::describe(tile_id);
+    return SDT_OK;
+}
+
+extern "C" int sdt_stagger_auto(int64_t K, int bk) {
+    if (K <= 0 || bk <= 0) return 0;
+    return sdt::is_pow2(sdt::ceil_div(K, bk)) ? 1 : 0;
+}
+
+// FlyDSL PR, Changes: each workgroup starts at its own k-tile and wraps with
+// a mask, one add and one and per trip.
+extern "C" int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt) {
+    if (!sdt::is_pow2(nkt) || wg < 0 || i < 0) return -1;
+    return (wg + i) & (nkt - 1);
+}
+
+extern "C" int sdt_check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A,
+                                   int64_t lda, const void* B, int64_t ldb,
+                                   const void* C, int64_t ldc) {
+    return sdt::check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
+}
+
+extern "C" const char* sdt_status_string(int status) {
+    switch (status) {
+        case SDT_OK: return "SDT_OK";
+        case SDT_ERR_INVALID_ARG: return "SDT_ERR_INVALID_ARG: invalid argument";
+        case SDT_ERR_UNSUPPORTED:
+            return "SDT_ERR_UNSUPPORTED: misaligned pointer/stride or size limit";
+        case SDT_ERR_HIP: return "SDT_ERR_HIP: HIP runtime error (see sdt_last_hip_error)";
+        default: return "unknown sdt status";
+    }
+}

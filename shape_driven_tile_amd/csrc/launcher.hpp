@@ -1,0 +1,44 @@
+// Host-side launch decisions for the fp16 GEMM: the tile ladder, pick_tile,
+// the k-loop stagger rule and argument validation.  Pure C++ (no HIP headers)
+// so that every decision can be tested on a machine without a GPU.
+#pragma once
+
+#include <cstdint>
+
+#include "sdt.h"
+
+namespace sdt {
+
+// k-tile depth shared by every rung: 64 fp16 = one 128-byte row segment.
+constexpr int kBK = 64;
+
+// A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
+// each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
+struct TileDesc {
+    int bm, bn, waves_m, waves_n;
+};
+
+// Largest tile first.  The indices are the ABI's tile ids.
+constexpr TileDesc kLadder[] = {
+    {256, 256, 2, 4},  // 8 waves, 128x64 per wave
+    {256, 128, 2, 2},  // 4 waves, 128x64 per wave
+    {128, 128, 2, 2},  // 4 waves, 64x64 per wave
+    {128, 64, 2, 2},   // 4 waves, 64x32 per wave
+    {64, 64, 2, 2},    // 4 waves, 32x32 per wave
+};
+constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
+
+// Largest leading dimension accepted: a workgroup addresses its operand rows
+// through one buffer descriptor with 32-bit byte offsets below 2^31.
+constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
+
+sdt_tile describe(int id);
+int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
+              const int64_t* min_blocks);
+int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);
+bool is_pow2(int64_t v);
+int64_t ceil_div(int64_t a, int64_t b);
+int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                    const void* B, int64_t ldb, const void* C, int64_t ldc);
+
+}  // namespace sdt

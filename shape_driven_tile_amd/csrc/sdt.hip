@@ -1,0 +1,220 @@
+// C ABI of the MI355X fp16 GEMM / M=1 GEMV library (declared in sdt.h).
+// Validates arguments on the host, picks the kernel instantiation and
+// enqueues it on the caller's stream.  Allocates nothing.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+#include <mutex>
+
+#include "gemm_kernel.hpp"
+#include "gemv_kernel.hpp"
+#include "launcher.hpp"
+#include "sdt.h"
+
+namespace sdt {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+struct DeviceInfo {
+    int num_cu = 0;
+    int nxcd = 1;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[kMaxDevices];
+
+int fail_hip(hipError_t e) {
+    g_last_hip_error = (int)e;
+    return SDT_ERR_HIP;
+}
+
+// CU count of the current device, read once per device.  MI355X deals
+// workgroups round-robin over its XCDs of 32 CUs each (8 in the single-
+// partition mode); a partition with fewer CUs has proportionally fewer XCDs.
+int device_info(DeviceInfo* out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) return SDT_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (g_dev[dev].num_cu <= 0) {
+        int cu = 0;
+        e = hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail_hip(e);
+        if (cu <= 0) return SDT_ERR_UNSUPPORTED;
+        int nxcd = (cu % 32 == 0) ? cu / 32 : 1;
+        if (nxcd > 8) nxcd = 8;
+        g_dev[dev].num_cu = cu;
+        g_dev[dev].nxcd = nxcd < 1 ? 1 : nxcd;
+    }
+    *out = g_dev[dev];
+    return SDT_OK;
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_f16_kernel<BM, BN, WM, WN>),
+                           dim3(p.gm * p.gn), dim3(WM * WN * 64), args, 0, stream);
+}
+
+template <int I>
+hipError_t launch_rung(GemmParams p, hipStream_t s) {
+    return launch_gemm_tile<kLadder[I].bm, kLadder[I].bn, kLadder[I].waves_m,
+                            kLadder[I].waves_n>(p, s);
+}
+
+hipError_t launch_gemm(int id, GemmParams p, hipStream_t s) {
+    static_assert(kNumTiles == 5, "dispatch table below lists every rung");
+    switch (id) {
+        case 0: return launch_rung<0>(p, s);
+        case 1: return launch_rung<1>(p, s);
+        case 2: return launch_rung<2>(p, s);
+        case 3: return launch_rung<3>(p, s);
+        default: return launch_rung<4>(p, s);
+    }
+}
+
+int fill_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream) {
+    const int64_t total = M * N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    int Mi = (int)M, Ni = (int)N;
+    void* args[] = {&C, &ldc, &Mi, &Ni};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fill_zero_kernel),
+                                   dim3((unsigned)blocks), dim3(256), args, 0, stream);
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
+}
+
+// GEMV instantiations: rows per wave; the activations are held as 8 chunks
+// of 8 fp16 per lane (4096 k per pass).
+constexpr int kGemvRpw[] = {4, 1, 2, 8};
+constexpr int kGemvVariants = sizeof(kGemvRpw) / sizeof(kGemvRpw[0]);
+
+template <int RPW>
+hipError_t launch_gemv_rpw(GemvParams p, hipStream_t stream) {
+    const int64_t waves = (p.N + RPW - 1) / RPW;
+    const int64_t blocks = (waves + 3) / 4;
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_f16_m1_kernel<RPW, 8>),
+                           dim3((unsigned)blocks), dim3(256), args, 0, stream);
+}
+
+int launch_gemv(int variant, int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                void* y, hipStream_t stream) {
+    if (N > INT_MAX) return SDT_ERR_UNSUPPORTED;
+    if (K == 0) return fill_zero(static_cast<uint16_t*>(y), N, 1, N, stream);
+    GemvParams p;
+    p.x = static_cast<const uint16_t*>(x);
+    p.B = static_cast<const uint16_t*>(B);
+    p.y = static_cast<uint16_t*>(y);
+    p.ldb = ldb;
+    p.N = (int)N;
+    p.K = (int)K;
+    hipError_t e;
+    switch (kGemvRpw[variant]) {
+        case 1: e = launch_gemv_rpw<1>(p, stream); break;
+        case 2: e = launch_gemv_rpw<2>(p, stream); break;
+        case 8: e = launch_gemv_rpw<8>(p, stream); break;
+        default: e = launch_gemv_rpw<4>(p, stream); break;
+    }
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
+}
+
+int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
+              int64_t ldb, void* C, int64_t ldc, void* stream, int tile_id, int stagger,
+              bool route_m1) {
+    int st = check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SDT_OK) return st;
+    if (tile_id < -1 || tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
+    if (stagger < -1 || stagger > 1) return SDT_ERR_INVALID_ARG;
+    if (M == 0 || N == 0) return SDT_OK;
+    if (M > INT_MAX || N > INT_MAX) return SDT_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (K == 0) return fill_zero(static_cast<uint16_t*>(C), ldc, M, N, s);
+    if (route_m1 && M == 1) return launch_gemv(0, N, K, A, B, ldb, C, s);
+
+    DeviceInfo dev;
+    st = device_info(&dev);
+    if (st != SDT_OK) return st;
+
+    const int id = tile_id >= 0 ? tile_id : pick_tile(M, N, K, dev.num_cu);
+    const TileDesc& td = kLadder[id];
+    const int64_t nkt = ceil_div(K, kBK);
+    int use_stagger = is_pow2(nkt) ? 1 : 0;
+    if (stagger == 0) use_stagger = 0;
+    if (stagger == 1) {
+        if (!is_pow2(nkt)) return SDT_ERR_UNSUPPORTED;
+        use_stagger = 1;
+    }
+    const int64_t gm = ceil_div(M, td.bm);
+    const int64_t gn = ceil_div(N, td.bn);
+    if (gm * gn > INT_MAX) return SDT_ERR_UNSUPPORTED;
+
+    GemmParams p;
+    p.A = static_cast<const uint16_t*>(A);
+    p.B = static_cast<const uint16_t*>(B);
+    p.C = static_cast<uint16_t*>(C);
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.gm = (int)gm;
+    p.gn = (int)gn;
+    p.nkt = (int)nkt;
+    p.stagger = use_stagger;
+    p.nxcd = dev.nxcd;
+    hipError_t e = launch_gemm(id, p, s);
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
+}
+
+}  // namespace
+}  // namespace sdt
+
+extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    return sdt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
+}
+
+extern "C" int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                           const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                           int tile_id, int stagger) {
+    return sdt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger, false);
+}
+
+extern "C" int gemv_f16_m1(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                           void* y, void* stream) {
+    int st = sdt::check_gemm_args(1, N, K, x, K, B, ldb, y, N);
+    if (st != SDT_OK) return st;
+    if (N == 0) return SDT_OK;
+    return sdt::launch_gemv(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                              void* y, void* stream, int variant) {
+    if (variant < 0 || variant >= sdt::kGemvVariants) return SDT_ERR_INVALID_ARG;
+    int st = sdt::check_gemm_args(1, N, K, x, K, B, ldb, y, N);
+    if (st != SDT_OK) return st;
+    if (N == 0) return SDT_OK;
+    return sdt::launch_gemv(variant, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int sdt_gemv_num_variants(void) { return sdt::kGemvVariants; }
+
+extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out) {
+    if (M < 0 || N < 0 || K < 0 || !out) return SDT_ERR_INVALID_ARG;
+    if (num_cu <= 0) {
+        sdt::DeviceInfo dev;
+        int st = sdt::device_info(&dev);
+        if (st != SDT_OK) return st;
+        num_cu = dev.num_cu;
+    }
+    *out = sdt::describe(sdt::pick_tile(M, N, K, num_cu));
+    return SDT_OK;
+}
+
+extern "C" int sdt_last_hip_error(void) { return sdt::g_last_hip_error; }

@@ -1,0 +1,94 @@
+"""Shared helpers for the GPU parity tests: move seeded host operands to the
+device, run the library through its C ABI, and compare with the CPU oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+import oracle
+
+DEV = "cuda:0"
+
+
+def say(msg: str) -> None:
+    """Name the case before any GPU step, so a failed run points at it."""
+    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+
+
+def to_dev(a: np.ndarray):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None):
+    """A: (M, lda) float16, B: (N, ldb) float16 host buffers (K-contiguous rows).
+    Returns the (M, N) float16 result and whether the C padding was untouched."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    M, lda = A.shape
+    N, ldb = B.shape
+    K = lda if K is None else K
+    dA = to_dev(A)[:, :K]
+    dB = to_dev(B)[:, :K]
+    # ldc: N plus ldc_pad, rounded up to the 8-element multiple the ABI needs
+    # for more than one row
+    ldc = N + ldc_pad if M == 1 else -(-(N + ldc_pad) // 8) * 8
+    full = torch.full((M, ldc), float("nan"), dtype=torch.float16, device=DEV)
+    dC = full[:, :N]
+    if tile is None and stagger == -1:
+        sdt.gemm_f16(dA, dB, dC, stream=stream)
+    else:
+        sdt.gemm_f16_ex(dA, dB, dC, tile_id=-1 if tile is None else tile, stagger=stagger,
+                        stream=stream)
+    torch.cuda.synchronize()
+    pad_ok = bool(torch.isnan(full[:, N:]).all().item()) if ldc > N else True
+    return dC.cpu().numpy(), pad_ok
+
+
+def run_gemv(x, W, K=None, variant=None):
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    N, ldb = W.shape
+    K = x.shape[0] if K is None else K
+    dx = to_dev(x[:K])
+    dW = to_dev(W)[:, :K]
+    dy = torch.full((N,), float("nan"), dtype=torch.float16, device=DEV)
+    sdt.gemv_f16_m1(dx, dW, dy, variant=variant)
+    torch.cuda.synchronize()
+    return dy.cpu().numpy()
+
+
+def tol_report(gpu16: np.ndarray, ref: np.ndarray) -> tuple[bool, str]:
+    """The acceptance bound |C_gpu - C_ref| <= 1e-2 + 2e-3 |C_ref| per element
+    (NaN or inf where the reference is finite fails)."""
+    g = gpu16.astype(np.float64)
+    tol = oracle.tolerance(ref)
+    err = np.abs(g - ref)
+    ok = err <= tol
+    bad = int((~ok).sum())
+    worst = float(np.nanmax(np.where(np.isfinite(err), err / tol, np.inf))) if err.size else 0.0
+    return bad == 0, f"{bad} of {g.size} outside tolerance, worst |d|/tol = {worst:.3g}"
+
+
+def assert_close(gpu16, ref):
+    ok, msg = tol_report(gpu16, ref)
+    assert ok, msg
+
+
+def assert_bitexact(gpu16, ref):
+    want = oracle.f16_encode_rne(ref)
+    got = np.ascontiguousarray(gpu16).view(np.uint16)
+    diff = got != want
+    assert not diff.any(), f"{int(diff.sum())} of {got.size} differ from the RNE oracle"
+
+
+def sample_positions(M, N, rows=32, cols=32, extra=4096, seed=0):
+    """Whole rows and columns (first, last, tile seams, random) plus random
+    elements, as (row, col) index arrays."""
+    rng = np.random.default_rng(seed)
+    rs = sorted(set([0, 1, M // 2, M - 1] + list(rng.integers(0, M, rows))))
+    cs = sorted(set([0, 1, N // 2, N - 1] + list(rng.integers(0, N, cols))))
+    r = [np.full(N, i) for i in rs] + [np.arange(M) for _ in cs] + [rng.integers(0, M, extra)]
+    c = [np.arange(N) for _ in rs] + [np.full(M, j) for j in cs] + [rng.integers(0, N, extra)]
+    return np.concatenate(r).astype(np.int64), np.concatenate(c).astype(np.int64)

@@ -1,0 +1,203 @@
+"""Host-side tests of the C ABI (no GPU): the library loads and exports every
+declared symbol, argument validation, the tile ladder and pick_tile, and the
+k-loop stagger arithmetic.  No compute call reaches a device here: every
+gemm_f16 call below is rejected (or is a no-op) before the HIP runtime is
+touched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from shape_driven_tile_amd import binding as sdt
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sdt.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden", "gfx1100_tile_ladder.tsv")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert "gemm_f16" in names and "gemv_f16_m1" in names
+    assert sorted(sdt.EXPORTS) == names
+
+
+def test_library_exports_every_declared_symbol():
+    L = ctypes.CDLL(sdt.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(L, name), f"libsdt.so does not export {name}"
+
+
+def test_status_strings():
+    for code in (0, 1, 2, 3):
+        assert sdt.status_string(code).startswith(["SDT_OK", "SDT_ERR_INVALID_ARG",
+                                                   "SDT_ERR_UNSUPPORTED", "SDT_ERR_HIP"][code])
+    assert "unknown" in sdt.status_string(99)
+    assert sdt.last_hip_error() == 0
+
+
+# ---- argument validation ------------------------------------------------------
+
+A16 = 0x10000   # fake, 16-byte aligned addresses: never dereferenced here
+B16 = 0x20000
+C16 = 0x30000
+
+
+@pytest.mark.parametrize("args,want", [
+    ((64, 64, 64, A16, 64, B16, 64, C16, 64), sdt.SDT_OK),
+    ((-1, 64, 64, A16, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, -1, 64, A16, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, -1, A16, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, 64, A16, 56, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),   # lda < K
+    ((64, 64, 64, A16, 64, B16, 56, C16, 64), sdt.SDT_ERR_INVALID_ARG),   # ldb < K
+    ((64, 64, 64, A16, 64, B16, 64, C16, 56), sdt.SDT_ERR_INVALID_ARG),   # ldc < N
+    ((64, 64, 64, None, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, 64, A16, 64, None, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, 64, A16, 64, B16, 64, None, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((0, 64, 64, None, 64, None, 64, None, 64), sdt.SDT_OK),             # empty: no-op
+    ((64, 0, 64, None, 64, None, 64, None, 0), sdt.SDT_OK),
+    ((64, 64, 0, None, 0, None, 0, C16, 64), sdt.SDT_OK),                # K = 0: zeros
+    ((64, 64, 64, A16 + 8, 64, B16, 64, C16, 64), sdt.SDT_ERR_UNSUPPORTED),
+    ((64, 64, 64, A16, 64, B16 + 2, 64, C16, 64), sdt.SDT_ERR_UNSUPPORTED),
+    ((64, 64, 64, A16, 64, B16, 64, C16 + 4, 64), sdt.SDT_ERR_UNSUPPORTED),
+    ((64, 64, 60, A16, 60, B16, 64, C16, 64), sdt.SDT_ERR_UNSUPPORTED),  # lda % 8
+    ((64, 64, 60, A16, 64, B16, 60, C16, 64), sdt.SDT_ERR_UNSUPPORTED),  # ldb % 8
+    ((64, 60, 64, A16, 64, B16, 64, C16, 60), sdt.SDT_ERR_UNSUPPORTED),  # ldc % 8
+    ((1, 64, 61, A16, 61, B16, 64, C16, 64), sdt.SDT_OK),                # one row: lda free
+    ((64, 1, 61, A16, 64, B16, 61, C16, 8), sdt.SDT_OK),                 # one column: ldb free
+    ((8, 8, 8, A16, (1 << 22), B16, 8, C16, 8), sdt.SDT_ERR_UNSUPPORTED),  # ld limit
+])
+def test_check_gemm_args(args, want):
+    assert sdt.check_gemm_args(*args) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((-1, 64, 64, A16, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, 64, None, 64, B16, 64, C16, 64), sdt.SDT_ERR_INVALID_ARG),
+    ((64, 64, 64, A16 + 8, 64, B16, 64, C16, 64), sdt.SDT_ERR_UNSUPPORTED),
+    ((0, 64, 64, None, 64, None, 64, None, 64), sdt.SDT_OK),
+])
+def test_gemm_f16_rejects_before_launch(args, want):
+    """The entry point returns the validation status and launches nothing."""
+    assert sdt.gemm_f16_raw(*args) == want
+
+
+def test_gemm_f16_ex_rejects_bad_choices():
+    L = sdt.lib()
+    base = (64, 64, 64, A16, 64, B16, 64, C16, 64, None)
+    assert L.gemm_f16_ex(*base, sdt.num_tiles(), -1) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemm_f16_ex(*base, -2, -1) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemm_f16_ex(*base, 0, 2) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_ex(64, 64, A16, B16, 64, C16, None, -1) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_ex(64, 64, A16, B16, 64, C16, None,
+                            sdt.gemv_num_variants()) == sdt.SDT_ERR_INVALID_ARG
+
+
+def test_gemv_rejects_before_launch():
+    assert sdt.gemv_f16_m1_raw(-1, 64, A16, B16, 64, C16) == sdt.SDT_ERR_INVALID_ARG
+    assert sdt.gemv_f16_m1_raw(64, 64, A16, B16, 60, C16) == sdt.SDT_ERR_INVALID_ARG
+    assert sdt.gemv_f16_m1_raw(64, 64, A16 + 2, B16, 64, C16) == sdt.SDT_ERR_UNSUPPORTED
+    assert sdt.gemv_f16_m1_raw(0, 64, None, None, 64, None) == sdt.SDT_OK
+
+
+# ---- the tile ladder and pick_tile -------------------------------------------
+
+def ladder():
+    return [sdt.tile_info(i) for i in range(sdt.num_tiles())]
+
+
+def test_ladder_is_well_formed():
+    tiles = ladder()
+    areas = [t["bm"] * t["bn"] for t in tiles]
+    assert areas == sorted(areas, reverse=True), "largest tile first"
+    for t in tiles:
+        assert t["bk"] == 64
+        assert t["threads"] == 64 * t["waves_m"] * t["waves_n"]
+        assert t["bm"] % (32 * t["waves_m"]) == 0 and t["bn"] % (32 * t["waves_n"]) == 0
+        assert t["lds_bytes"] == 2 * (t["bm"] + t["bn"]) * 64 * 2
+        assert t["lds_bytes"] <= 160 * 1024, "fits MI355X LDS"
+    with pytest.raises(sdt.SdtError):
+        sdt.tile_info(len(tiles))
+
+
+def test_pick_rung_reproduces_printed_gfx1100_ladder():
+    """The pages' rule with gfx1100 constants reproduces the printed tile,
+    warp layout and grid of all ten measured sizes."""
+    rungs = [((128, 128), "4x2"), ((64, 128), "2x4"), ((64, 64), "2x2")]
+    thresholds = [96, 64, 0]           # in 128x128-equivalent blocks
+    rows = [l.split("\t") for l in open(GOLDEN) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 10
+    for size, tile, warps, grid in rows:
+        n = int(size)
+        r = sdt.pick_rung(n, n, 128, 128, thresholds)
+        (bm, bn), w = rungs[r]
+        assert tile == f"{bm}x{bn}x32", (n, tile)
+        assert warps == w
+        gx, gy = (int(v) for v in grid.split("x"))
+        assert sorted((gx, gy)) == sorted((n // bm, n // bn))
+
+
+def test_pick_rung_edges():
+    assert sdt.pick_rung(0, 0, 128, 128, [96, 64, 0]) == 2
+    assert sdt.pick_rung(100, 100, 128, 128, [1, 0]) == 0     # ceil division
+    assert sdt.pick_rung(10, 10, 0, 128, [1]) == -1
+    assert sdt.pick_rung(10, 10, 128, 128, []) == -1
+
+
+def test_pick_tile_properties():
+    tiles = ladder()
+    for num_cu in (32, 80, 256, 304):
+        prev_area = 0
+        for n in [64 * i for i in range(1, 200)]:
+            t = sdt.pick_tile(n, n, n, num_cu)
+            assert 0 <= t["id"] < len(tiles)
+            assert t == sdt.pick_tile(n, n, n, num_cu), "deterministic"
+            area = t["bm"] * t["bn"]
+            assert area >= prev_area, "tile grows with the square size"
+            prev_area = area
+            # never off the largest tile while its grid alone fills the machine
+            big = tiles[0]
+            if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
+                assert t["id"] == 0
+    # any shape, even degenerate ones, gets a valid rung
+    for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
+        assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
+
+
+# ---- k-loop stagger -----------------------------------------------------------
+
+def test_stagger_enable_rule_on_k_sweep():
+    """On the K sweep only K=2048 has a power-of-two k-tile count (FlyDSL PR,
+    Motivation: the stagger is wired up exactly then)."""
+    for K in (1920, 1984, 2048, 2112, 2176, 2304):
+        assert sdt.stagger_auto(K, 64) == (K == 2048)
+        assert sdt.stagger_auto(K, 32) == (K == 2048)
+    assert sdt.stagger_auto(64, 64) and sdt.stagger_auto(8192, 64)
+    assert not sdt.stagger_auto(0, 64)
+    assert sdt.stagger_auto(65, 64)          # 2 k-tiles
+    assert not sdt.stagger_auto(129, 64)     # 3 k-tiles
+
+
+def test_stagger_is_a_permutation():
+    nkt = 1
+    while nkt <= 4096:
+        wgs = range(nkt) if nkt <= 64 else (0, 1, 2, 3, nkt // 2, nkt - 1, nkt, 12345)
+        for wg in wgs:
+            seq = [sdt.stagger_ktile(wg, i, nkt) for i in range(nkt)]
+            assert sorted(seq) == list(range(nkt)), (nkt, wg)
+            assert seq[0] == wg % nkt
+        nkt *= 2
+    assert sdt.stagger_ktile(0, 0, 3) == -1
+
+
+def test_decode_shape_bytes():
+    """The decode weights are 4096 x 12288 fp16 = 100,663,296 bytes ("100.7 MB" on
+    the mojo-baro page, section "Four rounds on the decode shape")."""
+    from shape_driven_tile_amd import inputs
+    assert inputs.DECODE_K * inputs.DECODE_N * 2 == 100_663_296

@@ -1,0 +1,298 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element
+by element, on the same seeded inputs.
+
+Tolerance for uniform inputs: |C_gpu - C_ref| <= 1e-2 + 2e-3*|C_ref| with C_ref
+the unrounded fp64 oracle.  Exact regimes (small integers, all-ones, identity,
+K=1, overflow) are compared bit for bit with the oracle's RNE fp16 rounding.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_helpers import (assert_bitexact, assert_close, run_gemm, run_gemv, sample_positions,
+                         say, to_dev)
+from shape_driven_tile_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _ntiles():
+    from shape_driven_tile_amd import binding as sdt
+    return sdt.num_tiles()
+
+
+# ---- the five workloads -------------------------------------------------------
+
+def test_square_256():
+    say("square 256^3 uniform, auto tile")
+    A, B = inputs.square_operands(256, 0)
+    C, _ = run_gemm(A, B)
+    assert_close(C, oracle.gemm(A, B))
+
+
+@pytest.mark.parametrize("n", inputs.SQUARE_SWEEP)
+def test_square_sweep(n):
+    say(f"square {n}^3 uniform, auto tile, full oracle")
+    A, B = inputs.square_operands(n, 1)
+    C, _ = run_gemm(A, B)
+    assert_close(C, oracle.gemm(A, B))
+
+
+@pytest.mark.parametrize("n", inputs.SQUARE_LARGE)
+def test_square_large_sampled(n):
+    say(f"square {n}^3 uniform, auto tile, sampled oracle")
+    A, B = inputs.square_operands(n, 2)
+    C, _ = run_gemm(A, B)
+    r, c = sample_positions(n, n, rows=24, cols=24, extra=8192, seed=n)
+    ref = oracle.gemm_sample(A, B, r, c)
+    assert_close(C[r, c], ref)
+    assert np.isfinite(C.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("K", inputs.K_SWEEP_K)
+def test_k_sweep(K):
+    say(f"K sweep M=N=2048 K={K}, auto tile/stagger, full oracle")
+    A, B = inputs.square_operands(2048, 3, k=K)
+    C, _ = run_gemm(A, B)
+    assert_close(C, oracle.gemm(A, B))
+
+
+def test_k_sweep_stagger_arms_at_2048():
+    """K=2048 is the one sweep point with a power-of-two k-tile count: both
+    stagger arms match the oracle and agree bit for bit on integer inputs."""
+    say("K=2048 stagger on/off")
+    A, B = inputs.square_operands(2048, 3, k=2048)
+    ref = oracle.gemm(A, B)
+    for st in (0, 1):
+        C, _ = run_gemm(A, B, tile=2, stagger=st)
+        assert_close(C, ref)
+    Ai = inputs.integer_f16((2048, 2048), 7)
+    Bi = inputs.integer_f16((2048, 2048), 8)
+    ref_i = oracle.gemm(Ai, Bi)
+    for st in (0, 1):
+        C, _ = run_gemm(Ai, Bi, tile=2, stagger=st)
+        assert_bitexact(C, ref_i)
+
+
+def test_decode_gemv_all_buffers():
+    say("decode GEMV N=12288 K=4096, 8 weight buffers")
+    x = inputs.decode_activations()
+    for r in range(inputs.DECODE_BUFFERS):
+        W = inputs.decode_weights(r)
+        y = run_gemv(x, W)
+        assert_close(y, oracle.gemv_m1(x, W))
+
+
+# ---- exact regimes (bit for bit) ---------------------------------------------
+
+@pytest.mark.parametrize("shape", [(300, 200, 1024), (257, 129, 1000), (64, 64, 64),
+                                   (513, 771, 520)])
+def test_integer_exact_every_tile(shape):
+    M, N, K = shape
+    A = inputs.integer_f16((M, K), 11)
+    B = inputs.integer_f16((N, K), 12)
+    ref = oracle.gemm(A, B)
+    nkt = -(-K // 64)
+    staggers = (0, 1) if nkt & (nkt - 1) == 0 else (0,)
+    for tile in range(_ntiles()):
+        for st in staggers:
+            say(f"integer {shape} tile={tile} stagger={st}")
+            C, _ = run_gemm(A, B, tile=tile, stagger=st)
+            assert_bitexact(C, ref)
+
+
+@pytest.mark.parametrize("K", [1, 8, 256, 1920, 2048, 2304, 4096, 8192, 16384])
+def test_all_ones(K):
+    say(f"all-ones K={K}")
+    A = np.ones((96, max(K, 8)), np.float16)
+    B = np.ones((160, max(K, 8)), np.float16)
+    C, _ = run_gemm(A, B, K=K)
+    assert (C.astype(np.float64) == K).all()
+
+
+def test_identity():
+    say("identity B, M != K")
+    A = inputs.uniform_f16((384, 256), 13)
+    B = np.eye(256, dtype=np.float16)
+    C, _ = run_gemm(A, B)
+    assert (C.view(np.uint16) == A.view(np.uint16)).all()
+
+
+def test_k1_outer_product():
+    say("K=1 outer product, padded rows")
+    a = inputs.padded(inputs.uniform_f16((70, 1), 14), 8)
+    b = inputs.padded(inputs.uniform_f16((90, 1), 15), 8)
+    C, _ = run_gemm(a, b, K=1)
+    assert_bitexact(C, oracle.gemm(a, b, K=1))
+
+
+def test_overflow_rounds_to_inf():
+    say("overflow to inf")
+    A = np.full((64, 64), 255.0, np.float16)
+    B = np.full((64, 64), 255.0, np.float16)
+    B[::2] = -255.0
+    C, _ = run_gemm(A, B)
+    ref = oracle.gemm(A, B)
+    assert ((oracle.f16_encode_rne(ref) & 0x7FFF) == 0x7C00).all(), "every fp16 result is +-inf"
+    assert_bitexact(C, ref)
+
+
+# ---- ragged shapes, strides and padding --------------------------------------
+
+@pytest.mark.parametrize("M,N,K,pa,pb,pc", [
+    (1, 1, 1, 7, 7, 7), (3, 5, 7, 1, 9, 3), (65, 129, 72, 8, 0, 8), (257, 511, 8, 0, 8, 0),
+    (100, 90, 37, 3, 11, 6), (300, 200, 1000, 24, 0, 40), (129, 1025, 200, 64, 64, 64),
+    (520, 260, 4100, 0, 0, 0), (2, 3000, 300, 4, 4, 8)])
+def test_ragged_and_padded(M, N, K, pa, pb, pc):
+    """Ragged M, N, K with padded leading dimensions full of NaN: the padding
+    never reaches C, and nothing past column N of C is written."""
+    say(f"ragged M={M} N={N} K={K} pads={pa},{pb},{pc}")
+    ka = -(-(K + pa) // 8) * 8
+    kb = -(-(K + pb) // 8) * 8
+    A = inputs.padded(inputs.uniform_f16((M, K), 21), ka)
+    B = inputs.padded(inputs.uniform_f16((N, K), 22), kb)
+    C, pad_ok = run_gemm(A, B, K=K, ldc_pad=pc)
+    assert_close(C, oracle.gemm(A, B, K=K))
+    assert pad_ok, "kernel wrote past column N"
+
+
+def test_every_tile_forced_uniform():
+    A, B = inputs.square_operands(520, 4)
+    ref = oracle.gemm(A, B)
+    for tile in range(_ntiles()):
+        say(f"uniform 520^3 tile={tile}")
+        C, _ = run_gemm(A, B, tile=tile, stagger=0)
+        assert_close(C, ref)
+
+
+def test_padded_and_tight_same_shape():
+    """A padded slice and a tight operand of one shape give the same result
+    (strides are runtime arguments, so no kernel is shared at the wrong pitch;
+    FlyDSL PR, Changes: the resolve-cache stride key)."""
+    say("padded vs tight same shape")
+    A, B = inputs.square_operands(512, 5)
+    Ct, _ = run_gemm(A, B)
+    Cp, _ = run_gemm(inputs.padded(A, 512 + 64), inputs.padded(B, 512 + 32), K=512)
+    assert (Ct.view(np.uint16) == Cp.view(np.uint16)).all()
+
+
+# ---- M = 1 and the GEMV -------------------------------------------------------
+
+def test_m1_routes_to_gemv():
+    say("gemm_f16 M=1 == gemv_f16_m1; gemm_f16_ex M=1 via the MFMA kernel")
+    x = inputs.decode_activations()
+    W = inputs.decode_weights(0)
+    y = run_gemv(x, W)
+    C, _ = run_gemm(x[None, :], W)
+    assert (C[0].view(np.uint16) == y.view(np.uint16)).all()
+    C2, _ = run_gemm(x[None, :], W, tile=-1, stagger=0)
+    assert_close(C2[0], oracle.gemv_m1(x, W))
+
+
+@pytest.mark.parametrize("N,K", [(12288, 4096), (12289, 1000), (100, 37), (77, 5000),
+                                 (4096, 8), (33, 1)])
+def test_gemv_variants_agree(N, K):
+    from shape_driven_tile_amd import binding as sdt
+    x = inputs.uniform_f16((K,), 31)
+    W = inputs.padded(inputs.normal_f16((N, K), 32), -(-K // 8) * 8 + 8)
+    ref = oracle.gemv_m1(x, W, K=K)
+    base = None
+    for v in range(sdt.gemv_num_variants()):
+        say(f"gemv N={N} K={K} variant={v}")
+        y = run_gemv(x, W, K=K, variant=v)
+        assert_close(y, ref)
+        if base is None:
+            base = y
+        assert (y.view(np.uint16) == base.view(np.uint16)).all(), "variants differ"
+
+
+def test_gemv_exact_cases():
+    say("gemv one-hot and integer inputs")
+    K, N = 4096, 12288
+    W = inputs.normal_f16((N, K), 41)
+    for j in (0, 4095, 1234):
+        e = np.zeros(K, np.float16)
+        e[j] = 1
+        y = run_gemv(e, W)
+        assert (y.view(np.uint16) == W[:, j].view(np.uint16)).all()
+    xi = inputs.integer_f16((K,), 42)
+    Wi = inputs.integer_f16((N, K), 43)
+    assert_bitexact(run_gemv(xi, Wi), oracle.gemv_m1(xi, Wi))
+
+
+# ---- degenerate calls, errors, streams, determinism ---------------------------
+
+def test_k0_writes_zeros_and_empty_is_noop():
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    say("K=0 zeros, M=0/N=0 no-op")
+    A = torch.empty((70, 0), dtype=torch.float16, device="cuda:0")
+    B = torch.empty((50, 0), dtype=torch.float16, device="cuda:0")
+    C = torch.full((70, 56), 7.0, dtype=torch.float16, device="cuda:0")[:, :50]
+    sdt.gemm_f16(A, B, C)
+    torch.cuda.synchronize()
+    assert (C == 0).all().item()
+    C2 = torch.full((0, 50), 7.0, dtype=torch.float16, device="cuda:0")
+    sdt.gemm_f16(torch.empty((0, 64), dtype=torch.float16, device="cuda:0"),
+                 torch.ones((50, 64), dtype=torch.float16, device="cuda:0"), C2)
+    y = torch.full((12,), 7.0, dtype=torch.float16, device="cuda:0")
+    sdt.gemv_f16_m1(torch.empty((0,), dtype=torch.float16, device="cuda:0"),
+                    torch.empty((12, 0), dtype=torch.float16, device="cuda:0"), y)
+    torch.cuda.synchronize()
+    assert (y == 0).all().item()
+
+
+def test_misaligned_operands_are_rejected():
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    say("misaligned operands rejected before launch")
+    buf = torch.zeros((64, 72), dtype=torch.float16, device="cuda:0")
+    B = torch.zeros((64, 64), dtype=torch.float16, device="cuda:0")
+    C = torch.full((64, 64), 3.0, dtype=torch.float16, device="cuda:0")
+    with pytest.raises(sdt.SdtError) as e:
+        sdt.gemm_f16(buf[:, 1:65], B, C)
+    assert e.value.status == sdt.SDT_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (C == 3.0).all().item()
+
+
+def test_nondefault_stream():
+    import torch
+    say("non-default stream")
+    A, B = inputs.square_operands(640, 6)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        C, _ = run_gemm(A, B, stream=s)
+    assert_close(C, oracle.gemm(A, B))
+
+
+def test_determinism_repeated_launches():
+    """No atomics on the path: repeated launches are bit-identical (a missing
+    barrier or an LDS race would show up as run-to-run differences)."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    A, B = inputs.square_operands(1536, 7)
+    dA, dB = to_dev(A), to_dev(B)
+    outs = []
+    for tile in range(_ntiles()):
+        say(f"determinism 1536^3 tile={tile}")
+        first = None
+        for _ in range(10):
+            C = torch.empty((1536, 1536), dtype=torch.float16, device="cuda:0")
+            sdt.gemm_f16_ex(dA, dB, C, tile_id=tile)
+            torch.cuda.synchronize()
+            if first is None:
+                first = C
+            else:
+                assert torch.equal(first.view(torch.int16), C.view(torch.int16))
+        outs.append(first)
+    x = to_dev(inputs.decode_activations())
+    W = to_dev(inputs.decode_weights(1))
+    ys = []
+    for _ in range(10):
+        y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device="cuda:0")
+        sdt.gemv_f16_m1(x, W, y)
+        ys.append(y)
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
