@@ -53,11 +53,55 @@ def parse():
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--profile", default=None, metavar="KERNEL",
+                    help="instead of the benchmark, launch one kernel repeatedly for a "
+                         "profiler: gemm<N> (N^3, e.g. gemm8192), gemv (decode, rotating "
+                         "buffers) or copy<MB> (a plain device copy, for counter scaling)")
+    ap.add_argument("--launches", type=int, default=20)
+    ap.add_argument("--tile", type=int, default=-1)
     return ap.parse_args()
+
+
+def profile_mode(args):
+    """Repeated launches of one kernel, no oracle and no timing: the workload a
+    rocprofv3 kernel-trace or counter pass is taken on."""
+    import torch
+
+    from shape_driven_tile_amd import binding as sdt
+    from shape_driven_tile_amd import inputs
+    dev = torch.device("cuda:0")
+    name = args.profile
+    if name.startswith("gemm"):
+        n = int(name[4:])
+        A, B = inputs.square_operands(n, SEED_INDEX.get(n, 2))
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+        C = torch.empty((n, n), dtype=torch.float16, device=dev)
+        for _ in range(args.launches):
+            sdt.gemm_f16_ex(dA, dB, C, tile_id=args.tile)
+    elif name == "gemv":
+        x = torch.from_numpy(inputs.decode_activations()).to(dev)
+        Ws = [torch.from_numpy(inputs.decode_weights(r)).to(dev)
+              for r in range(inputs.DECODE_BUFFERS)]
+        y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
+        for j in range(args.launches):
+            sdt.gemv_f16_m1(x, Ws[j % len(Ws)], y)
+    elif name.startswith("copy"):
+        mb = int(name[4:])
+        src = torch.ones((mb * 1024 * 1024 // 2,), dtype=torch.float16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.launches):
+            dst.copy_(src)
+    else:
+        raise SystemExit(f"unknown --profile kernel {name}")
+    torch.cuda.synchronize()
+    log(f"profile mode: {args.launches} launches of {name} done")
 
 
 def main():
     args = parse()
+    if args.profile:
+        return profile_mode(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}), flush=True)

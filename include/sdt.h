@@ -68,8 +68,8 @@ typedef struct sdt_tile {
  * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
  * definition).  The tile is chosen by sdt_pick_tile from the device's CU
- * count; the k-tile stagger is enabled exactly when the k-tile count is a
- * power of two (FlyDSL PR, Changes: stagger). */
+ * count; the k-tile stagger is enabled exactly when the count of full
+ * 64-deep k-tiles is a power of two (FlyDSL PR, Changes: stagger). */
 int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
              const void* B, int64_t ldb,
@@ -124,8 +124,9 @@ int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 
-/* Host-only: 1 if the k-loop stagger is used for K with k-tile depth bk
- * (the k-tile count ceil(K/bk) is a power of two), else 0. */
+/* Host-only: 1 if the k-loop stagger is used for K with k-tile depth bk,
+ * i.e. the number of full k-tiles floor(K/bk) is a power of two (a partial
+ * last k-tile, if any, is always visited last), else 0. */
 int sdt_stagger_auto(int64_t K, int bk);
 
 /* Host-only: the k-tile visited at step i by workgroup wg when staggered:

@@ -1,38 +1,50 @@
 // gfx950 fp16 GEMM kernel family: C = A.B, fp32 accumulation on MFMA, fp16
 // (round-to-nearest-even) output.
 //
-// Design, after "Beating hipBLASLt on a Gaming GPU" (section "The result":
-// two LDS buffers, one barrier per K-step, a two-deep global prefetch, A
-// XOR-swizzled, B stored transposed) and "The part that actually mattered"
-// (the tile is a compile-time parameter with its own wave layout),
-// re-designed for CDNA4:
+// After "Beating hipBLASLt on a Gaming GPU" (section "The result": two LDS
+// buffers, one barrier per K-step, prefetch of the next tiles while the
+// current one is consumed, an XOR swizzle, B stored transposed) and "The part
+// that actually mattered" (the tile is a compile-time parameter with its own
+// wave layout), re-designed for CDNA4:
 //   * wave64 and v_mfma_f32_32x32x16_f16: each wave owns a (BM/WM) x (BN/WN)
 //     block of 32x32 accumulator tiles;
-//   * both operands are K-contiguous rows (A row-major, B "K-major"), so both
-//     are staged the same way: a k-tile is BM (or BN) rows of 64 fp16 =
-//     128 bytes, eight 16-byte chunks per row;
-//   * LDS: two stages; chunk c of row r lives at chunk c ^ swz(r), so the
-//     16-byte fragment reads of 16 consecutive rows hit distinct bank groups;
-//   * prefetch: while tile i is multiplied out of one LDS stage, tile i+1 is
-//     written from registers into the other and tile i+2 is in flight in
-//     registers -- one barrier per k-tile;
-//   * stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by choosing the
-//     tile from the shape", Changes): workgroup w visits k-tiles in the order
-//     (w + i) & (nkt - 1) when nkt is a power of two;
-//   * edges: operand rows come through a buffer descriptor clipped to the
-//     valid rows, so rows past M or N read as zero; the k tail is masked; the
-//     store is masked.  One code path serves every shape.
-//   * MI355X has 8 XCDs with private L2s and the dispatcher deals workgroup
-//     ids round-robin over them; ids are remapped so each XCD works on a
-//     contiguous, GROUP_M-grouped band of output tiles.
+//   * both operands are K-contiguous rows (A row-major, B "K-major"), staged
+//     the same way: a k-tile is BM (or BN) rows of 64 fp16 = 128 bytes, eight
+//     16-byte chunks per row; chunk c of row r is stored at chunk c ^ swz(r),
+//     which keeps the 16-byte fragment reads of 16 consecutive rows on
+//     distinct LDS bank groups;
+//   * global -> LDS without registers: buffer_load_dwordx4 ... lds writes a
+//     wave's 64 lanes to 1 KB of consecutive LDS, so each lane fetches the
+//     global chunk that belongs at its swizzled LDS slot;
+//   * two LDS stages: while tile i is multiplied out of one stage, tile i+1 is
+//     landing in the other; right after the single barrier of step i the
+//     loads of tile i+2 are issued into the stage tile i just freed;
+//   * MFMA fragments are double-buffered in registers across the four 16-deep
+//     sub-steps of a k-tile, so the LDS reads of sub-step kk+1 are in flight
+//     under the MFMAs of sub-step kk, and the first reads of tile i+1 go out
+//     under the last MFMAs of tile i, past the barrier;
+//   * k-loop stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by
+//     choosing the tile from the shape", Changes): when the number of full
+//     k-tiles is a power of two, workgroup w visits them in the order
+//     (w + i) & (nfull - 1);
+//   * edges: operand rows come through buffer descriptors clipped to the
+//     valid rows, so rows past M or N read as zero; a partial last k-tile is
+//     loaded through registers with per-element masking; stores are masked;
+//   * MI355X deals workgroup ids round-robin over its XCDs, each with a
+//     private L2; ids are remapped so every XCD works through a contiguous,
+//     GROUP_M-grouped band of output tiles.
 //
-// The MFMA is issued as D = B_tile . A_tile^T (operand "A" of the instruction
-// takes rows of B), so each lane's four consecutive accumulator rows are four
-// consecutive n of one output row m and leave as one 8-byte store.
+// The MFMA is issued as D = B_frag . A_frag^T (the instruction's first
+// operand takes rows of B), so each lane's four consecutive accumulator rows
+// are four consecutive n of one output row m and leave as one 8-byte store.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
+
+#include "launcher.hpp"
 
 namespace sdt {
 
@@ -41,10 +53,8 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// Byte offset used for a row that does not exist: past the end of every
-// descriptor (whose byte count stays below 2^31), so the load returns zero.
-constexpr uint32_t kOutOfRange = 0x80000000u;
 // Raw-buffer descriptor word 3 for gfx9-family parts (32-bit data format).
 constexpr int kRsrcWord3 = 0x00020000;
 constexpr int kGroupM = 8;
@@ -56,50 +66,69 @@ struct GemmParams {
     int64_t lda, ldb, ldc;
     int M, N, K;
     int gm, gn;    // output tiles along M and N
-    int nkt;       // k-tiles, ceil(K / 64)
-    int stagger;   // 1: (w + i) & (nkt - 1) order
+    int stagger;   // 1: full k-tiles in (w + i) & (K/64 - 1) order
     int nxcd;      // XCDs the dispatcher deals workgroups over
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// Buffer descriptor over `bytes` bytes from `base`.  Both are workgroup-
+// uniform; readfirstlane says so to the compiler, which keeps the descriptor
+// in scalar registers (in vector registers every load would become a
+// waterfall loop).  Offsets at or past `bytes` read as zero.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             kRsrcWord3);
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void* ub = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    return __builtin_amdgcn_make_buffer_rsrc(ub, (short)0, (int)n, kRsrcWord3);
 }
 
-// A chunk of eight fp16 at byte offset `off` whose k range [k, k+8) straddles
-// K: read the valid elements one by one so nothing past K is touched.
-__device__ __noinline__ int4_t load_partial_chunk(__amdgpu_buffer_rsrc_t r, uint32_t off,
-                                                  int soff, int valid) {
-    uint16_t h[8];
+// 16 bytes per lane from global memory straight into LDS at
+// lds_wave_base + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int4_t* lds_wave_base,
+                                      uint32_t voff, int soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// Eight fp16 at byte offset `off` of which only the first `valid` lie below K
+// (valid >= 8: all; valid <= 0: none, zero returned).  Nothing at or past K
+// is read.
+__device__ __forceinline__ int4_t load16_tail(__amdgpu_buffer_rsrc_t r, uint32_t off, int soff,
+                                              int valid) {
+    if (valid >= 8)
+        return __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
+    int4_t v = {0, 0, 0, 0};
+    if (valid > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-        h[e] = (e < valid && off != kOutOfRange)
-                   ? __builtin_amdgcn_raw_buffer_load_b16(r, off + 2 * e, soff, 0)
-                   : (uint16_t)0;
-    int4_t v;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) v[d] = (int)((uint32_t)h[2 * d] | ((uint32_t)h[2 * d + 1] << 16));
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t lo = (2 * d < valid)
+                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * d, soff, 0) : 0u;
+            const uint32_t hi = (2 * d + 1 < valid)
+                ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off + 4 * d + 2, soff, 0) : 0u;
+            v[d] = (int)(lo | (hi << 16));
+        }
+    }
     return v;
 }
 
+// s_waitcnt vmcnt(0), leaving the LDS and export counters alone.
+__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
-    constexpr int BK = 64;
-    constexpr int NT = WM * WN * 64;
-    constexpr int WTM = BM / WM;
-    constexpr int WTN = BN / WN;
-    constexpr int FM = WTM / 32;
-    constexpr int FN = WTN / 32;
-    constexpr int RPP = NT / 8;        // operand rows covered by one load pass
-    constexpr int A_LD = BM / RPP;     // 16-byte chunks per thread per k-tile
-    constexpr int B_LD = BN / RPP;
-    constexpr int A_UNITS = BM * 8;    // 16-byte LDS units per stage
-    constexpr int STAGE = (BM + BN) * 8;
+    constexpr int BK = kBK;
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
+    constexpr int STAGE = A_UNITS + B_UNITS;
+    constexpr int A_DMA = A_UNITS / (64 * NW);         // 1 KB loads per wave per k-tile
+    constexpr int B_DMA = B_UNITS / (64 * NW);
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
-    static_assert(BM % RPP == 0 && BN % RPP == 0, "rows must split evenly over passes");
-    static_assert(RPP % 16 == 0, "swizzle assumes 16-row periodicity per pass");
+    static_assert(A_UNITS % (64 * NW) == 0 && B_UNITS % (64 * NW) == 0,
+                  "each wave loads whole 8-row slabs");
 
     __shared__ int4_t smem[2 * STAGE];
 
@@ -109,14 +138,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     const int wave_m = wave % WM;
     const int wave_n = wave / WM;
 
-    // ---- workgroup -> output tile (XCD-aware, grouped) -------------------
+    // ---- workgroup -> output tile (XCD-aware, grouped) -----------------------
     const int nwg = p.gm * p.gn;
     const int w = blockIdx.x;
     int logical = w;
     if (p.nxcd > 1) {
-        const int xcd = w % p.nxcd;
-        const int q = nwg / p.nxcd;
-        const int r = nwg % p.nxcd;
+        const int xcd = w % p.nxcd, q = nwg / p.nxcd, r = nwg % p.nxcd;
         logical = xcd * q + min(xcd, r) + w / p.nxcd;
     }
     const int group_span = kGroupM * p.gn;
@@ -124,81 +151,69 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     const int first_m = g * kGroupM;
     const int gsz = min(p.gm - first_m, kGroupM);
     const int within = logical - g * group_span;
-    const int tm = first_m + within % gsz;
-    const int tn = within / gsz;
-    const int64_t m0 = (int64_t)tm * BM;
-    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)(first_m + within % gsz) * BM;
+    const int64_t n0 = (int64_t)(within / gsz) * BN;
 
-    // ---- operand descriptors and per-thread row offsets ------------------
-    const int rows_a = min((int64_t)BM, (int64_t)p.M - m0);
-    const int rows_b = min((int64_t)BN, (int64_t)p.N - n0);
+    // ---- operand descriptors: only this tile's valid rows are addressable ----
+    const int rows_a = (int)min((int64_t)BM, (int64_t)p.M - m0);
+    const int rows_b = (int)min((int64_t)BN, (int64_t)p.N - n0);
     const __amdgpu_buffer_rsrc_t ra =
         make_rsrc(p.A + m0 * p.lda, (uint32_t)((int64_t)rows_a * p.lda * 2));
     const __amdgpu_buffer_rsrc_t rb =
         make_rsrc(p.B + n0 * p.ldb, (uint32_t)((int64_t)rows_b * p.ldb * 2));
-    const int lrow = t >> 3;   // row within a pass
-    const int lchk = t & 7;    // 16-byte chunk within the 128-byte k-slice
-    uint32_t off_a[A_LD], off_b[B_LD];
+
+    // Load j of this wave fills LDS units [(wave*X + j)*64, +64): 8 rows of
+    // the stage; lane l lands in unit +l, i.e. row l/8 at swizzled position
+    // l%8, which holds logical chunk (l%8) ^ swz(row).  A row past the valid
+    // ones has an offset past the descriptor and reads as zero.
+    uint32_t voff_a[A_DMA], voff_b[B_DMA];
+    int chk_a[A_DMA], chk_b[B_DMA];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) {
-        const int row = lrow + i * RPP;
-        off_a[i] = row < rows_a ? (uint32_t)(row * p.lda * 2 + lchk * 16) : kOutOfRange;
+    for (int j = 0; j < A_DMA; ++j) {
+        const int row = (wave * A_DMA + j) * 8 + (lane >> 3);
+        chk_a[j] = (lane & 7) ^ swz(row);
+        voff_a[j] = (uint32_t)(row * p.lda * 2 + chk_a[j] * 16);
     }
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) {
-        const int row = lrow + i * RPP;
-        off_b[i] = row < rows_b ? (uint32_t)(row * p.ldb * 2 + lchk * 16) : kOutOfRange;
+    for (int j = 0; j < B_DMA; ++j) {
+        const int row = (wave * B_DMA + j) * 8 + (lane >> 3);
+        chk_b[j] = (lane & 7) ^ swz(row);
+        voff_b[j] = (uint32_t)(row * p.ldb * 2 + chk_b[j] * 16);
     }
-    // LDS unit this thread writes for pass i: row (lrow + i*RPP), chunk lchk.
-    const int st_unit = lrow * 8 + (lchk ^ swz(lrow));
 
-    const int nkt = p.nkt;
-    const int k_tail = p.K - (nkt - 1) * BK;   // valid k in the last tile, 1..64
-    const int k0 = p.stagger ? (w & (nkt - 1)) : 0;
+    // ---- k-tile sequence: the full tiles (staggered), then a partial one ------
+    const int nfull = p.K / BK;
+    const int ktail = p.K - nfull * BK;
+    const int nseq = nfull + (ktail > 0 ? 1 : 0);
+    const int kmask = p.stagger ? (nfull - 1) : 0x7fffffff;
+    const int k0 = p.stagger ? (w & (nfull - 1)) : 0;
 
-    int4_t rga[A_LD], rgb[B_LD];
-
-    auto load_tile = [&](int i) {
-        const int kt = p.stagger ? ((k0 + i) & (nkt - 1)) : i;
-        const int soff = kt * BK * 2;
-        if (kt == nkt - 1 && k_tail < BK) {
-            const int valid = k_tail - lchk * 8;   // elements of this chunk below K
-#pragma unroll
-            for (int j = 0; j < A_LD; ++j) {
-                if (valid >= 8)
-                    rga[j] = __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, off_a[j], soff, 0));
-                else if (valid <= 0)
-                    rga[j] = (int4_t){0, 0, 0, 0};
-                else
-                    rga[j] = load_partial_chunk(ra, off_a[j], soff, valid);
-            }
-#pragma unroll
-            for (int j = 0; j < B_LD; ++j) {
-                if (valid >= 8)
-                    rgb[j] = __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, off_b[j], soff, 0));
-                else if (valid <= 0)
-                    rgb[j] = (int4_t){0, 0, 0, 0};
-                else
-                    rgb[j] = load_partial_chunk(rb, off_b[j], soff, valid);
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < A_LD; ++j)
-                rga[j] = __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, off_a[j], soff, 0));
-#pragma unroll
-            for (int j = 0; j < B_LD; ++j)
-                rgb[j] = __builtin_bit_cast(int4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, off_b[j], soff, 0));
-        }
-    };
-
-    auto store_tile = [&](int stage) {
+    auto dma_tile = [&](int step, int stage) {   // a full k-tile, straight into LDS
+        const int soff = ((k0 + step) & kmask) * (BK * 2);
         int4_t* base = smem + stage * STAGE;
 #pragma unroll
-        for (int j = 0; j < A_LD; ++j) base[st_unit + j * RPP * 8] = rga[j];
+        for (int j = 0; j < A_DMA; ++j) dma16(ra, base + (wave * A_DMA + j) * 64, voff_a[j], soff);
 #pragma unroll
-        for (int j = 0; j < B_LD; ++j) base[A_UNITS + st_unit + j * RPP * 8] = rgb[j];
+        for (int j = 0; j < B_DMA; ++j)
+            dma16(rb, base + A_UNITS + (wave * B_DMA + j) * 64, voff_b[j], soff);
+    };
+    auto tail_tile = [&](int stage) {            // the partial k-tile, masked
+        const int soff = nfull * (BK * 2);
+        int4_t* base = smem + stage * STAGE;
+#pragma unroll
+        for (int j = 0; j < A_DMA; ++j)
+            base[(wave * A_DMA + j) * 64 + lane] =
+                load16_tail(ra, voff_a[j], soff, ktail - chk_a[j] * 8);
+#pragma unroll
+        for (int j = 0; j < B_DMA; ++j)
+            base[A_UNITS + (wave * B_DMA + j) * 64 + lane] =
+                load16_tail(rb, voff_b[j], soff, ktail - chk_b[j] * 8);
+    };
+    auto load_step = [&](int step, int stage) {
+        if (step < nfull) dma_tile(step, stage); else tail_tile(stage);
     };
 
+    // ---- accumulators and fragments ----------------------------------------------
     floatx16_t acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
@@ -207,54 +222,100 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // Fragment addressing: lane reads row (lane % 32) of a 32-row block,
-    // 16-byte chunk 2*kk + lane/32 of the k-tile.
+    // Lane reads row (lane % 32) of a 32-row block, chunk 2*kk + lane/32.
     const int frow = lane & 31;
     const int fsw = swz(frow);
     const int fhalf = lane >> 5;
     const int a_row0 = wave_m * WTM + frow;
     const int b_row0 = wave_n * WTN + frow;
-
-    auto compute = [&](int stage, int kk) {
+    half8_t fa[2][FM], fb[2][FN];
+    auto read_frags = [&](int stage, int kk, int set) {
         const int4_t* base = smem + stage * STAGE;
         const int chunk = (2 * kk + fhalf) ^ fsw;
-        half8_t fa[FM], fb[FN];
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-            fa[j] = __builtin_bit_cast(half8_t, base[(a_row0 + j * 32) * 8 + chunk]);
+            fa[set][j] = __builtin_bit_cast(half8_t, base[(a_row0 + j * 32) * 8 + chunk]);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            fb[i] = __builtin_bit_cast(half8_t, base[A_UNITS + (b_row0 + i * 32) * 8 + chunk]);
+            fb[set][i] = __builtin_bit_cast(half8_t, base[A_UNITS + (b_row0 + i * 32) * 8 + chunk]);
+    };
+    auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[i], fa[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set][i], fa[set][j],
+                                                                   acc[i][j], 0, 0, 0);
     };
-
-    // ---- prologue: tile 0 into stage 0, tile 1 in flight -----------------
-    load_tile(0);
-    store_tile(0);
-    if (nkt > 1) load_tile(1);
-    __syncthreads();
-
-    // ---- main loop: one barrier per k-tile -------------------------------
-    for (int i = 0; i < nkt; ++i) {
-        const int s = i & 1;
-        compute(s, 0);
-        compute(s, 1);
-        if (i + 1 < nkt) {
-            store_tile(s ^ 1);
-            if (i + 2 < nkt) load_tile(i + 2);
+    // One MFMA, then one fragment read and one global load while any remain
+    // (scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x020 global read).
+    auto interleave = [&](auto n_reads, auto n_loads) {
+        constexpr int R = decltype(n_reads)::value, V = decltype(n_loads)::value;
+#pragma unroll
+        for (int m = 0; m < FM * FN; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (m < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            if (m < V) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
-        compute(s, 2);
-        compute(s, 3);
+    };
+    using Reads = std::integral_constant<int, FM + FN>;
+    using Loads = std::integral_constant<int, A_DMA + B_DMA>;
+    using None = std::integral_constant<int, 0>;
+
+    // ---- prologue: tile 0 landed in stage 0, tile 1 on its way to stage 1 ------
+    load_step(0, 0);
+    wait_global_loads();
+    __syncthreads();
+    if (nseq > 1) load_step(1, 1);
+    read_frags(0, 0, 0);
+
+    // ---- steady state: one basic block per k-tile ----------------------------------
+    // (A) kk1 reads under kk0 MFMAs, (B) kk2 reads under kk1, (C) kk3 reads
+    // under kk2; then tile i+1 must have landed and every wave must be done
+    // with stage s: wait, barrier; (D) tile i+2's loads into stage s and the
+    // next stage's kk0 reads under the kk3 MFMAs.
+    int i = 0;
+    for (; i + 2 < nfull; ++i) {
+        const int s = i & 1;
+        read_frags(s, 1, 1);
+        mfmas(0);
+        interleave(Reads{}, None{});
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 2, 0);
+        mfmas(1);
+        interleave(Reads{}, None{});
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(s, 3, 1);
+        mfmas(0);
+        interleave(Reads{}, None{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_global_loads();
         __syncthreads();
+        dma_tile(i + 2, s);
+        read_frags(s ^ 1, 0, 0);
+        mfmas(1);
+        interleave(Reads{}, Loads{});
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- the last (at most two) steps, and the partial tile, if any -----------------
+    for (; i < nseq; ++i) {
+        const int s = i & 1;
+        read_frags(s, 1, 1);
+        mfmas(0);
+        read_frags(s, 2, 0);
+        mfmas(1);
+        read_frags(s, 3, 1);
+        mfmas(0);
+        wait_global_loads();
+        __syncthreads();
+        if (i + 2 < nseq) load_step(i + 2, s);
+        if (i + 1 < nseq) read_frags(s ^ 1, 0, 0);
+        mfmas(1);
     }
 
-    // ---- epilogue: fp32 -> fp16 (RNE), masked 8-byte stores --------------
+    // ---- epilogue: fp32 -> fp16 (RNE), masked 8-byte stores ------------------------
 #pragma unroll
-    for (int i = 0; i < FN; ++i) {
+    for (int i2 = 0; i2 < FN; ++i2) {
 #pragma unroll
         for (int j = 0; j < FM; ++j) {
             const int64_t m = m0 + wave_m * WTM + j * 32 + frow;
@@ -262,12 +323,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
             uint16_t* crow = p.C + m * p.ldc;
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const int64_t n = n0 + wave_n * WTN + i * 32 + 8 * gq + 4 * fhalf;
+                const int64_t n = n0 + wave_n * WTN + i2 * 32 + 8 * gq + 4 * fhalf;
                 half4_t h;
-                h[0] = (_Float16)acc[i][j][4 * gq + 0];
-                h[1] = (_Float16)acc[i][j][4 * gq + 1];
-                h[2] = (_Float16)acc[i][j][4 * gq + 2];
-                h[3] = (_Float16)acc[i][j][4 * gq + 3];
+                h[0] = (_Float16)acc[i2][j][4 * gq + 0];
+                h[1] = (_Float16)acc[i2][j][4 * gq + 1];
+                h[2] = (_Float16)acc[i2][j][4 * gq + 2];
+                h[3] = (_Float16)acc[i2][j][4 * gq + 3];
                 if (n + 3 < p.N) {
                     *reinterpret_cast<uint2_t*>(crow + n) = __builtin_bit_cast(uint2_t, h);
                 } else {

@@ -94,7 +94,7 @@ extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
 
 extern "C" int sdt_stagger_auto(int64_t K, int bk) {
     if (K <= 0 || bk <= 0) return 0;
-    return sdt::is_pow2(sdt::ceil_div(K, bk)) ? 1 : 0;
+    return sdt::is_pow2(K / bk) ? 1 : 0;
 }
 
 // FlyDSL PR, Changes: each workgroup starts at its own k-tile and wraps with

@@ -142,11 +142,13 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
 
     const int id = tile_id >= 0 ? tile_id : pick_tile(M, N, K, dev.num_cu);
     const TileDesc& td = kLadder[id];
-    const int64_t nkt = ceil_div(K, kBK);
-    int use_stagger = is_pow2(nkt) ? 1 : 0;
+    // The stagger wraps with a mask over the full k-tiles, so it needs their
+    // count to be a power of two (a partial last tile always comes last).
+    const int64_t nfull = K / kBK;
+    int use_stagger = is_pow2(nfull) ? 1 : 0;
     if (stagger == 0) use_stagger = 0;
     if (stagger == 1) {
-        if (!is_pow2(nkt)) return SDT_ERR_UNSUPPORTED;
+        if (!is_pow2(nfull)) return SDT_ERR_UNSUPPORTED;
         use_stagger = 1;
     }
     const int64_t gm = ceil_div(M, td.bm);
@@ -165,7 +167,6 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     p.K = (int)K;
     p.gm = (int)gm;
     p.gn = (int)gn;
-    p.nkt = (int)nkt;
     p.stagger = use_stagger;
     p.nxcd = dev.nxcd;
     hipError_t e = launch_gemm(id, p, s);

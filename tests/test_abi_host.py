@@ -179,9 +179,10 @@ def test_stagger_enable_rule_on_k_sweep():
         assert sdt.stagger_auto(K, 64) == (K == 2048)
         assert sdt.stagger_auto(K, 32) == (K == 2048)
     assert sdt.stagger_auto(64, 64) and sdt.stagger_auto(8192, 64)
-    assert not sdt.stagger_auto(0, 64)
-    assert sdt.stagger_auto(65, 64)          # 2 k-tiles
-    assert not sdt.stagger_auto(129, 64)     # 3 k-tiles
+    assert not sdt.stagger_auto(0, 64) and not sdt.stagger_auto(63, 64)   # no full tile
+    assert sdt.stagger_auto(65, 64)          # 1 full k-tile + a partial one
+    assert sdt.stagger_auto(129, 64)         # 2 full k-tiles + a partial one
+    assert not sdt.stagger_auto(192, 64)     # 3 full k-tiles
 
 
 def test_stagger_is_a_permutation():
