@@ -59,6 +59,7 @@ def parse():
                          "buffers) or copy<MB> (a plain device copy, for counter scaling)")
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 auto, 0 off, 1 on")
     return ap.parse_args()
 
 
@@ -78,7 +79,7 @@ def profile_mode(args):
         dB = torch.from_numpy(B).to(dev)
         C = torch.empty((n, n), dtype=torch.float16, device=dev)
         for _ in range(args.launches):
-            sdt.gemm_f16_ex(dA, dB, C, tile_id=args.tile)
+            sdt.gemm_f16_ex(dA, dB, C, tile_id=args.tile, stagger=args.stagger)
     elif name == "gemv":
         x = torch.from_numpy(inputs.decode_activations()).to(dev)
         Ws = [torch.from_numpy(inputs.decode_weights(r)).to(dev)
@@ -245,7 +246,9 @@ def main():
             "peak": round(PEAK_FP16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": counted_traffic("gemm_f16_256x256_8192_counters.md",
+                                       "shape_driven_tile_amd/csrc/gemm_kernel.hpp"),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_launch_us": round(dom_avg_us, 2),
         },
         "decode": {
@@ -264,6 +267,23 @@ def main():
         result["cpu_baseline"] = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def counted_traffic(profile: str, source: str):
+    """HBM bytes per launch from a committed counter summary under profiles/
+    (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the kernel source has
+    changed since the counters were taken."""
+    import hashlib
+    try:
+        text = open(os.path.join(ROOT, "profiles", profile)).read()
+        src = open(os.path.join(ROOT, source), "rb").read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines()
+                  if line.startswith(("kernel_source_sha256_16: ", "traffic_bytes_per_launch: ")))
+    if fields.get("kernel_source_sha256_16") != hashlib.sha256(src).hexdigest()[:16]:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
 
 
 def _ranges(vals):
@@ -320,7 +340,8 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             det["k_sweep"][f"{K}_{name}"] = {
                 "us": _ranges(us),
                 "tflops_median": round(2.0 * 2048 * 2048 * K / (med * 1e-6) / 1e12, 1),
-                "stagger": bool(sdt.stagger_auto(K)) if st == -1 else bool(st),
+                "stagger": (bool(sdt.stagger_auto(2048, 2048, K, sdt.pick_tile(2048, 2048, K, 0)["id"], 0))
+                            if st == -1 else bool(st)),
             }
     # Cold-cache decode: 8 rotating 100.7 MB weight buffers (805 MB >> 256 MB
     # Infinity Cache), ~1 s warm-up, 200 launches x 10 repeats.

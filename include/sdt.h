@@ -68,8 +68,8 @@ typedef struct sdt_tile {
  * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
  * definition).  The tile is chosen by sdt_pick_tile from the device's CU
- * count; the k-tile stagger is enabled exactly when the count of full
- * 64-deep k-tiles is a power of two (FlyDSL PR, Changes: stagger). */
+ * count; the k-tile stagger is chosen by sdt_stagger_auto (FlyDSL PR,
+ * Changes: stagger). */
 int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
              const void* B, int64_t ldb,
@@ -124,10 +124,13 @@ int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 
-/* Host-only: 1 if the k-loop stagger is used for K with k-tile depth bk,
- * i.e. the number of full k-tiles floor(K/bk) is a power of two (a partial
- * last k-tile, if any, is always visited last), else 0. */
-int sdt_stagger_auto(int64_t K, int bk);
+/* Host-only: 1 if gemm_f16 staggers the k-loop of an M x N x K product run
+ * with ladder tile tile_id on num_cu CUs (num_cu <= 0: 256), else 0.  The
+ * stagger needs the number of full 64-deep k-tiles floor(K/64) to be a power
+ * of two (the wrap-around is a mask; FlyDSL PR, Changes) and, on MI355X, a
+ * grid of at most num_cu workgroups: with more, staggering workgroups that
+ * share operand rows through one XCD's L2 multiplies the HBM traffic. */
+int sdt_stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu);
 
 /* Host-only: the k-tile visited at step i by workgroup wg when staggered:
  * (wg + i) & (nkt - 1); nkt must be a power of two (else -1). */

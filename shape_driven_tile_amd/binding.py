@@ -69,7 +69,7 @@ def lib():
     L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
     L.sdt_num_tiles.argtypes = []
     L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
-    L.sdt_stagger_auto.argtypes = [_i64, _int]
+    L.sdt_stagger_auto.argtypes = [_i64, _i64, _i64, _int, _int]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
     L.sdt_check_gemm_args.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
@@ -120,8 +120,8 @@ def pick_rung(M: int, N: int, ref_bm: int, ref_bn: int, min_blocks) -> int:
     return int(lib().sdt_pick_rung(int(M), int(N), int(ref_bm), int(ref_bn), len(min_blocks), arr))
 
 
-def stagger_auto(K: int, bk: int = 64) -> bool:
-    return bool(lib().sdt_stagger_auto(int(K), int(bk)))
+def stagger_auto(M: int, N: int, K: int, tile_id: int, num_cu: int = 256) -> bool:
+    return bool(lib().sdt_stagger_auto(int(M), int(N), int(K), int(tile_id), int(num_cu)))
 
 
 def stagger_ktile(wg: int, i: int, nkt: int) -> int:

@@ -7,9 +7,15 @@
 // contiguous data per thread (v3) and by a kernel specialised for one row of
 // activations instead of staging eight (v4).  Here the weights are K-major,
 // so each output column is one contiguous run of K fp16:
-//   * one wave owns RPW consecutive columns; for each, its 64 lanes issue
-//     16-byte loads at consecutive addresses (1 KB per instruction), all
-//     RPW * XCH loads of a pass in flight before any arithmetic;
+//   * one wave owns RPW consecutive columns (one, by default: 12288 waves
+//     for the decode shape, every one streaming 8 KB); for each column its 64
+//     lanes issue 16-byte loads at consecutive addresses (1 KB per
+//     instruction), all RPW * XCH loads of a pass in flight before any
+//     arithmetic;
+//   * a pass that lies wholly below K (uniform across the wave) uses plain
+//     loads with no per-lane bounds test -- a per-chunk test is a divergent
+//     branch around every load and cost about a tenth of the bandwidth --
+//     and only a ragged last pass masks element by element;
 //   * the activations stay in registers (XCH chunks of 8 per lane, i.e. K up
 //     to XCH * 512 per pass);
 //   * products go through v_dot2_f32_f16 into fp32; one cross-lane reduction
@@ -81,17 +87,36 @@ __global__ __launch_bounds__(256) void gemv_f16_m1_kernel(GemvParams p) {
     for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
 
     for (int kb = 0; kb < p.K; kb += KP) {
-        int4_t wv[RPW][XCH];
-#pragma unroll
-        for (int r = 0; r < RPW; ++r) {
-            const int64_t n = min(n0 + r, (int64_t)p.N - 1);   // clamped rows are discarded
-            const uint16_t* row = p.B + n * p.ldb;
-#pragma unroll
-            for (int j = 0; j < XCH; ++j) wv[r][j] = gemv_chunk(row, kb + (lane + 64 * j) * 8, p.K, true);
-        }
         int4_t xr[XCH];
+        int4_t wv[RPW][XCH];
+        if (kb + KP <= p.K) {
+            // the whole pass lies below K (uniform across the wave): plain
+            // 16-byte loads, activations first (cached), then the weights
 #pragma unroll
-        for (int j = 0; j < XCH; ++j) xr[j] = gemv_chunk(p.x, kb + (lane + 64 * j) * 8, p.K, false);
+            for (int j = 0; j < XCH; ++j)
+                xr[j] = *reinterpret_cast<const int4_t*>(p.x + kb + (lane + 64 * j) * 8);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int64_t n = min(n0 + r, (int64_t)p.N - 1);   // clamped rows are discarded
+                const uint16_t* row = p.B + n * p.ldb + kb;
+#pragma unroll
+                for (int j = 0; j < XCH; ++j)
+                    wv[r][j] = __builtin_nontemporal_load(
+                        reinterpret_cast<const int4_t*>(row + (lane + 64 * j) * 8));
+            }
+        } else {
+            // the ragged last pass: element-exact masking, nothing past K read
+#pragma unroll
+            for (int j = 0; j < XCH; ++j) xr[j] = gemv_chunk(p.x, kb + (lane + 64 * j) * 8, p.K, false);
+#pragma unroll
+            for (int r = 0; r < RPW; ++r) {
+                const int64_t n = min(n0 + r, (int64_t)p.N - 1);
+                const uint16_t* row = p.B + n * p.ldb;
+#pragma unroll
+                for (int j = 0; j < XCH; ++j)
+                    wv[r][j] = gemv_chunk(row, kb + (lane + 64 * j) * 8, p.K, true);
+            }
+        }
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll

@@ -53,6 +53,20 @@ int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     return pick_rung(M, N, 64, 64, kNumTiles, thresholds);
 }
 
+// FlyDSL PR, Changes: the k-loop stagger is wired up only when the k-tile
+// count is a power of two (the wrap-around is a mask).  On MI355X the tile
+// order is XCD-grouped so that workgroups sharing A or B rows read them out
+// of one L2 at about the same time; staggering those workgroups multiplies
+// the HBM traffic once the grid runs in several waves, so the stagger is
+// also limited to grids that are resident all at once.
+bool stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu) {
+    if (K < kBK || tile_id < 0 || tile_id >= kNumTiles) return false;
+    if (!is_pow2(K / kBK)) return false;
+    if (num_cu <= 0) num_cu = 256;
+    const int64_t wgs = ceil_div(M, kLadder[tile_id].bm) * ceil_div(N, kLadder[tile_id].bn);
+    return wgs <= num_cu;
+}
+
 static bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
@@ -92,9 +106,9 @@ extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
     return SDT_OK;
 }
 
-extern "C" int sdt_stagger_auto(int64_t K, int bk) {
-    if (K <= 0 || bk <= 0) return 0;
-    return sdt::is_pow2(K / bk) ? 1 : 0;
+extern "C" int sdt_stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu) {
+    if (M < 0 || N < 0 || K < 0) return 0;
+    return sdt::stagger_auto(M, N, K, tile_id, num_cu) ? 1 : 0;
 }
 
 // FlyDSL PR, Changes: each workgroup starts at its own k-tile and wraps with

@@ -173,16 +173,24 @@ def test_pick_tile_properties():
 # ---- k-loop stagger -----------------------------------------------------------
 
 def test_stagger_enable_rule_on_k_sweep():
-    """On the K sweep only K=2048 has a power-of-two k-tile count (FlyDSL PR,
-    Motivation: the stagger is wired up exactly then)."""
+    """On the K sweep (M=N=2048, one 128x128 tile per CU) only K=2048 has a
+    power-of-two k-tile count (FlyDSL PR, Motivation: the stagger is wired up
+    exactly then)."""
+    t = sdt.pick_tile(2048, 2048, 2048, 256)["id"]
     for K in (1920, 1984, 2048, 2112, 2176, 2304):
-        assert sdt.stagger_auto(K, 64) == (K == 2048)
-        assert sdt.stagger_auto(K, 32) == (K == 2048)
-    assert sdt.stagger_auto(64, 64) and sdt.stagger_auto(8192, 64)
-    assert not sdt.stagger_auto(0, 64) and not sdt.stagger_auto(63, 64)   # no full tile
-    assert sdt.stagger_auto(65, 64)          # 1 full k-tile + a partial one
-    assert sdt.stagger_auto(129, 64)         # 2 full k-tiles + a partial one
-    assert not sdt.stagger_auto(192, 64)     # 3 full k-tiles
+        assert sdt.stagger_auto(2048, 2048, K, t, 256) == (K == 2048), K
+
+
+def test_stagger_rule_details():
+    t0 = 0   # the largest rung
+    assert not sdt.stagger_auto(256, 256, 0, t0) and not sdt.stagger_auto(256, 256, 63, t0)
+    assert sdt.stagger_auto(256, 256, 65, t0)           # 1 full k-tile + a partial one
+    assert sdt.stagger_auto(256, 256, 129, t0)          # 2 full k-tiles + a partial one
+    assert not sdt.stagger_auto(256, 256, 192, t0)      # 3 full k-tiles
+    # a grid that needs several waves of workgroups keeps the L2-friendly order
+    assert sdt.stagger_auto(4096, 4096, 8192, t0, 256)      # 256 workgroups
+    assert not sdt.stagger_auto(8192, 8192, 8192, t0, 256)  # 1024 workgroups
+    assert sdt.stagger_auto(8192, 8192, 8192, t0, 1024)
 
 
 def test_stagger_is_a_permutation():
