@@ -59,7 +59,7 @@ def parse():
                          "buffers) or copy<MB> (a plain device copy, for counter scaling)")
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--tile", type=int, default=-1)
-    ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 auto, 0 off, 1 on")
+    ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 default (off), 0 off, 1 on")
     return ap.parse_args()
 
 
@@ -323,14 +323,15 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             "tile": sdt.pick_tile(n, n, n, 0)["id"],
         }
         log(f"square {n}: median {med:.2f} us {det['square'][str(n)]['tflops_median']} TFLOP/s")
-    # K sweep at M=N=2048: automatic arm, plus the stagger-off arm at K=2048
+    # K sweep at M=N=2048: the default arm (plain k order) at every K, plus
+    # the forced stagger at K=2048, the one K whose k-tile count allows it
     for K in inputs.K_SWEEP_K:
         A, B = inputs.square_operands(inputs.K_SWEEP_MN, 3, k=K)
         dA, dB = dev_tensor(A), dev_tensor(B)
         C = torch.empty((2048, 2048), dtype=torch.float16, device=dev)
         arms = {"auto": (-1, -1)}
         if K == 2048:
-            arms["stagger_off"] = (-1, 0)
+            arms["stagger_on"] = (-1, 1)
         for name, (tile, st) in arms.items():
             f = (lambda j, tile=tile, st=st: sdt.gemm_f16_ex(dA, dB, C, tile_id=tile, stagger=st))
             for j in range(50):
@@ -340,8 +341,8 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             det["k_sweep"][f"{K}_{name}"] = {
                 "us": _ranges(us),
                 "tflops_median": round(2.0 * 2048 * 2048 * K / (med * 1e-6) / 1e12, 1),
-                "stagger": (bool(sdt.stagger_auto(2048, 2048, K, sdt.pick_tile(2048, 2048, K, 0)["id"], 0))
-                            if st == -1 else bool(st)),
+                "stagger": st == 1,
+                "tile": sdt.pick_tile(2048, 2048, K, 0)["id"],
             }
     # Cold-cache decode: 8 rotating 100.7 MB weight buffers (805 MB >> 256 MB
     # Infinity Cache), ~1 s warm-up, 200 launches x 10 repeats.

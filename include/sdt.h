@@ -55,7 +55,8 @@ typedef struct sdt_tile {
     int bm, bn, bk;
     int waves_m, waves_n;
     int threads;     /* 64 * waves_m * waves_n */
-    int lds_bytes;   /* two LDS stages of (bm + bn) x bk fp16 */
+    int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep */
+    int lds_bytes;   /* stages x (bm + bn) x bk fp16 */
 } sdt_tile;
 
 /* ---- main entry points ---------------------------------------------------- */
@@ -68,8 +69,9 @@ typedef struct sdt_tile {
  * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
  * definition).  The tile is chosen by sdt_pick_tile from the device's CU
- * count; the k-tile stagger is chosen by sdt_stagger_auto (FlyDSL PR,
- * Changes: stagger). */
+ * count.  The k-loop runs in plain k order: the k-tile stagger of the
+ * FlyDSL PR is available through gemm_f16_ex but measured no faster on
+ * MI355X (sdt_stagger_eligible). */
 int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
              const void* B, int64_t ldb,
@@ -88,9 +90,8 @@ int gemv_f16_m1(int64_t N, int64_t K, const void* x,
 
 /* gemm_f16 with the launcher's choices forced.  tile_id: -1 = automatic,
  * else a ladder index (SDT_ERR_INVALID_ARG if out of range).  stagger: -1 =
- * automatic (on iff the k-tile count is a power of two), 0 = off, 1 = on
- * (SDT_ERR_UNSUPPORTED when the k-tile count is not a power of two, since the
- * wrap-around is a mask).  M == 1 is not rerouted to the GEMV here. */
+ * what gemm_f16 does (off), 0 = off, 1 = on (SDT_ERR_UNSUPPORTED unless
+ * sdt_stagger_eligible(K)).  M == 1 is not rerouted to the GEMV here. */
 int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 const void* A, int64_t lda,
                 const void* B, int64_t ldb,
@@ -124,13 +125,14 @@ int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 
-/* Host-only: 1 if gemm_f16 staggers the k-loop of an M x N x K product run
- * with ladder tile tile_id on num_cu CUs (num_cu <= 0: 256), else 0.  The
- * stagger needs the number of full 64-deep k-tiles floor(K/64) to be a power
- * of two (the wrap-around is a mask; FlyDSL PR, Changes) and, on MI355X, a
- * grid of at most num_cu workgroups: with more, staggering workgroups that
- * share operand rows through one XCD's L2 multiplies the HBM traffic. */
-int sdt_stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu);
+/* Host-only: 1 if the k-loop of a product with inner size K can be staggered,
+ * else 0: the number of full 64-deep k-tiles floor(K/64) must be a power of
+ * two, since the wrap-around is a mask (FlyDSL PR, Changes; the PR enables
+ * the stagger exactly then).  gemm_f16 does not stagger by itself on MI355X:
+ * measured against plain k order it gains at most 2% (1536x1536x4096) and
+ * loses up to 53% (2048x2048x8192), since workgroups that share operand rows
+ * through one XCD's L2 stop reading the same k-tile at the same time. */
+int sdt_stagger_eligible(int64_t K);
 
 /* Host-only: the k-tile visited at step i by workgroup wg when staggered:
  * (wg + i) & (nkt - 1); nkt must be a power of two (else -1). */

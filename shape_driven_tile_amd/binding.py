@@ -23,7 +23,7 @@ SDT_ERR_HIP = 3
 EXPORTS = (
     "gemm_f16", "gemv_f16_m1", "gemm_f16_ex", "gemv_f16_m1_ex", "sdt_gemv_num_variants",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
-    "sdt_stagger_auto", "sdt_stagger_ktile", "sdt_check_gemm_args",
+    "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
     "sdt_status_string", "sdt_last_hip_error",
 )
 
@@ -31,7 +31,8 @@ EXPORTS = (
 class SdtTile(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
                 ("bk", ctypes.c_int), ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
-                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int)]
+                ("threads", ctypes.c_int), ("stages", ctypes.c_int),
+                ("lds_bytes", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -69,7 +70,7 @@ def lib():
     L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
     L.sdt_num_tiles.argtypes = []
     L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
-    L.sdt_stagger_auto.argtypes = [_i64, _i64, _i64, _int, _int]
+    L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
     L.sdt_check_gemm_args.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64]
@@ -78,7 +79,7 @@ def lib():
     L.sdt_last_hip_error.argtypes = []
     for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
-                 "sdt_tile_info", "sdt_stagger_auto", "sdt_check_gemm_args",
+                 "sdt_tile_info", "sdt_stagger_eligible", "sdt_check_gemm_args",
                  "sdt_last_hip_error"):
         getattr(L, name).restype = _int
     _lib = L
@@ -120,8 +121,8 @@ def pick_rung(M: int, N: int, ref_bm: int, ref_bn: int, min_blocks) -> int:
     return int(lib().sdt_pick_rung(int(M), int(N), int(ref_bm), int(ref_bn), len(min_blocks), arr))
 
 
-def stagger_auto(M: int, N: int, K: int, tile_id: int, num_cu: int = 256) -> bool:
-    return bool(lib().sdt_stagger_auto(int(M), int(N), int(K), int(tile_id), int(num_cu)))
+def stagger_eligible(K: int) -> bool:
+    return bool(lib().sdt_stagger_eligible(int(K)))
 
 
 def stagger_ktile(wg: int, i: int, nkt: int) -> int:

@@ -16,9 +16,11 @@
 //   * global -> LDS without registers: buffer_load_dwordx4 ... lds writes a
 //     wave's 64 lanes to 1 KB of consecutive LDS, so each lane fetches the
 //     global chunk that belongs at its swizzled LDS slot;
-//   * two LDS stages: while tile i is multiplied out of one stage, tile i+1 is
-//     landing in the other; right after the single barrier of step i the
-//     loads of tile i+2 are issued into the stage tile i just freed;
+//   * NS LDS stages (a compile-time parameter of the rung: as many as fit):
+//     while tile i is multiplied out of its stage, tiles i+1 .. i+NS-1 are
+//     landing in the others; right after the single barrier of step i the
+//     loads of tile i+NS are issued into the stage tile i just freed, so the
+//     global prefetch runs NS-1 tiles deep;
 //   * MFMA fragments are double-buffered in registers across the four 16-deep
 //     sub-steps of a k-tile, so the LDS reads of sub-step kk+1 are in flight
 //     under the MFMAs of sub-step kk, and the first reads of tile i+1 go out
@@ -113,10 +115,16 @@ __device__ __forceinline__ int4_t load16_tail(__amdgpu_buffer_rsrc_t r, uint32_t
     return v;
 }
 
-// s_waitcnt vmcnt(0), leaving the LDS and export counters alone.
-__device__ __forceinline__ void wait_global_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N) (at most N global loads of this wave still in flight),
+// leaving the LDS and export counters alone.  gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int N>
+__device__ __forceinline__ void wait_global_loads() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     constexpr int BK = kBK;
     constexpr int NW = WM * WN;
@@ -129,8 +137,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
     static_assert(A_UNITS % (64 * NW) == 0 && B_UNITS % (64 * NW) == 0,
                   "each wave loads whole 8-row slabs");
+    static_assert(NS >= 2 && NS * STAGE * 16 <= 160 * 1024, "stages must fit the LDS");
+    constexpr int L = A_DMA + B_DMA;   // global loads per wave per k-tile
 
-    __shared__ int4_t smem[2 * STAGE];
+    __shared__ int4_t smem[NS * STAGE];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -262,21 +272,26 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     using Loads = std::integral_constant<int, A_DMA + B_DMA>;
     using None = std::integral_constant<int, 0>;
 
-    // ---- prologue: tile 0 landed in stage 0, tile 1 on its way to stage 1 ------
-    load_step(0, 0);
-    wait_global_loads();
+    // ---- prologue: tiles 0 .. NS-1 issued, tile 0 landed ------------------------
+    const int npro = min(nseq, NS);
+    for (int j = 0; j < npro; ++j) load_step(j, j);
+    if (nseq > NS)
+        wait_global_loads<(NS - 1) * L>();   // all NS prologue tiles are full ones
+    else
+        wait_global_loads<0>();
     __syncthreads();
-    if (nseq > 1) load_step(1, 1);
     read_frags(0, 0, 0);
 
     // ---- steady state: one basic block per k-tile ----------------------------------
     // (A) kk1 reads under kk0 MFMAs, (B) kk2 reads under kk1, (C) kk3 reads
-    // under kk2; then tile i+1 must have landed and every wave must be done
-    // with stage s: wait, barrier; (D) tile i+2's loads into stage s and the
-    // next stage's kk0 reads under the kk3 MFMAs.
+    // under kk2; then tile i+1 must have landed (at most NS-2 younger tiles of
+    // this wave still in flight) and every wave must be done with stage s:
+    // wait, barrier; (D) tile i+NS's loads into stage s and the next stage's
+    // kk0 reads under the kk3 MFMAs.
     int i = 0;
-    for (; i + 2 < nfull; ++i) {
-        const int s = i & 1;
+    int s = 0;                               // stage of tile i
+    for (; i + NS < nfull; ++i) {
+        const int sn = (s + 1 == NS) ? 0 : s + 1;
         read_frags(s, 1, 1);
         mfmas(0);
         interleave(Reads{}, None{});
@@ -289,28 +304,30 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
         mfmas(0);
         interleave(Reads{}, None{});
         __builtin_amdgcn_sched_barrier(0);
-        wait_global_loads();
+        wait_global_loads<(NS - 2) * L>();
         __syncthreads();
-        dma_tile(i + 2, s);
-        read_frags(s ^ 1, 0, 0);
+        dma_tile(i + NS, s);
+        read_frags(sn, 0, 0);
         mfmas(1);
         interleave(Reads{}, Loads{});
         __builtin_amdgcn_sched_barrier(0);
+        s = sn;
     }
-    // ---- the last (at most two) steps, and the partial tile, if any -----------------
+    // ---- the last steps (every condition spelled out, full waits) -------------------
     for (; i < nseq; ++i) {
-        const int s = i & 1;
+        const int sn = (s + 1 == NS) ? 0 : s + 1;
         read_frags(s, 1, 1);
         mfmas(0);
         read_frags(s, 2, 0);
         mfmas(1);
         read_frags(s, 3, 1);
         mfmas(0);
-        wait_global_loads();
+        wait_global_loads<0>();
         __syncthreads();
-        if (i + 2 < nseq) load_step(i + 2, s);
-        if (i + 1 < nseq) read_frags(s ^ 1, 0, 0);
+        if (i + NS < nseq) load_step(i + NS, s);
+        if (i + 1 < nseq) read_frags(sn, 0, 0);
         mfmas(1);
+        s = sn;
     }
 
     // ---- epilogue: fp32 -> fp16 (RNE), masked 8-byte stores ------------------------

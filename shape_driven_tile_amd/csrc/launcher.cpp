@@ -19,7 +19,8 @@ sdt_tile describe(int id) {
     t.waves_m = d.waves_m;
     t.waves_n = d.waves_n;
     t.threads = 64 * d.waves_m * d.waves_n;
-    t.lds_bytes = 2 * (d.bm + d.bn) * kBK * 2;
+    t.stages = d.stages;
+    t.lds_bytes = d.stages * (d.bm + d.bn) * kBK * 2;
     return t;
 }
 
@@ -37,35 +38,32 @@ int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
     return rungs - 1;
 }
 
-// MI355X rule.  Blocks are counted in units of the smallest rung (64x64), so
-// a rung of area a*64*64 produces blocks/a workgroups on a shape its tile
-// divides.  A rung qualifies when it still hands every CU at least
-// kFill[r] workgroups' worth of 64x64 blocks scaled by its area: the largest
-// tile that still fills the machine wins, as in the pages' ladder.
+// MI355X rule, in the pages' form (thresholds on the count of reference-
+// sized blocks, largest tile first).  Blocks are counted in units of the
+// smallest rung (64x64), so a rung of area a*64*64 yields blocks/a
+// workgroups on a shape its tile divides.  A rung qualifies once it yields
+// more workgroups than half the CUs: on MI355X a large tile does about twice
+// the work per CU of the next smaller ones (fewer L2 and LDS bytes per
+// MFMA), so it stays ahead while it occupies over half the machine.  Fitted to
+// a sweep of every rung over square shapes 256..8192 at 256 CUs; the larger
+// rung is picked at 3072 (144 WGs of 256x256), 2560 (200 WGs of 256x128) and
+// 1536 (144 WGs of 128x128), and the smaller at 2560 / 2048 / 1024, where the
+// larger would leave half the CUs or more idle.
 int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     if (num_cu <= 0) num_cu = 256;
     int64_t thresholds[kNumTiles];
     for (int r = 0; r < kNumTiles; ++r) {
         const int64_t area = int64_t(kLadder[r].bm / 64) * (kLadder[r].bn / 64);
-        thresholds[r] = area * num_cu;
+        thresholds[r] = area * (num_cu / 2 + 1);
     }
     thresholds[kNumTiles - 1] = 0;
     return pick_rung(M, N, 64, 64, kNumTiles, thresholds);
 }
 
-// FlyDSL PR, Changes: the k-loop stagger is wired up only when the k-tile
-// count is a power of two (the wrap-around is a mask).  On MI355X the tile
-// order is XCD-grouped so that workgroups sharing A or B rows read them out
-// of one L2 at about the same time; staggering those workgroups multiplies
-// the HBM traffic once the grid runs in several waves, so the stagger is
-// also limited to grids that are resident all at once.
-bool stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu) {
-    if (K < kBK || tile_id < 0 || tile_id >= kNumTiles) return false;
-    if (!is_pow2(K / kBK)) return false;
-    if (num_cu <= 0) num_cu = 256;
-    const int64_t wgs = ceil_div(M, kLadder[tile_id].bm) * ceil_div(N, kLadder[tile_id].bn);
-    return wgs <= num_cu;
-}
+// FlyDSL PR, Changes: the k-loop stagger wraps with a mask over the full
+// k-tiles, so it exists only when their count is a power of two (a partial
+// last tile always runs last, outside the wrap).
+bool stagger_eligible(int64_t K) { return K >= kBK && is_pow2(K / kBK); }
 
 static bool aligned16(const void* p) {
     return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
@@ -106,10 +104,7 @@ extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
     return SDT_OK;
 }
 
-extern "C" int sdt_stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu) {
-    if (M < 0 || N < 0 || K < 0) return 0;
-    return sdt::stagger_auto(M, N, K, tile_id, num_cu) ? 1 : 0;
-}
+extern "C" int sdt_stagger_eligible(int64_t K) { return sdt::stagger_eligible(K) ? 1 : 0; }
 
 // FlyDSL PR, Changes: each workgroup starts at its own k-tile and wraps with
 // a mask, one add and one and per trip.

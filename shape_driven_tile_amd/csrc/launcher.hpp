@@ -14,17 +14,23 @@ constexpr int kBK = 64;
 
 // A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
 // each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
+// `stages` LDS stages of (bm + bn) x 64 fp16 each: the global prefetch runs
+// stages - 1 k-tiles deep.  Per rung, the count is the one that measured
+// fastest on MI355X across square shapes 256..8192: a third stage pays on the
+// mid-size tiles, whose grids are resident at once and wait on latency
+// (128x64 at 1280^3: 10.4 us with 3 stages, 13.2 us with 2); 64x64, on
+// grids of at most 16 k-tiles, is fastest with 2.
 struct TileDesc {
-    int bm, bn, waves_m, waves_n;
+    int bm, bn, waves_m, waves_n, stages;
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4},  // 8 waves, 128x64 per wave
-    {256, 128, 2, 2},  // 4 waves, 128x64 per wave
-    {128, 128, 2, 2},  // 4 waves, 64x64 per wave
-    {128, 64, 2, 2},   // 4 waves, 64x32 per wave
-    {64, 64, 2, 2},    // 4 waves, 32x32 per wave
+    {256, 256, 2, 4, 2},  // 8 waves, 128x64 per wave, 2 x 64 KB LDS
+    {256, 128, 2, 2, 3},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3},   // 4 waves, 64x32 per wave, 3 x 24 KB
+    {64, 64, 2, 2, 2},    // 4 waves, 32x32 per wave, 2 x 16 KB
 };
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 
@@ -36,7 +42,7 @@ sdt_tile describe(int id);
 int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks);
 int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);
-bool stagger_auto(int64_t M, int64_t N, int64_t K, int tile_id, int num_cu);
+bool stagger_eligible(int64_t K);
 bool is_pow2(int64_t v);
 int64_t ceil_div(int64_t a, int64_t b);
 int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

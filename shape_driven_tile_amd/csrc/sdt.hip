@@ -53,17 +53,17 @@ int device_info(DeviceInfo* out) {
     return SDT_OK;
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_f16_kernel<BM, BN, WM, WN>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_f16_kernel<BM, BN, WM, WN, NS>),
                            dim3(p.gm * p.gn), dim3(WM * WN * 64), args, 0, stream);
 }
 
 template <int I>
 hipError_t launch_rung(GemmParams p, hipStream_t s) {
     return launch_gemm_tile<kLadder[I].bm, kLadder[I].bn, kLadder[I].waves_m,
-                            kLadder[I].waves_n>(p, s);
+                            kLadder[I].waves_n, kLadder[I].stages>(p, s);
 }
 
 hipError_t launch_gemm(int id, GemmParams p, hipStream_t s) {
@@ -132,6 +132,10 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (st != SDT_OK) return st;
     if (tile_id < -1 || tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
     if (stagger < -1 || stagger > 1) return SDT_ERR_INVALID_ARG;
+    // Plain k order unless a caller forces the stagger (see
+    // sdt_stagger_eligible for why it is not used by default).
+    if (stagger == 1 && !stagger_eligible(K)) return SDT_ERR_UNSUPPORTED;
+    const int use_stagger = stagger == 1 ? 1 : 0;
     if (M == 0 || N == 0) return SDT_OK;
     if (M > INT_MAX || N > INT_MAX) return SDT_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -144,15 +148,6 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
 
     const int id = tile_id >= 0 ? tile_id : pick_tile(M, N, K, dev.num_cu);
     const TileDesc& td = kLadder[id];
-    // The stagger wraps with a mask over the full k-tiles, so it needs their
-    // count to be a power of two (a partial last tile always comes last).
-    const int64_t nfull = K / kBK;
-    int use_stagger = stagger_auto(M, N, K, id, dev.num_cu) ? 1 : 0;
-    if (stagger == 0) use_stagger = 0;
-    if (stagger == 1) {
-        if (!is_pow2(nfull)) return SDT_ERR_UNSUPPORTED;
-        use_stagger = 1;
-    }
     const int64_t gm = ceil_div(M, td.bm);
     const int64_t gn = ceil_div(N, td.bn);
     if (gm * gn > INT_MAX) return SDT_ERR_UNSUPPORTED;

@@ -1,0 +1,137 @@
+"""Sweep every ladder rung over a list of GEMM shapes on the current GPU.
+
+The FlyDSL pull request "Speed up the RDNA3 GEMM up to 1.85x by choosing the
+tile from the shape" fits its pick_tile heuristic to a sweep of every feasible
+tile over a set of shapes (Changes); this is that sweep for this library's
+ladder, used to set and check the MI355X rule in launcher.cpp.
+
+Each (shape, rung) is timed as a captured HIP graph of `--chain` dependent
+launches (graph edges serialize them and no host launch cost is counted),
+replayed `--repeats` times back to back; one more replay into a cleared C is
+compared bit for bit with an eager launch of the same rung.
+
+    python -m shape_driven_tile_amd.sweep [--shapes 512,1024,...] [--out file.json]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+
+DEFAULT_SQUARES = (256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072, 3584, 4096,
+                   6144, 8192)
+
+
+def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats):
+    """Median microseconds per launch of rung `tile` over `repeats` back-to-back
+    graph replays, all of them, and whether a replay into a cleared C
+    reproduced the eager result bit for bit."""
+    sdt.gemm_f16_ex(A, B, C, tile_id=tile, stagger=stagger)
+    torch.cuda.synchronize()
+    eager = C.clone()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(chain):
+                sdt.gemm_f16_ex(A, B, C, tile_id=tile, stagger=stagger)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 0.05      # ~50 ms of replays to settle the clocks
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(repeats)]
+    for e0, e1 in ev:
+        e0.record()
+        g.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    per_launch = sorted(1e3 * e0.elapsed_time(e1) / chain for e0, e1 in ev)
+    C.zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(C.view(torch.int16), eager.view(torch.int16)))
+    return per_launch[len(per_launch) // 2], per_launch, same
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--shapes", default=None,
+                    help="comma list of M=N=K squares, or MxNxK entries")
+    ap.add_argument("--repeats", type=int, default=7)
+    ap.add_argument("--out", default=None)
+    args = ap.parse_args(argv)
+
+    import torch
+
+    from shape_driven_tile_amd import binding as sdt
+    from shape_driven_tile_amd import inputs
+
+    dev = torch.device("cuda:0")
+    num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    shapes = []
+    for tok in (args.shapes.split(",") if args.shapes else [str(n) for n in DEFAULT_SQUARES]):
+        if "x" in tok:
+            m, n, k = (int(v) for v in tok.split("x"))
+        else:
+            m = n = k = int(tok)
+        shapes.append((m, n, k))
+
+    # warm the clocks
+    wa, wb = inputs.square_operands(4096, 2)
+    WA = torch.from_numpy(wa).to(dev)
+    WB = torch.from_numpy(wb).to(dev)
+    WC = torch.empty((4096, 4096), dtype=torch.float16, device=dev)
+    for _ in range(200):
+        sdt.gemm_f16_ex(WA, WB, WC)
+    torch.cuda.synchronize()
+
+    results = []
+    for (M, N, K) in shapes:
+        A = torch.from_numpy(inputs.uniform_f16((M, K), 11)).to(dev)
+        B = torch.from_numpy(inputs.uniform_f16((N, K), 12)).to(dev)
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        flop = 2.0 * M * N * K
+        chain = max(4, min(400, int(2e12 / max(flop, 1.0))))
+        auto = sdt.pick_tile(M, N, K, num_cu)["id"]
+        row = {"M": M, "N": N, "K": K, "auto_tile": auto, "rungs": {}}
+        for tile in range(sdt.num_tiles()):
+            med, allv, same = time_rung(sdt, torch, A, B, C, tile, -1, chain, args.repeats)
+            row["rungs"][tile] = {"us": round(med, 3), "tflops": round(flop / med / 1e6, 1),
+                                  "min_us": round(allv[0], 3), "max_us": round(allv[-1], 3),
+                                  "replays_match_eager": same}
+        if sdt.stagger_eligible(K):
+            row["stagger_arms"] = {}
+            for st in (0, 1):
+                med, allv, same = time_rung(sdt, torch, A, B, C, auto, st, chain, args.repeats)
+                row["stagger_arms"][st] = {"us": round(med, 3), "min_us": round(allv[0], 3),
+                                           "max_us": round(allv[-1], 3),
+                                           "replays_match_eager": same}
+        best = min(row["rungs"], key=lambda t: row["rungs"][t]["us"])
+        row["best_tile"] = best
+        results.append(row)
+        cells = "  ".join(f"t{t}:{v['us']:8.2f}" for t, v in row["rungs"].items())
+        print(f"{M}x{N}x{K}: {cells}   best t{best}  auto t{auto}"
+              f"{'' if all(v['replays_match_eager'] for v in row['rungs'].values()) else '  REPLAY MISMATCH'}",
+              flush=True)
+        if "stagger_arms" in row:
+            a = row["stagger_arms"]
+            print(f"    t{auto} stagger off {a[0]['us']:.2f} [{a[0]['min_us']:.2f}, {a[0]['max_us']:.2f}]"
+                  f"  on {a[1]['us']:.2f} [{a[1]['min_us']:.2f}, {a[1]['max_us']:.2f}]"
+                  , flush=True)
+    out = {"num_cu": num_cu, "device": torch.cuda.get_device_properties(dev).name,
+           "ladder": [sdt.tile_info(t) for t in range(sdt.num_tiles())], "shapes": results}
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(out, f, indent=1)
+    ok = all(v["replays_match_eager"] for r in results
+             for v in list(r["rungs"].values()) + list(r.get("stagger_arms", {}).values()))
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

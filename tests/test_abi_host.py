@@ -120,7 +120,8 @@ def test_ladder_is_well_formed():
         assert t["bk"] == 64
         assert t["threads"] == 64 * t["waves_m"] * t["waves_n"]
         assert t["bm"] % (32 * t["waves_m"]) == 0 and t["bn"] % (32 * t["waves_n"]) == 0
-        assert t["lds_bytes"] == 2 * (t["bm"] + t["bn"]) * 64 * 2
+        assert 2 <= t["stages"] <= 4
+        assert t["lds_bytes"] == t["stages"] * (t["bm"] + t["bn"]) * 64 * 2
         assert t["lds_bytes"] <= 160 * 1024, "fits MI355X LDS"
     with pytest.raises(sdt.SdtError):
         sdt.tile_info(len(tiles))
@@ -165,32 +166,63 @@ def test_pick_tile_properties():
             big = tiles[0]
             if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
                 assert t["id"] == 0
+    # the largest rung whose grid, counted in 64x64 blocks scaled by the
+    # rung's area, exceeds half the CUs (exactly its workgroup count when the
+    # tile divides the shape)
+    for num_cu in (80, 256, 304):
+        for n in [64 * i for i in range(1, 200)]:
+            t = sdt.pick_tile(n, n, n, num_cu)
+            blocks = (n // 64) ** 2
+            area = [(r["bm"] // 64) * (r["bn"] // 64) for r in tiles]
+            want = next((i for i, a in enumerate(area[:-1]) if blocks >= a * (num_cu // 2 + 1)),
+                        len(tiles) - 1)
+            assert t["id"] == want, (num_cu, n)
+            if n % 256 == 0:
+                wgs = (n // t["bm"]) * (n // t["bn"])
+                assert t["id"] == len(tiles) - 1 or wgs > num_cu // 2
     # any shape, even degenerate ones, gets a valid rung
     for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
         assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
 
 
+def test_pick_tile_on_mi355x_square_sweep():
+    """The rungs a sweep of every rung over square shapes measured fastest on
+    MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
+    want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
+            1536: (128, 128), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
+            3072: (256, 256), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
+            8192: (256, 256)}
+    for n, (bm, bn) in want.items():
+        t = sdt.pick_tile(n, n, n, 256)
+        assert (t["bm"], t["bn"]) == (bm, bn), n
+    # the K sweep keeps one tile for every K
+    assert len({sdt.pick_tile(2048, 2048, K, 256)["id"]
+                for K in (1920, 1984, 2048, 2112, 2176, 2304)}) == 1
+
+
 # ---- k-loop stagger -----------------------------------------------------------
 
-def test_stagger_enable_rule_on_k_sweep():
-    """On the K sweep (M=N=2048, one 128x128 tile per CU) only K=2048 has a
-    power-of-two k-tile count (FlyDSL PR, Motivation: the stagger is wired up
-    exactly then)."""
-    t = sdt.pick_tile(2048, 2048, 2048, 256)["id"]
+def test_stagger_eligibility_on_k_sweep():
+    """On the K sweep (M=N=2048) only K=2048 has a power-of-two k-tile count,
+    the one K where the FlyDSL PR (Motivation) wires the stagger up."""
     for K in (1920, 1984, 2048, 2112, 2176, 2304):
-        assert sdt.stagger_auto(2048, 2048, K, t, 256) == (K == 2048), K
+        assert sdt.stagger_eligible(K) == (K == 2048), K
 
 
-def test_stagger_rule_details():
-    t0 = 0   # the largest rung
-    assert not sdt.stagger_auto(256, 256, 0, t0) and not sdt.stagger_auto(256, 256, 63, t0)
-    assert sdt.stagger_auto(256, 256, 65, t0)           # 1 full k-tile + a partial one
-    assert sdt.stagger_auto(256, 256, 129, t0)          # 2 full k-tiles + a partial one
-    assert not sdt.stagger_auto(256, 256, 192, t0)      # 3 full k-tiles
-    # a grid that needs several waves of workgroups keeps the L2-friendly order
-    assert sdt.stagger_auto(4096, 4096, 8192, t0, 256)      # 256 workgroups
-    assert not sdt.stagger_auto(8192, 8192, 8192, t0, 256)  # 1024 workgroups
-    assert sdt.stagger_auto(8192, 8192, 8192, t0, 1024)
+def test_stagger_eligibility_details():
+    assert not sdt.stagger_eligible(0) and not sdt.stagger_eligible(63)
+    assert sdt.stagger_eligible(64) and sdt.stagger_eligible(65)  # 1 full k-tile (+ a partial)
+    assert sdt.stagger_eligible(129)                               # 2 full k-tiles + a partial
+    assert not sdt.stagger_eligible(192)                           # 3 full k-tiles
+    assert sdt.stagger_eligible(8192) and not sdt.stagger_eligible(8192 + 64)
+    assert not sdt.stagger_eligible(-64)
+
+
+def test_forced_stagger_needs_eligibility():
+    """gemm_f16_ex(stagger=1) on a K whose k-tile count is not a power of two
+    is rejected before anything is launched (null stream, fake pointers)."""
+    rc = sdt.lib().gemm_f16_ex(256, 256, 192, 4096, 192, 8192, 192, 16384, 256, None, -1, 1)
+    assert rc == sdt.SDT_ERR_UNSUPPORTED
 
 
 def test_stagger_is_a_permutation():
