@@ -306,9 +306,100 @@ def time_launches(torch, fn, launches, repeats=10):
     return out
 
 
+def graph_launches(torch, fn, chain, repeats=10):
+    """Per-launch microseconds of `chain` calls captured in one HIP graph and
+    replayed `repeats` times back to back (graph edges serialize the launches;
+    no host launch cost), after ~50 ms of replays to settle the clocks."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for j in range(chain):
+                fn(j)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    t_end = time.perf_counter() + 0.05
+    while time.perf_counter() < t_end:
+        g.replay()
+        torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(repeats)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    return [1e3 * a.elapsed_time(b) / chain for a, b in ev], g
+
+
+def smi_reading():
+    """GFX clocks (MHz, per XCD), socket power (W) and temperatures from
+    amd-smi, or None where the tool is not available."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["amd-smi", "metric", "-c", "-p", "-t"], capture_output=True,
+                             text=True, timeout=30).stdout
+    except (OSError, subprocess.SubprocessError):
+        return None
+    clocks = []
+    for m in re.finditer(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out):
+        clocks.append(int(m.group(1)))
+    power = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", out)
+    temps = {k.lower(): int(v) for k, v in re.findall(r"(EDGE|HOTSPOT|MEM):\s*(\d+)\s*\S*C", out)}
+    if not clocks and not power:
+        return None
+    return {"gfx_clk_mhz": clocks, "gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1)
+            if clocks else None, "socket_power_w": int(power.group(1)) if power else None,
+            "temperature_c": temps}
+
+
 def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, bytes_gemv,
            bytes_gemv_all):
-    det = {"square": {}, "k_sweep": {}, "decode_cold": {}}
+    det = {"square": {}, "square_graph": {}, "k_sweep": {}, "decode_cold": {}}
+    # launch floor: an empty kernel, eager and graph-replayed
+    e = (lambda j: sdt.empty_kernel())
+    for j in range(200):
+        e(j)
+    eager = time_launches(torch, e, 200)
+    graph, _ = graph_launches(torch, e, 200)
+    det["launch_floor"] = {"eager_us": _ranges(eager), "graph_us": _ranges(graph),
+                           "kernel": "sdt_empty_kernel (1 workgroup, no memory access)"}
+    log(f"launch floor: eager {sorted(eager)[5]:.2f} us, graph {sorted(graph)[5]:.2f} us")
+    # every square size as a graph of back-to-back launches; one more replay
+    # into a cleared C must reproduce the eager result bit for bit
+    for n, (A, B, C) in ops.items():
+        chain = 200 if n <= 2048 else (20 if n == 4096 else 5)
+        sdt.gemm_f16(A, B, C)
+        torch.cuda.synchronize()
+        ref = C.clone()
+        us, g = graph_launches(torch, (lambda j, A=A, B=B, C=C: sdt.gemm_f16(A, B, C)), chain)
+        C.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = bool(torch.equal(C.view(torch.int16), ref.view(torch.int16)))
+        med = sorted(us)[len(us) // 2]
+        det["square_graph"][str(n)] = {
+            "us": _ranges(us), "launches_per_graph": chain,
+            "tflops_median": round(flop_gemm[n] / (med * 1e-6) / 1e12, 1),
+            "peak_frac_median": round(flop_gemm[n] / (med * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+            "replay_matches_eager": same,
+        }
+        log(f"square {n} (graph): median {med:.2f} us {det['square_graph'][str(n)]['tflops_median']}"
+            f" TFLOP/s{'' if same else '  REPLAY MISMATCH'}")
+    # clocks and power while the dominant product runs (~1 s of launches queued)
+    A, B, C = ops[DOMINANT]
+    for _ in range(1100):
+        sdt.gemm_f16(A, B, C)
+    smi = smi_reading()
+    torch.cuda.synchronize()
+    if smi:
+        det["clock_under_load"] = smi
+        if smi.get("gfx_clk_mhz_mean"):
+            ceil = 256 * 4096 * smi["gfx_clk_mhz_mean"] * 1e6 / 1e12
+            det["clock_under_load"]["mfma_ceiling_at_clock_tflops"] = round(ceil, 1)
+        log(f"under load: {smi}")
     for n, (A, B, C) in ops.items():
         launches = 200 if n <= 2048 else (50 if n == 4096 else 20)
         f = (lambda j, A=A, B=B, C=C: sdt.gemm_f16(A, B, C))

@@ -138,6 +138,12 @@ int sdt_stagger_eligible(int64_t K);
  * (wg + i) & (nkt - 1); nkt must be a power of two (else -1). */
 int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt);
 
+/* Measurement: enqueue an empty kernel (one workgroup of 64 lanes, no memory
+ * access) on `stream`.  Timed back to back it gives the launch floor that the
+ * smallest products are compared with (the pages report small shapes next to
+ * such a floor).  Returns SDT_OK or SDT_ERR_HIP. */
+int sdt_empty_kernel(void* stream);
+
 /* Host-only argument check used by gemm_f16 before anything is enqueued.
  * Returns the status gemm_f16 would return for these arguments (SDT_OK when
  * the call would be launched). */

@@ -24,7 +24,7 @@ EXPORTS = (
     "gemm_f16", "gemv_f16_m1", "gemm_f16_ex", "gemv_f16_m1_ex", "sdt_gemv_num_variants",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
-    "sdt_status_string", "sdt_last_hip_error",
+    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel",
 )
 
 
@@ -77,10 +77,11 @@ def lib():
     L.sdt_status_string.argtypes = [_int]
     L.sdt_status_string.restype = ctypes.c_char_p
     L.sdt_last_hip_error.argtypes = []
+    L.sdt_empty_kernel.argtypes = [_vp]
     for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_check_gemm_args",
-                 "sdt_last_hip_error"):
+                 "sdt_last_hip_error", "sdt_empty_kernel"):
         getattr(L, name).restype = _int
     _lib = L
     return L
@@ -204,6 +205,13 @@ def gemv_f16_m1(x, B, y, stream=None, variant: int | None = None) -> None:
         rc = lib().gemv_f16_m1_ex(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h, int(variant))
     if rc != SDT_OK:
         raise SdtError(rc, "gemv_f16_m1")
+
+
+def empty_kernel(stream=None) -> None:
+    """Enqueue the library's empty kernel (launch-floor measurement)."""
+    rc = lib().sdt_empty_kernel(_stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_empty_kernel")
 
 
 def gemm_f16_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream_ptr=None) -> int:
