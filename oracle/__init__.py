@@ -76,6 +76,9 @@ class Oracle:
         lib.sdt_oracle_gemv_m1.argtypes = [_i64, _i64, _u16p, _u16p, _i64, _f64p,
                                            ctypes.c_int]
         lib.sdt_oracle_gemv_m1.restype = ctypes.c_int
+        lib.sdt_oracle_gemv_kn.argtypes = [_i64, _i64, _u16p, _u16p, _i64, _f64p,
+                                           ctypes.c_int]
+        lib.sdt_oracle_gemv_kn.restype = ctypes.c_int
         self.path = path
         self._lib = lib
 
@@ -148,6 +151,22 @@ class Oracle:
             raise ValueError("oracle gemv rejected its arguments")
         return y
 
+    def gemv_kn(self, x, B, N: int | None = None, threads: int = 0) -> np.ndarray:
+        """y = x.B in fp64 with the weights as K rows of ldb >= N elements
+        (B is (K, ldb), the N of one row contiguous)."""
+        xv = _bits(x).reshape(-1)
+        b = _bits(B)
+        K, ldb = b.shape
+        N = ldb if N is None else int(N)
+        if xv.size < K:
+            raise ValueError("x shorter than K")
+        y = np.empty(N, dtype=np.float64)
+        rc = self._lib.sdt_oracle_gemv_kn(N, K, _p(xv, _u16p), _p(b, _u16p), ldb,
+                                          _p(y, _f64p), threads)
+        if rc != 0:
+            raise ValueError("oracle gemv_kn rejected its arguments")
+        return y
+
 
 _default = None
 
@@ -181,6 +200,10 @@ def gemm_sample(A, B, rows, cols, K=None, threads=0):
 
 def gemv_m1(x, B, K=None, threads=0):
     return default().gemv_m1(x, B, K, threads)
+
+
+def gemv_kn(x, B, N=None, threads=0):
+    return default().gemv_kn(x, B, N, threads)
 
 
 def tolerance(c_ref) -> np.ndarray:

@@ -1,6 +1,6 @@
 /*
  * sdt oracle: a plain, slow, obviously correct CPU reference for the fp16
- * GEMM C = A.B and the M=1 GEMV y = x.B.
+ * GEMM C = A.B and the M=1 GEMV y = x.B (weights stored either way round).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
  * load or call this file.  It is used by the test suite, by the smoke check
@@ -191,6 +191,28 @@ int sdt_oracle_gemv_m1(int64_t N, int64_t K, const uint16_t* x,
         const uint16_t* col = B + n * ldb;
         for (int64_t k = 0; k < K; ++k)
             s += g_dec[x[k]] * g_dec[col[k]];
+        y[n] = s;
+    }
+    return 0;
+}
+
+/* y(n) = sum_k dec(x[k]) * dec(B[k*ldb + n]) for n in [0, N): the same decode
+ * product with the weights stored the other way round, K rows of ldb >= N
+ * elements, the N of one row contiguous (the "B-layout" the mojo-baro page
+ * reaches by transposing the weights at load, section "Four rounds on the
+ * decode shape", rounds v1-v3).  Same fp64 ascending-k sum per column. */
+int sdt_oracle_gemv_kn(int64_t N, int64_t K, const uint16_t* x,
+                       const uint16_t* B, int64_t ldb, double* y, int threads)
+{
+    if (N < 0 || K < 0 || (K > 0 && ldb < N))
+        return -1;
+    build_decode_table();
+    int nt = threads > 0 ? threads : omp_get_max_threads();
+    #pragma omp parallel for schedule(static) num_threads(nt)
+    for (int64_t n = 0; n < N; ++n) {
+        double s = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            s += g_dec[x[k]] * g_dec[B[k * ldb + n]];
         y[n] = s;
     }
     return 0;

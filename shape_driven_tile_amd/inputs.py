@@ -76,3 +76,9 @@ def decode_activations(k: int = DECODE_K) -> np.ndarray:
 def decode_weights(r: int, n: int = DECODE_N, k: int = DECODE_K) -> np.ndarray:
     """Rotating weight buffer r, stored as [n][k] (K contiguous per column)."""
     return normal_f16((n, k), SEED_W + r)
+
+
+def decode_weights_kn(r: int, n: int = DECODE_N, k: int = DECODE_K) -> np.ndarray:
+    """The same matrix as decode_weights(r), stored the other way round:
+    K rows of N contiguous values (a layout change only)."""
+    return np.ascontiguousarray(decode_weights(r, n, k).T)

@@ -242,4 +242,34 @@ def pin_gemv(o):
     assert (np.abs(y - ref) <= 2 * K * U * mag).all()
 
 
+def pin_gemv_kn(o):
+    """The [K][N] weight layout: the same products summed in the same ascending
+    k order as the [N][K] form, so the two agree bit for bit on transposed
+    copies; plus closed forms that do not go through the other function."""
+    K, N = 300, 50
+    x = inputs.uniform_f16((K,), 73)
+    W = inputs.normal_f16((K, N), 74)          # K rows, N contiguous
+    Wp = inputs.padded(W, 56)
+    y = o.gemv_kn(x, Wp, N=N)
+    assert (y == o.gemv_m1(x, np.ascontiguousarray(W.T))).all()
+    # one-hot activations select row k of the weights
+    for j in (0, 1, 150, K - 1):
+        e = np.zeros(K, np.float16)
+        e[j] = 1
+        assert (o.gemv_kn(e, Wp, N=N) == W[j].astype(np.float64)).all(), j
+    # a single nonzero weight column n sees only its own column
+    Z = np.zeros((K, N), np.float16)
+    Z[:, 7] = 1
+    z = o.gemv_kn(np.ones(K, np.float16), Z)
+    assert z[7] == K and (np.delete(z, 7) == 0).all()
+    # exact rationals on a tiny case
+    xs = inputs.uniform_f16((5,), 75)
+    Ws = inputs.uniform_f16((5, 3), 76)
+    ys = o.gemv_kn(xs, Ws)
+    for n in range(3):
+        exact = sum(Fraction(float(xs[k])) * Fraction(float(Ws[k, n])) for k in range(5))
+        assert abs(Fraction(ys[n]) - exact) <= Fraction(4 * U) * sum(
+            abs(Fraction(float(xs[k])) * Fraction(float(Ws[k, n]))) for k in range(5))
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -36,6 +36,10 @@ MUTANTS = {
     "subnormal_floor": ("if (E < -14)\n        E = -14;", "if (E < -15)\n        E = -15;"),
     "gemv_column_stride": ("const uint16_t* col = B + n * ldb;", "const uint16_t* col = B + n * K;"),
     "gemv_reads_x_twice": ("s += g_dec[x[k]] * g_dec[col[k]];", "s += g_dec[x[k]] * g_dec[x[k]];"),
+    "gemv_kn_row_stride": ("g_dec[B[k * ldb + n]]", "g_dec[B[k * N + n]]"),
+    "gemv_kn_transposed": ("g_dec[B[k * ldb + n]]", "g_dec[B[n * ldb + k]]"),
+    "gemv_kn_first_row_dropped": ("for (int64_t k = 0; k < K; ++k)\n            s += g_dec[x[k]] * g_dec[B[k",
+                                  "for (int64_t k = 1; k < K; ++k)\n            s += g_dec[x[k]] * g_dec[B[k"),
     "sample_swaps_index": ("dot_f16_f64(A + rows[i] * lda, B + cols[i] * ldb, K)",
                            "dot_f16_f64(A + rows[i] * lda, B + rows[i] * ldb, K)"),
 }
