@@ -56,9 +56,11 @@ def parse():
     ap.add_argument("--profile", default=None, metavar="KERNEL",
                     help="instead of the benchmark, launch one kernel repeatedly for a "
                          "profiler: gemm<N> (N^3, e.g. gemm8192), gemv (decode, rotating "
-                         "buffers) or copy<MB> (a plain device copy, for counter scaling)")
+                         "buffers), gemvkn (decode with the weights as K rows of N) or "
+                         "copy<MB> (a plain device copy, for counter scaling)")
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--variant", type=int, default=-1, help="profile mode: GEMV variant")
     ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 default (off), 0 off, 1 on")
     return ap.parse_args()
 
@@ -87,6 +89,14 @@ def profile_mode(args):
         y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
         for j in range(args.launches):
             sdt.gemv_f16_m1(x, Ws[j % len(Ws)], y)
+    elif name == "gemvkn":
+        x = torch.from_numpy(inputs.decode_activations()).to(dev)
+        Ws = [torch.from_numpy(inputs.decode_weights_kn(r)).to(dev)
+              for r in range(inputs.DECODE_BUFFERS)]
+        y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
+        v = None if args.variant < 0 else args.variant
+        for j in range(args.launches):
+            sdt.gemv_f16_m1_kn(x, Ws[j % len(Ws)], y, variant=v)
     elif name.startswith("copy"):
         mb = int(name[4:])
         src = torch.ones((mb * 1024 * 1024 // 2,), dtype=torch.float16, device=dev)
@@ -457,6 +467,48 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         "protocol": "8 rotating buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
     }
     log(f"decode cold: median {med:.2f} us = {det['decode_cold']['GBps_weights_median']} GB/s")
+
+    # The same decode product with the weights stored as K rows of N (the
+    # pages' B-layout): gated against the oracle, then the same cold protocol
+    # for every instantiation (variant 0 is the default).
+    import oracle
+    x_h = inputs.decode_activations()
+    Wkn_h = [inputs.decode_weights_kn(r) for r in range(inputs.DECODE_BUFFERS)]
+    Wkn = [dev_tensor(w) for w in Wkn_h]
+    det["decode_kn_cold"] = {"variants": {}}
+    for v in range(sdt.gemv_kn_num_variants()):
+        bad = 0
+        for r in range(inputs.DECODE_BUFFERS):
+            sdt.gemv_f16_m1_kn(x, Wkn[r], y, variant=v)
+            torch.cuda.synchronize()
+            ref = oracle.gemv_kn(x_h, Wkn_h[r])
+            got = y.cpu().numpy().astype(np.float64)
+            bad += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+        if bad:
+            det["decode_kn_cold"]["variants"][str(v)] = {"gate": f"{bad} outside tolerance"}
+            log(f"decode [K][N] variant {v}: PARITY FAILED ({bad}), not timed")
+            continue
+        h = (lambda j, v=v: sdt.gemv_f16_m1_kn(x, Wkn[j % len(Wkn)], y, variant=v))
+        t0 = time.time()
+        j = 0
+        while time.time() - t0 < 1.0:
+            h(j)
+            j += 1
+            if j % 200 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        us = time_launches(torch, h, 200)
+        med = sorted(us)[len(us) // 2]
+        det["decode_kn_cold"]["variants"][str(v)] = {
+            "us": _ranges(us),
+            "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
+            "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "gate": "pass",
+        }
+        log(f"decode [K][N] variant {v}: median {med:.2f} us = "
+            f"{det['decode_kn_cold']['variants'][str(v)]['GBps_weights_median']} GB/s")
+    det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
+                                         "200 launches x 10 repeats, event-timed")
     return det
 
 

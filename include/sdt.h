@@ -86,6 +86,18 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
 int gemv_f16_m1(int64_t N, int64_t K, const void* x,
                 const void* B, int64_t ldb, void* y, void* stream);
 
+/* y(n) = sum_k x(k) * B[k*ldb + n], n < N: the same M=1 decode product with
+ * the weights stored as K rows of ldb >= N elements, the N of one row
+ * contiguous (the "B-layout" of the mojo-baro page, "Four rounds on the decode
+ * shape", where each thread owns contiguous columns).  x holds K fp16, y
+ * receives N fp16 (round-to-nearest-even from an fp32 sum).  Requirements:
+ * N, K >= 0 and ldb >= N when K > 0 (else SDT_ERR_INVALID_ARG); x and B
+ * 16-byte aligned, ldb % 8 == 0 when K > 1, y 2-byte aligned (else
+ * SDT_ERR_UNSUPPORTED).  N == 0 is a no-op, K == 0 writes zeros.  Deterministic:
+ * the partial sums over K are combined in a fixed order; no workspace. */
+int gemv_f16_m1_kn(int64_t N, int64_t K, const void* x,
+                   const void* B, int64_t ldb, void* y, void* stream);
+
 /* ---- test / benchmark extras ---------------------------------------------- */
 
 /* gemm_f16 with the launcher's choices forced.  tile_id: -1 = automatic,
@@ -105,6 +117,15 @@ int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x,
                    const void* B, int64_t ldb, void* y, void* stream,
                    int variant);
 int sdt_gemv_num_variants(void);
+
+/* gemv_f16_m1_kn with the instantiation forced: variant in
+ * [0, sdt_gemv_kn_num_variants()) selects the column band per workgroup and
+ * the number of waves splitting K (variant 0 is what gemv_f16_m1_kn uses).
+ * Same result definition; the combination order of partial sums differs. */
+int gemv_f16_m1_kn_ex(int64_t N, int64_t K, const void* x,
+                      const void* B, int64_t ldb, void* y, void* stream,
+                      int variant);
+int sdt_gemv_kn_num_variants(void);
 
 /* Host-only: the tile the launcher would use for an M x N x K product on a
  * device with num_cu compute units (num_cu <= 0 reads the current device).
@@ -143,6 +164,11 @@ int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt);
  * smallest products are compared with (the pages report small shapes next to
  * such a floor).  Returns SDT_OK or SDT_ERR_HIP. */
 int sdt_empty_kernel(void* stream);
+
+/* Host-only argument check used by gemv_f16_m1_kn before anything is
+ * enqueued (the status it would return for these arguments). */
+int sdt_check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B,
+                           int64_t ldb, const void* y);
 
 /* Host-only argument check used by gemm_f16 before anything is enqueued.
  * Returns the status gemm_f16 would return for these arguments (SDT_OK when

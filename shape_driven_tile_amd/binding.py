@@ -22,6 +22,7 @@ SDT_ERR_HIP = 3
 # Every function include/sdt.h declares.
 EXPORTS = (
     "gemm_f16", "gemv_f16_m1", "gemm_f16_ex", "gemv_f16_m1_ex", "sdt_gemv_num_variants",
+    "gemv_f16_m1_kn", "gemv_f16_m1_kn_ex", "sdt_gemv_kn_num_variants", "sdt_check_gemv_kn_args",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
     "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel",
@@ -66,6 +67,10 @@ def lib():
     L.gemv_f16_m1.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp, _vp]
     L.gemv_f16_m1_ex.argtypes = L.gemv_f16_m1.argtypes + [_int]
     L.sdt_gemv_num_variants.argtypes = []
+    L.gemv_f16_m1_kn.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp, _vp]
+    L.gemv_f16_m1_kn_ex.argtypes = L.gemv_f16_m1_kn.argtypes + [_int]
+    L.sdt_gemv_kn_num_variants.argtypes = []
+    L.sdt_check_gemv_kn_args.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp]
     L.sdt_pick_tile.argtypes = [_i64, _i64, _i64, _int, ctypes.POINTER(SdtTile)]
     L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
     L.sdt_num_tiles.argtypes = []
@@ -79,6 +84,8 @@ def lib():
     L.sdt_last_hip_error.argtypes = []
     L.sdt_empty_kernel.argtypes = [_vp]
     for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
+                 "gemv_f16_m1_kn", "gemv_f16_m1_kn_ex", "sdt_gemv_kn_num_variants",
+                 "sdt_check_gemv_kn_args",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_check_gemm_args",
                  "sdt_last_hip_error", "sdt_empty_kernel"):
@@ -137,6 +144,14 @@ def check_gemm_args(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc) -> int:
 
 def gemv_num_variants() -> int:
     return int(lib().sdt_gemv_num_variants())
+
+
+def gemv_kn_num_variants() -> int:
+    return int(lib().sdt_gemv_kn_num_variants())
+
+
+def check_gemv_kn_args(N, K, x_ptr, B_ptr, ldb, y_ptr) -> int:
+    return int(lib().sdt_check_gemv_kn_args(int(N), int(K), x_ptr, B_ptr, int(ldb), y_ptr))
 
 
 # ---- compute entry points (torch tensors on a ROCm device) -------------------
@@ -212,6 +227,27 @@ def empty_kernel(stream=None) -> None:
     rc = lib().sdt_empty_kernel(_stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, "sdt_empty_kernel")
+
+
+def gemv_f16_m1_kn(x, B, y, stream=None, variant: int | None = None) -> None:
+    """y[N] = x[K] . B[K, N] for the M=1 decode shape with the weights stored
+    as K rows of N (the N of a row contiguous)."""
+    import torch
+    if x.dtype != torch.float16 or y.dtype != torch.float16:
+        raise TypeError("x and y must be float16")
+    if x.dim() != 1 or y.dim() != 1 or x.stride(0) != 1 or y.stride(0) != 1:
+        raise ValueError("x and y must be contiguous vectors")
+    K, N = B.shape
+    if x.shape[0] != K or y.shape[0] != N:
+        raise ValueError(f"shape mismatch x{tuple(x.shape)} B{tuple(B.shape)} y{tuple(y.shape)}")
+    pb, ldb = _rows(B, "B")
+    h = _stream_handle(stream)
+    if variant is None:
+        rc = lib().gemv_f16_m1_kn(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h)
+    else:
+        rc = lib().gemv_f16_m1_kn_ex(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h, int(variant))
+    if rc != SDT_OK:
+        raise SdtError(rc, "gemv_f16_m1_kn")
 
 
 def gemm_f16_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream_ptr=None) -> int:

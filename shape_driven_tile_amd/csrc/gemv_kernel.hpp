@@ -135,4 +135,148 @@ __global__ __launch_bounds__(256) void gemv_f16_m1_kernel(GemvParams p) {
     }
 }
 
+// ---- the same product with the weights as K rows of N ("B-layout") ---------
+//
+// y(n) = sum_k x(k) * B[k*ldb + n].  This is the layout the mojo-baro page
+// reaches by transposing the weights at load (rounds v1-v3 of "Four rounds on
+// the decode shape"), where each thread owns CPT contiguous columns so that
+// its loads are wide vectors, CPT = 8 measuring best.  On MI355X:
+//   * a lane owns 8 contiguous columns (one 16-byte load per weight row) and
+//     SEG lanes side by side cover one SEG*8-column band, SEG*16 contiguous
+//     bytes of every row; a workgroup owns one band;
+//   * a band alone is too little work for a CU, so the workgroup splits K:
+//     its lanes form RG row groups, and group g takes the blocks of eight
+//     consecutive rows b = g, g + RG, g + 2*RG, ...; one 16-byte load gives
+//     the eight activations of a block, eight loads its weights;
+//   * two blocks per trip keep 18 loads per lane in flight;
+//   * the RG partial sums of each column are combined in LDS in a fixed order
+//     (RG/PARTS groups per partial, then the PARTS partials), so the result
+//     is deterministic and needs no workspace and no second launch;
+//   * only a ragged last band (N not a multiple of the band) takes the
+//     element-masked loads, and a ragged last block of rows (K not a multiple
+//     of 8) is taken by one row group with masking.
+
+struct GemvKnParams {
+    const uint16_t* x;
+    const uint16_t* B;
+    uint16_t* y;
+    int64_t ldb;
+    int N, K;
+};
+
+// acc[c] += x(r) * w(r, c) for the first `rows` of eight rows.  The chunks are
+// reinterpreted whole, then indexed (see dot8).
+__device__ __forceinline__ void kn_block(int4_t xv, const int4_t* w, int rows, float* acc) {
+    const half8_t xh = __builtin_bit_cast(half8_t, xv);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        if (r < rows) {
+            const half8_t wh = __builtin_bit_cast(half8_t, w[r]);
+            const float xr = (float)xh[r];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[c] = __builtin_fmaf(xr, (float)wh[c], acc[c]);
+        }
+    }
+}
+
+template <int SEG, int NW>
+__global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
+    constexpr int BW = SEG * 8;          // columns per workgroup
+    constexpr int RGW = 64 / SEG;        // row groups per wave
+    constexpr int RG = NW * RGW;         // row groups per workgroup
+    constexpr int NT = NW * 64;
+    constexpr int PARTS = NT / BW;       // first-level partial sums per column
+    static_assert(64 % SEG == 0 && NT % BW == 0 && RG % PARTS == 0, "reduction shape");
+    __shared__ float red[RG * BW];
+    __shared__ float part[PARTS * BW];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    const int seg = lane % SEG;
+    const int rg = wave * RGW + lane / SEG;
+    const int nb = blockIdx.x * BW;
+    const int n0 = nb + seg * 8;
+    const int nblk = p.K / 8;            // blocks of eight rows wholly below K
+    const int krem = p.K - nblk * 8;
+
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.0f;
+
+    const uint16_t* col = p.B + n0;
+    if (nb + BW <= p.N) {                // whole band below N (uniform)
+        int b = rg;
+        for (; b + RG < nblk; b += 2 * RG) {
+            const int k0 = 8 * b, k1 = 8 * (b + RG);
+            const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
+            const int4_t x1 = *reinterpret_cast<const int4_t*>(p.x + k1);
+            int4_t w0[8], w1[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                w0[r] = __builtin_nontemporal_load(
+                    reinterpret_cast<const int4_t*>(col + (int64_t)(k0 + r) * p.ldb));
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                w1[r] = __builtin_nontemporal_load(
+                    reinterpret_cast<const int4_t*>(col + (int64_t)(k1 + r) * p.ldb));
+            kn_block(x0, w0, 8, acc);
+            kn_block(x1, w1, 8, acc);
+        }
+        if (b < nblk) {
+            const int k0 = 8 * b;
+            const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
+            int4_t w0[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                w0[r] = __builtin_nontemporal_load(
+                    reinterpret_cast<const int4_t*>(col + (int64_t)(k0 + r) * p.ldb));
+            kn_block(x0, w0, 8, acc);
+        }
+    } else {                             // ragged last band: masked columns
+        for (int b = rg; b < nblk; b += RG) {
+            const int k0 = 8 * b;
+            const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
+            int4_t w0[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                w0[r] = gemv_chunk(p.B + (int64_t)(k0 + r) * p.ldb, n0, p.N, true);
+            kn_block(x0, w0, 8, acc);
+        }
+    }
+    if (krem > 0 && rg == nblk % RG) {   // ragged last block of rows
+        const int k0 = 8 * nblk;
+        const int4_t x0 = gemv_chunk(p.x, k0, p.K, false);
+        int4_t w0[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            w0[r] = (r < krem) ? gemv_chunk(p.B + (int64_t)(k0 + r) * p.ldb, n0, p.N, true)
+                               : int4_t{0, 0, 0, 0};
+        kn_block(x0, w0, krem, acc);
+    }
+
+    // fixed-order reduction of the RG partial sums of each column
+#pragma unroll
+    for (int c = 0; c < 8; ++c) red[rg * BW + seg * 8 + c] = acc[c];
+    __syncthreads();
+    {
+        const int c = t % BW, q = t / BW;
+        constexpr int PER = RG / PARTS;
+        float s = 0.0f;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) s += red[(q * PER + j) * BW + c];
+        part[q * BW + c] = s;
+    }
+    __syncthreads();
+    if (t < BW) {
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < PARTS; ++q) s += part[q * BW + t];
+        if (nb + t < p.N) {
+            const _Float16 h = (_Float16)s;
+            p.y[nb + t] = __builtin_bit_cast(uint16_t, h);
+        }
+    }
+}
+
 }  // namespace sdt

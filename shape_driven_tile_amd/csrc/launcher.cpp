@@ -87,6 +87,25 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
     return SDT_OK;
 }
 
+// The [K][N] decode product: K rows of ldb >= N weights.  Rows are read with
+// 16-byte loads at column offsets that are multiples of 8, so B must be
+// 16-byte aligned with ldb a multiple of 8 whenever there is a second row;
+// the activations are read 8 at a time from a 16-byte aligned x.
+int check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                       const void* y) {
+    if (N < 0 || K < 0) return SDT_ERR_INVALID_ARG;
+    if (K > 0 && ldb < N) return SDT_ERR_INVALID_ARG;
+    if (N == 0) return SDT_OK;
+    if (!y) return SDT_ERR_INVALID_ARG;
+    if (K > 0 && (!x || !B)) return SDT_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(y) & 1u) != 0) return SDT_ERR_UNSUPPORTED;
+    if (K > 0) {
+        if (!aligned16(x) || !aligned16(B)) return SDT_ERR_UNSUPPORTED;
+        if (K > 1 && ldb % 8 != 0) return SDT_ERR_UNSUPPORTED;
+    }
+    return SDT_OK;
+}
+
 }  // namespace sdt
 
 // ---- host-only C ABI --------------------------------------------------------
@@ -111,6 +130,11 @@ extern "C" int sdt_stagger_eligible(int64_t K) { return sdt::stagger_eligible(K)
 extern "C" int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt) {
     if (!sdt::is_pow2(nkt) || wg < 0 || i < 0) return -1;
     return (wg + i) & (nkt - 1);
+}
+
+extern "C" int sdt_check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B,
+                                      int64_t ldb, const void* y) {
+    return sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
 }
 
 extern "C" int sdt_check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A,

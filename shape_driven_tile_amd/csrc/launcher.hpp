@@ -43,6 +43,8 @@ int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks);
 int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);
 bool stagger_eligible(int64_t K);
+int check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                       const void* y);
 bool is_pow2(int64_t v);
 int64_t ceil_div(int64_t a, int64_t b);
 int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,

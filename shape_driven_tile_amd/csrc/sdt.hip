@@ -125,6 +125,44 @@ int launch_gemv(int variant, int64_t N, int64_t K, const void* x, const void* B,
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
+// [K][N] GEMV instantiations: (lanes per 16-byte column segment, waves per
+// workgroup).  A workgroup covers 8 * SEG columns and all of K.
+struct GemvKnVariant {
+    int seg, waves;
+};
+constexpr GemvKnVariant kGemvKn[] = {{8, 16}, {8, 8}, {4, 16}, {4, 8}};
+constexpr int kGemvKnVariants = sizeof(kGemvKn) / sizeof(kGemvKn[0]);
+
+template <int SEG, int NW>
+hipError_t launch_gemv_kn_tile(GemvKnParams p, hipStream_t stream) {
+    const int64_t blocks = ((int64_t)p.N + SEG * 8 - 1) / (SEG * 8);
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_kn_kernel<SEG, NW>),
+                           dim3((unsigned)blocks), dim3(NW * 64), args, 0, stream);
+}
+
+int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                   void* y, hipStream_t stream) {
+    if (N > INT_MAX || K > INT_MAX) return SDT_ERR_UNSUPPORTED;
+    if (K == 0) return fill_zero(static_cast<uint16_t*>(y), N, 1, N, stream);
+    GemvKnParams p;
+    p.x = static_cast<const uint16_t*>(x);
+    p.B = static_cast<const uint16_t*>(B);
+    p.y = static_cast<uint16_t*>(y);
+    p.ldb = ldb;
+    p.N = (int)N;
+    p.K = (int)K;
+    static_assert(kGemvKnVariants == 4, "dispatch below lists every variant");
+    hipError_t e;
+    switch (variant) {
+        case 1: e = launch_gemv_kn_tile<8, 8>(p, stream); break;
+        case 2: e = launch_gemv_kn_tile<4, 16>(p, stream); break;
+        case 3: e = launch_gemv_kn_tile<4, 8>(p, stream); break;
+        default: e = launch_gemv_kn_tile<8, 16>(p, stream); break;
+    }
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
+}
+
 int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
               int64_t ldb, void* C, int64_t ldc, void* stream, int tile_id, int stagger,
               bool route_m1) {
@@ -206,6 +244,23 @@ extern "C" int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x, const void* B
 }
 
 extern "C" int sdt_gemv_num_variants(void) { return sdt::kGemvVariants; }
+
+extern "C" int gemv_f16_m1_kn(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                              void* y, void* stream) {
+    int st = sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
+    if (st != SDT_OK || N == 0) return st;
+    return sdt::launch_gemv_kn(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int gemv_f16_m1_kn_ex(int64_t N, int64_t K, const void* x, const void* B,
+                                 int64_t ldb, void* y, void* stream, int variant) {
+    if (variant < 0 || variant >= sdt::kGemvKnVariants) return SDT_ERR_INVALID_ARG;
+    int st = sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
+    if (st != SDT_OK || N == 0) return st;
+    return sdt::launch_gemv_kn(variant, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int sdt_gemv_kn_num_variants(void) { return sdt::kGemvKnVariants; }
 
 extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out) {
     if (M < 0 || N < 0 || K < 0 || !out) return SDT_ERR_INVALID_ARG;

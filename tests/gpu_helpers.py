@@ -92,3 +92,21 @@ def sample_positions(M, N, rows=32, cols=32, extra=4096, seed=0):
     r = [np.full(N, i) for i in rs] + [np.arange(M) for _ in cs] + [rng.integers(0, M, extra)]
     c = [np.arange(N) for _ in rs] + [np.full(M, j) for j in cs] + [rng.integers(0, N, extra)]
     return np.concatenate(r).astype(np.int64), np.concatenate(c).astype(np.int64)
+
+
+def run_gemv_kn(x, W, N=None, variant=None, y_pad=8):
+    """x: (K,) float16; W: (K, ldb) float16 host buffer, the N of a row
+    contiguous.  Returns y (N,) and whether the y_pad elements past N stayed
+    untouched."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    K, ldb = W.shape
+    N = ldb if N is None else N
+    dx = to_dev(x[:K])
+    dW = to_dev(W)[:, :N]
+    full = torch.full((N + y_pad,), float("nan"), dtype=torch.float16, device=DEV)
+    dy = full[:N]
+    sdt.gemv_f16_m1_kn(dx, dW, dy, variant=variant)
+    torch.cuda.synchronize()
+    pad_ok = bool(torch.isnan(full[N:]).all().item())
+    return dy.cpu().numpy(), pad_ok

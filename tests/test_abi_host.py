@@ -99,6 +99,41 @@ def test_gemm_f16_ex_rejects_bad_choices():
                             sdt.gemv_num_variants()) == sdt.SDT_ERR_INVALID_ARG
 
 
+KN_OK = (0x10000, 0x20000, 0x30000)   # fake 16-byte aligned x, B, y
+
+
+@pytest.mark.parametrize("args,want", [
+    ((12288, 4096, *KN_OK[:2], 12288, KN_OK[2]), 0),
+    ((-1, 4, *KN_OK[:2], 8, KN_OK[2]), 1),
+    ((8, -1, *KN_OK[:2], 8, KN_OK[2]), 1),
+    ((16, 4, *KN_OK[:2], 8, KN_OK[2]), 1),            # ldb < N
+    ((0, 4, None, None, 0, None), 0),                  # nothing to do
+    ((16, 4, None, KN_OK[1], 16, KN_OK[2]), 1),        # null x
+    ((16, 4, KN_OK[0], KN_OK[1], 16, None), 1),        # null y
+    ((16, 0, None, None, 0, KN_OK[2]), 0),             # K=0: only y is touched
+    ((16, 4, KN_OK[0] + 2, KN_OK[1], 16, KN_OK[2]), 2),
+    ((16, 4, KN_OK[0], KN_OK[1] + 8, 16, KN_OK[2]), 2),
+    ((16, 4, KN_OK[0], KN_OK[1], 20, KN_OK[2]), 2),    # ldb % 8
+    ((16, 1, KN_OK[0], KN_OK[1], 20, KN_OK[2]), 0),    # one row: ldb unconstrained
+    ((16, 4, KN_OK[0], KN_OK[1], 16, KN_OK[2] + 1), 2),  # y odd address
+    ((16, 4, KN_OK[0], KN_OK[1], 16, KN_OK[2] + 2), 0),
+])
+def test_check_gemv_kn_args(args, want):
+    assert sdt.check_gemv_kn_args(*args) == want
+
+
+def test_gemv_kn_rejects_before_launch():
+    """Every invalid call returns its status without touching a device."""
+    L = sdt.lib()
+    assert L.gemv_f16_m1_kn(16, 4, KN_OK[0] + 2, KN_OK[1], 16, KN_OK[2], None) == 2
+    assert L.gemv_f16_m1_kn(16, 4, KN_OK[0], KN_OK[1], 8, KN_OK[2], None) == 1
+    assert L.gemv_f16_m1_kn(0, 4, None, None, 0, None, None) == 0
+    assert L.gemv_f16_m1_kn_ex(16, 4, *KN_OK[:2], 16, KN_OK[2], None, -1) == 1
+    assert L.gemv_f16_m1_kn_ex(16, 4, *KN_OK[:2], 16, KN_OK[2], None,
+                               sdt.gemv_kn_num_variants()) == 1
+    assert sdt.gemv_kn_num_variants() >= 1
+
+
 def test_gemv_rejects_before_launch():
     assert sdt.gemv_f16_m1_raw(-1, 64, A16, B16, 64, C16) == sdt.SDT_ERR_INVALID_ARG
     assert sdt.gemv_f16_m1_raw(64, 64, A16, B16, 60, C16) == sdt.SDT_ERR_INVALID_ARG
