@@ -1,4 +1,4 @@
-"""CPU oracle for the fp16 GEMM / M=1 GEMV: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for the fp16 / bf16 GEMM and M=1 GEMV: TEST INFRASTRUCTURE ONLY.
 
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
 import this package.  The GPU library never loads it, and it shares no code
@@ -14,6 +14,9 @@ tile from the shape", Performance section):
   * ``B``: uint16 array, shape (N, ldb); element (k, n) of the math B is
     ``B[n, k]`` (K contiguous, "K-major").
   * result: fp64 array (M, N), unrounded.
+Element type: ``dtype="f16"`` (IEEE binary16, the default) or ``"bf16"``
+(bfloat16); bit patterns are passed as uint16 either way (a float16 array is
+viewed as its bits).
 """
 from __future__ import annotations
 
@@ -45,6 +48,12 @@ def _p(a, t):
     return a.ctypes.data_as(t)
 
 
+def _dt(dtype: str) -> int:
+    if dtype not in ("f16", "bf16"):
+        raise ValueError(f"dtype must be 'f16' or 'bf16', got {dtype!r}")
+    return 1 if dtype == "bf16" else 0
+
+
 class Oracle:
     """The oracle's entry points over one build of ``sdt_oracle.c``.
 
@@ -66,19 +75,25 @@ class Oracle:
         lib.sdt_oracle_encode_array.restype = None
         lib.sdt_oracle_max_threads.argtypes = []
         lib.sdt_oracle_max_threads.restype = ctypes.c_int
-        lib.sdt_oracle_gemm.argtypes = [_i64, _i64, _i64, _u16p, _i64, _u16p, _i64,
-                                        _f64p, _i64, ctypes.c_int]
-        lib.sdt_oracle_gemm.restype = ctypes.c_int
-        lib.sdt_oracle_gemm_sample.argtypes = [_i64, _i64, _i64, _u16p, _i64, _u16p,
-                                               _i64, _i64, _i64p, _i64p, _f64p,
-                                               ctypes.c_int]
-        lib.sdt_oracle_gemm_sample.restype = ctypes.c_int
-        lib.sdt_oracle_gemv_m1.argtypes = [_i64, _i64, _u16p, _u16p, _i64, _f64p,
-                                           ctypes.c_int]
-        lib.sdt_oracle_gemv_m1.restype = ctypes.c_int
-        lib.sdt_oracle_gemv_kn.argtypes = [_i64, _i64, _u16p, _u16p, _i64, _f64p,
-                                           ctypes.c_int]
-        lib.sdt_oracle_gemv_kn.restype = ctypes.c_int
+        _c = ctypes.c_int
+        lib.sdt_oracle_bf16_decode.argtypes = [ctypes.c_uint16]
+        lib.sdt_oracle_bf16_decode.restype = ctypes.c_double
+        lib.sdt_oracle_bf16_encode_rne.argtypes = [ctypes.c_double]
+        lib.sdt_oracle_bf16_encode_rne.restype = ctypes.c_uint16
+        lib.sdt_oracle_bf16_decode_array.argtypes = [_u16p, _f64p, _i64]
+        lib.sdt_oracle_bf16_decode_array.restype = None
+        lib.sdt_oracle_bf16_encode_array.argtypes = [_f64p, _u16p, _i64]
+        lib.sdt_oracle_bf16_encode_array.restype = None
+        lib.sdt_oracle_gemm_t.argtypes = [_c, _i64, _i64, _i64, _u16p, _i64, _u16p, _i64,
+                                          _f64p, _i64, _c]
+        lib.sdt_oracle_gemm_t.restype = _c
+        lib.sdt_oracle_gemm_sample_t.argtypes = [_c, _i64, _i64, _i64, _u16p, _i64, _u16p,
+                                                 _i64, _i64, _i64p, _i64p, _f64p, _c]
+        lib.sdt_oracle_gemm_sample_t.restype = _c
+        lib.sdt_oracle_gemv_m1_t.argtypes = [_c, _i64, _i64, _u16p, _u16p, _i64, _f64p, _c]
+        lib.sdt_oracle_gemv_m1_t.restype = _c
+        lib.sdt_oracle_gemv_kn_t.argtypes = [_c, _i64, _i64, _u16p, _u16p, _i64, _f64p, _c]
+        lib.sdt_oracle_gemv_kn_t.restype = _c
         self.path = path
         self._lib = lib
 
@@ -96,10 +111,28 @@ class Oracle:
         self._lib.sdt_oracle_encode_array(_p(x, _f64p), _p(out, _u16p), x.size)
         return out
 
+    def bf16_decode(self, bits) -> np.ndarray:
+        """Exact bfloat16 -> fp64 decode of uint16 bit patterns, elementwise."""
+        b = _bits(bits)
+        out = np.empty(b.shape, dtype=np.float64)
+        self._lib.sdt_oracle_bf16_decode_array(_p(b, _u16p), _p(out, _f64p), b.size)
+        return out
+
+    def bf16_encode_rne(self, x) -> np.ndarray:
+        """fp64 -> bfloat16 bit patterns, round to nearest, ties to even."""
+        x = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        out = np.empty(x.shape, dtype=np.uint16)
+        self._lib.sdt_oracle_bf16_encode_array(_p(x, _f64p), _p(out, _u16p), x.size)
+        return out
+
+    def encode_rne(self, x, dtype: str = "f16") -> np.ndarray:
+        return self.bf16_encode_rne(x) if dtype == "bf16" else self.f16_encode_rne(x)
+
     def max_threads(self) -> int:
         return int(self._lib.sdt_oracle_max_threads())
 
-    def gemm(self, A, B, K: int | None = None, threads: int = 0) -> np.ndarray:
+    def gemm(self, A, B, K: int | None = None, threads: int = 0,
+             dtype: str = "f16") -> np.ndarray:
         """C = A.B in fp64 (unrounded); A is (M, lda), B is (N, ldb), K-contiguous."""
         a = _bits(A)
         b = _bits(B)
@@ -109,15 +142,15 @@ class Oracle:
         N, ldb = b.shape
         K = lda if K is None else int(K)
         C = np.empty((M, N), dtype=np.float64)
-        rc = self._lib.sdt_oracle_gemm(M, N, K, _p(a, _u16p), lda, _p(b, _u16p), ldb,
-                                       _p(C, _f64p), max(N, 1), threads)
+        rc = self._lib.sdt_oracle_gemm_t(_dt(dtype), M, N, K, _p(a, _u16p), lda,
+                                         _p(b, _u16p), ldb, _p(C, _f64p), max(N, 1), threads)
         if rc != 0:
             raise ValueError(
                 f"oracle gemm rejected M={M} N={N} K={K} lda={lda} ldb={ldb}")
         return C
 
     def gemm_sample(self, A, B, rows, cols, K: int | None = None,
-                    threads: int = 0) -> np.ndarray:
+                    threads: int = 0, dtype: str = "f16") -> np.ndarray:
         """C(rows[i], cols[i]) for each i, by the same definition as :meth:`gemm`."""
         a = _bits(A)
         b = _bits(B)
@@ -129,14 +162,15 @@ class Oracle:
         if r.shape != c.shape:
             raise ValueError("rows and cols must have the same shape")
         out = np.empty(r.shape, dtype=np.float64)
-        rc = self._lib.sdt_oracle_gemm_sample(M, N, K, _p(a, _u16p), lda, _p(b, _u16p),
-                                              ldb, r.size, _p(r, _i64p), _p(c, _i64p),
-                                              _p(out, _f64p), threads)
+        rc = self._lib.sdt_oracle_gemm_sample_t(_dt(dtype), M, N, K, _p(a, _u16p), lda,
+                                                _p(b, _u16p), ldb, r.size, _p(r, _i64p),
+                                                _p(c, _i64p), _p(out, _f64p), threads)
         if rc != 0:
             raise ValueError("oracle gemm_sample rejected its arguments")
         return out
 
-    def gemv_m1(self, x, B, K: int | None = None, threads: int = 0) -> np.ndarray:
+    def gemv_m1(self, x, B, K: int | None = None, threads: int = 0,
+                dtype: str = "f16") -> np.ndarray:
         """y = x.B in fp64 for the M=1 decode shape; B is (N, ldb), K-contiguous."""
         xv = _bits(x).reshape(-1)
         b = _bits(B)
@@ -145,13 +179,14 @@ class Oracle:
         if xv.size < K:
             raise ValueError("x shorter than K")
         y = np.empty(N, dtype=np.float64)
-        rc = self._lib.sdt_oracle_gemv_m1(N, K, _p(xv, _u16p), _p(b, _u16p), ldb,
-                                          _p(y, _f64p), threads)
+        rc = self._lib.sdt_oracle_gemv_m1_t(_dt(dtype), N, K, _p(xv, _u16p), _p(b, _u16p),
+                                            ldb, _p(y, _f64p), threads)
         if rc != 0:
             raise ValueError("oracle gemv rejected its arguments")
         return y
 
-    def gemv_kn(self, x, B, N: int | None = None, threads: int = 0) -> np.ndarray:
+    def gemv_kn(self, x, B, N: int | None = None, threads: int = 0,
+                dtype: str = "f16") -> np.ndarray:
         """y = x.B in fp64 with the weights as K rows of ldb >= N elements
         (B is (K, ldb), the N of one row contiguous)."""
         xv = _bits(x).reshape(-1)
@@ -161,8 +196,8 @@ class Oracle:
         if xv.size < K:
             raise ValueError("x shorter than K")
         y = np.empty(N, dtype=np.float64)
-        rc = self._lib.sdt_oracle_gemv_kn(N, K, _p(xv, _u16p), _p(b, _u16p), ldb,
-                                          _p(y, _f64p), threads)
+        rc = self._lib.sdt_oracle_gemv_kn_t(_dt(dtype), N, K, _p(xv, _u16p), _p(b, _u16p),
+                                            ldb, _p(y, _f64p), threads)
         if rc != 0:
             raise ValueError("oracle gemv_kn rejected its arguments")
         return y
@@ -190,20 +225,32 @@ def max_threads() -> int:
     return default().max_threads()
 
 
-def gemm(A, B, K=None, threads=0):
-    return default().gemm(A, B, K, threads)
+def bf16_decode(bits):
+    return default().bf16_decode(bits)
 
 
-def gemm_sample(A, B, rows, cols, K=None, threads=0):
-    return default().gemm_sample(A, B, rows, cols, K, threads)
+def bf16_encode_rne(x):
+    return default().bf16_encode_rne(x)
 
 
-def gemv_m1(x, B, K=None, threads=0):
-    return default().gemv_m1(x, B, K, threads)
+def encode_rne(x, dtype="f16"):
+    return default().encode_rne(x, dtype)
 
 
-def gemv_kn(x, B, N=None, threads=0):
-    return default().gemv_kn(x, B, N, threads)
+def gemm(A, B, K=None, threads=0, dtype="f16"):
+    return default().gemm(A, B, K, threads, dtype)
+
+
+def gemm_sample(A, B, rows, cols, K=None, threads=0, dtype="f16"):
+    return default().gemm_sample(A, B, rows, cols, K, threads, dtype)
+
+
+def gemv_m1(x, B, K=None, threads=0, dtype="f16"):
+    return default().gemv_m1(x, B, K, threads, dtype)
+
+
+def gemv_kn(x, B, N=None, threads=0, dtype="f16"):
+    return default().gemv_kn(x, B, N, threads, dtype)
 
 
 def tolerance(c_ref) -> np.ndarray:

@@ -89,7 +89,60 @@ uint16_t sdt_oracle_f16_encode_rne(double x)
     return (uint16_t)(sign | (uint16_t)bits);
 }
 
-static double g_dec[65536];
+/* ---- bfloat16 codec ------------------------------------------------------
+ * The upper half of an IEEE 754 binary32: 1 sign bit, 8 exponent bits with
+ * bias 127, 7 fraction bits; exponent 0 is the subnormal range with quantum
+ * 2^-133, exponent 255 is inf/NaN. */
+
+double sdt_oracle_bf16_decode(uint16_t h)
+{
+    int neg = (h >> 15) & 1;
+    int ebits = (h >> 7) & 0xff;
+    int man = h & 0x7f;
+    double v;
+    if (ebits == 0) {
+        v = ldexp((double)man, -133);              /* zero and subnormals */
+    } else if (ebits == 255) {
+        v = man ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(128 + man), ebits - 134); /* 1.m * 2^(e-127) */
+    }
+    return neg ? -v : v;
+}
+
+/* Round x to the nearest bfloat16 value, ties to even.  Same construction as
+ * the binary16 encoder: with P = max(floor(log2|x|), -126) every value of the
+ * binade (or of the subnormal range) is q * 2^(P-7), encoded as
+ * (P+126)*128 + q for q in [0, 256]. */
+uint16_t sdt_oracle_bf16_encode_rne(double x)
+{
+    uint16_t sgn = signbit(x) ? 0x8000 : 0;
+    if (isnan(x))
+        return (uint16_t)(sgn | 0x7fc0);
+    double mag = fabs(x);
+    /* the largest finite value is 255 * 2^120 (odd significand), so the
+     * midpoint 255.5 * 2^120 rounds up, out of range */
+    if (mag >= ldexp(255.5, 120))
+        return (uint16_t)(sgn | 0x7f80);
+    if (mag == 0.0)
+        return sgn;
+    int e2;
+    (void)frexp(mag, &e2);
+    int P = e2 - 1;
+    if (P < -126)
+        P = -126;
+    double q = ldexp(mag, 7 - P);   /* exact */
+    double lo = floor(q);
+    double rem = q - lo;            /* exact */
+    double qr = lo;
+    if (rem > 0.5 || (rem == 0.5 && fmod(lo, 2.0) == 1.0))
+        qr = lo + 1.0;
+    long code = (long)(P + 126) * 128L + (long)qr;
+    return (uint16_t)(sgn | (uint16_t)code);
+}
+
+static double g_dec[65536];        /* binary16 bit pattern -> value */
+static double g_dec_bf16[65536];   /* bfloat16 bit pattern -> value */
 static int g_dec_ready = 0;
 
 static void build_decode_table(void)
@@ -97,11 +150,20 @@ static void build_decode_table(void)
     #pragma omp critical(sdt_oracle_table)
     {
         if (!g_dec_ready) {
-            for (int h = 0; h < 65536; ++h)
+            for (int h = 0; h < 65536; ++h) {
                 g_dec[h] = sdt_oracle_f16_decode((uint16_t)h);
+                g_dec_bf16[h] = sdt_oracle_bf16_decode((uint16_t)h);
+            }
             g_dec_ready = 1;
         }
     }
+}
+
+/* The decode table of element type `dtype`: 0 binary16, 1 bfloat16. */
+static const double* table_of(int dtype)
+{
+    build_decode_table();
+    return dtype == 1 ? g_dec_bf16 : (dtype == 0 ? g_dec : 0);
 }
 
 void sdt_oracle_decode_array(const uint16_t* in, double* out, int64_t n)
@@ -117,6 +179,19 @@ void sdt_oracle_encode_array(const double* in, uint16_t* out, int64_t n)
         out[i] = sdt_oracle_f16_encode_rne(in[i]);
 }
 
+void sdt_oracle_bf16_decode_array(const uint16_t* in, double* out, int64_t n)
+{
+    build_decode_table();
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = g_dec_bf16[in[i]];
+}
+
+void sdt_oracle_bf16_encode_array(const double* in, uint16_t* out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = sdt_oracle_bf16_encode_rne(in[i]);
+}
+
 int sdt_oracle_max_threads(void)
 {
     return omp_get_max_threads();
@@ -124,73 +199,77 @@ int sdt_oracle_max_threads(void)
 
 /* ---- GEMM and GEMV ----------------------------------------------------- */
 
+/* Every entry point below takes `dtype` (0 binary16, 1 bfloat16), which
+ * only selects the decode table: the sums are the same for both.  Products
+ * of two bfloat16 values are exact in fp64 as well (8-bit significands). */
+
 /* One output element: the plain dot product of row m of A with row n of the
  * K-contiguous B buffer, in ascending k, in fp64. */
-static double dot_f16_f64(const uint16_t* a, const uint16_t* b, int64_t K)
+static double dot_f64(const double* dec, const uint16_t* a, const uint16_t* b, int64_t K)
 {
     double s = 0.0;
     for (int64_t k = 0; k < K; ++k)
-        s += g_dec[a[k]] * g_dec[b[k]];
+        s += dec[a[k]] * dec[b[k]];
     return s;
 }
 
 /* C (fp64, row-major, ldc) = A.B for the whole M x N output.
  * Returns 0, or -1 for an invalid argument.  threads <= 0 uses the OpenMP
  * default. */
-int sdt_oracle_gemm(int64_t M, int64_t N, int64_t K,
-                    const uint16_t* A, int64_t lda,
-                    const uint16_t* B, int64_t ldb,
-                    double* C, int64_t ldc, int threads)
+int sdt_oracle_gemm_t(int dtype, int64_t M, int64_t N, int64_t K,
+                      const uint16_t* A, int64_t lda,
+                      const uint16_t* B, int64_t ldb,
+                      double* C, int64_t ldc, int threads)
 {
-    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N)
+    const double* dec = table_of(dtype);
+    if (!dec || M < 0 || N < 0 || K < 0 || lda < K || ldb < K || ldc < N)
         return -1;
-    build_decode_table();
     int nt = threads > 0 ? threads : omp_get_max_threads();
     #pragma omp parallel for schedule(dynamic, 1) num_threads(nt)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n)
-            C[m * ldc + n] = dot_f16_f64(A + m * lda, B + n * ldb, K);
+            C[m * ldc + n] = dot_f64(dec, A + m * lda, B + n * ldb, K);
     return 0;
 }
 
 /* The same definition at `count` chosen output elements (rows[i], cols[i]);
  * out[i] receives C(rows[i], cols[i]).  Used where the full product is too
  * large for the host. */
-int sdt_oracle_gemm_sample(int64_t M, int64_t N, int64_t K,
-                           const uint16_t* A, int64_t lda,
-                           const uint16_t* B, int64_t ldb,
-                           int64_t count, const int64_t* rows,
-                           const int64_t* cols, double* out, int threads)
+int sdt_oracle_gemm_sample_t(int dtype, int64_t M, int64_t N, int64_t K,
+                             const uint16_t* A, int64_t lda,
+                             const uint16_t* B, int64_t ldb,
+                             int64_t count, const int64_t* rows,
+                             const int64_t* cols, double* out, int threads)
 {
-    if (M < 0 || N < 0 || K < 0 || lda < K || ldb < K || count < 0)
+    const double* dec = table_of(dtype);
+    if (!dec || M < 0 || N < 0 || K < 0 || lda < K || ldb < K || count < 0)
         return -1;
     for (int64_t i = 0; i < count; ++i)
         if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N)
             return -1;
-    build_decode_table();
     int nt = threads > 0 ? threads : omp_get_max_threads();
     #pragma omp parallel for schedule(dynamic, 64) num_threads(nt)
     for (int64_t i = 0; i < count; ++i)
-        out[i] = dot_f16_f64(A + rows[i] * lda, B + cols[i] * ldb, K);
+        out[i] = dot_f64(dec, A + rows[i] * lda, B + cols[i] * ldb, K);
     return 0;
 }
 
 /* y(n) = sum_k dec(x[k]) * dec(B[n*ldb + k]) for n in [0, N): the M=1 decode
  * product of the mojo-baro page ("Four rounds on the decode shape"), with
  * the weights stored K-contiguous per output column. */
-int sdt_oracle_gemv_m1(int64_t N, int64_t K, const uint16_t* x,
-                       const uint16_t* B, int64_t ldb, double* y, int threads)
+int sdt_oracle_gemv_m1_t(int dtype, int64_t N, int64_t K, const uint16_t* x,
+                         const uint16_t* B, int64_t ldb, double* y, int threads)
 {
-    if (N < 0 || K < 0 || ldb < K)
+    const double* dec = table_of(dtype);
+    if (!dec || N < 0 || K < 0 || ldb < K)
         return -1;
-    build_decode_table();
     int nt = threads > 0 ? threads : omp_get_max_threads();
     #pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t n = 0; n < N; ++n) {
         double s = 0.0;
         const uint16_t* col = B + n * ldb;
         for (int64_t k = 0; k < K; ++k)
-            s += g_dec[x[k]] * g_dec[col[k]];
+            s += dec[x[k]] * dec[col[k]];
         y[n] = s;
     }
     return 0;
@@ -201,18 +280,18 @@ int sdt_oracle_gemv_m1(int64_t N, int64_t K, const uint16_t* x,
  * elements, the N of one row contiguous (the "B-layout" the mojo-baro page
  * reaches by transposing the weights at load, section "Four rounds on the
  * decode shape", rounds v1-v3).  Same fp64 ascending-k sum per column. */
-int sdt_oracle_gemv_kn(int64_t N, int64_t K, const uint16_t* x,
-                       const uint16_t* B, int64_t ldb, double* y, int threads)
+int sdt_oracle_gemv_kn_t(int dtype, int64_t N, int64_t K, const uint16_t* x,
+                         const uint16_t* B, int64_t ldb, double* y, int threads)
 {
-    if (N < 0 || K < 0 || (K > 0 && ldb < N))
+    const double* dec = table_of(dtype);
+    if (!dec || N < 0 || K < 0 || (K > 0 && ldb < N))
         return -1;
-    build_decode_table();
     int nt = threads > 0 ? threads : omp_get_max_threads();
     #pragma omp parallel for schedule(static) num_threads(nt)
     for (int64_t n = 0; n < N; ++n) {
         double s = 0.0;
         for (int64_t k = 0; k < K; ++k)
-            s += g_dec[x[k]] * g_dec[B[k * ldb + n]];
+            s += dec[x[k]] * dec[B[k * ldb + n]];
         y[n] = s;
     }
     return 0;

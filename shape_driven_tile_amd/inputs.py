@@ -5,6 +5,10 @@ tests.  It holds no arithmetic of the method: it only draws numbers and lays
 them out in memory.  Every array is a host numpy array of float16; callers copy
 it to the device themselves.
 
+bfloat16 arrays are handed around as uint16 bit patterns (numpy has no
+bfloat16 type): the fp64 draw is cast to float32 by numpy and then to
+bfloat16 by torch, both rounding to nearest even.
+
 Distributions (the pages state the shapes, not the generator):
   * square GEMM operands: uniform in [-1, 1], drawn in fp64 with numpy's PCG64
     ``default_rng(seed).uniform``, then cast to float16 (round to nearest even);
@@ -82,3 +86,54 @@ def decode_weights_kn(r: int, n: int = DECODE_N, k: int = DECODE_K) -> np.ndarra
     """The same matrix as decode_weights(r), stored the other way round:
     K rows of N contiguous values (a layout change only)."""
     return np.ascontiguousarray(decode_weights(r, n, k).T)
+
+
+# ---- bfloat16 (uint16 bit patterns) --------------------------------------------
+
+BF16_NAN_BITS = 0x7FC0
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """Cast an array of draws to bfloat16 bit patterns (float32 by numpy, then
+    bfloat16 by torch; both round to nearest even)."""
+    import torch
+    f32 = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    return torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def uniform_bf16(shape, seed: int) -> np.ndarray:
+    """bfloat16 bits, values uniform in [-1, 1]."""
+    return to_bf16_bits(np.random.default_rng(seed).uniform(-1.0, 1.0, size=shape))
+
+
+def normal_bf16(shape, seed: int, std: float = 0.02) -> np.ndarray:
+    return to_bf16_bits(np.random.default_rng(seed).normal(0.0, std, size=shape))
+
+
+def integer_bf16(shape, seed: int, lo: int = -2, hi: int = 2) -> np.ndarray:
+    """bfloat16 bits of integers drawn uniformly from [lo, hi] (exact)."""
+    return to_bf16_bits(np.random.default_rng(seed).integers(lo, hi + 1, size=shape))
+
+
+def padded_bits(a: np.ndarray, ld: int, fill_bits: int = BF16_NAN_BITS) -> np.ndarray:
+    """Copy a 2-D uint16 bit array into (rows, ld) with `fill_bits` (a
+    bfloat16 NaN by default) in the columns past the original width."""
+    rows, cols = a.shape
+    if ld < cols:
+        raise ValueError("ld smaller than the row length")
+    out = np.full((rows, ld), fill_bits, dtype=np.uint16)
+    out[:, :cols] = a
+    return out
+
+
+def square_operands_bf16(n: int, c: int, k: int | None = None):
+    k = n if k is None else k
+    return uniform_bf16((n, k), SEED_A + c), uniform_bf16((n, k), SEED_B + c)
+
+
+def decode_activations_bf16(k: int = DECODE_K) -> np.ndarray:
+    return uniform_bf16((k,), SEED_X)
+
+
+def decode_weights_bf16(r: int, n: int = DECODE_N, k: int = DECODE_K) -> np.ndarray:
+    return normal_bf16((n, k), SEED_W + r)

@@ -272,4 +272,105 @@ def pin_gemv_kn(o):
             abs(Fraction(float(xs[k])) * Fraction(float(Ws[k, n]))) for k in range(5))
 
 
+# ---- bfloat16 -------------------------------------------------------------------
+
+def _torch_bf16_dec(bits):
+    import torch
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def pin_bf16_decode_exhaustive(o):
+    got = o.bf16_decode(ALL_BITS)
+    want = _torch_bf16_dec(ALL_BITS)
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all()
+    assert (got[~nan] == want[~nan]).all()
+    assert (np.signbit(got[~nan]) == np.signbit(want[~nan])).all()
+
+
+def pin_bf16_encode_roundtrip(o):
+    v = _torch_bf16_dec(ALL_BITS)
+    fin = np.isfinite(v)
+    assert (o.bf16_encode_rne(v[fin]) == ALL_BITS[fin]).all()
+
+
+def pin_bf16_encode_rne_ties(o):
+    """Every midpoint between adjacent positive finite values rounds to the
+    even pattern; one fp64 ulp either side rounds to the nearer neighbour."""
+    lo = np.arange(0, 0x7F7F, dtype=np.uint16)
+    a = _torch_bf16_dec(lo)
+    b = _torch_bf16_dec(lo + 1)
+    mid = (a + b) / 2                        # exact in fp64
+    even = np.where(lo % 2 == 0, lo, lo + 1).astype(np.uint16)
+    assert (o.bf16_encode_rne(mid) == even).all()
+    assert (o.bf16_encode_rne(np.nextafter(mid, 0)) == lo).all()
+    assert (o.bf16_encode_rne(np.nextafter(mid, np.inf)) == lo + 1).all()
+    assert (o.bf16_encode_rne(-mid) == (even | 0x8000)).all()
+
+
+def pin_bf16_encode_vs_torch(o):
+    """fp32 values over the whole range, rounded by torch's float -> bfloat16."""
+    import torch
+    rng = np.random.default_rng(91)
+    m = rng.uniform(1.0, 2.0, 400_000)
+    e = rng.integers(-140, 128, 400_000)
+    x = (np.where(rng.integers(0, 2, 400_000) == 1, -1.0, 1.0) * np.ldexp(m, e)).astype(np.float32)
+    x = x[np.isfinite(x)]
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert (o.bf16_encode_rne(x.astype(np.float64)) == want).all()
+
+
+def pin_bf16_encode_special_values(o):
+    cases = [(1.0, 0x3F80), (-2.0, 0xC000), (0.0, 0x0000), (-0.0, 0x8000),
+             (255 * 2.0 ** 120, 0x7F7F), (255.5 * 2.0 ** 120, 0x7F80),
+             (np.nextafter(255.5 * 2.0 ** 120, 0), 0x7F7F), (np.inf, 0x7F80),
+             (-np.inf, 0xFF80), (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000),
+             (3 * 2.0 ** -134, 0x0002), (2.0 ** -126, 0x0080), (1.0 + 2.0 ** -8, 0x3F80),
+             (1.0 + 3 * 2.0 ** -8, 0x3F82)]
+    for x, bits in cases:
+        assert int(o.bf16_encode_rne(np.array([x]))[0]) == bits, (x, hex(bits))
+    n = int(o.bf16_encode_rne(np.array([np.nan]))[0])
+    assert (n & 0x7F80) == 0x7F80 and (n & 0x7F) != 0
+
+
+def pin_bf16_gemm(o):
+    """The bfloat16 entry points: the same sums over the bfloat16 decode."""
+    # exact integers
+    A = inputs.integer_bf16((13, 70), 92)
+    B = inputs.integer_bf16((11, 70), 93)
+    Ai = _torch_bf16_dec(A).astype(np.int64)
+    Bi = _torch_bf16_dec(B).astype(np.int64)
+    assert (o.gemm(A, B, dtype="bf16") == (Ai @ Bi.T).astype(np.float64)).all()
+    # 0x3F80 is 1.0 in bfloat16 (and 1.875 in binary16): all-ones -> K
+    ones = np.full((3, 257), 0x3F80, np.uint16)
+    assert (o.gemm(ones, ones, dtype="bf16") == 257).all()
+    # exact rationals
+    a = inputs.uniform_bf16((2, 6), 94)
+    b = inputs.uniform_bf16((3, 6), 95)
+    C = o.gemm(a, b, dtype="bf16")
+    fa, fb = _torch_bf16_dec(a), _torch_bf16_dec(b)
+    for i in range(2):
+        for j in range(3):
+            terms = [Fraction(float(fa[i, k])) * Fraction(float(fb[j, k])) for k in range(6)]
+            assert abs(Fraction(C[i, j]) - sum(terms)) <= Fraction(6 * U) * sum(abs(t) for t in terms)
+    # fp64 cross-check with a bound, padding ignored, sampled = full
+    A = inputs.uniform_bf16((40, 300), 96)
+    B = inputs.uniform_bf16((30, 300), 97)
+    Cf = o.gemm(inputs.padded_bits(A, 312), inputs.padded_bits(B, 304), K=300, dtype="bf16")
+    fa, fb = _torch_bf16_dec(A), _torch_bf16_dec(B)
+    assert (np.abs(Cf - fa @ fb.T) <= 2 * 300 * U * (np.abs(fa) @ np.abs(fb).T)).all()
+    r = np.array([0, 39, 7, 21])
+    c = np.array([0, 29, 3, 17])
+    assert (o.gemm_sample(A, B, r, c, dtype="bf16") == Cf[r, c]).all()
+    # GEMV in both layouts = the one-row GEMM
+    x = inputs.uniform_bf16((300,), 98)
+    y = o.gemv_m1(x, inputs.padded_bits(B, 304), K=300, dtype="bf16")
+    assert (y == o.gemm(x[None, :], B, dtype="bf16")[0]).all()
+    assert (o.gemv_kn(x, np.ascontiguousarray(B.T), dtype="bf16") == y).all()
+    e = np.zeros(300, np.uint16)
+    e[123] = 0x3F80
+    assert (o.gemv_m1(e, B, dtype="bf16") == fb[:, 123]).all()
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
