@@ -509,7 +509,81 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             f"{det['decode_kn_cold']['variants'][str(v)]['GBps_weights_median']} GB/s")
     det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
                                          "200 launches x 10 repeats, event-timed")
+    det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)
     return det
+
+
+def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):
+    """The bfloat16 entry points on the same shapes: a sampled oracle gate,
+    then graph-timed squares and the cold decode protocol."""
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def bits(t):
+        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+    out = {"square_graph": {}, "decode_cold": {}}
+    for n in SIZES:
+        A, B = inputs.square_operands_bf16(n, SEED_INDEX[n])
+        dA, dB = to_dev(A), to_dev(B)
+        C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+        sdt.gemm_bf16(dA, dB, C)
+        torch.cuda.synchronize()
+        rng = np.random.default_rng(n + 1)
+        r = rng.integers(0, n, 1024)
+        c = rng.integers(0, n, 1024)
+        ref = oracle.gemm_sample(A, B, r, c, dtype="bf16")
+        got = oracle.bf16_decode(bits(C)[r, c])
+        bad = int((~(np.abs(got - ref) <= oracle.tolerance(ref, "bf16"))).sum())
+        if bad:
+            out["square_graph"][str(n)] = {"gate": f"{bad} of 1024 sampled outside tolerance"}
+            log(f"bf16 square {n}: PARITY FAILED ({bad}), not timed")
+            continue
+        chain = 200 if n <= 2048 else (20 if n == 4096 else 5)
+        us, _ = graph_launches(torch, (lambda j, dA=dA, dB=dB, C=C: sdt.gemm_bf16(dA, dB, C)), chain)
+        med = sorted(us)[len(us) // 2]
+        out["square_graph"][str(n)] = {
+            "us": _ranges(us), "launches_per_graph": chain, "gate": "pass",
+            "tflops_median": round(flop_gemm[n] / (med * 1e-6) / 1e12, 1),
+            "peak_frac_median": round(flop_gemm[n] / (med * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4),
+        }
+        log(f"bf16 square {n} (graph): median {med:.2f} us "
+            f"{out['square_graph'][str(n)]['tflops_median']} TFLOP/s")
+        del dA, dB, C
+    x_h = inputs.decode_activations_bf16()
+    W_h = [inputs.decode_weights_bf16(r) for r in range(inputs.DECODE_BUFFERS)]
+    x = to_dev(x_h)
+    Ws = [to_dev(w) for w in W_h]
+    y = torch.empty((inputs.DECODE_N,), dtype=torch.bfloat16, device=dev)
+    bad = 0
+    for r in range(inputs.DECODE_BUFFERS):
+        sdt.gemv_bf16_m1(x, Ws[r], y)
+        torch.cuda.synchronize()
+        ref = oracle.gemv_m1(x_h, W_h[r], dtype="bf16")
+        bad += int((~(np.abs(oracle.bf16_decode(bits(y)) - ref) <= oracle.tolerance(ref, "bf16"))).sum())
+    if bad:
+        out["decode_cold"] = {"gate": f"{bad} outside tolerance"}
+        log(f"bf16 decode: PARITY FAILED ({bad}), not timed")
+        return out
+    g = (lambda j: sdt.gemv_bf16_m1(x, Ws[j % len(Ws)], y))
+    t0 = time.time()
+    j = 0
+    while time.time() - t0 < 1.0:
+        g(j)
+        j += 1
+        if j % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    us = time_launches(torch, g, 200)
+    med = sorted(us)[len(us) // 2]
+    out["decode_cold"] = {
+        "us": _ranges(us), "gate": "pass",
+        "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
+        "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "protocol": "8 rotating bf16 buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
+    }
+    log(f"bf16 decode cold: median {med:.2f} us = {out['decode_cold']['GBps_weights_median']} GB/s")
+    return out
 
 
 def cpu_baseline(oracle, AB, target_s):

@@ -98,6 +98,24 @@ int gemv_f16_m1(int64_t N, int64_t K, const void* x,
 int gemv_f16_m1_kn(int64_t N, int64_t K, const void* x,
                    const void* B, int64_t ldb, void* y, void* stream);
 
+/* ---- bfloat16 variants ------------------------------------------------------
+ * The same products with bfloat16 operands and output (1 sign, 8 exponent,
+ * 7 fraction bits; fp32 accumulation on v_mfma_f32_32x32x16_bf16 /
+ * v_dot2_f32_bf16; fp32 -> bf16 round-to-nearest-even).  The FlyDSL pull
+ * request measures its square GEMMs in bf16 (Performance), and the mojo-baro
+ * page's decode rounds run bf16 weight arms ("Four rounds on the decode
+ * shape").  Same layouts, requirements, tile choice, statuses and
+ * degenerate-size behaviour as the fp16 entry point of the same name;
+ * gemm_bf16 with M == 1 runs gemv_bf16_m1. */
+int gemm_bf16(int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda,
+              const void* B, int64_t ldb,
+              void* C, int64_t ldc, void* stream);
+int gemv_bf16_m1(int64_t N, int64_t K, const void* x,
+                 const void* B, int64_t ldb, void* y, void* stream);
+int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x,
+                    const void* B, int64_t ldb, void* y, void* stream);
+
 /* ---- test / benchmark extras ---------------------------------------------- */
 
 /* gemm_f16 with the launcher's choices forced.  tile_id: -1 = automatic,
@@ -109,6 +127,13 @@ int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 const void* B, int64_t ldb,
                 void* C, int64_t ldc, void* stream,
                 int tile_id, int stagger);
+
+/* gemm_bf16 with the launcher's choices forced (as gemm_f16_ex). */
+int gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc, void* stream,
+                 int tile_id, int stagger);
 
 /* gemv_f16_m1 with the kernel instantiation forced: variant in
  * [0, sdt_gemv_num_variants()) selects how many output columns one wave

@@ -23,6 +23,7 @@ SDT_ERR_HIP = 3
 EXPORTS = (
     "gemm_f16", "gemv_f16_m1", "gemm_f16_ex", "gemv_f16_m1_ex", "sdt_gemv_num_variants",
     "gemv_f16_m1_kn", "gemv_f16_m1_kn_ex", "sdt_gemv_kn_num_variants", "sdt_check_gemv_kn_args",
+    "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
     "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel",
@@ -68,6 +69,10 @@ def lib():
     L.gemv_f16_m1_ex.argtypes = L.gemv_f16_m1.argtypes + [_int]
     L.sdt_gemv_num_variants.argtypes = []
     L.gemv_f16_m1_kn.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp, _vp]
+    L.gemm_bf16.argtypes = L.gemm_f16.argtypes
+    L.gemm_bf16_ex.argtypes = L.gemm_f16_ex.argtypes
+    L.gemv_bf16_m1.argtypes = L.gemv_f16_m1.argtypes
+    L.gemv_bf16_m1_kn.argtypes = L.gemv_f16_m1_kn.argtypes
     L.gemv_f16_m1_kn_ex.argtypes = L.gemv_f16_m1_kn.argtypes + [_int]
     L.sdt_gemv_kn_num_variants.argtypes = []
     L.sdt_check_gemv_kn_args.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp]
@@ -85,6 +90,7 @@ def lib():
     L.sdt_empty_kernel.argtypes = [_vp]
     for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
                  "gemv_f16_m1_kn", "gemv_f16_m1_kn_ex", "sdt_gemv_kn_num_variants",
+                 "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
                  "sdt_check_gemv_kn_args",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_check_gemm_args",
@@ -163,10 +169,11 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _rows(t, name):
+def _rows(t, name, dtype=None):
     import torch
-    if t.dtype != torch.float16:
-        raise TypeError(f"{name} must be float16, got {t.dtype}")
+    dtype = torch.float16 if dtype is None else dtype
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a device tensor")
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -248,6 +255,61 @@ def gemv_f16_m1_kn(x, B, y, stream=None, variant: int | None = None) -> None:
         rc = lib().gemv_f16_m1_kn_ex(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h, int(variant))
     if rc != SDT_OK:
         raise SdtError(rc, "gemv_f16_m1_kn")
+
+
+def _gemm_16(entry, A, B, C, stream, dtype, extra=()):
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    pa, lda = _rows(A, "A", dtype)
+    pb, ldb = _rows(B, "B", dtype)
+    pc, ldc = _rows(C, "C", dtype)
+    rc = getattr(lib(), entry)(M, N, K, pa, lda, pb, ldb, pc, ldc, _stream_handle(stream),
+                               *extra)
+    if rc != SDT_OK:
+        raise SdtError(rc, entry)
+
+
+def gemm_bf16(A, B, C, stream=None) -> None:
+    """C[M, N] = A[M, K] . B[N, K]^T with torch.bfloat16 tensors, fp32
+    accumulate, bf16 out (round to nearest even)."""
+    import torch
+    _gemm_16("gemm_bf16", A, B, C, stream, torch.bfloat16)
+
+
+def gemm_bf16_ex(A, B, C, tile_id: int = -1, stagger: int = -1, stream=None) -> None:
+    import torch
+    _gemm_16("gemm_bf16_ex", A, B, C, stream, torch.bfloat16, (int(tile_id), int(stagger)))
+
+
+def _gemv_16(entry, x, B, y, stream, dtype, kn):
+    if x.dtype != dtype or y.dtype != dtype:
+        raise TypeError(f"x and y must be {dtype}")
+    if x.dim() != 1 or y.dim() != 1 or x.stride(0) != 1 or y.stride(0) != 1:
+        raise ValueError("x and y must be contiguous vectors")
+    if kn:
+        K, N = B.shape
+    else:
+        N, K = B.shape
+    if x.shape[0] != K or y.shape[0] != N:
+        raise ValueError(f"shape mismatch x{tuple(x.shape)} B{tuple(B.shape)} y{tuple(y.shape)}")
+    pb, ldb = _rows(B, "B", dtype)
+    rc = getattr(lib(), entry)(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, entry)
+
+
+def gemv_bf16_m1(x, B, y, stream=None) -> None:
+    """y[N] = x[K] . B[N, K]^T with torch.bfloat16 tensors (B stored K-major)."""
+    import torch
+    _gemv_16("gemv_bf16_m1", x, B, y, stream, torch.bfloat16, kn=False)
+
+
+def gemv_bf16_m1_kn(x, B, y, stream=None) -> None:
+    """y[N] = x[K] . B[K, N] with torch.bfloat16 tensors (B as K rows of N)."""
+    import torch
+    _gemv_16("gemv_bf16_m1_kn", x, B, y, stream, torch.bfloat16, kn=True)
 
 
 def gemm_f16_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream_ptr=None) -> int:

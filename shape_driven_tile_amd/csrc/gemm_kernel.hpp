@@ -1,13 +1,14 @@
-// gfx950 fp16 GEMM kernel family: C = A.B, fp32 accumulation on MFMA, fp16
-// (round-to-nearest-even) output.
+// gfx950 GEMM kernel family: C = A.B for fp16 or bf16 operands, fp32
+// accumulation on MFMA, output in the operand type (round-to-nearest-even).
 //
 // After "Beating hipBLASLt on a Gaming GPU" (section "The result": two LDS
 // buffers, one barrier per K-step, prefetch of the next tiles while the
 // current one is consumed, an XOR swizzle, B stored transposed) and "The part
 // that actually mattered" (the tile is a compile-time parameter with its own
 // wave layout), re-designed for CDNA4:
-//   * wave64 and v_mfma_f32_32x32x16_f16: each wave owns a (BM/WM) x (BN/WN)
-//     block of 32x32 accumulator tiles;
+//   * wave64 and v_mfma_f32_32x32x16_f16 (v_mfma_f32_32x32x16_bf16 for the
+//     bf16 variant): each wave owns a (BM/WM) x (BN/WN) block of 32x32
+//     accumulator tiles;
 //   * both operands are K-contiguous rows (A row-major, B "K-major"), staged
 //     the same way: a k-tile is BM (or BN) rows of 64 fp16 = 128 bytes, eight
 //     16-byte chunks per row; chunk c of row r is stored at chunk c ^ swz(r),
@@ -52,6 +53,10 @@ namespace sdt {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
@@ -70,6 +75,35 @@ struct GemmParams {
     int gm, gn;    // output tiles along M and N
     int stagger;   // 1: full k-tiles in (w + i) & (K/64 - 1) order
     int nxcd;      // XCDs the dispatcher deals workgroups over
+};
+
+// Element types.  Each names its vector types, the 32x32x16 MFMA, the
+// two-term dot product into fp32 used by the GEMV kernels, and (through
+// `scalar`) the fp32 -> 16-bit conversion of the epilogues, which rounds to
+// nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32 under the default mode).
+struct F16 {
+    typedef half8_t frag8;
+    typedef half4_t vec4;
+    typedef half2_t vec2;
+    typedef _Float16 scalar;
+    static __device__ __forceinline__ floatx16_t mfma(frag8 a, frag8 b, floatx16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
+        return __builtin_amdgcn_fdot2(a, b, c, false);
+    }
+};
+struct BF16 {
+    typedef bf16x8_t frag8;
+    typedef bf16x4_t vec4;
+    typedef bf16x2_t vec2;
+    typedef __bf16 scalar;
+    static __device__ __forceinline__ floatx16_t mfma(frag8 a, frag8 b, floatx16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
+        return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+    }
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
@@ -124,8 +158,11 @@ __device__ __forceinline__ void wait_global_loads() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
+template <typename Elt, int BM, int BN, int WM, int WN, int NS>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
+    typedef typename Elt::frag8 frag8;
+    typedef typename Elt::vec4 vec4;
+    typedef typename Elt::scalar scalar;
     constexpr int BK = kBK;
     constexpr int NW = WM * WN;
     constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -238,24 +275,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
     const int fhalf = lane >> 5;
     const int a_row0 = wave_m * WTM + frow;
     const int b_row0 = wave_n * WTN + frow;
-    half8_t fa[2][FM], fb[2][FN];
+    frag8 fa[2][FM], fb[2][FN];
     auto read_frags = [&](int stage, int kk, int set) {
         const int4_t* base = smem + stage * STAGE;
         const int chunk = (2 * kk + fhalf) ^ fsw;
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-            fa[set][j] = __builtin_bit_cast(half8_t, base[(a_row0 + j * 32) * 8 + chunk]);
+            fa[set][j] = __builtin_bit_cast(frag8, base[(a_row0 + j * 32) * 8 + chunk]);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            fb[set][i] = __builtin_bit_cast(half8_t, base[A_UNITS + (b_row0 + i * 32) * 8 + chunk]);
+            fb[set][i] = __builtin_bit_cast(frag8, base[A_UNITS + (b_row0 + i * 32) * 8 + chunk]);
     };
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fb[set][i], fa[set][j],
-                                                                   acc[i][j], 0, 0, 0);
+                acc[i][j] = Elt::mfma(fb[set][i], fa[set][j], acc[i][j]);
     };
     // One MFMA, then one fragment read and one global load while any remain
     // (scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x020 global read).
@@ -330,7 +366,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
         s = sn;
     }
 
-    // ---- epilogue: fp32 -> fp16 (RNE), masked 8-byte stores ------------------------
+    // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked 8-byte stores -----------------
 #pragma unroll
     for (int i2 = 0; i2 < FN; ++i2) {
 #pragma unroll
@@ -341,17 +377,17 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_f16_kernel(GemmParams p) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
                 const int64_t n = n0 + wave_n * WTN + i2 * 32 + 8 * gq + 4 * fhalf;
-                half4_t h;
-                h[0] = (_Float16)acc[i2][j][4 * gq + 0];
-                h[1] = (_Float16)acc[i2][j][4 * gq + 1];
-                h[2] = (_Float16)acc[i2][j][4 * gq + 2];
-                h[3] = (_Float16)acc[i2][j][4 * gq + 3];
+                vec4 h;
+                h[0] = (scalar)acc[i2][j][4 * gq + 0];
+                h[1] = (scalar)acc[i2][j][4 * gq + 1];
+                h[2] = (scalar)acc[i2][j][4 * gq + 2];
+                h[3] = (scalar)acc[i2][j][4 * gq + 3];
                 if (n + 3 < p.N) {
                     *reinterpret_cast<uint2_t*>(crow + n) = __builtin_bit_cast(uint2_t, h);
                 } else {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const _Float16 v = h[e];   // element first, then reinterpret
+                        const scalar v = h[e];   // element first, then reinterpret
                         if (n + e < p.N) crow[n + e] = __builtin_bit_cast(uint16_t, v);
                     }
                 }

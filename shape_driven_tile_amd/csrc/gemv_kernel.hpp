@@ -1,5 +1,6 @@
-// gfx950 M=1 decode GEMV: y(n) = sum_k x(k) * B[n*ldb + k], fp32 accumulation,
-// fp16 (round-to-nearest-even) output.
+// gfx950 M=1 decode GEMV: y(n) = sum_k x(k) * B[n*ldb + k] for fp16 or bf16
+// operands, fp32 accumulation, output in the operand type (round-to-nearest-
+// even).
 //
 // The mojo-baro page ("Four rounds on the decode shape") finds this shape
 // bound by how well the weight stream is coalesced (v1), by bandwidth
@@ -18,8 +19,8 @@
 //     and only a ragged last pass masks element by element;
 //   * the activations stay in registers (XCH chunks of 8 per lane, i.e. K up
 //     to XCH * 512 per pass);
-//   * products go through v_dot2_f32_f16 into fp32; one cross-lane reduction
-//     per column at the end; nothing is staged in LDS.
+//   * products go through v_dot2_f32_f16 (v_dot2_f32_bf16) into fp32; one
+//     cross-lane reduction per column at the end; nothing is staged in LDS.
 // Weight loads are non-temporal: every byte is used once.
 #pragma once
 
@@ -29,8 +30,6 @@
 #include "gemm_kernel.hpp"
 
 namespace sdt {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 struct GemvParams {
     const uint16_t* x;
@@ -58,24 +57,27 @@ __device__ __forceinline__ int4_t gemv_chunk(const uint16_t* row, int k, int K, 
     return v;
 }
 
-// Four v_dot2_f32_f16 over one 16-byte chunk of weights and activations.
-// The chunks are reinterpreted whole and then indexed: reinterpreting a
-// single element of an int vector with __builtin_bit_cast is lowered by this
-// compiler as if it were always element 0.
+// Four two-term dot products over one 16-byte chunk of weights and
+// activations.  The chunks are reinterpreted whole and then indexed:
+// reinterpreting a single element of an int vector with __builtin_bit_cast
+// is lowered by this compiler as if it were always element 0.
+template <typename Elt>
 __device__ __forceinline__ float dot8(int4_t w, int4_t x, float acc) {
-    const half8_t wh = __builtin_bit_cast(half8_t, w);
-    const half8_t xh = __builtin_bit_cast(half8_t, x);
+    typedef typename Elt::frag8 frag8;
+    typedef typename Elt::vec2 vec2;
+    const frag8 wh = __builtin_bit_cast(frag8, w);
+    const frag8 xh = __builtin_bit_cast(frag8, x);
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        const half2_t a = {wh[2 * d], wh[2 * d + 1]};
-        const half2_t b = {xh[2 * d], xh[2 * d + 1]};
-        acc = __builtin_amdgcn_fdot2(a, b, acc, false);
+        const vec2 a = {wh[2 * d], wh[2 * d + 1]};
+        const vec2 b = {xh[2 * d], xh[2 * d + 1]};
+        acc = Elt::dot2(a, b, acc);
     }
     return acc;
 }
 
-template <int RPW, int XCH>
-__global__ __launch_bounds__(256) void gemv_f16_m1_kernel(GemvParams p) {
+template <typename Elt, int RPW, int XCH>
+__global__ __launch_bounds__(256) void gemv_m1_kernel(GemvParams p) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int64_t n0 = wave * RPW;
@@ -120,7 +122,7 @@ __global__ __launch_bounds__(256) void gemv_f16_m1_kernel(GemvParams p) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
-            for (int j = 0; j < XCH; ++j) acc[r] = dot8(wv[r][j], xr[j], acc[r]);
+            for (int j = 0; j < XCH; ++j) acc[r] = dot8<Elt>(wv[r][j], xr[j], acc[r]);
     }
 
 #pragma unroll
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(256) void gemv_f16_m1_kernel(GemvParams p) {
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
         if (lane == 0 && n0 + r < p.N) {
-            const _Float16 h = (_Float16)v;
+            const typename Elt::scalar h = (typename Elt::scalar)v;
             p.y[n0 + r] = __builtin_bit_cast(uint16_t, h);
         }
     }
@@ -166,12 +168,14 @@ struct GemvKnParams {
 
 // acc[c] += x(r) * w(r, c) for the first `rows` of eight rows.  The chunks are
 // reinterpreted whole, then indexed (see dot8).
+template <typename Elt>
 __device__ __forceinline__ void kn_block(int4_t xv, const int4_t* w, int rows, float* acc) {
-    const half8_t xh = __builtin_bit_cast(half8_t, xv);
+    typedef typename Elt::frag8 frag8;
+    const frag8 xh = __builtin_bit_cast(frag8, xv);
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
         if (r < rows) {
-            const half8_t wh = __builtin_bit_cast(half8_t, w[r]);
+            const frag8 wh = __builtin_bit_cast(frag8, w[r]);
             const float xr = (float)xh[r];
 #pragma unroll
             for (int c = 0; c < 8; ++c) acc[c] = __builtin_fmaf(xr, (float)wh[c], acc[c]);
@@ -179,7 +183,7 @@ __device__ __forceinline__ void kn_block(int4_t xv, const int4_t* w, int rows, f
     }
 }
 
-template <int SEG, int NW>
+template <typename Elt, int SEG, int NW>
 __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
     constexpr int BW = SEG * 8;          // columns per workgroup
     constexpr int RGW = 64 / SEG;        // row groups per wave
@@ -220,8 +224,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
             for (int r = 0; r < 8; ++r)
                 w1[r] = __builtin_nontemporal_load(
                     reinterpret_cast<const int4_t*>(col + (int64_t)(k1 + r) * p.ldb));
-            kn_block(x0, w0, 8, acc);
-            kn_block(x1, w1, 8, acc);
+            kn_block<Elt>(x0, w0, 8, acc);
+            kn_block<Elt>(x1, w1, 8, acc);
         }
         if (b < nblk) {
             const int k0 = 8 * b;
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
             for (int r = 0; r < 8; ++r)
                 w0[r] = __builtin_nontemporal_load(
                     reinterpret_cast<const int4_t*>(col + (int64_t)(k0 + r) * p.ldb));
-            kn_block(x0, w0, 8, acc);
+            kn_block<Elt>(x0, w0, 8, acc);
         }
     } else {                             // ragged last band: masked columns
         for (int b = rg; b < nblk; b += RG) {
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
 #pragma unroll
             for (int r = 0; r < 8; ++r)
                 w0[r] = gemv_chunk(p.B + (int64_t)(k0 + r) * p.ldb, n0, p.N, true);
-            kn_block(x0, w0, 8, acc);
+            kn_block<Elt>(x0, w0, 8, acc);
         }
     }
     if (krem > 0 && rg == nblk % RG) {   // ragged last block of rows
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
         for (int r = 0; r < 8; ++r)
             w0[r] = (r < krem) ? gemv_chunk(p.B + (int64_t)(k0 + r) * p.ldb, n0, p.N, true)
                                : int4_t{0, 0, 0, 0};
-        kn_block(x0, w0, krem, acc);
+        kn_block<Elt>(x0, w0, krem, acc);
     }
 
     // fixed-order reduction of the RG partial sums of each column
@@ -273,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
 #pragma unroll
         for (int q = 0; q < PARTS; ++q) s += part[q * BW + t];
         if (nb + t < p.N) {
-            const _Float16 h = (_Float16)s;
+            const typename Elt::scalar h = (typename Elt::scalar)s;
             p.y[nb + t] = __builtin_bit_cast(uint16_t, h);
         }
     }

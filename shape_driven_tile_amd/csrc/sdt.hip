@@ -1,4 +1,5 @@
-// C ABI of the MI355X fp16 GEMM / M=1 GEMV library (declared in sdt.h).
+// C ABI of the MI355X fp16 / bf16 GEMM and M=1 GEMV library (declared in
+// sdt.h).
 // Validates arguments on the host, picks the kernel instantiation and
 // enqueues it on the caller's stream.  Allocates nothing.
 #include <hip/hip_runtime.h>
@@ -53,27 +54,28 @@ int device_info(DeviceInfo* out) {
     return SDT_OK;
 }
 
-template <int BM, int BN, int WM, int WN, int NS>
+template <typename Elt, int BM, int BN, int WM, int WN, int NS>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_f16_kernel<BM, BN, WM, WN, NS>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS>),
                            dim3(p.gm * p.gn), dim3(WM * WN * 64), args, 0, stream);
 }
 
-template <int I>
+template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, hipStream_t s) {
-    return launch_gemm_tile<kLadder[I].bm, kLadder[I].bn, kLadder[I].waves_m,
+    return launch_gemm_tile<Elt, kLadder[I].bm, kLadder[I].bn, kLadder[I].waves_m,
                             kLadder[I].waves_n, kLadder[I].stages>(p, s);
 }
 
+template <typename Elt>
 hipError_t launch_gemm(int id, GemmParams p, hipStream_t s) {
     static_assert(kNumTiles == 5, "dispatch table below lists every rung");
     switch (id) {
-        case 0: return launch_rung<0>(p, s);
-        case 1: return launch_rung<1>(p, s);
-        case 2: return launch_rung<2>(p, s);
-        case 3: return launch_rung<3>(p, s);
-        default: return launch_rung<4>(p, s);
+        case 0: return launch_rung<Elt, 0>(p, s);
+        case 1: return launch_rung<Elt, 1>(p, s);
+        case 2: return launch_rung<Elt, 2>(p, s);
+        case 3: return launch_rung<Elt, 3>(p, s);
+        default: return launch_rung<Elt, 4>(p, s);
     }
 }
 
@@ -95,15 +97,16 @@ int fill_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream
 constexpr int kGemvRpw[] = {1, 2, 4, 8};
 constexpr int kGemvVariants = sizeof(kGemvRpw) / sizeof(kGemvRpw[0]);
 
-template <int RPW>
+template <typename Elt, int RPW>
 hipError_t launch_gemv_rpw(GemvParams p, hipStream_t stream) {
     const int64_t waves = (p.N + RPW - 1) / RPW;
     const int64_t blocks = (waves + 3) / 4;
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_f16_m1_kernel<RPW, 8>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8>),
                            dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
+template <typename Elt>
 int launch_gemv(int variant, int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
                 void* y, hipStream_t stream) {
     if (N > INT_MAX) return SDT_ERR_UNSUPPORTED;
@@ -117,10 +120,10 @@ int launch_gemv(int variant, int64_t N, int64_t K, const void* x, const void* B,
     p.K = (int)K;
     hipError_t e;
     switch (kGemvRpw[variant]) {
-        case 1: e = launch_gemv_rpw<1>(p, stream); break;
-        case 2: e = launch_gemv_rpw<2>(p, stream); break;
-        case 8: e = launch_gemv_rpw<8>(p, stream); break;
-        default: e = launch_gemv_rpw<4>(p, stream); break;
+        case 1: e = launch_gemv_rpw<Elt, 1>(p, stream); break;
+        case 2: e = launch_gemv_rpw<Elt, 2>(p, stream); break;
+        case 8: e = launch_gemv_rpw<Elt, 8>(p, stream); break;
+        default: e = launch_gemv_rpw<Elt, 4>(p, stream); break;
     }
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
@@ -133,14 +136,15 @@ struct GemvKnVariant {
 constexpr GemvKnVariant kGemvKn[] = {{8, 16}, {8, 8}, {4, 16}, {4, 8}};
 constexpr int kGemvKnVariants = sizeof(kGemvKn) / sizeof(kGemvKn[0]);
 
-template <int SEG, int NW>
+template <typename Elt, int SEG, int NW>
 hipError_t launch_gemv_kn_tile(GemvKnParams p, hipStream_t stream) {
     const int64_t blocks = ((int64_t)p.N + SEG * 8 - 1) / (SEG * 8);
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_kn_kernel<SEG, NW>),
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_kn_kernel<Elt, SEG, NW>),
                            dim3((unsigned)blocks), dim3(NW * 64), args, 0, stream);
 }
 
+template <typename Elt>
 int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
                    void* y, hipStream_t stream) {
     if (N > INT_MAX || K > INT_MAX) return SDT_ERR_UNSUPPORTED;
@@ -155,14 +159,15 @@ int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void*
     static_assert(kGemvKnVariants == 4, "dispatch below lists every variant");
     hipError_t e;
     switch (variant) {
-        case 1: e = launch_gemv_kn_tile<8, 8>(p, stream); break;
-        case 2: e = launch_gemv_kn_tile<4, 16>(p, stream); break;
-        case 3: e = launch_gemv_kn_tile<4, 8>(p, stream); break;
-        default: e = launch_gemv_kn_tile<8, 16>(p, stream); break;
+        case 1: e = launch_gemv_kn_tile<Elt, 8, 8>(p, stream); break;
+        case 2: e = launch_gemv_kn_tile<Elt, 4, 16>(p, stream); break;
+        case 3: e = launch_gemv_kn_tile<Elt, 4, 8>(p, stream); break;
+        default: e = launch_gemv_kn_tile<Elt, 8, 16>(p, stream); break;
     }
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
+template <typename Elt>
 int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
               int64_t ldb, void* C, int64_t ldc, void* stream, int tile_id, int stagger,
               bool route_m1) {
@@ -178,7 +183,7 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (M > INT_MAX || N > INT_MAX) return SDT_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (K == 0) return fill_zero(static_cast<uint16_t*>(C), ldc, M, N, s);
-    if (route_m1 && M == 1) return launch_gemv(0, N, K, A, B, ldb, C, s);
+    if (route_m1 && M == 1) return launch_gemv<Elt>(0, N, K, A, B, ldb, C, s);
 
     DeviceInfo dev;
     st = device_info(&dev);
@@ -204,7 +209,7 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     p.gn = (int)gn;
     p.stagger = use_stagger;
     p.nxcd = dev.nxcd;
-    hipError_t e = launch_gemm(id, p, s);
+    hipError_t e = launch_gemm<Elt>(id, p, s);
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
@@ -217,13 +222,26 @@ __global__ void empty_kernel() {}
 
 extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    return sdt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
 }
 
 extern "C" int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                            int tile_id, int stagger) {
-    return sdt::gemm_impl(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger, false);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger,
+                                    false);
+}
+
+extern "C" int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
+}
+
+extern "C" int gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                            int tile_id, int stagger) {
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger,
+                                     false);
 }
 
 extern "C" int gemv_f16_m1(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
@@ -231,7 +249,15 @@ extern "C" int gemv_f16_m1(int64_t N, int64_t K, const void* x, const void* B, i
     int st = sdt::check_gemm_args(1, N, K, x, K, B, ldb, y, N);
     if (st != SDT_OK) return st;
     if (N == 0) return SDT_OK;
-    return sdt::launch_gemv(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+    return sdt::launch_gemv<sdt::F16>(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+}
+
+extern "C" int gemv_bf16_m1(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                            void* y, void* stream) {
+    int st = sdt::check_gemm_args(1, N, K, x, K, B, ldb, y, N);
+    if (st != SDT_OK) return st;
+    if (N == 0) return SDT_OK;
+    return sdt::launch_gemv<sdt::BF16>(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
@@ -240,7 +266,8 @@ extern "C" int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x, const void* B
     int st = sdt::check_gemm_args(1, N, K, x, K, B, ldb, y, N);
     if (st != SDT_OK) return st;
     if (N == 0) return SDT_OK;
-    return sdt::launch_gemv(variant, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+    return sdt::launch_gemv<sdt::F16>(variant, N, K, x, B, ldb, y,
+                                      static_cast<hipStream_t>(stream));
 }
 
 extern "C" int sdt_gemv_num_variants(void) { return sdt::kGemvVariants; }
@@ -249,7 +276,16 @@ extern "C" int gemv_f16_m1_kn(int64_t N, int64_t K, const void* x, const void* B
                               void* y, void* stream) {
     int st = sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
     if (st != SDT_OK || N == 0) return st;
-    return sdt::launch_gemv_kn(0, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+    return sdt::launch_gemv_kn<sdt::F16>(0, N, K, x, B, ldb, y,
+                                         static_cast<hipStream_t>(stream));
+}
+
+extern "C" int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x, const void* B,
+                               int64_t ldb, void* y, void* stream) {
+    int st = sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
+    if (st != SDT_OK || N == 0) return st;
+    return sdt::launch_gemv_kn<sdt::BF16>(0, N, K, x, B, ldb, y,
+                                          static_cast<hipStream_t>(stream));
 }
 
 extern "C" int gemv_f16_m1_kn_ex(int64_t N, int64_t K, const void* x, const void* B,
@@ -257,7 +293,8 @@ extern "C" int gemv_f16_m1_kn_ex(int64_t N, int64_t K, const void* x, const void
     if (variant < 0 || variant >= sdt::kGemvKnVariants) return SDT_ERR_INVALID_ARG;
     int st = sdt::check_gemv_kn_args(N, K, x, B, ldb, y);
     if (st != SDT_OK || N == 0) return st;
-    return sdt::launch_gemv_kn(variant, N, K, x, B, ldb, y, static_cast<hipStream_t>(stream));
+    return sdt::launch_gemv_kn<sdt::F16>(variant, N, K, x, B, ldb, y,
+                                         static_cast<hipStream_t>(stream));
 }
 
 extern "C" int sdt_gemv_kn_num_variants(void) { return sdt::kGemvKnVariants; }

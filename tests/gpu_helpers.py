@@ -110,3 +110,58 @@ def run_gemv_kn(x, W, N=None, variant=None, y_pad=8):
     torch.cuda.synchronize()
     pad_ok = bool(torch.isnan(full[N:]).all().item())
     return dy.cpu().numpy(), pad_ok
+
+
+# ---- bfloat16 (uint16 bit patterns on the host) -----------------------------------
+
+def bits_to_dev_bf16(a: np.ndarray):
+    import torch
+    b = np.ascontiguousarray(np.asarray(a, dtype=np.uint16))
+    return torch.from_numpy(b.view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev_bf16_to_bits(t) -> np.ndarray:
+    import torch
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run_gemm_bf16(A, B, K=None, tile=None, stagger=-1):
+    """A: (M, lda), B: (N, ldb) uint16 bfloat16 bit arrays.  Returns C's bits
+    (M, N) and whether the C padding (NaN) stayed untouched."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    M, lda = A.shape
+    N, ldb = B.shape
+    K = lda if K is None else K
+    dA = bits_to_dev_bf16(A)[:, :K]
+    dB = bits_to_dev_bf16(B)[:, :K]
+    ldc = N if M == 1 else -(-N // 8) * 8 + 8
+    full = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
+    dC = full[:, :N]
+    if tile is None and stagger == -1:
+        sdt.gemm_bf16(dA, dB, dC)
+    else:
+        sdt.gemm_bf16_ex(dA, dB, dC, tile_id=-1 if tile is None else tile, stagger=stagger)
+    torch.cuda.synchronize()
+    pad_ok = bool(torch.isnan(full[:, N:]).all().item()) if ldc > N else True
+    return dev_bf16_to_bits(dC), pad_ok
+
+
+def assert_close_bf16(bits, ref):
+    ok, msg = tol_report_values(oracle.bf16_decode(bits), ref, "bf16")
+    assert ok, msg
+
+
+def tol_report_values(got64: np.ndarray, ref: np.ndarray, dtype: str) -> tuple[bool, str]:
+    tol = oracle.tolerance(ref, dtype)
+    err = np.abs(got64 - ref)
+    ok = err <= tol
+    bad = int((~ok).sum())
+    worst = float(np.nanmax(np.where(np.isfinite(err), err / tol, np.inf))) if err.size else 0.0
+    return bad == 0, f"{bad} of {got64.size} outside tolerance, worst |d|/tol = {worst:.3g}"
+
+
+def assert_bitexact_bf16(bits, ref):
+    want = oracle.bf16_encode_rne(ref)
+    diff = np.ascontiguousarray(bits) != want
+    assert not diff.any(), f"{int(diff.sum())} of {want.size} differ from the RNE oracle"
