@@ -55,7 +55,9 @@ typedef struct sdt_tile {
     int bm, bn, bk;
     int waves_m, waves_n;
     int threads;     /* 64 * waves_m * waves_n */
-    int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep */
+    int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep
+                        (sdt_pick_tile: the count a launch of that shape uses;
+                        sdt_tile_info: the rung's deep pipeline) */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16 */
 } sdt_tile;
 
@@ -167,9 +169,16 @@ int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
 int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
                   int rungs, const int64_t* min_blocks);
 
-/* Host-only: number of ladder rungs, and the description of rung tile_id. */
+/* Host-only: number of ladder rungs, and the description of rung tile_id
+ * (with its deep pipeline). */
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
+
+/* Host-only: the LDS stage count a launch of rung tile_id on an M x N x K
+ * product uses: 2 while the operands, 2*K*(M+N) bytes, fit in one MI355X
+ * XCD's 4 MiB L2 (the tiles arrive within a one-tile prefetch and the shorter
+ * prologue wins), else the rung's deep pipeline.  -1 on invalid input. */
+int sdt_stages_for(int tile_id, int64_t M, int64_t N, int64_t K);
 
 /* Host-only: 1 if the k-loop of a product with inner size K can be staggered,
  * else 0: the number of full 64-deep k-tiles floor(K/64) must be a power of

@@ -26,7 +26,7 @@ EXPORTS = (
     "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
-    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel",
+    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stages_for",
 )
 
 
@@ -80,6 +80,7 @@ def lib():
     L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
     L.sdt_num_tiles.argtypes = []
     L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
+    L.sdt_stages_for.argtypes = [_int, _i64, _i64, _i64]
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -93,7 +94,7 @@ def lib():
                  "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
                  "sdt_check_gemv_kn_args",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
-                 "sdt_tile_info", "sdt_stagger_eligible", "sdt_check_gemm_args",
+                 "sdt_tile_info", "sdt_stagger_eligible", "sdt_stages_for", "sdt_check_gemm_args",
                  "sdt_last_hip_error", "sdt_empty_kernel"):
         getattr(L, name).restype = _int
     _lib = L
@@ -120,6 +121,10 @@ def tile_info(tile_id: int) -> dict:
     if rc != SDT_OK:
         raise SdtError(rc, "sdt_tile_info")
     return t.as_dict()
+
+
+def stages_for(tile_id: int, M: int, N: int, K: int) -> int:
+    return int(lib().sdt_stages_for(int(tile_id), int(M), int(N), int(K)))
 
 
 def pick_tile(M: int, N: int, K: int, num_cu: int) -> dict:

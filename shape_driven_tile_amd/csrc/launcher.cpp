@@ -9,7 +9,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-sdt_tile describe(int id) {
+sdt_tile describe(int id, int stages) {
     const TileDesc& d = kLadder[id];
     sdt_tile t;
     t.id = id;
@@ -19,9 +19,16 @@ sdt_tile describe(int id) {
     t.waves_m = d.waves_m;
     t.waves_n = d.waves_n;
     t.threads = 64 * d.waves_m * d.waves_n;
-    t.stages = d.stages;
-    t.lds_bytes = d.stages * (d.bm + d.bn) * kBK * 2;
+    t.stages = stages;
+    t.lds_bytes = stages * (d.bm + d.bn) * kBK * 2;
     return t;
+}
+
+// 2 stages while A and B (2 bytes per element) fit in one XCD's L2, else the
+// rung's deep pipeline.
+int stages_for(int id, int64_t M, int64_t N, int64_t K) {
+    const int64_t operand_bytes = 2 * K * (M + N);
+    return operand_bytes <= kShallowOperandBytes ? 2 : kLadder[id].stages;
 }
 
 // "Beating hipBLASLt on a Gaming GPU", section "The part that actually
@@ -119,8 +126,13 @@ extern "C" int sdt_num_tiles(void) { return sdt::kNumTiles; }
 
 extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
     if (tile_id < 0 || tile_id >= sdt::kNumTiles || !out) return SDT_ERR_INVALID_ARG;
-    *out = sdt::describe(tile_id);
+    *out = sdt::describe(tile_id, sdt::kLadder[tile_id].stages);
     return SDT_OK;
+}
+
+extern "C" int sdt_stages_for(int tile_id, int64_t M, int64_t N, int64_t K) {
+    if (tile_id < 0 || tile_id >= sdt::kNumTiles || M < 0 || N < 0 || K < 0) return -1;
+    return sdt::stages_for(tile_id, M, N, K);
 }
 
 extern "C" int sdt_stagger_eligible(int64_t K) { return sdt::stagger_eligible(K) ? 1 : 0; }

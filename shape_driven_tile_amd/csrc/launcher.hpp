@@ -14,31 +14,39 @@ constexpr int kBK = 64;
 
 // A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
 // each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
-// `stages` LDS stages of (bm + bn) x 64 fp16 each: the global prefetch runs
-// stages - 1 k-tiles deep.  Per rung, the count is the one that measured
-// fastest on MI355X across square shapes 256..8192: a third stage pays on the
-// mid-size tiles, whose grids are resident at once and wait on latency
-// (128x64 at 1280^3: 10.4 us with 3 stages, 13.2 us with 2); 64x64, on
-// grids of at most 16 k-tiles, is fastest with 2.
+// A launch uses 2 or `stages` LDS stages of (bm + bn) x 64 elements each (see
+// stages_for); the global prefetch runs stages - 1 k-tiles deep.
 struct TileDesc {
     int bm, bn, waves_m, waves_n, stages;
 };
 
-// Largest tile first.  The indices are the ABI's tile ids.
+// Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
+// deep pipeline of the rung: as many stages as fit next to a useful
+// occupancy, 3 measuring as fast as 4 or faster on every rung below the
+// largest (whose two 64 KB stages fill 128 of the 160 KB).
 constexpr TileDesc kLadder[] = {
     {256, 256, 2, 4, 2},  // 8 waves, 128x64 per wave, 2 x 64 KB LDS
     {256, 128, 2, 2, 3},  // 4 waves, 128x64 per wave, 3 x 48 KB
     {128, 128, 2, 2, 3},  // 4 waves, 64x64 per wave, 3 x 32 KB
     {128, 64, 2, 2, 3},   // 4 waves, 64x32 per wave, 3 x 24 KB
-    {64, 64, 2, 2, 2},    // 4 waves, 32x32 per wave, 2 x 16 KB
+    {64, 64, 2, 2, 3},    // 4 waves, 32x32 per wave, 3 x 16 KB
 };
+
+// Operand bytes up to which a launch runs the shallow 2-stage pipeline: one
+// MI355X XCD's L2.  While A and B together fit there, a k-tile arrives within
+// the one-tile prefetch and the shorter prologue wins (about 1% at 256^3 ..
+// 1024^3); past it the tiles stream from the Infinity Cache or HBM and the
+// deeper prefetch wins by up to 40% (64x64 at 512x512x4096: 29.3 us with 2
+// stages, 18.0 us with 3).
+constexpr int64_t kShallowOperandBytes = int64_t(4) << 20;
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 
 // Largest leading dimension accepted: a workgroup addresses its operand rows
 // through one buffer descriptor with 32-bit byte offsets below 2^31.
 constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
-sdt_tile describe(int id);
+sdt_tile describe(int id, int stages);
+int stages_for(int id, int64_t M, int64_t N, int64_t K);
 int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks);
 int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);

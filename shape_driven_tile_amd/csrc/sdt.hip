@@ -61,21 +61,24 @@ hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
                            dim3(p.gm * p.gn), dim3(WM * WN * 64), args, 0, stream);
 }
 
+// Rung I with its shallow (2-stage) or deep pipeline.
 template <typename Elt, int I>
-hipError_t launch_rung(GemmParams p, hipStream_t s) {
-    return launch_gemm_tile<Elt, kLadder[I].bm, kLadder[I].bn, kLadder[I].waves_m,
-                            kLadder[I].waves_n, kLadder[I].stages>(p, s);
+hipError_t launch_rung(GemmParams p, int stages, hipStream_t s) {
+    constexpr TileDesc d = kLadder[I];
+    if (stages == 2)
+        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2>(p, s);
+    return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages>(p, s);
 }
 
 template <typename Elt>
-hipError_t launch_gemm(int id, GemmParams p, hipStream_t s) {
+hipError_t launch_gemm(int id, int stages, GemmParams p, hipStream_t s) {
     static_assert(kNumTiles == 5, "dispatch table below lists every rung");
     switch (id) {
-        case 0: return launch_rung<Elt, 0>(p, s);
-        case 1: return launch_rung<Elt, 1>(p, s);
-        case 2: return launch_rung<Elt, 2>(p, s);
-        case 3: return launch_rung<Elt, 3>(p, s);
-        default: return launch_rung<Elt, 4>(p, s);
+        case 0: return launch_rung<Elt, 0>(p, stages, s);
+        case 1: return launch_rung<Elt, 1>(p, stages, s);
+        case 2: return launch_rung<Elt, 2>(p, stages, s);
+        case 3: return launch_rung<Elt, 3>(p, stages, s);
+        default: return launch_rung<Elt, 4>(p, stages, s);
     }
 }
 
@@ -209,7 +212,7 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     p.gn = (int)gn;
     p.stagger = use_stagger;
     p.nxcd = dev.nxcd;
-    hipError_t e = launch_gemm<Elt>(id, p, s);
+    hipError_t e = launch_gemm<Elt>(id, stages_for(id, M, N, K), p, s);
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
@@ -307,7 +310,8 @@ extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_ti
         if (st != SDT_OK) return st;
         num_cu = dev.num_cu;
     }
-    *out = sdt::describe(sdt::pick_tile(M, N, K, num_cu));
+    const int id = sdt::pick_tile(M, N, K, num_cu);
+    *out = sdt::describe(id, sdt::stages_for(id, M, N, K));
     return SDT_OK;
 }
 

@@ -162,6 +162,25 @@ def test_ladder_is_well_formed():
         sdt.tile_info(len(tiles))
 
 
+def test_stage_count_follows_operand_bytes():
+    """2 stages while A and B (2*K*(M+N) bytes) fit in 4 MiB, one XCD's L2;
+    the rung's deep pipeline past that; both fit the LDS."""
+    tiles = ladder()
+    for t in tiles:
+        deep = t["stages"]
+        for (M, N, K) in [(256, 256, 256), (1024, 1024, 1024), (512, 512, 2048),
+                          (1024, 1024, 1025), (512, 512, 4096), (8192, 8192, 8192), (1, 1, 1)]:
+            want = 2 if 2 * K * (M + N) <= 4 * 1024 * 1024 else deep
+            assert sdt.stages_for(t["id"], M, N, K) == want, (t["id"], M, N, K)
+    assert sdt.stages_for(-1, 1, 1, 1) == -1 and sdt.stages_for(len(tiles), 1, 1, 1) == -1
+    assert sdt.stages_for(0, -1, 1, 1) == -1
+    # pick_tile reports the count the launch uses, and its LDS
+    small = sdt.pick_tile(1024, 1024, 1024, 256)
+    assert small["stages"] == 2 and small["lds_bytes"] == 2 * (64 + 64) * 64 * 2
+    longk = sdt.pick_tile(1024, 1024, 4096, 256)
+    assert longk["id"] == small["id"] and longk["stages"] == tiles[small["id"]]["stages"]
+
+
 def test_pick_rung_reproduces_printed_gfx1100_ladder():
     """The pages' rule with gfx1100 constants reproduces the printed tile,
     warp layout and grid of all ten measured sizes."""

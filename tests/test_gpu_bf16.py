@@ -37,7 +37,8 @@ def test_bf16_square_large_sampled(n):
     assert_close_bf16(C[r, c], ref)
 
 
-@pytest.mark.parametrize("shape", [(200, 136, 136), (257, 129, 200), (64, 64, 4096)])
+@pytest.mark.parametrize("shape", [(200, 136, 136), (257, 129, 200), (64, 64, 4096),
+                                   (257, 259, 4160)])
 def test_bf16_integer_exact_every_tile(shape):
     from shape_driven_tile_amd import binding as sdt
     M, N, K = shape

@@ -101,6 +101,24 @@ def test_integer_exact_every_tile(shape):
             assert_bitexact(C, ref)
 
 
+@pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
+def test_integer_exact_every_tile_deep_pipeline(shape):
+    """Operands past 4 MiB run every rung's deep pipeline (sdt_stages_for);
+    exact integer sums, bit for bit, with a ragged last k-tile in the second
+    shape and ragged M/N in both."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    A = inputs.integer_f16((M, K), 13)
+    B = inputs.integer_f16((N, K), 14)
+    ref = oracle.gemm(A, B)
+    for tile in range(_ntiles()):
+        assert sdt.stages_for(tile, M, N, K) == sdt.tile_info(tile)["stages"]
+        say(f"integer deep {shape} tile={tile} stages={sdt.stages_for(tile, M, N, K)}")
+        C, pad_ok = run_gemm(A, B, tile=tile, stagger=0)
+        assert pad_ok
+        assert_bitexact(C, ref)
+
+
 @pytest.mark.parametrize("K", [1, 8, 256, 1920, 2048, 2304, 4096, 8192, 16384])
 def test_all_ones(K):
     say(f"all-ones K={K}")
