@@ -54,12 +54,23 @@ typedef struct sdt_tile {
     int id;          /* index in the ladder, 0 = largest tile */
     int bm, bn, bk;
     int waves_m, waves_n;
-    int threads;     /* 64 * waves_m * waves_n */
+    int threads;     /* 64 * waves_m * waves_n * kgroups */
     int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep
                         (sdt_pick_tile: the count a launch of that shape uses;
                         sdt_tile_info: the rung's deep pipeline) */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16 */
+    int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
+                        sub-steps (1 or 2; sdt_tile_info: the most the rung is
+                        built with) */
 } sdt_tile;
+
+/* A launch configuration; -1 in a field = the automatic choice. */
+typedef struct sdt_launch {
+    int tile_id;     /* ladder rung */
+    int stages;      /* 2 or the rung's deep count (sdt_tile_info().stages) */
+    int kgroups;     /* 1, or 2 on rungs built with two (needs the deep count) */
+    int stagger;     /* 0 off, 1 on (power-of-two full k-tile count only) */
+} sdt_launch;
 
 /* ---- main entry points ---------------------------------------------------- */
 
@@ -130,6 +141,19 @@ int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 void* C, int64_t ldc, void* stream,
                 int tile_id, int stagger);
 
+/* gemm_f16 / gemm_bf16 with any part of the launch configuration forced
+ * (NULL cfg, an index out of range, or a combination the library has no
+ * kernel for: SDT_ERR_INVALID_ARG; a forced stagger on an ineligible K:
+ * SDT_ERR_UNSUPPORTED).  M == 1 is not rerouted to the GEMV here. */
+int gemm_f16_cfg(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc, void* stream, const sdt_launch* cfg);
+int gemm_bf16_cfg(int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda,
+                  const void* B, int64_t ldb,
+                  void* C, int64_t ldc, void* stream, const sdt_launch* cfg);
+
 /* gemm_bf16 with the launcher's choices forced (as gemm_f16_ex). */
 int gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
                  const void* A, int64_t lda,
@@ -174,11 +198,16 @@ int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 
-/* Host-only: the LDS stage count a launch of rung tile_id on an M x N x K
- * product uses: 2 while the operands, 2*K*(M+N) bytes, fit in one MI355X
- * XCD's 4 MiB L2 (the tiles arrive within a one-tile prefetch and the shorter
- * prologue wins), else the rung's deep pipeline.  -1 on invalid input. */
-int sdt_stages_for(int tile_id, int64_t M, int64_t N, int64_t K);
+/* Host-only: how a launch of rung tile_id on an M x N x K product on num_cu
+ * CUs (num_cu <= 0: 256) is configured (stages, kgroups, threads, LDS).
+ * k-groups: 2 on rungs built with them when the grid has at most num_cu
+ * workgroups and K spans at least 12 k-tiles, else 1.  Stages: the deep count
+ * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
+ * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the
+ * shorter prologue wins), else the deep count.  SDT_OK or
+ * SDT_ERR_INVALID_ARG. */
+int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
+                  sdt_tile* out);
 
 /* Host-only: 1 if the k-loop of a product with inner size K can be staggered,
  * else 0: the number of full 64-deep k-tiles floor(K/64) must be a power of

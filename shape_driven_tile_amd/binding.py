@@ -26,7 +26,8 @@ EXPORTS = (
     "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
-    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stages_for",
+    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_plan_tile",
+    "gemm_f16_cfg", "gemm_bf16_cfg",
 )
 
 
@@ -34,10 +35,16 @@ class SdtTile(ctypes.Structure):
     _fields_ = [("id", ctypes.c_int), ("bm", ctypes.c_int), ("bn", ctypes.c_int),
                 ("bk", ctypes.c_int), ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
                 ("threads", ctypes.c_int), ("stages", ctypes.c_int),
-                ("lds_bytes", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("kgroups", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class SdtLaunch(ctypes.Structure):
+    """sdt_launch: -1 in a field = the automatic choice."""
+    _fields_ = [("tile_id", ctypes.c_int), ("stages", ctypes.c_int),
+                ("kgroups", ctypes.c_int), ("stagger", ctypes.c_int)]
 
 
 class SdtError(RuntimeError):
@@ -80,7 +87,9 @@ def lib():
     L.sdt_pick_rung.argtypes = [_i64, _i64, _int, _int, _int, ctypes.POINTER(_i64)]
     L.sdt_num_tiles.argtypes = []
     L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
-    L.sdt_stages_for.argtypes = [_int, _i64, _i64, _i64]
+    L.sdt_plan_tile.argtypes = [_int, _i64, _i64, _i64, _int, ctypes.POINTER(SdtTile)]
+    L.gemm_f16_cfg.argtypes = L.gemm_f16.argtypes + [ctypes.POINTER(SdtLaunch)]
+    L.gemm_bf16_cfg.argtypes = L.gemm_f16_cfg.argtypes
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -94,7 +103,8 @@ def lib():
                  "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
                  "sdt_check_gemv_kn_args",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
-                 "sdt_tile_info", "sdt_stagger_eligible", "sdt_stages_for", "sdt_check_gemm_args",
+                 "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
+                 "gemm_f16_cfg", "gemm_bf16_cfg",
                  "sdt_last_hip_error", "sdt_empty_kernel"):
         getattr(L, name).restype = _int
     _lib = L
@@ -123,8 +133,17 @@ def tile_info(tile_id: int) -> dict:
     return t.as_dict()
 
 
-def stages_for(tile_id: int, M: int, N: int, K: int) -> int:
-    return int(lib().sdt_stages_for(int(tile_id), int(M), int(N), int(K)))
+def plan_tile(tile_id: int, M: int, N: int, K: int, num_cu: int = 256) -> dict:
+    """How a launch of rung tile_id on M x N x K is configured (stages, kgroups)."""
+    t = SdtTile()
+    rc = lib().sdt_plan_tile(int(tile_id), int(M), int(N), int(K), int(num_cu), ctypes.byref(t))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_plan_tile")
+    return t.as_dict()
+
+
+def launch_cfg(tile_id=-1, stages=-1, kgroups=-1, stagger=-1) -> SdtLaunch:
+    return SdtLaunch(int(tile_id), int(stages), int(kgroups), int(stagger))
 
 
 def pick_tile(M: int, N: int, K: int, num_cu: int) -> dict:
@@ -274,6 +293,19 @@ def _gemm_16(entry, A, B, C, stream, dtype, extra=()):
                                *extra)
     if rc != SDT_OK:
         raise SdtError(rc, entry)
+
+
+def gemm_f16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, stream=None) -> None:
+    """gemm_f16 with any part of the launch configuration forced (-1 = automatic)."""
+    import torch
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger)
+    _gemm_16("gemm_f16_cfg", A, B, C, stream, torch.float16, (ctypes.byref(cfg),))
+
+
+def gemm_bf16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, stream=None) -> None:
+    import torch
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger)
+    _gemm_16("gemm_bf16_cfg", A, B, C, stream, torch.bfloat16, (ctypes.byref(cfg),))
 
 
 def gemm_bf16(A, B, C, stream=None) -> None:

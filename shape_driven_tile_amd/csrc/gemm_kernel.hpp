@@ -26,6 +26,11 @@
 //     sub-steps of a k-tile, so the LDS reads of sub-step kk+1 are in flight
 //     under the MFMAs of sub-step kk, and the first reads of tile i+1 go out
 //     under the last MFMAs of tile i, past the barrier;
+//   * KS = 2 k-groups: a second set of waves takes sub-steps 1 and 3 of every
+//     k-tile while the first takes 0 and 2, halving each wave's dependent MFMA
+//     chain per k-tile and doubling the waves a small grid keeps in flight;
+//     the second group's partial sums are added to the first's through LDS
+//     (a fixed order: the result is deterministic) before the epilogue;
 //   * k-loop stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by
 //     choosing the tile from the shape", Changes): when the number of full
 //     k-tiles is a power of two, workgroup w visits them in the order
@@ -158,13 +163,15 @@ __device__ __forceinline__ void wait_global_loads() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS>
-__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
+__global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
     typedef typename Elt::vec4 vec4;
     typedef typename Elt::scalar scalar;
     constexpr int BK = kBK;
-    constexpr int NW = WM * WN;
+    constexpr int NMN = WM * WN;       // waves per k-group (one output block each)
+    constexpr int NW = NMN * KS;       // waves per workgroup
+    static_assert(KS == 1 || KS == 2, "k-groups: 1 or 2");
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / 32, FN = WTN / 32;
     constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
@@ -175,6 +182,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     static_assert(A_UNITS % (64 * NW) == 0 && B_UNITS % (64 * NW) == 0,
                   "each wave loads whole 8-row slabs");
     static_assert(NS >= 2 && NS * STAGE * 16 <= 160 * 1024, "stages must fit the LDS");
+    static_assert(KS == 1 || BM * BN * 4 <= NS * STAGE * 16, "k-group partials fit the LDS");
     constexpr int L = A_DMA + B_DMA;   // global loads per wave per k-tile
 
     __shared__ int4_t smem[NS * STAGE];
@@ -182,8 +190,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const int wave_m = wave % WM;
-    const int wave_n = wave / WM;
+    const int kg = wave / NMN;         // k-group: sub-steps kg, kg + KS, ... of each k-tile
+    const int wmn = wave % NMN;
+    const int wave_m = wmn % WM;
+    const int wave_n = wmn / WM;
 
     // ---- workgroup -> output tile (XCD-aware, grouped) -----------------------
     const int nwg = p.gm * p.gn;
@@ -316,7 +326,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     else
         wait_global_loads<0>();
     __syncthreads();
-    read_frags(0, 0, 0);
+    read_frags(0, kg, 0);
 
     // ---- steady state: one basic block per k-tile ----------------------------------
     // (A) kk1 reads under kk0 MFMAs, (B) kk2 reads under kk1, (C) kk3 reads
@@ -328,22 +338,29 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     int s = 0;                               // stage of tile i
     for (; i + NS < nfull; ++i) {
         const int sn = (s + 1 == NS) ? 0 : s + 1;
-        read_frags(s, 1, 1);
-        mfmas(0);
-        interleave(Reads{}, None{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(s, 2, 0);
-        mfmas(1);
-        interleave(Reads{}, None{});
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(s, 3, 1);
-        mfmas(0);
-        interleave(Reads{}, None{});
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (KS == 1) {
+            read_frags(s, 1, 1);
+            mfmas(0);
+            interleave(Reads{}, None{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(s, 2, 0);
+            mfmas(1);
+            interleave(Reads{}, None{});
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(s, 3, 1);
+            mfmas(0);
+            interleave(Reads{}, None{});
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            read_frags(s, kg + 2, 1);
+            mfmas(0);
+            interleave(Reads{}, None{});
+            __builtin_amdgcn_sched_barrier(0);
+        }
         wait_global_loads<(NS - 2) * L>();
         __syncthreads();
         dma_tile(i + NS, s);
-        read_frags(sn, 0, 0);
+        read_frags(sn, kg, 0);
         mfmas(1);
         interleave(Reads{}, Loads{});
         __builtin_amdgcn_sched_barrier(0);
@@ -352,18 +369,47 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(GemmParams p) {
     // ---- the last steps (every condition spelled out, full waits) -------------------
     for (; i < nseq; ++i) {
         const int sn = (s + 1 == NS) ? 0 : s + 1;
-        read_frags(s, 1, 1);
-        mfmas(0);
-        read_frags(s, 2, 0);
-        mfmas(1);
-        read_frags(s, 3, 1);
-        mfmas(0);
+        if constexpr (KS == 1) {
+            read_frags(s, 1, 1);
+            mfmas(0);
+            read_frags(s, 2, 0);
+            mfmas(1);
+            read_frags(s, 3, 1);
+            mfmas(0);
+        } else {
+            read_frags(s, kg + 2, 1);
+            mfmas(0);
+        }
         wait_global_loads<0>();
         __syncthreads();
         if (i + NS < nseq) load_step(i + NS, s);
-        if (i + 1 < nseq) read_frags(sn, 0, 0);
+        if (i + 1 < nseq) read_frags(sn, kg, 0);
         mfmas(1);
         s = sn;
+    }
+
+    // ---- k-groups: group 1 hands its partial sums to group 0 through LDS ----------
+    if constexpr (KS > 1) {
+        __syncthreads();                 // every wave is done reading the stages
+        float* red = reinterpret_cast<float*>(smem);
+        if (kg == 1) {
+#pragma unroll
+            for (int i2 = 0; i2 < FN; ++i2)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        red[((wmn * FN * FM + i2 * FM + j) * 16 + e) * 64 + lane] = acc[i2][j][e];
+        }
+        __syncthreads();
+        if (kg == 1) return;
+#pragma unroll
+        for (int i2 = 0; i2 < FN; ++i2)
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    acc[i2][j][e] += red[((wmn * FN * FM + i2 * FM + j) * 16 + e) * 64 + lane];
     }
 
     // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked 8-byte stores -----------------

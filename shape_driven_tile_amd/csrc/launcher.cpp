@@ -9,7 +9,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-sdt_tile describe(int id, int stages) {
+sdt_tile describe(int id, int stages, int kgroups) {
     const TileDesc& d = kLadder[id];
     sdt_tile t;
     t.id = id;
@@ -18,7 +18,8 @@ sdt_tile describe(int id, int stages) {
     t.bk = kBK;
     t.waves_m = d.waves_m;
     t.waves_n = d.waves_n;
-    t.threads = 64 * d.waves_m * d.waves_n;
+    t.threads = 64 * d.waves_m * d.waves_n * kgroups;
+    t.kgroups = kgroups;
     t.stages = stages;
     t.lds_bytes = stages * (d.bm + d.bn) * kBK * 2;
     return t;
@@ -29,6 +30,38 @@ sdt_tile describe(int id, int stages) {
 int stages_for(int id, int64_t M, int64_t N, int64_t K) {
     const int64_t operand_bytes = 2 * K * (M + N);
     return operand_bytes <= kShallowOperandBytes ? 2 : kLadder[id].stages;
+}
+
+// Two k-groups on a rung built with them, when its grid is resident all at
+// once (at most one workgroup per CU) and the k-loop is long enough.
+int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
+    const TileDesc& d = kLadder[id];
+    if (d.kgroups < 2) return 1;
+    if (num_cu <= 0) num_cu = 256;
+    const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    const int64_t nkt = ceil_div(K, kBK);
+    return (wgs <= num_cu && nkt >= kSplitMinKTiles) ? 2 : 1;
+}
+
+// The automatic plan on rung `id`: two k-groups always run the deep
+// pipeline, one k-group the pipeline stages_for picks.
+Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
+    Plan p;
+    p.tile = id;
+    p.kgroups = kgroups_for(id, M, N, K, num_cu);
+    p.stages = p.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
+    return p;
+}
+
+// A plan the library has a kernel for: stages 2 or the rung's deep count;
+// two k-groups only on rungs built with them, and with the deep pipeline.
+int check_plan(const Plan& p) {
+    if (p.tile < 0 || p.tile >= kNumTiles) return SDT_ERR_INVALID_ARG;
+    const TileDesc& d = kLadder[p.tile];
+    if (p.stages != 2 && p.stages != d.stages) return SDT_ERR_INVALID_ARG;
+    if (p.kgroups != 1 && p.kgroups != 2) return SDT_ERR_INVALID_ARG;
+    if (p.kgroups == 2 && (d.kgroups < 2 || p.stages != d.stages)) return SDT_ERR_INVALID_ARG;
+    return SDT_OK;
 }
 
 // "Beating hipBLASLt on a Gaming GPU", section "The part that actually
@@ -126,13 +159,18 @@ extern "C" int sdt_num_tiles(void) { return sdt::kNumTiles; }
 
 extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
     if (tile_id < 0 || tile_id >= sdt::kNumTiles || !out) return SDT_ERR_INVALID_ARG;
-    *out = sdt::describe(tile_id, sdt::kLadder[tile_id].stages);
+    *out = sdt::describe(tile_id, sdt::kLadder[tile_id].stages, sdt::kLadder[tile_id].kgroups);
     return SDT_OK;
 }
 
-extern "C" int sdt_stages_for(int tile_id, int64_t M, int64_t N, int64_t K) {
-    if (tile_id < 0 || tile_id >= sdt::kNumTiles || M < 0 || N < 0 || K < 0) return -1;
-    return sdt::stages_for(tile_id, M, N, K);
+extern "C" int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
+                             sdt_tile* out) {
+    if (tile_id < 0 || tile_id >= sdt::kNumTiles || M < 0 || N < 0 || K < 0 || !out)
+        return SDT_ERR_INVALID_ARG;
+    if (num_cu <= 0) num_cu = 256;
+    const sdt::Plan p = sdt::plan_for(tile_id, M, N, K, num_cu);
+    *out = sdt::describe(p.tile, p.stages, p.kgroups);
+    return SDT_OK;
 }
 
 extern "C" int sdt_stagger_eligible(int64_t K) { return sdt::stagger_eligible(K) ? 1 : 0; }

@@ -18,6 +18,7 @@ constexpr int kBK = 64;
 // stages_for); the global prefetch runs stages - 1 k-tiles deep.
 struct TileDesc {
     int bm, bn, waves_m, waves_n, stages;
+    int kgroups;   // 2: also built with two k-groups of waves (see kgroups_for)
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
@@ -25,11 +26,11 @@ struct TileDesc {
 // occupancy, 3 measuring as fast as 4 or faster on every rung below the
 // largest (whose two 64 KB stages fill 128 of the 160 KB).
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 2},  // 8 waves, 128x64 per wave, 2 x 64 KB LDS
-    {256, 128, 2, 2, 3},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3},   // 4 waves, 64x32 per wave, 3 x 24 KB
-    {64, 64, 2, 2, 3},    // 4 waves, 32x32 per wave, 3 x 16 KB
+    {256, 256, 2, 4, 2, 1},  // 8 waves, 128x64 per wave, 2 x 64 KB LDS
+    {256, 128, 2, 2, 3, 2},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3, 2},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3, 2},   // 4 waves, 64x32 per wave, 3 x 24 KB
+    {64, 64, 2, 2, 3, 2},    // 4 waves, 32x32 per wave, 3 x 16 KB
 };
 
 // Operand bytes up to which a launch runs the shallow 2-stage pipeline: one
@@ -39,14 +40,30 @@ constexpr TileDesc kLadder[] = {
 // deeper prefetch wins by up to 40% (64x64 at 512x512x4096: 29.3 us with 2
 // stages, 18.0 us with 3).
 constexpr int64_t kShallowOperandBytes = int64_t(4) << 20;
+
+// Shortest k-loop (in 64-deep k-tiles) that a second k-group of waves pays
+// on: a grid resident all at once spends each k-tile on one chain of
+// barrier, fragment reads and dependent MFMAs; splitting every tile's four
+// sub-steps over two wave groups halves that chain (1024^3: 7.05 -> 6.21 us,
+// 1536^3: 15.8 -> 14.8 us) but costs a reduction through LDS that loops of
+// 8 k-tiles or fewer do not earn back (256^3: 3.69 -> 3.85 us).
+constexpr int kSplitMinKTiles = 12;
+
+// How one product is launched: rung, LDS stages, k-groups of waves.
+struct Plan {
+    int tile, stages, kgroups;
+};
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 
 // Largest leading dimension accepted: a workgroup addresses its operand rows
 // through one buffer descriptor with 32-bit byte offsets below 2^31.
 constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
-sdt_tile describe(int id, int stages);
+sdt_tile describe(int id, int stages, int kgroups);
 int stages_for(int id, int64_t M, int64_t N, int64_t K);
+int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
+Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
+int check_plan(const Plan& p);
 int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks);
 int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);

@@ -18,6 +18,8 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
+constexpr sdt_launch kAuto = {-1, -1, -1, -1};
+
 struct DeviceInfo {
     int num_cu = 0;
     int nxcd = 1;
@@ -54,31 +56,37 @@ int device_info(DeviceInfo* out) {
     return SDT_OK;
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS>
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS>),
-                           dim3(p.gm * p.gn), dim3(WM * WN * 64), args, 0, stream);
+    return hipLaunchKernel(
+        reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS>),
+        dim3(p.gm * p.gn), dim3(WM * WN * KS * 64), args, 0, stream);
 }
 
-// Rung I with its shallow (2-stage) or deep pipeline.
+// Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
+// pipeline with one k-group, or the deep pipeline with two.
 template <typename Elt, int I>
-hipError_t launch_rung(GemmParams p, int stages, hipStream_t s) {
+hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
-    if (stages == 2)
-        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2>(p, s);
-    return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages>(p, s);
+    if constexpr (d.kgroups == 2) {
+        if (pl.kgroups == 2)
+            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 2>(p, s);
+    }
+    if (pl.stages == 2)
+        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
+    return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1>(p, s);
 }
 
 template <typename Elt>
-hipError_t launch_gemm(int id, int stages, GemmParams p, hipStream_t s) {
+hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
     static_assert(kNumTiles == 5, "dispatch table below lists every rung");
-    switch (id) {
-        case 0: return launch_rung<Elt, 0>(p, stages, s);
-        case 1: return launch_rung<Elt, 1>(p, stages, s);
-        case 2: return launch_rung<Elt, 2>(p, stages, s);
-        case 3: return launch_rung<Elt, 3>(p, stages, s);
-        default: return launch_rung<Elt, 4>(p, stages, s);
+    switch (pl.tile) {
+        case 0: return launch_rung<Elt, 0>(p, pl, s);
+        case 1: return launch_rung<Elt, 1>(p, pl, s);
+        case 2: return launch_rung<Elt, 2>(p, pl, s);
+        case 3: return launch_rung<Elt, 3>(p, pl, s);
+        default: return launch_rung<Elt, 4>(p, pl, s);
     }
 }
 
@@ -170,14 +178,26 @@ int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void*
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
+// cfg fields: -1 = the automatic choice.  route_m1: M == 1 runs the GEMV.
 template <typename Elt>
 int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
-              int64_t ldb, void* C, int64_t ldc, void* stream, int tile_id, int stagger,
+              int64_t ldb, void* C, int64_t ldc, void* stream, const sdt_launch& cfg,
               bool route_m1) {
     int st = check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != SDT_OK) return st;
+    const int tile_id = cfg.tile_id, stagger = cfg.stagger;
     if (tile_id < -1 || tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
     if (stagger < -1 || stagger > 1) return SDT_ERR_INVALID_ARG;
+    if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
+    if (tile_id >= 0) {   // a forced rung: its forced fields must name a kernel it has
+        const TileDesc& d = kLadder[tile_id];
+        if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages) return SDT_ERR_INVALID_ARG;
+        if (cfg.kgroups >= 0 && cfg.kgroups != 1 && !(cfg.kgroups == 2 && d.kgroups == 2))
+            return SDT_ERR_INVALID_ARG;
+        if (cfg.kgroups == 2 && cfg.stages == 2 && d.stages != 2) return SDT_ERR_INVALID_ARG;
+    } else if (cfg.stages >= 0 || cfg.kgroups >= 0) {
+        if (cfg.stages > 4 || cfg.kgroups > 2) return SDT_ERR_INVALID_ARG;
+    }
     // Plain k order unless a caller forces the stagger (see
     // sdt_stagger_eligible for why it is not used by default).
     if (stagger == 1 && !stagger_eligible(K)) return SDT_ERR_UNSUPPORTED;
@@ -193,6 +213,14 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (st != SDT_OK) return st;
 
     const int id = tile_id >= 0 ? tile_id : pick_tile(M, N, K, dev.num_cu);
+    Plan pl = plan_for(id, M, N, K, dev.num_cu);
+    if (cfg.kgroups >= 0) {
+        pl.kgroups = cfg.kgroups;
+        if (cfg.stages < 0) pl.stages = pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
+    }
+    if (cfg.stages >= 0) pl.stages = cfg.stages;
+    st = check_plan(pl);
+    if (st != SDT_OK) return st;
     const TileDesc& td = kLadder[id];
     const int64_t gm = ceil_div(M, td.bm);
     const int64_t gn = ceil_div(N, td.bn);
@@ -212,7 +240,7 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     p.gn = (int)gn;
     p.stagger = use_stagger;
     p.nxcd = dev.nxcd;
-    hipError_t e = launch_gemm<Elt>(id, stages_for(id, M, N, K), p, s);
+    hipError_t e = launch_gemm<Elt>(pl, p, s);
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
@@ -225,26 +253,40 @@ __global__ void empty_kernel() {}
 
 extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true);
 }
 
 extern "C" int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                            int tile_id, int stagger) {
-    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger,
-                                    false);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                                    sdt_launch{tile_id, -1, -1, stagger}, false);
 }
 
 extern "C" int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, -1, -1, true);
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true);
 }
 
 extern "C" int gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                             int tile_id, int stagger) {
-    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, tile_id, stagger,
-                                     false);
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
+                                     sdt_launch{tile_id, -1, -1, stagger}, false);
+}
+
+extern "C" int gemm_f16_cfg(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                            const sdt_launch* cfg) {
+    if (!cfg) return SDT_ERR_INVALID_ARG;
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false);
+}
+
+extern "C" int gemm_bf16_cfg(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
+                             const sdt_launch* cfg) {
+    if (!cfg) return SDT_ERR_INVALID_ARG;
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false);
 }
 
 extern "C" int gemv_f16_m1(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
@@ -310,8 +352,8 @@ extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_ti
         if (st != SDT_OK) return st;
         num_cu = dev.num_cu;
     }
-    const int id = sdt::pick_tile(M, N, K, num_cu);
-    *out = sdt::describe(id, sdt::stages_for(id, M, N, K));
+    const sdt::Plan p = sdt::plan_for(sdt::pick_tile(M, N, K, num_cu), M, N, K, num_cu);
+    *out = sdt::describe(p.tile, p.stages, p.kgroups);
     return SDT_OK;
 }
 

@@ -23,11 +23,13 @@ DEFAULT_SQUARES = (256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072, 3584
                    6144, 8192)
 
 
-def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats):
+def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats, kgroups=-1):
     """Median microseconds per launch of rung `tile` over `repeats` back-to-back
     graph replays, all of them, and whether a replay into a cleared C
     reproduced the eager result bit for bit."""
-    sdt.gemm_f16_ex(A, B, C, tile_id=tile, stagger=stagger)
+    def launch():
+        sdt.gemm_f16_cfg(A, B, C, tile_id=tile, kgroups=kgroups, stagger=stagger)
+    launch()
     torch.cuda.synchronize()
     eager = C.clone()
     g = torch.cuda.CUDAGraph()
@@ -36,7 +38,7 @@ def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats):
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
             for _ in range(chain):
-                sdt.gemm_f16_ex(A, B, C, tile_id=tile, stagger=stagger)
+                launch()
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     t_end = time.perf_counter() + 0.05      # ~50 ms of replays to settle the clocks
@@ -111,6 +113,13 @@ def main(argv=None):
                 row["stagger_arms"][st] = {"us": round(med, 3), "min_us": round(allv[0], 3),
                                            "max_us": round(allv[-1], 3),
                                            "replays_match_eager": same}
+        if sdt.tile_info(auto)["kgroups"] == 2:
+            row["kgroup_arms"] = {}
+            for kg in (1, 2):
+                med, allv, same = time_rung(sdt, torch, A, B, C, auto, -1, chain, args.repeats, kg)
+                row["kgroup_arms"][kg] = {"us": round(med, 3), "min_us": round(allv[0], 3),
+                                          "max_us": round(allv[-1], 3),
+                                          "replays_match_eager": same}
         best = min(row["rungs"], key=lambda t: row["rungs"][t]["us"])
         row["best_tile"] = best
         results.append(row)
@@ -118,6 +127,10 @@ def main(argv=None):
         print(f"{M}x{N}x{K}: {cells}   best t{best}  auto t{auto}"
               f"{'' if all(v['replays_match_eager'] for v in row['rungs'].values()) else '  REPLAY MISMATCH'}",
               flush=True)
+        if "kgroup_arms" in row:
+            a = row["kgroup_arms"]
+            print(f"    t{auto} one k-group {a[1]['us']:.2f}  two {a[2]['us']:.2f}"
+                  f"  auto {sdt.pick_tile(M, N, K, num_cu)['kgroups']}", flush=True)
         if "stagger_arms" in row:
             a = row["stagger_arms"]
             print(f"    t{auto} stagger off {a[0]['us']:.2f} [{a[0]['min_us']:.2f}, {a[0]['max_us']:.2f}]"
@@ -129,7 +142,8 @@ def main(argv=None):
         with open(args.out, "w") as f:
             json.dump(out, f, indent=1)
     ok = all(v["replays_match_eager"] for r in results
-             for v in list(r["rungs"].values()) + list(r.get("stagger_arms", {}).values()))
+             for v in (list(r["rungs"].values()) + list(r.get("stagger_arms", {}).values())
+                       + list(r.get("kgroup_arms", {}).values())))
     return 0 if ok else 1
 
 

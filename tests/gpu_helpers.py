@@ -21,7 +21,8 @@ def to_dev(a: np.ndarray):
     return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
 
 
-def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None):
+def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None, stages=-1,
+             kgroups=-1):
     """A: (M, lda) float16, B: (N, ldb) float16 host buffers (K-contiguous rows).
     Returns the (M, N) float16 result and whether the C padding was untouched."""
     import torch
@@ -36,7 +37,10 @@ def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None):
     ldc = N + ldc_pad if M == 1 else -(-(N + ldc_pad) // 8) * 8
     full = torch.full((M, ldc), float("nan"), dtype=torch.float16, device=DEV)
     dC = full[:, :N]
-    if tile is None and stagger == -1:
+    if stages != -1 or kgroups != -1:
+        sdt.gemm_f16_cfg(dA, dB, dC, tile_id=-1 if tile is None else tile, stages=stages,
+                         kgroups=kgroups, stagger=stagger, stream=stream)
+    elif tile is None and stagger == -1:
         sdt.gemm_f16(dA, dB, dC, stream=stream)
     else:
         sdt.gemm_f16_ex(dA, dB, dC, tile_id=-1 if tile is None else tile, stagger=stagger,
@@ -125,7 +129,7 @@ def dev_bf16_to_bits(t) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run_gemm_bf16(A, B, K=None, tile=None, stagger=-1):
+def run_gemm_bf16(A, B, K=None, tile=None, stagger=-1, stages=-1, kgroups=-1):
     """A: (M, lda), B: (N, ldb) uint16 bfloat16 bit arrays.  Returns C's bits
     (M, N) and whether the C padding (NaN) stayed untouched."""
     import torch
@@ -138,7 +142,10 @@ def run_gemm_bf16(A, B, K=None, tile=None, stagger=-1):
     ldc = N if M == 1 else -(-N // 8) * 8 + 8
     full = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device=DEV)
     dC = full[:, :N]
-    if tile is None and stagger == -1:
+    if stages != -1 or kgroups != -1:
+        sdt.gemm_bf16_cfg(dA, dB, dC, tile_id=-1 if tile is None else tile, stages=stages,
+                          kgroups=kgroups, stagger=stagger)
+    elif tile is None and stagger == -1:
         sdt.gemm_bf16(dA, dB, dC)
     else:
         sdt.gemm_bf16_ex(dA, dB, dC, tile_id=-1 if tile is None else tile, stagger=stagger)

@@ -153,7 +153,8 @@ def test_ladder_is_well_formed():
     assert areas == sorted(areas, reverse=True), "largest tile first"
     for t in tiles:
         assert t["bk"] == 64
-        assert t["threads"] == 64 * t["waves_m"] * t["waves_n"]
+        assert t["kgroups"] in (1, 2)
+        assert t["threads"] == 64 * t["waves_m"] * t["waves_n"] * t["kgroups"]
         assert t["bm"] % (32 * t["waves_m"]) == 0 and t["bn"] % (32 * t["waves_n"]) == 0
         assert 2 <= t["stages"] <= 4
         assert t["lds_bytes"] == t["stages"] * (t["bm"] + t["bn"]) * 64 * 2
@@ -162,23 +163,57 @@ def test_ladder_is_well_formed():
         sdt.tile_info(len(tiles))
 
 
-def test_stage_count_follows_operand_bytes():
-    """2 stages while A and B (2*K*(M+N) bytes) fit in 4 MiB, one XCD's L2;
-    the rung's deep pipeline past that; both fit the LDS."""
+def test_launch_plan_rules():
+    """k-groups: 2 on rungs built with them when the grid has at most num_cu
+    workgroups and K spans at least 12 k-tiles.  Stages: the deep count with
+    two k-groups; with one, 2 while A and B (2*K*(M+N) bytes) fit in 4 MiB."""
     tiles = ladder()
+    shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
+              (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
+              (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700)]
+    for num_cu in (80, 256):
+        for t in tiles:
+            for (M, N, K) in shapes:
+                p = sdt.plan_tile(t["id"], M, N, K, num_cu)
+                wgs = -(-M // t["bm"]) * -(-N // t["bn"])
+                kg = 2 if (t["kgroups"] == 2 and wgs <= num_cu and -(-K // 64) >= 12) else 1
+                st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
+                                                  else t["stages"])
+                assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
+                assert p["threads"] == 64 * t["waves_m"] * t["waves_n"] * kg
+                assert p["lds_bytes"] == st * (t["bm"] + t["bn"]) * 64 * 2
+    with pytest.raises(sdt.SdtError):
+        sdt.plan_tile(len(tiles), 1, 1, 1)
+    with pytest.raises(sdt.SdtError):
+        sdt.plan_tile(0, -1, 1, 1)
+    # pick_tile reports the plan of the rung it picks
+    for (M, N, K) in shapes:
+        p = sdt.pick_tile(M, N, K, 256)
+        assert p == sdt.plan_tile(p["id"], M, N, K, 256)
+    assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 2
+    assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
+    assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
+
+
+def test_gemm_cfg_rejects_kernels_that_do_not_exist():
+    """Forced combinations without a kernel are refused before any device
+    call (fake aligned pointers, null stream)."""
+    L = sdt.lib()
+    args = (512, 512, 512, 0x10000, 512, 0x20000, 512, 0x30000, 512, None)
+    tiles = ladder()
+    def cfg(*v):
+        return ctypes.byref(sdt.launch_cfg(*v))
+    assert L.gemm_f16_cfg(*args, None) == sdt.SDT_ERR_INVALID_ARG
     for t in tiles:
-        deep = t["stages"]
-        for (M, N, K) in [(256, 256, 256), (1024, 1024, 1024), (512, 512, 2048),
-                          (1024, 1024, 1025), (512, 512, 4096), (8192, 8192, 8192), (1, 1, 1)]:
-            want = 2 if 2 * K * (M + N) <= 4 * 1024 * 1024 else deep
-            assert sdt.stages_for(t["id"], M, N, K) == want, (t["id"], M, N, K)
-    assert sdt.stages_for(-1, 1, 1, 1) == -1 and sdt.stages_for(len(tiles), 1, 1, 1) == -1
-    assert sdt.stages_for(0, -1, 1, 1) == -1
-    # pick_tile reports the count the launch uses, and its LDS
-    small = sdt.pick_tile(1024, 1024, 1024, 256)
-    assert small["stages"] == 2 and small["lds_bytes"] == 2 * (64 + 64) * 64 * 2
-    longk = sdt.pick_tile(1024, 1024, 4096, 256)
-    assert longk["id"] == small["id"] and longk["stages"] == tiles[small["id"]]["stages"]
+        assert L.gemm_f16_cfg(*args, cfg(t["id"], 5, -1, -1)) == sdt.SDT_ERR_INVALID_ARG
+        assert L.gemm_f16_cfg(*args, cfg(t["id"], -1, 3, -1)) == sdt.SDT_ERR_INVALID_ARG
+        if t["kgroups"] == 1:
+            assert L.gemm_f16_cfg(*args, cfg(t["id"], -1, 2, -1)) == sdt.SDT_ERR_INVALID_ARG
+        if t["stages"] != 2:
+            assert L.gemm_bf16_cfg(*args, cfg(t["id"], 2, 2, -1)) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemm_f16_cfg(*args, cfg(len(tiles), -1, -1, -1)) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemm_f16_cfg(*args, cfg(-1, -2, -1, -1)) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemm_f16_cfg(*args, cfg(-1, -1, -1, 2)) == sdt.SDT_ERR_INVALID_ARG
 
 
 def test_pick_rung_reproduces_printed_gfx1100_ladder():

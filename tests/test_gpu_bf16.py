@@ -52,6 +52,21 @@ def test_bf16_integer_exact_every_tile(shape):
         assert_bitexact_bf16(C, ref)
 
 
+def test_bf16_two_kgroups_integer():
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = 257, 259, 4160
+    A = inputs.integer_bf16((M, K), 107)
+    B = inputs.integer_bf16((N, K), 108)
+    ref = oracle.gemm(A, B, dtype="bf16")
+    for tile in range(sdt.num_tiles()):
+        if sdt.tile_info(tile)["kgroups"] != 2:
+            continue
+        say(f"bf16 two k-groups integer tile={tile}")
+        C, pad_ok = run_gemm_bf16(A, B, tile=tile, stagger=0, kgroups=2)
+        assert pad_ok
+        assert_bitexact_bf16(C, ref)
+
+
 @pytest.mark.parametrize("M,N,K", [(77, 91, 65), (300, 260, 1000), (129, 255, 8)])
 def test_bf16_ragged_padded(M, N, K):
     from shape_driven_tile_amd import binding as sdt

@@ -103,20 +103,66 @@ def test_integer_exact_every_tile(shape):
 
 @pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
 def test_integer_exact_every_tile_deep_pipeline(shape):
-    """Operands past 4 MiB run every rung's deep pipeline (sdt_stages_for);
+    """Operands past 4 MiB run every rung's deep pipeline (sdt_plan_tile);
     exact integer sums, bit for bit, with a ragged last k-tile in the second
-    shape and ragged M/N in both."""
+    shape and ragged M/N in both; one k-group and, where built, two."""
     from shape_driven_tile_amd import binding as sdt
     M, N, K = shape
     A = inputs.integer_f16((M, K), 13)
     B = inputs.integer_f16((N, K), 14)
     ref = oracle.gemm(A, B)
     for tile in range(_ntiles()):
-        assert sdt.stages_for(tile, M, N, K) == sdt.tile_info(tile)["stages"]
-        say(f"integer deep {shape} tile={tile} stages={sdt.stages_for(tile, M, N, K)}")
-        C, pad_ok = run_gemm(A, B, tile=tile, stagger=0)
+        info = sdt.tile_info(tile)
+        assert sdt.plan_tile(tile, M, N, K, 1 << 20)["stages"] == info["stages"]
+        for kg in ((1, 2) if info["kgroups"] == 2 else (1,)):
+            say(f"integer deep {shape} tile={tile} stages={info['stages']} kgroups={kg}")
+            C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=info["stages"], kgroups=kg)
+            assert pad_ok
+            assert_bitexact(C, ref)
+
+
+@pytest.mark.parametrize("shape", [(200, 136, 136), (64, 64, 64), (513, 771, 520), (1, 700, 1000)])
+def test_two_kgroups_every_rung(shape):
+    """Two k-groups of waves (the second takes sub-steps 1 and 3 of every
+    k-tile, its partial sums added through LDS) on every rung built with
+    them: integer inputs bit for bit, uniform inputs within tolerance, ragged
+    M/N/K (K = 136 and 520 end in a partial k-tile), NaN-padded C."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    Ai = inputs.integer_f16((M, K), 15)
+    Bi = inputs.integer_f16((N, K), 16)
+    refi = oracle.gemm(Ai, Bi)
+    Au = inputs.uniform_f16((M, K), 17)
+    Bu = inputs.uniform_f16((N, K), 18)
+    refu = oracle.gemm(Au, Bu)
+    for tile in range(_ntiles()):
+        info = sdt.tile_info(tile)
+        if info["kgroups"] != 2:
+            continue
+        say(f"two k-groups {shape} tile={tile}")
+        C, pad_ok = run_gemm(Ai, Bi, tile=tile, stagger=0, kgroups=2)
         assert pad_ok
-        assert_bitexact(C, ref)
+        assert_bitexact(C, refi)
+        C, pad_ok = run_gemm(Au, Bu, tile=tile, stagger=0, kgroups=2)
+        assert pad_ok
+        assert_close(C, refu)
+
+
+def test_two_kgroups_auto_plan_matches_oracle():
+    """Shapes whose automatic plan uses two k-groups (resident grid, >= 12
+    k-tiles) against the oracle, and bit-identical to the forced plan."""
+    from shape_driven_tile_amd import binding as sdt
+    for (M, N, K) in [(1024, 1024, 1024), (768, 768, 768), (1536, 1536, 1536)]:
+        p = sdt.pick_tile(M, N, K, 256)
+        assert p["kgroups"] == 2, (M, N, K)
+        say(f"auto two k-groups {M}x{N}x{K} tile={p['id']}")
+        A = inputs.uniform_f16((M, K), 19)
+        B = inputs.uniform_f16((N, K), 20)
+        C, _ = run_gemm(A, B)
+        C2, _ = run_gemm(A, B, tile=p["id"], stagger=0, stages=p["stages"], kgroups=2)
+        assert (C.view(np.uint16) == C2.view(np.uint16)).all()
+        r, c = sample_positions(M, N, rows=8, cols=8, extra=2048, seed=M)
+        assert_close(C[r, c], oracle.gemm_sample(A, B, r, c))
 
 
 @pytest.mark.parametrize("K", [1, 8, 256, 1920, 2048, 2304, 4096, 8192, 16384])
