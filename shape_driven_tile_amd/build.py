@@ -50,6 +50,24 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     return LIB
 
 
+CAPI_SRC = os.path.join(ROOT, "tests", "capi", "capi_check.cpp")
+CAPI_BIN = os.path.join(ROOT, "tests", "capi", "capi_check")
+
+
+def build_capi_check() -> str:
+    """The C-ABI test program (host code only): links libsdt.so and the CPU
+    oracle's libsdt_oracle.so, found next to it through an $ORIGIN rpath."""
+    tmp = CAPI_BIN + ".tmp"
+    cmd = [hipcc(), "-O2", "-std=c++17", "-Wall", "-I", INCLUDE, CAPI_SRC, "-o", tmp,
+           "-L", HERE, "-lsdt", "-L", os.path.join(ROOT, "oracle"), "-lsdt_oracle",
+           "-Wl,-rpath,$ORIGIN/../../shape_driven_tile_amd:$ORIGIN/../../oracle"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    os.replace(tmp, CAPI_BIN)
+    return CAPI_BIN
+
+
 if __name__ == "__main__":
     build(resource_usage="--resource-usage" in sys.argv, verbose="-v" in sys.argv)
     print(LIB)

@@ -331,3 +331,16 @@ def test_decode_shape_bytes():
     the mojo-baro page, section "Four rounds on the decode shape")."""
     from shape_driven_tile_amd import inputs
     assert inputs.DECODE_K * inputs.DECODE_N * 2 == 100_663_296
+
+
+def test_capi_program_links_only_the_c_abi():
+    """The C-ABI test program needs nothing but libsdt.so, the CPU oracle and
+    the HIP runtime (no Python, no torch)."""
+    import subprocess
+    binp = os.path.join(os.path.dirname(os.path.abspath(__file__)), "capi", "capi_check")
+    if not os.path.exists(binp):
+        pytest.skip("tests/capi/capi_check not built")
+    out = subprocess.run(["readelf", "-d", binp], capture_output=True, text=True).stdout
+    needed = set(re.findall(r"NEEDED\)\s+Shared library: \[([^\]]+)\]", out))
+    assert "libsdt.so" in needed and "libsdt_oracle.so" in needed
+    assert not any("torch" in n or "python" in n for n in needed), needed

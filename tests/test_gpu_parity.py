@@ -360,3 +360,58 @@ def test_determinism_repeated_launches():
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
+def test_graph_capture_replays_match_eager():
+    """Calls captured in a HIP graph (the library allocates nothing and
+    records no memset, so a caller may capture it) replay bit for bit like
+    eager launches, several times in a row with eager work and syncs between
+    replays: a 2-stage, a deep and a two-k-group GEMM, the K = 0 fill, and
+    both decode GEMVs."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    dev = "cuda:0"
+    shapes = [(256, 256, 256), (1000, 1000, 1000), (300, 260, 4104), (64, 48, 0)]
+    ops = []
+    for i, (M, N, K) in enumerate(shapes):
+        A = torch.from_numpy(inputs.uniform_f16((M, K), 40 + i)).to(dev)
+        B = torch.from_numpy(inputs.uniform_f16((N, K), 50 + i)).to(dev)
+        ldc = -(-N // 8) * 8
+        C = torch.empty((M, ldc), dtype=torch.float16, device=dev)[:, :N]
+        ops.append((A, B, C))
+    x = torch.from_numpy(inputs.decode_activations()).to(dev)
+    W = torch.from_numpy(inputs.decode_weights(2)).to(dev)
+    Wkn = torch.from_numpy(inputs.decode_weights_kn(2)).to(dev)
+    y1 = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
+    y2 = torch.empty_like(y1)
+
+    def work():
+        for A, B, C in ops:
+            sdt.gemm_f16(A, B, C)
+        sdt.gemv_f16_m1(x, W, y1)
+        sdt.gemv_f16_m1_kn(x, Wkn, y2)
+
+    say("graph capture: eager reference")
+    work()
+    torch.cuda.synchronize()
+    ref = [C.clone() for _, _, C in ops] + [y1.clone(), y2.clone()]
+    outs = [C for _, _, C in ops] + [y1, y2]
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            work()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        say(f"graph capture: replay {rep}")
+        for o in outs:
+            o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o.contiguous().view(torch.int16), r.contiguous().view(torch.int16)), rep
+        work()                       # eager work between replays
+        torch.cuda.synchronize()
