@@ -57,8 +57,11 @@ typedef struct sdt_tile {
     int threads;     /* 64 * waves_m * waves_n * kgroups */
     int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep
                         (sdt_pick_tile: the count a launch of that shape uses;
-                        sdt_tile_info: the rung's deep pipeline) */
-    int lds_bytes;   /* stages x (bm + bn) x bk fp16 */
+                        sdt_tile_info: the rung's deep pipeline).  On rung 0
+                        the deep count (3) is the ping-pong kernel: two groups
+                        of 4 waves one phase apart, A in 2 stages, B in 3 */
+    int lds_bytes;   /* stages x (bm + bn) x bk fp16; rung 0 deep:
+                        (2 bm + 3 bn) x bk fp16 = 160 KB */
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
                         sub-steps (1 or 2; sdt_tile_info: the most the rung is
                         built with) */

@@ -157,10 +157,52 @@ __device__ __forceinline__ int4_t load16_tail(__amdgpu_buffer_rsrc_t r, uint32_t
 // s_waitcnt vmcnt(N) (at most N global loads of this wave still in flight),
 // leaving the LDS and export counters alone.  gfx9 encoding: vmcnt in bits
 // [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+// s_waitcnt lgkmcnt(0): every LDS access of this wave has completed.
+__device__ __forceinline__ void wait_lds() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
 template <int N>
 __device__ __forceinline__ void wait_global_loads() {
     static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Epilogue of one wave: its FN x FM accumulator tiles of 32 x 32 (tile (i, j)
+// covers rows mb + 32 j .., columns nb + 32 i ..) rounded to the output type
+// (nearest even) and stored with 8-byte stores, masked at the M and N edges.
+// Lane l holds row (l % 32) of each tile, columns 8 g + 4 (l / 32) + 0..3 in
+// accumulator elements 4 g .. 4 g + 3.
+template <typename Elt, int FM, int FN>
+__device__ __forceinline__ void store_block(const GemmParams& p, const floatx16_t (&acc)[FN][FM],
+                                            int64_t mb, int64_t nb, int frow, int fhalf) {
+    typedef typename Elt::vec4 vec4;
+    typedef typename Elt::scalar scalar;
+#pragma unroll
+    for (int i2 = 0; i2 < FN; ++i2) {
+#pragma unroll
+        for (int j = 0; j < FM; ++j) {
+            const int64_t m = mb + j * 32 + frow;
+            if (m >= p.M) continue;
+            uint16_t* crow = p.C + m * p.ldc;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const int64_t n = nb + i2 * 32 + 8 * gq + 4 * fhalf;
+                vec4 h;
+                h[0] = (scalar)acc[i2][j][4 * gq + 0];
+                h[1] = (scalar)acc[i2][j][4 * gq + 1];
+                h[2] = (scalar)acc[i2][j][4 * gq + 2];
+                h[3] = (scalar)acc[i2][j][4 * gq + 3];
+                if (n + 3 < p.N) {
+                    *reinterpret_cast<uint2_t*>(crow + n) = __builtin_bit_cast(uint2_t, h);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const scalar v = h[e];   // element first, then reinterpret
+                        if (n + e < p.N) crow[n + e] = __builtin_bit_cast(uint16_t, v);
+                    }
+                }
+            }
+        }
+    }
 }
 
 template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
@@ -416,33 +458,232 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     }
 
     // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked 8-byte stores -----------------
-#pragma unroll
-    for (int i2 = 0; i2 < FN; ++i2) {
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-            const int64_t m = m0 + wave_m * WTM + j * 32 + frow;
-            if (m >= p.M) continue;
-            uint16_t* crow = p.C + m * p.ldc;
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const int64_t n = n0 + wave_n * WTN + i2 * 32 + 8 * gq + 4 * fhalf;
-                vec4 h;
-                h[0] = (scalar)acc[i2][j][4 * gq + 0];
-                h[1] = (scalar)acc[i2][j][4 * gq + 1];
-                h[2] = (scalar)acc[i2][j][4 * gq + 2];
-                h[3] = (scalar)acc[i2][j][4 * gq + 3];
-                if (n + 3 < p.N) {
-                    *reinterpret_cast<uint2_t*>(crow + n) = __builtin_bit_cast(uint2_t, h);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const scalar v = h[e];   // element first, then reinterpret
-                        if (n + e < p.N) crow[n + e] = __builtin_bit_cast(uint16_t, v);
-                    }
-                }
-            }
-        }
+    store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
+}
+
+// The 256 x 256 rung with a ping-pong schedule (8 waves, 2 per SIMD).
+//
+// Same staging as above (swizzled K-contiguous rows, direct global -> LDS
+// loads), but the two waves that share a SIMD never compete for the MFMA
+// pipe: waves 0-3 (group 0, columns 0-127 of the tile) and waves 4-7 (group
+// 1, columns 128-255) run the same loop one phase apart.  A phase is one
+// barrier interval; in every phase one group issues the 32 MFMAs of a whole
+// k-tile from fragments already in registers while the other reads the 24
+// fragments of its next k-tile from LDS and issues global -> LDS loads.  On
+// MI355X a CU's global -> LDS writes take LDS cycles that fragment reads then
+// wait for, and a CU takes in 64 bytes per clock, so issuing a k-tile's 64 KB
+// stalls the issuing wave for about a phase; here neither delay reaches the
+// MFMA pipe, and each group's barrier falls inside the other's MFMA stream.
+//
+// The LDS (160 KB) holds A in two 32 KB stages and B in three, so that every
+// load goes into a stage that is already free when it is issued and overlaps
+// the issuing group's fragment reads; each group issues half a k-tile per
+// read phase.  Timeline (P = barrier interval; A of tile t in A stage t % 2,
+// B in B stage t % 3):
+//   group 0: P 2t   loads A(t+1), reads tile t    | P 2t+1 MFMAs of tile t,
+//                                                    then waits for A(t+1)
+//   group 1: P 2t+1 loads B(t+2), reads tile t,   | P 2t+2 MFMAs of tile t
+//                   then waits for B(t+1)
+// A(t+1) goes into the stage of A(t-1) and B(t+2) into that of B(t-1), whose
+// last reads (group 1's) ended with P 2t-1; both are complete before group 0
+// reads tile t+1 in P 2t+2.  Group 1 takes one extra barrier before its loop
+// and group 0 one after it, so every wave executes the same number of
+// barriers.
+template <typename Elt>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
+    typedef typename Elt::frag8 frag8;
+    constexpr int BM = 256, BN = 256, BK = kBK;
+    constexpr int WTM = 128, WTN = 64;          // per wave: 2 x 4 waves
+    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
+    constexpr int B_BASE = 2 * A_UNITS;                 // A stages first, then B stages
+    constexpr int DMA = 8;                      // loads per operand k-tile per wave: 64 rows
+
+    __shared__ int4_t smem[2 * A_UNITS + 3 * B_UNITS];   // 160 KB
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int grp = wave >> 2;
+    const int wave_m = wave & 1;
+    const int wave_n = wave >> 1;
+    const int lw = wave & 3;                    // loader index within the group
+
+    // ---- workgroup -> output tile (XCD-aware, grouped), as gemm_kernel ----------
+    const int nwg = p.gm * p.gn;
+    const int w = blockIdx.x;
+    int logical = w;
+    if (p.nxcd > 1) {
+        const int xcd = w % p.nxcd, q = nwg / p.nxcd, r = nwg % p.nxcd;
+        logical = xcd * q + min(xcd, r) + w / p.nxcd;
     }
+    const int group_span = kGroupM * p.gn;
+    const int g = logical / group_span;
+    const int first_m = g * kGroupM;
+    const int gsz = min(p.gm - first_m, kGroupM);
+    const int within = logical - g * group_span;
+    const int64_t m0 = (int64_t)(first_m + within % gsz) * BM;
+    const int64_t n0 = (int64_t)(within / gsz) * BN;
+
+    const int rows_a = (int)min((int64_t)BM, (int64_t)p.M - m0);
+    const int rows_b = (int)min((int64_t)BN, (int64_t)p.N - n0);
+    const __amdgpu_buffer_rsrc_t ra =
+        make_rsrc(p.A + m0 * p.lda, (uint32_t)((int64_t)rows_a * p.lda * 2));
+    const __amdgpu_buffer_rsrc_t rb =
+        make_rsrc(p.B + n0 * p.ldb, (uint32_t)((int64_t)rows_b * p.ldb * 2));
+
+    // Load j of loader lw fills LDS units [(8 lw + j) * 64, +64): rows
+    // 64 lw + 8 j + lane/8 at swizzled position lane % 8.  The row offset
+    // stays in the lane offset (vaddr), which the buffer range check covers,
+    // so rows past M or N read as zero.
+    uint32_t voff_a[DMA], voff_b[DMA];
+    int chk[DMA];
+#pragma unroll
+    for (int j = 0; j < DMA; ++j) {
+        const int row = lw * 64 + j * 8 + (lane >> 3);
+        chk[j] = (lane & 7) ^ swz(row);
+        voff_a[j] = (uint32_t)(row * p.lda * 2 + chk[j] * 16);
+        voff_b[j] = (uint32_t)(row * p.ldb * 2 + chk[j] * 16);
+    }
+
+    const int nfull = p.K / BK;
+    const int ktail = p.K - nfull * BK;
+    const int nseq = nfull + (ktail > 0 ? 1 : 0);
+    const int kmask = p.stagger ? (nfull - 1) : 0x7fffffff;
+    const int k0 = p.stagger ? (w & (nfull - 1)) : 0;
+
+    floatx16_t acc[FN][FM];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    const int frow = lane & 31;
+    const int fsw = swz(frow);
+    const int fhalf = lane >> 5;
+    const int a_row0 = wave_m * WTM + frow;
+    const int b_row0 = wave_n * WTN + frow;
+    frag8 fa[4][FM], fb[4][FN];                 // every sub-step of one k-tile
+    // Fragments of one k-tile from A stage sa and B stage sb.
+    auto read_tile = [&](int sa, int sb) {
+        const int4_t* abase = smem + sa * A_UNITS;
+        const int4_t* bbase = smem + B_BASE + sb * B_UNITS;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int chunk = (2 * kk + fhalf) ^ fsw;
+#pragma unroll
+            for (int j = 0; j < FM; ++j)
+                fa[kk][j] = __builtin_bit_cast(frag8, abase[(a_row0 + j * 32) * 8 + chunk]);
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+                fb[kk][i] = __builtin_bit_cast(frag8, bbase[(b_row0 + i * 32) * 8 + chunk]);
+        }
+    };
+    // One group's loads of one operand's full k-tile (8 per wave) into a stage.
+    auto dma_a = [&](int step, int sa) {
+        int4_t* base = smem + sa * A_UNITS;
+        const int soff = ((k0 + step) & kmask) * (BK * 2);
+#pragma unroll
+        for (int j = 0; j < DMA; ++j) dma16(ra, base + (lw * DMA + j) * 64, voff_a[j], soff);
+    };
+    auto dma_b = [&](int step, int sb) {
+        int4_t* base = smem + B_BASE + sb * B_UNITS;
+        const int soff = ((k0 + step) & kmask) * (BK * 2);
+#pragma unroll
+        for (int j = 0; j < DMA; ++j) dma16(rb, base + (lw * DMA + j) * 64, voff_b[j], soff);
+    };
+    auto mfma_tile = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int i = 0; i < FN; ++i)
+#pragma unroll
+                for (int j = 0; j < FM; ++j)
+                    acc[i][j] = Elt::mfma(fb[kk][i], fa[kk][j], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- prologue: A(0), B(0), B(1) --------------------------------------------------
+    if (grp == 1) {
+        if (nfull > 0) {
+            dma_a(0, 0);
+            dma_b(0, 0);
+        }
+        if (nfull > 1) dma_b(1, 1);
+        wait_global_loads<0>();
+    }
+    __syncthreads();
+    if (grp == 1) __syncthreads();            // one phase behind group 0
+
+    // ---- one full k-tile per iteration: read phase, then MFMA phase ---------------
+    int sb = 0;                               // B stage of tile i (i % 3)
+    for (int i = 0; i < nfull; ++i) {
+        const int sa = i & 1;
+        const int sb2 = (sb == 0) ? 2 : sb - 1;   // (i + 2) % 3
+        if (grp == 0) {
+            if (i + 1 < nfull) dma_a(i + 1, sa ^ 1);
+        } else {
+            if (i + 2 < nfull) dma_b(i + 2, sb2);
+        }
+        read_tile(sa, sb);
+        // 8 loads and 24 fragment reads per wave, interleaved (masks: 0x020
+        // global read, 0x100 LDS read).
+#pragma unroll
+        for (int m = 0; m < DMA; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        }
+        if (grp == 1) {
+            // B(i+1) (issued in the previous read phase) must be in LDS before
+            // group 0 reads tile i+1 in the next phase; B(i+2) may stay in flight.
+            if (i + 2 < nfull)
+                wait_global_loads<DMA>();
+            else
+                wait_global_loads<0>();
+        }
+        // A __syncthreads here would be a release, which on this target also
+        // waits for every direct-to-LDS load in flight.
+        wait_lds();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        mfma_tile();
+        if (grp == 0) wait_global_loads<0>();  // A(i+1), read by both groups next
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+        sb = (sb == 2) ? 0 : sb + 1;
+    }
+    if (grp == 0) __syncthreads();            // matches group 1's extra barrier
+
+    // ---- a partial last k-tile: every wave loads an eighth, masked, through
+    // registers into A stage 0 and B stage 0 (all reads of the full tiles are
+    // done and no load is in flight) -------------------------------------------------
+    if (ktail > 0) {
+        const int soff = nfull * (BK * 2);
+#pragma unroll
+        for (int r = 0; r < (A_UNITS + B_UNITS) / 512; ++r) {
+            const int u = r * 512 + t;
+            const bool is_a = u < A_UNITS;
+            const int ul = is_a ? u : u - A_UNITS;
+            const int row = ul >> 3;
+            const int c = (ul & 7) ^ swz(row);
+            const uint32_t voff = (uint32_t)(row * (is_a ? p.lda : p.ldb) * 2 + c * 16);
+            smem[is_a ? ul : B_BASE + ul] = is_a ? load16_tail(ra, voff, soff, ktail - c * 8)
+                                                 : load16_tail(rb, voff, soff, ktail - c * 8);
+        }
+        __syncthreads();
+        read_tile(0, 0);
+        mfma_tile();
+    }
+
+    // ---- epilogue ----------------------------------------------------------------------
+    store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
 }
 
 // C = 0 for K == 0 (the empty sum), M x N with stride ldc.

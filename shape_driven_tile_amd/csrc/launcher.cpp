@@ -21,7 +21,9 @@ sdt_tile describe(int id, int stages, int kgroups) {
     t.threads = 64 * d.waves_m * d.waves_n * kgroups;
     t.kgroups = kgroups;
     t.stages = stages;
-    t.lds_bytes = stages * (d.bm + d.bn) * kBK * 2;
+    t.lds_bytes = (d.pingpong && stages == d.stages)
+                      ? (2 * d.bm + d.stages * d.bn) * kBK * 2   // A in 2 stages, B in `stages`
+                      : stages * (d.bm + d.bn) * kBK * 2;
     return t;
 }
 

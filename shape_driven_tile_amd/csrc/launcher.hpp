@@ -15,22 +15,25 @@ constexpr int kBK = 64;
 // A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
 // each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
 // A launch uses 2 or `stages` LDS stages of (bm + bn) x 64 elements each (see
-// stages_for); the global prefetch runs stages - 1 k-tiles deep.
+// stages_for); the global prefetch runs stages - 1 k-tiles deep.  A ping-pong
+// rung's deep pipeline is its own kernel (gemm_pp_kernel): two wave groups
+// one phase apart, A in two LDS stages and B in `stages` (three).
 struct TileDesc {
     int bm, bn, waves_m, waves_n, stages;
-    int kgroups;   // 2: also built with two k-groups of waves (see kgroups_for)
+    int kgroups;    // 2: also built with two k-groups of waves (see kgroups_for)
+    int pingpong;   // 1: the deep pipeline is the ping-pong kernel
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
 // deep pipeline of the rung: as many stages as fit next to a useful
 // occupancy, 3 measuring as fast as 4 or faster on every rung below the
-// largest (whose two 64 KB stages fill 128 of the 160 KB).
+// largest, whose deep pipeline (2 A + 3 B stages) fills all 160 KB.
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 2, 1},  // 8 waves, 128x64 per wave, 2 x 64 KB LDS
-    {256, 128, 2, 2, 3, 2},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3, 2},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3, 2},   // 4 waves, 64x32 per wave, 3 x 24 KB
-    {64, 64, 2, 2, 3, 2},    // 4 waves, 32x32 per wave, 3 x 16 KB
+    {256, 256, 2, 4, 3, 1, 1},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
+    {256, 128, 2, 2, 3, 2, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3, 2, 0},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3, 2, 0},   // 4 waves, 64x32 per wave, 3 x 24 KB
+    {64, 64, 2, 2, 3, 2, 0},    // 4 waves, 32x32 per wave, 3 x 16 KB
 };
 
 // Operand bytes up to which a launch runs the shallow 2-stage pipeline: one

@@ -66,16 +66,31 @@ hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
 
 // Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
 // pipeline with one k-group, or the deep pipeline with two.
+template <typename Elt>
+hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
+    void* args[] = {&p};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_pp_kernel<Elt>),
+                           dim3(p.gm * p.gn), dim3(512), args, 0, stream);
+}
+
 template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
-    if constexpr (d.kgroups == 2) {
-        if (pl.kgroups == 2)
-            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 2>(p, s);
-    }
-    if (pl.stages == 2)
+    if constexpr (d.pingpong) {
+        static_assert(d.bm == 256 && d.bn == 256 && d.waves_m == 2 && d.waves_n == 4 &&
+                          d.stages == 3 && d.kgroups == 1,
+                      "the ping-pong kernel's tile");
+        if (pl.stages != 2) return launch_gemm_pp<Elt>(p, s);
         return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
-    return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1>(p, s);
+    } else {
+        if constexpr (d.kgroups == 2) {
+            if (pl.kgroups == 2)
+                return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 2>(p, s);
+        }
+        if (pl.stages == 2)
+            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
+        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1>(p, s);
+    }
 }
 
 template <typename Elt>
