@@ -205,6 +205,66 @@ __device__ __forceinline__ void store_block(const GemmParams& p, const floatx16_
     }
 }
 
+// Epilogue of one wave of the ping-pong kernel (128 x 64 outputs: FM = 4
+// row blocks of 32, FN = 2 column blocks of 32) through 4 KB of LDS owned by
+// the wave, 32 rows at a time.  Stored directly, each 8-byte store of a
+// 32 x 32 accumulator tile touches 32 rows; staged, every lane stores 16
+// contiguous bytes and 8 lanes cover a row's 128 bytes.  Row r of the stage
+// keeps its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte writes (32 rows,
+// one chunk) and the 16-byte reads (2 rows, 8 chunks per 16 lanes) then both
+// fall on distinct banks.  Masked at the M and N edges.
+template <typename Elt>
+__device__ __forceinline__ void store_block_staged(const GemmParams& p,
+                                                   const floatx16_t (&acc)[2][4], int64_t mb,
+                                                   int64_t nb, int lane, int4_t* stage) {
+    typedef typename Elt::vec4 vec4;
+    typedef typename Elt::scalar scalar;
+    char* lds = reinterpret_cast<char*>(stage);
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    const int wsw = (frow >> 1) & 7;
+    const int rr = lane >> 3;          // read: rows 8 k + rr, chunk lane % 8
+    const int rc = lane & 7;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                vec4 h;
+                h[0] = (scalar)acc[i][j][4 * gq + 0];
+                h[1] = (scalar)acc[i][j][4 * gq + 1];
+                h[2] = (scalar)acc[i][j][4 * gq + 2];
+                h[3] = (scalar)acc[i][j][4 * gq + 3];
+                *reinterpret_cast<uint2_t*>(lds + frow * 128 + (((4 * i + gq) ^ wsw) * 16) +
+                                            fhalf * 8) = __builtin_bit_cast(uint2_t, h);
+            }
+        // Other lanes of this wave read what these wrote: LDS runs a wave's
+        // accesses in order; the fence keeps the compiler from reordering them.
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + rr;
+            const int4_t v = *reinterpret_cast<const int4_t*>(
+                lds + r * 128 + ((rc ^ ((r >> 1) & 7)) * 16));
+            const int64_t m = mb + j * 32 + r;
+            const int64_t n = nb + 8 * rc;
+            if (m < p.M) {
+                uint16_t* dst = p.C + m * p.ldc + n;
+                if (n + 7 < p.N) {
+                    *reinterpret_cast<int4_t*>(dst) = v;
+                } else {
+                    const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.N) dst[e] = e16[e];
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+}
+
 template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
@@ -659,7 +719,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
         sb = (sb == 2) ? 0 : sb + 1;
     }
-    if (grp == 0) __syncthreads();            // matches group 1's extra barrier
+    // Group 1 has taken one barrier more than group 0 (its extra one).  A
+    // partial k-tile needs both groups in step: group 0 catches up first.
+    // Otherwise group 0 stores while group 1 runs its last MFMA phase and
+    // takes the matching barrier at the very end.
+    if (grp == 0 && ktail > 0) __syncthreads();
 
     // ---- a partial last k-tile: every wave loads an eighth, masked, through
     // registers into A stage 0 and B stage 0 (all reads of the full tiles are
@@ -682,8 +746,11 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
         mfma_tile();
     }
 
-    // ---- epilogue ----------------------------------------------------------------------
-    store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
+    // ---- epilogue through 4 KB of LDS per wave, in A stage 1 (not used by the
+    // partial k-tile; every read of the full k-tiles has completed) ----------------
+    store_block_staged<Elt>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
+                            smem + A_UNITS + wave * 256);
+    if (grp == 0 && ktail == 0) __syncthreads();   // matches group 1's extra barrier
 }
 
 // C = 0 for K == 0 (the empty sum), M x N with stride ldc.
