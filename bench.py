@@ -251,12 +251,12 @@ def main():
         },
         "roofline": {
             "bound": "mfma",
-            "kernel": f"gemm_f16_kernel at {DOMINANT}^3",
+            "kernel": f"gemm_pp_kernel (256x256 ping-pong) at {DOMINANT}^3",
             "achieved": round(achieved, 1),
             "peak": round(PEAK_FP16_TFLOPS, 1),
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_FP16_TFLOPS, 4),
-            "traffic": counted_traffic("gemm_f16_256x256_8192_counters.md",
+            "traffic": counted_traffic("gemm_pp_256x256_8192_counters.md",
                                        "shape_driven_tile_amd/csrc/gemm_kernel.hpp"),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_launch_us": round(dom_avg_us, 2),
