@@ -63,6 +63,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
@@ -82,7 +83,7 @@ struct GemmParams {
     int nxcd;      // XCDs the dispatcher deals workgroups over
 };
 
-// Element types.  Each names its vector types, the 32x32x16 MFMA, the
+// Element types.  Each names its vector types, the 32x32x16 and 16x16x32 MFMAs, the
 // two-term dot product into fp32 used by the GEMV kernels, and (through
 // `scalar`) the fp32 -> 16-bit conversion of the epilogues, which rounds to
 // nearest even (v_cvt_f16_f32 / v_cvt_pk_bf16_f32 under the default mode).
@@ -93,6 +94,9 @@ struct F16 {
     typedef _Float16 scalar;
     static __device__ __forceinline__ floatx16_t mfma(frag8 a, frag8 b, floatx16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ floatx4_t mfma16(frag8 a, frag8 b, floatx4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
     static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
         return __builtin_amdgcn_fdot2(a, b, c, false);
@@ -106,12 +110,26 @@ struct BF16 {
     static __device__ __forceinline__ floatx16_t mfma(frag8 a, frag8 b, floatx16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
+    static __device__ __forceinline__ floatx4_t mfma16(frag8 a, frag8 b, floatx4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
     static __device__ __forceinline__ float dot2(vec2 a, vec2 b, float c) {
         return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
     }
 };
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// The ping-pong kernel's 16x16x32 fragment reads put 16 consecutive rows
+// and one 16-byte chunk on each group of 16 lanes (four chunks per read).
+// With swz() above those reads run at half the LDS rate (SQ_LDS_BANK_CONFLICT
+// at 8192^3: 102M cycles).  Chunk c of row r is stored at c ^ swz_pp(r), an
+// XOR-linear map of the row's three low bits (bit 0 -> 4, bit 1 -> 5,
+// bit 2 -> 3) chosen by timing every such map on MI355X: the reads then run
+// at the rate of contiguous 16-byte reads (245 B/clk per CU).
+__device__ __forceinline__ int swz_pp(int row) {
+    return ((row & 1) ? 4 : 0) ^ ((row & 2) ? 5 : 0) ^ ((row & 4) ? 3 : 0);
+}
 
 // Buffer descriptor over `bytes` bytes from `base`.  Both are workgroup-
 // uniform; readfirstlane says so to the compiler, which keeps the descriptor
@@ -205,40 +223,47 @@ __device__ __forceinline__ void store_block(const GemmParams& p, const floatx16_
     }
 }
 
-// Epilogue of one wave of the ping-pong kernel (128 x 64 outputs: FM = 4
-// row blocks of 32, FN = 2 column blocks of 32) through 4 KB of LDS owned by
-// the wave, 32 rows at a time.  Stored directly, each 8-byte store of a
-// 32 x 32 accumulator tile touches 32 rows; staged, every lane stores 16
-// contiguous bytes and 8 lanes cover a row's 128 bytes.  Row r of the stage
-// keeps its 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte writes (32 rows,
-// one chunk) and the 16-byte reads (2 rows, 8 chunks per 16 lanes) then both
-// fall on distinct banks.  Masked at the M and N edges.
+// Epilogue of one wave of the ping-pong kernel (128 x 64 outputs held as
+// FM = 8 row blocks x FN = 4 column blocks of 16 x 16 MFMA tiles; lane l has
+// row 16 j + l % 16, columns 16 i + 4 (l / 16) .. + 3 of tile (i, j)) through
+// 4 KB of LDS owned by the wave, 32 rows at a time.  Stored directly, each
+// 8-byte store would touch 16 rows; staged, every lane stores 16 contiguous
+// bytes and 8 lanes cover a row's 128 bytes.  Row r of the stage keeps its
+// 16-byte chunk c at c ^ ((r >> 1) & 7): the 8-byte writes (16 rows x one
+// chunk per 16 lanes) and the 16-byte reads (an even and an odd row x 8
+// chunks per 16 lanes served together) both fall on distinct banks.  Masked
+// at the M and N edges.
 template <typename Elt>
 __device__ __forceinline__ void store_block_staged(const GemmParams& p,
-                                                   const floatx16_t (&acc)[2][4], int64_t mb,
+                                                   const floatx4_t (&acc)[4][8], int64_t mb,
                                                    int64_t nb, int lane, int4_t* stage) {
     typedef typename Elt::vec4 vec4;
     typedef typename Elt::scalar scalar;
     char* lds = reinterpret_cast<char*>(stage);
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    const int wsw = (frow >> 1) & 7;
-    const int rr = lane >> 3;          // read: rows 8 k + rr, chunk lane % 8
+    const int wq = lane >> 4;          // write: column group 4 (l / 16) of a 16-wide tile
+    // read: rows 8 k + rr, chunk lane % 8; lanes 0-31 take the even rows and
+    // 32-63 the odd ones, so lanes l and l + 32 (served together) hit
+    // different halves of the banks
+    const int rr = 2 * ((lane >> 3) & 3) + (lane >> 5);
     const int rc = lane & 7;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int q = 0; q < 4; ++q) {      // rows 32 q .. 32 q + 31: tiles j = 2 q, 2 q + 1
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int jj = 0; jj < 2; ++jj) {
+            const int r = 16 * jj + (lane & 15);
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
+            for (int i = 0; i < 4; ++i) {
+                const floatx4_t& a = acc[i][2 * q + jj];
                 vec4 h;
-                h[0] = (scalar)acc[i][j][4 * gq + 0];
-                h[1] = (scalar)acc[i][j][4 * gq + 1];
-                h[2] = (scalar)acc[i][j][4 * gq + 2];
-                h[3] = (scalar)acc[i][j][4 * gq + 3];
-                *reinterpret_cast<uint2_t*>(lds + frow * 128 + (((4 * i + gq) ^ wsw) * 16) +
-                                            fhalf * 8) = __builtin_bit_cast(uint2_t, h);
+                h[0] = (scalar)a[0];
+                h[1] = (scalar)a[1];
+                h[2] = (scalar)a[2];
+                h[3] = (scalar)a[3];
+                const int chunk = 2 * i + (wq >> 1);
+                *reinterpret_cast<uint2_t*>(lds + r * 128 + ((chunk ^ ((r >> 1) & 7)) * 16) +
+                                            (wq & 1) * 8) = __builtin_bit_cast(uint2_t, h);
             }
+        }
         // Other lanes of this wave read what these wrote: LDS runs a wave's
         // accesses in order; the fence keeps the compiler from reordering them.
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -247,7 +272,7 @@ __device__ __forceinline__ void store_block_staged(const GemmParams& p,
             const int r = 8 * k + rr;
             const int4_t v = *reinterpret_cast<const int4_t*>(
                 lds + r * 128 + ((rc ^ ((r >> 1) & 7)) * 16));
-            const int64_t m = mb + j * 32 + r;
+            const int64_t m = mb + q * 32 + r;
             const int64_t n = nb + 8 * rc;
             if (m < p.M) {
                 uint16_t* dst = p.C + m * p.ldc + n;
@@ -554,7 +579,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
     constexpr int BM = 256, BN = 256, BK = kBK;
     constexpr int WTM = 128, WTN = 64;          // per wave: 2 x 4 waves
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int FM = WTM / 16, FN = WTN / 16;   // 16 x 16 MFMA tiles per wave
     constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
     constexpr int B_BASE = 2 * A_UNITS;                 // A stages first, then B stages
     constexpr int DMA = 8;                      // loads per operand k-tile per wave: 64 rows
@@ -601,7 +626,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < DMA; ++j) {
         const int row = lw * 64 + j * 8 + (lane >> 3);
-        chk[j] = (lane & 7) ^ swz(row);
+        chk[j] = (lane & 7) ^ swz_pp(row);
         voff_a[j] = (uint32_t)(row * p.lda * 2 + chk[j] * 16);
         voff_b[j] = (uint32_t)(row * p.ldb * 2 + chk[j] * 16);
     }
@@ -612,33 +637,36 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     const int kmask = p.stagger ? (nfull - 1) : 0x7fffffff;
     const int k0 = p.stagger ? (w & (nfull - 1)) : 0;
 
-    floatx16_t acc[FN][FM];
+    floatx4_t acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
 
-    const int frow = lane & 31;
-    const int fsw = swz(frow);
-    const int fhalf = lane >> 5;
+    // v_mfma_f32_16x16x32: lane l supplies row l % 16 of a 16-row block, k
+    // 8 (l / 16) .. + 7 of a 32-deep half k-tile: chunk 4 h + l / 16 of the row.
+    // Rows of one lane differ by multiples of 16, so their swizzle is the same.
+    const int frow = lane & 15;
+    const int fsw = swz_pp(frow);
+    const int fq = lane >> 4;
     const int a_row0 = wave_m * WTM + frow;
     const int b_row0 = wave_n * WTN + frow;
-    frag8 fa[4][FM], fb[4][FN];                 // every sub-step of one k-tile
+    frag8 fa[2][FM], fb[2][FN];                 // both 32-deep halves of one k-tile
     // Fragments of one k-tile from A stage sa and B stage sb.
     auto read_tile = [&](int sa, int sb) {
         const int4_t* abase = smem + sa * A_UNITS;
         const int4_t* bbase = smem + B_BASE + sb * B_UNITS;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int chunk = (2 * kk + fhalf) ^ fsw;
+        for (int h = 0; h < 2; ++h) {
+            const int chunk = (4 * h + fq) ^ fsw;
 #pragma unroll
             for (int j = 0; j < FM; ++j)
-                fa[kk][j] = __builtin_bit_cast(frag8, abase[(a_row0 + j * 32) * 8 + chunk]);
+                fa[h][j] = __builtin_bit_cast(frag8, abase[(a_row0 + j * 16) * 8 + chunk]);
 #pragma unroll
             for (int i = 0; i < FN; ++i)
-                fb[kk][i] = __builtin_bit_cast(frag8, bbase[(b_row0 + i * 32) * 8 + chunk]);
+                fb[h][i] = __builtin_bit_cast(frag8, bbase[(b_row0 + i * 16) * 8 + chunk]);
         }
     };
     // One group's loads of one operand's full k-tile (8 per wave) into a stage.
@@ -654,16 +682,18 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < DMA; ++j) dma16(rb, base + (lw * DMA + j) * 64, voff_b[j], soff);
     };
+    // The 64 MFMAs of one k-tile.  D = B_frag . A_frag^T: lane l's four
+    // accumulators are four consecutive n of output row m.
     auto mfma_tile = [&]() {
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int i = 0; i < FN; ++i)
 #pragma unroll
                 for (int j = 0; j < FM; ++j)
-                    acc[i][j] = Elt::mfma(fb[kk][i], fa[kk][j], acc[i][j]);
+                    acc[i][j] = Elt::mfma16(fb[h][i], fa[h][j], acc[i][j]);
         __builtin_amdgcn_s_setprio(0);
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -736,7 +766,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
             const bool is_a = u < A_UNITS;
             const int ul = is_a ? u : u - A_UNITS;
             const int row = ul >> 3;
-            const int c = (ul & 7) ^ swz(row);
+            const int c = (ul & 7) ^ swz_pp(row);
             const uint32_t voff = (uint32_t)(row * (is_a ? p.lda : p.ldb) * 2 + c * 16);
             smem[is_a ? ul : B_BASE + ul] = is_a ? load16_tail(ra, voff, soff, ktail - c * 8)
                                                  : load16_tail(rb, voff, soff, ktail - c * 8);
