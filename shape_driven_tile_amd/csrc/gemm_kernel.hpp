@@ -594,21 +594,38 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     const int wave_n = wave >> 1;
     const int lw = wave & 3;                    // loader index within the group
 
-    // ---- workgroup -> output tile (XCD-aware, grouped), as gemm_kernel ----------
+    // ---- workgroup -> output tile ---------------------------------------------------
+    // The dispatcher deals workgroup ids round-robin over the XCDs (32 CUs
+    // each), one workgroup per CU at a time.  When the tile grid is made of
+    // 16 x 16 blocks and there are 8 XCDs, the 256 workgroups in flight at once
+    // cover one such block: XCD x takes its 4 x 8 part (x % 4, x / 4), so each
+    // XCD's L2 serves 4 A and 8 B row bands and every band is shared by 2 or 4
+    // XCDs through the Infinity Cache; blocks are visited row by row.  Other
+    // grids use the grouped order of gemm_kernel.
     const int nwg = p.gm * p.gn;
     const int w = blockIdx.x;
-    int logical = w;
-    if (p.nxcd > 1) {
-        const int xcd = w % p.nxcd, q = nwg / p.nxcd, r = nwg % p.nxcd;
-        logical = xcd * q + min(xcd, r) + w / p.nxcd;
+    int64_t m0, n0;
+    if (p.nxcd == 8 && (p.gm & 15) == 0 && (p.gn & 15) == 0) {
+        const int x = w & 7, idx = w >> 3;      // idx-th workgroup of XCD x
+        const int blk = idx >> 5, k = idx & 31;
+        const int bn = p.gn >> 4;
+        const int bm_ = blk / bn, bn_ = blk - bm_ * bn;
+        m0 = (int64_t)(bm_ * 16 + (x & 3) * 4 + (k & 3)) * BM;
+        n0 = (int64_t)(bn_ * 16 + (x >> 2) * 8 + (k >> 2)) * BN;
+    } else {
+        int logical = w;
+        if (p.nxcd > 1) {
+            const int xcd = w % p.nxcd, q = nwg / p.nxcd, r = nwg % p.nxcd;
+            logical = xcd * q + min(xcd, r) + w / p.nxcd;
+        }
+        const int group_span = kGroupM * p.gn;
+        const int g = logical / group_span;
+        const int first_m = g * kGroupM;
+        const int gsz = min(p.gm - first_m, kGroupM);
+        const int within = logical - g * group_span;
+        m0 = (int64_t)(first_m + within % gsz) * BM;
+        n0 = (int64_t)(within / gsz) * BN;
     }
-    const int group_span = kGroupM * p.gn;
-    const int g = logical / group_span;
-    const int first_m = g * kGroupM;
-    const int gsz = min(p.gm - first_m, kGroupM);
-    const int within = logical - g * group_span;
-    const int64_t m0 = (int64_t)(first_m + within % gsz) * BM;
-    const int64_t n0 = (int64_t)(within / gsz) * BN;
 
     const int rows_a = (int)min((int64_t)BM, (int64_t)p.M - m0);
     const int rows_b = (int)min((int64_t)BN, (int64_t)p.N - n0);
