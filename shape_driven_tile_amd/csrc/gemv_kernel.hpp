@@ -11,8 +11,12 @@
 //   * one wave owns RPW consecutive columns (one, by default: 12288 waves
 //     for the decode shape, every one streaming 8 KB); for each column its 64
 //     lanes issue 16-byte loads at consecutive addresses (1 KB per
-//     instruction), all RPW * XCH loads of a pass in flight before any
-//     arithmetic;
+//     instruction); a pass's weight loads go out first and the activation
+//     loads interleave with them, all in flight before any arithmetic;
+//   * the kernel stays at 64 VGPRs, so 8 waves per SIMD are resident: the
+//     streaming rate follows the bytes in flight per CU (at 85 VGPRs, 5 waves
+//     per SIMD, the decode shape took 16.4 us, at 64 15.8 us); more bytes per
+//     wave do not help (two columns per wave 17.8 us);
 //   * a pass that lies wholly below K (uniform across the wave) uses plain
 //     loads with no per-lane bounds test -- a per-chunk test is a divergent
 //     branch around every load and cost about a tenth of the bandwidth --
@@ -76,53 +80,80 @@ __device__ __forceinline__ float dot8(int4_t w, int4_t x, float acc) {
     return acc;
 }
 
-template <typename Elt, int RPW, int XCH>
+// TAIL = false: K is a multiple of XCH * 512 (no ragged pass is compiled in,
+// which keeps the kernel at 61 VGPRs, 8 waves per SIMD).
+template <typename Elt, int RPW, int XCH, bool TAIL>
 __global__ __launch_bounds__(256) void gemv_m1_kernel(GemvParams p) {
     const int lane = threadIdx.x & 63;
     const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    // Waves past N (the last workgroup's, when N is not a multiple of 4 RPW)
+    // run on the clamped last row and store nothing: no early exit, whose
+    // test would have the wave load N and branch before it loads the rest of
+    // its arguments.
     const int64_t n0 = wave * RPW;
-    if (n0 >= p.N) return;   // whole wave leaves together
     constexpr int KP = XCH * 512;
 
     float acc[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) acc[r] = 0.0f;
 
-    for (int kb = 0; kb < p.K; kb += KP) {
+    // Whole passes (uniform across the wave): plain 16-byte loads, the weights
+    // first, then the activations (L2 hits).  The ragged last pass is a
+    // separate block after this loop, compiled only with TAIL: inside the
+    // loop it kept every one of a pass's loads live at once (85 VGPRs, 5
+    // waves per SIMD) and the decode shape took 16.4-16.9 us; without it the
+    // loop interleaves loads and dot products in fewer registers, 8 waves per
+    // SIMD stay resident, and it takes 15.8 us.
+    auto pass = [&](int kb) {
         int4_t xr[XCH];
         int4_t wv[RPW][XCH];
-        if (kb + KP <= p.K) {
-            // the whole pass lies below K (uniform across the wave): plain
-            // 16-byte loads, activations first (cached), then the weights
 #pragma unroll
-            for (int j = 0; j < XCH; ++j)
-                xr[j] = *reinterpret_cast<const int4_t*>(p.x + kb + (lane + 64 * j) * 8);
+        for (int r = 0; r < RPW; ++r) {
+            const int64_t n = min(n0 + r, (int64_t)p.N - 1);   // clamped rows are discarded
+            const uint16_t* row = p.B + n * p.ldb + kb;
 #pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const int64_t n = min(n0 + r, (int64_t)p.N - 1);   // clamped rows are discarded
-                const uint16_t* row = p.B + n * p.ldb + kb;
-#pragma unroll
-                for (int j = 0; j < XCH; ++j)
-                    wv[r][j] = __builtin_nontemporal_load(
-                        reinterpret_cast<const int4_t*>(row + (lane + 64 * j) * 8));
-            }
-        } else {
-            // the ragged last pass: element-exact masking, nothing past K read
-#pragma unroll
-            for (int j = 0; j < XCH; ++j) xr[j] = gemv_chunk(p.x, kb + (lane + 64 * j) * 8, p.K, false);
-#pragma unroll
-            for (int r = 0; r < RPW; ++r) {
-                const int64_t n = min(n0 + r, (int64_t)p.N - 1);
-                const uint16_t* row = p.B + n * p.ldb;
-#pragma unroll
-                for (int j = 0; j < XCH; ++j)
-                    wv[r][j] = gemv_chunk(row, kb + (lane + 64 * j) * 8, p.K, true);
+            for (int j = 0; j < XCH; ++j) {
+                wv[r][j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const int4_t*>(row + (lane + 64 * j) * 8));
+                // The first weight load goes out before anything else; the
+                // rest interleave with the activation loads as the scheduler
+                // places them.  Decode shape: every weight load first 16.4-16.6
+                // us, an activation load first 15.9-16.0 us, this 15.8-15.9 us.
+                if (r == 0 && j == 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
+#pragma unroll
+        for (int j = 0; j < XCH; ++j)
+            xr[j] = *reinterpret_cast<const int4_t*>(p.x + kb + (lane + 64 * j) * 8);
 #pragma unroll
         for (int r = 0; r < RPW; ++r)
 #pragma unroll
             for (int j = 0; j < XCH; ++j) acc[r] = dot8<Elt>(wv[r][j], xr[j], acc[r]);
+    };
+    int kb = 0;
+    if constexpr (!TAIL) {
+        // K is a positive multiple of KP: at least one pass, and no test of K
+        // ahead of the first loads
+        do {
+            pass(kb);
+            kb += KP;
+        } while (kb < p.K);
+    } else {
+        for (; kb + KP <= p.K; kb += KP) pass(kb);
+    }
+    if (TAIL && kb < p.K) {
+        // the ragged last pass: element-exact masking, nothing past K read
+        int4_t xr[XCH];
+#pragma unroll
+        for (int j = 0; j < XCH; ++j) xr[j] = gemv_chunk(p.x, kb + (lane + 64 * j) * 8, p.K, false);
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+            const int64_t n = min(n0 + r, (int64_t)p.N - 1);
+            const uint16_t* row = p.B + n * p.ldb;
+#pragma unroll
+            for (int j = 0; j < XCH; ++j)
+                acc[r] = dot8<Elt>(gemv_chunk(row, kb + (lane + 64 * j) * 8, p.K, true), xr[j], acc[r]);
+        }
     }
 
 #pragma unroll

@@ -128,8 +128,12 @@ hipError_t launch_gemv_rpw(GemvParams p, hipStream_t stream) {
     const int64_t waves = (p.N + RPW - 1) / RPW;
     const int64_t blocks = (waves + 3) / 4;
     void* args[] = {&p};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8>),
-                           dim3((unsigned)blocks), dim3(256), args, 0, stream);
+    // K a multiple of one pass (8 x 512 elements): the kernel without the
+    // ragged-pass code, which needs fewer registers.
+    const void* k = (p.K % (8 * 512) == 0)
+                        ? reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, false>)
+                        : reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, true>);
+    return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, stream);
 }
 
 template <typename Elt>
