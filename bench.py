@@ -343,26 +343,48 @@ def graph_launches(torch, fn, chain, repeats=10):
     return [1e3 * a.elapsed_time(b) / chain for a, b in ev], g
 
 
-def smi_reading():
-    """GFX clocks (MHz, per XCD), socket power (W) and temperatures from
-    amd-smi, or None where the tool is not available."""
+def smi_sampler(delay_s=1.0, samples=3, gap_s=0.4):
+    """Start a child process that waits `delay_s`, then takes `samples` amd-smi
+    readings of GFX clocks, socket power and temperatures `gap_s` apart.  It is
+    started before the launches it should see are queued: a reading taken by
+    the launching process itself comes only after the queue has drained.
+    Returns the process, or None where the tool is not available."""
+    import shutil
+    import subprocess
+    if shutil.which("amd-smi") is None:
+        return None
+    cmd = f"sleep {delay_s}; for i in $(seq {samples}); do amd-smi metric -c -p -t; sleep {gap_s}; done"
+    return subprocess.Popen(["bash", "-c", cmd], stdout=subprocess.PIPE,
+                            stderr=subprocess.STDOUT, text=True)
+
+
+def smi_reading(proc):
+    """Collect the sampler's readings: per-XCD clocks (MHz) of every sample,
+    their mean, socket power (W) per sample and the last temperatures."""
     import re
     import subprocess
-    try:
-        out = subprocess.run(["amd-smi", "metric", "-c", "-p", "-t"], capture_output=True,
-                             text=True, timeout=30).stdout
-    except (OSError, subprocess.SubprocessError):
+    if proc is None:
         return None
-    clocks = []
-    for m in re.finditer(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", out):
-        clocks.append(int(m.group(1)))
-    power = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", out)
-    temps = {k.lower(): int(v) for k, v in re.findall(r"(EDGE|HOTSPOT|MEM):\s*(\d+)\s*\S*C", out)}
+    try:
+        out, _ = proc.communicate(timeout=60)
+    except subprocess.SubprocessError:
+        proc.kill()
+        return None
+    clocks, power, temps = [], [], {}
+    for blk in out.split("GPU: ")[1:]:
+        c = [int(m) for m in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)\s*MHz", blk)]
+        if c:
+            clocks.append(round(sum(c) / len(c), 1))
+        pw = re.search(r"SOCKET_POWER:\s*(\d+)\s*W", blk)
+        if pw:
+            power.append(int(pw.group(1)))
+        temps = {k.lower(): int(v) for k, v in
+                 re.findall(r"(EDGE|HOTSPOT|MEM):\s*(\d+)\s*\S*C", blk)} or temps
     if not clocks and not power:
         return None
-    return {"gfx_clk_mhz": clocks, "gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1)
-            if clocks else None, "socket_power_w": int(power.group(1)) if power else None,
-            "temperature_c": temps}
+    return {"gfx_clk_mhz_per_sample": clocks,
+            "gfx_clk_mhz_mean": round(sum(clocks) / len(clocks), 1) if clocks else None,
+            "socket_power_w_per_sample": power, "temperature_c": temps}
 
 
 def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, bytes_gemv,
@@ -398,12 +420,14 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         }
         log(f"square {n} (graph): median {med:.2f} us {det['square_graph'][str(n)]['tflops_median']}"
             f" TFLOP/s{'' if same else '  REPLAY MISMATCH'}")
-    # clocks and power while the dominant product runs (~1 s of launches queued)
+    # clocks and power while the dominant product runs: ~3.5 s of launches
+    # queued, sampled from 1 s in by a process started before the queue
     A, B, C = ops[DOMINANT]
-    for _ in range(1100):
+    sampler = smi_sampler()
+    for _ in range(5000):
         sdt.gemm_f16(A, B, C)
-    smi = smi_reading()
     torch.cuda.synchronize()
+    smi = smi_reading(sampler)
     if smi:
         det["clock_under_load"] = smi
         if smi.get("gfx_clk_mhz_mean"):
