@@ -277,6 +277,71 @@ __device__ __forceinline__ void store_block_staged(const GemmParams& p,
             if (m < p.M) {
                 uint16_t* dst = p.C + m * p.ldc + n;
                 if (n + 7 < p.N) {
+                    // non-temporal: C goes out to memory as it is written
+                    // instead of staying dirty in L2 until the end-of-kernel
+                    // writeback (4096^3: 98.9 -> 98.1 us, 8192^3: 759 ->
+                    // 750 us).  The 8-byte stores of store_block, each
+                    // covering part of a line, measured 8-32% slower this way.
+                    __builtin_nontemporal_store(v, reinterpret_cast<int4_t*>(dst));
+                } else {
+                    const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.N) dst[e] = e16[e];
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+}
+
+// Epilogue of one wave of gemm_kernel whose wave tile is 64 columns wide
+// (FN = 2 tiles of 32 x 32, FM row blocks; lane l holds row l % 32 of a tile,
+// columns 8 g + 4 (l / 32) .. + 3 in accumulator elements 4 g .. 4 g + 3)
+// through 4 KB of LDS owned by the wave, 32 rows at a time, so that every
+// lane stores 16 contiguous bytes and 8 lanes a row's 128 bytes (the 8-byte
+// stores of store_block touch 32 rows per instruction).  Same stage layout as
+// store_block_staged: row r keeps its 16-byte chunk c at c ^ ((r >> 1) & 7);
+// the 8-byte writes (32 rows x one chunk, both halves) fall on every bank
+// exactly twice.  Masked at the M and N edges.
+template <typename Elt, int FM>
+__device__ __forceinline__ void store_block_staged32(const GemmParams& p,
+                                                     const floatx16_t (&acc)[2][FM], int64_t mb,
+                                                     int64_t nb, int lane, int4_t* stage) {
+    typedef typename Elt::vec4 vec4;
+    typedef typename Elt::scalar scalar;
+    char* lds = reinterpret_cast<char*>(stage);
+    const int wr = lane & 31;          // write: row of the 32-row block
+    const int wh = lane >> 5;          // write: which 8-byte half of the chunk
+    const int rr = 2 * ((lane >> 3) & 3) + (lane >> 5);
+    const int rc = lane & 7;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {     // rows 32 j .. 32 j + 31
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                vec4 h;
+                h[0] = (scalar)acc[i][j][4 * g + 0];
+                h[1] = (scalar)acc[i][j][4 * g + 1];
+                h[2] = (scalar)acc[i][j][4 * g + 2];
+                h[3] = (scalar)acc[i][j][4 * g + 3];
+                const int chunk = 4 * i + g;
+                *reinterpret_cast<uint2_t*>(lds + wr * 128 + ((chunk ^ ((wr >> 1) & 7)) * 16) +
+                                            wh * 8) = __builtin_bit_cast(uint2_t, h);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int r = 8 * k + rr;
+            const int4_t v = *reinterpret_cast<const int4_t*>(
+                lds + r * 128 + ((rc ^ ((r >> 1) & 7)) * 16));
+            const int64_t m = mb + j * 32 + r;
+            const int64_t n = nb + 8 * rc;
+            if (m < p.M) {
+                uint16_t* dst = p.C + m * p.ldc + n;
+                if (n + 7 < p.N) {
                     *reinterpret_cast<int4_t*>(dst) = v;
                 } else {
                     const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&v);
@@ -542,8 +607,17 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
                     acc[i2][j][e] += red[((wmn * FN * FM + i2 * FM + j) * 16 + e) * 64 + lane];
     }
 
-    // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked 8-byte stores -----------------
-    store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
+    // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked stores ---------------------------
+    // A 64-column wave tile goes through 4 KB of LDS per wave: with k-groups
+    // in the wave's own part of the partial-sum area (which only it reads),
+    // otherwise at the start of the stages, which no wave reads any more
+    // after the last k-step's barrier.
+    if constexpr (FN == 2) {
+        int4_t* stage = (KS > 1) ? smem + wmn * (FN * FM * 256) : smem + wmn * 256;
+        store_block_staged32<Elt, FM>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, stage);
+    } else {
+        store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
+    }
 }
 
 // The 256 x 256 rung with a ping-pong schedule (8 waves, 2 per SIMD).
