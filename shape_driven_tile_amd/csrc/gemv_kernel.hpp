@@ -81,12 +81,14 @@ __device__ __forceinline__ float dot8(int4_t w, int4_t x, float acc) {
 }
 
 // TAIL = false: K is a multiple of XCH * 512 (no ragged pass is compiled in,
-// which keeps the kernel at 61 VGPRs, 8 waves per SIMD).
-template <typename Elt, int RPW, int XCH, bool TAIL>
-__global__ __launch_bounds__(256) void gemv_m1_kernel(GemvParams p) {
+// which keeps the kernel at 64 VGPRs, 8 waves per SIMD).  WPB waves per
+// workgroup: one-wave workgroups streamed the decode shape 0.6% faster than
+// four-wave ones (15.85 vs 15.94 us, same box), two and eight slower.
+template <typename Elt, int RPW, int XCH, bool TAIL, int WPB>
+__global__ __launch_bounds__(WPB * 64) void gemv_m1_kernel(GemvParams p) {
     const int lane = threadIdx.x & 63;
-    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    // Waves past N (the last workgroup's, when N is not a multiple of 4 RPW)
+    const int64_t wave = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    // Waves past N (the last workgroup's, when N is not a multiple of WPB RPW)
     // run on the clamped last row and store nothing: no early exit, whose
     // test would have the wave load N and branch before it loads the rest of
     // its arguments.

@@ -125,15 +125,17 @@ constexpr int kGemvVariants = sizeof(kGemvRpw) / sizeof(kGemvRpw[0]);
 
 template <typename Elt, int RPW>
 hipError_t launch_gemv_rpw(GemvParams p, hipStream_t stream) {
+    // one-wave workgroups for one row per wave, four waves otherwise
+    constexpr int WPB = (RPW == 1) ? 1 : 4;
     const int64_t waves = (p.N + RPW - 1) / RPW;
-    const int64_t blocks = (waves + 3) / 4;
+    const int64_t blocks = (waves + WPB - 1) / WPB;
     void* args[] = {&p};
     // K a multiple of one pass (8 x 512 elements): the kernel without the
     // ragged-pass code, which needs fewer registers.
     const void* k = (p.K % (8 * 512) == 0)
-                        ? reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, false>)
-                        : reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, true>);
-    return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(256), args, 0, stream);
+                        ? reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, false, WPB>)
+                        : reinterpret_cast<const void*>(&gemv_m1_kernel<Elt, RPW, 8, true, WPB>);
+    return hipLaunchKernel(k, dim3((unsigned)blocks), dim3(WPB * 64), args, 0, stream);
 }
 
 template <typename Elt>
