@@ -48,7 +48,8 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=400)
+    # about 10 s of steps: the clock and power settle over seconds of this load
+    ap.add_argument("--warmup", type=int, default=10000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-detail", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -204,7 +205,8 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"warm-up {args.warmup} steps in {time.time() - t0:.2f} s")
+    warmup_s = time.time() - t0
+    log(f"warm-up {args.warmup} steps in {warmup_s:.2f} s")
 
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
@@ -233,6 +235,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_s": round(warmup_s, 2),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -272,6 +275,12 @@ def main():
     if not args.no_detail:
         result["detail"] = detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor,
                                   flop_gemm, bytes_gemv, bytes_gemv_all)
+        clk = result["detail"].get("clock_under_load") or {}
+        if clk.get("mfma_ceiling_at_clock_tflops"):
+            # the timed region's 8192^3 rate against 256 CU x 4096 FLOP/clk at
+            # the clock sampled in the separate under-load window
+            clk["timed_region_frac_of_clock_ceiling"] = round(
+                achieved / clk["mfma_ceiling_at_clock_tflops"], 4)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
@@ -491,6 +500,32 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         "protocol": "8 rotating buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
     }
     log(f"decode cold: median {med:.2f} us = {det['decode_cold']['GBps_weights_median']} GB/s")
+    # The streaming-read ceiling for the same rotation: the library's read-only
+    # kernel (the GEMV's load pattern and nothing else), same protocol.
+    words = torch.empty(int(bytes_gemv) // 8192, dtype=torch.int32, device=dev)
+    r = (lambda j: sdt.stream_read(Ws[j % len(Ws)], words))
+    t0 = time.time()
+    j = 0
+    while time.time() - t0 < 1.0:
+        r(j)
+        j += 1
+        if j % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    us_r = time_launches(torch, r, 200)
+    med_r = sorted(us_r)[len(us_r) // 2]
+    det["decode_read_ceiling"] = {
+        "us": _ranges(us_r),
+        "GBps_median": round(bytes_gemv / (med_r * 1e-6) / 1e9, 1),
+        "hbm_frac_median": round(bytes_gemv / (med_r * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "gemv_frac_of_ceiling_median": round(med_r / med, 4),
+        "kernel": "sdt_stream_read: 8 KB per wave, 8 non-temporal 16-byte loads per lane, "
+                  "no arithmetic or output beyond one word per 8 KB",
+        "protocol": "the same 8 rotating weight buffers, 1 s warm, 200 launches x 10 repeats",
+    }
+    log(f"decode read ceiling: median {med_r:.2f} us = "
+        f"{det['decode_read_ceiling']['GBps_median']} GB/s; the GEMV reaches "
+        f"{100 * med_r / med:.1f}% of it")
 
     # The same decode product with the weights stored as K rows of N (the
     # pages' B-layout): gated against the oracle, then the same cold protocol
@@ -617,18 +652,40 @@ def cpu_baseline(oracle, AB, target_s):
     A, B = AB
     n = A.shape[0]
     threads = oracle.max_threads()
+    # rate estimate on enough rows to occupy every thread
+    est = min(n, 8 * threads)
     t = time.time()
-    oracle.gemm(A[:4], B)
-    per_row = max((time.time() - t) / 4, 1e-6)
-    rows = int(min(n, max(4, target_s / per_row)))
+    oracle.gemm(A[:est], B)
+    per_row = max((time.time() - t) / est, 1e-6)
+    rows = int(min(n, max(est, target_s / per_row)))
     t = time.time()
     oracle.gemm(A[:rows], B)
     dt = time.time() - t
     flop = 2.0 * rows * n * n
+    # one thread at two small squares, for scale
+    one_thread = {}
+    for m in (256, 1024):
+        a = np.ascontiguousarray(A[:m, :m])
+        b = np.ascontiguousarray(B[:m, :m])
+        t = time.time()
+        oracle.gemm(a, b, threads=1)
+        d1 = time.time() - t
+        one_thread[f"{m}^3"] = {"s": round(d1, 4), "GFLOP_s": round(2.0 * m ** 3 / d1 / 1e9, 3)}
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{rows} full output rows of the {n}^3 product ({flop:.3g} FLOP) in "
-                      f"{dt:.2f} s, fp64 accumulation, {threads} OpenMP threads"}
+                      f"{dt:.2f} s, fp64 accumulation, {threads} OpenMP threads",
+            "GFLOP_s": round(flop / dt / 1e9, 3), "cpu_model": model,
+            "one_thread": one_thread}
 
 
 if __name__ == "__main__":

@@ -231,6 +231,20 @@ int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt);
  * such a floor).  Returns SDT_OK or SDT_ERR_HIP. */
 int sdt_empty_kernel(void* stream);
 
+/* Measurement: enqueue a read-only streaming kernel over `bytes` bytes of
+ * device memory at `buf` (one wave per 8 KB run, eight non-temporal 16-byte
+ * loads per lane: the access pattern of gemv_f16_m1, with no activations,
+ * arithmetic or output).  Each 8 KB run is folded into one 32-bit word written
+ * to out[run], so `out` (device, caller-owned) holds bytes / 8192 words; the
+ * words have no meaning beyond keeping every load live.  Timed back to back
+ * over the decode shape's rotating weight buffers it gives the streaming-read
+ * ceiling the decode GEMV is reported against.  bytes == 0: SDT_OK, nothing
+ * enqueued.  SDT_ERR_INVALID_ARG: bytes < 0 or a null pointer.
+ * SDT_ERR_UNSUPPORTED: bytes not a multiple of 8192 (or more than 2^31 - 1
+ * runs), buf not 16-byte aligned or out not 4-byte aligned.  SDT_ERR_HIP: the
+ * launch failed. */
+int sdt_stream_read(const void* buf, int64_t bytes, void* out, void* stream);
+
 /* Host-only argument check used by gemv_f16_m1_kn before anything is
  * enqueued (the status it would return for these arguments). */
 int sdt_check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B,

@@ -26,7 +26,8 @@ EXPORTS = (
     "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
     "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles", "sdt_tile_info",
     "sdt_stagger_eligible", "sdt_stagger_ktile", "sdt_check_gemm_args",
-    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_plan_tile",
+    "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read",
+    "sdt_plan_tile",
     "gemm_f16_cfg", "gemm_bf16_cfg",
 )
 
@@ -98,6 +99,7 @@ def lib():
     L.sdt_status_string.restype = ctypes.c_char_p
     L.sdt_last_hip_error.argtypes = []
     L.sdt_empty_kernel.argtypes = [_vp]
+    L.sdt_stream_read.argtypes = [_vp, _i64, _vp, _vp]
     for name in ("gemm_f16", "gemm_f16_ex", "gemv_f16_m1", "gemv_f16_m1_ex",
                  "gemv_f16_m1_kn", "gemv_f16_m1_kn_ex", "sdt_gemv_kn_num_variants",
                  "gemm_bf16", "gemm_bf16_ex", "gemv_bf16_m1", "gemv_bf16_m1_kn",
@@ -105,7 +107,7 @@ def lib():
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
                  "gemm_f16_cfg", "gemm_bf16_cfg",
-                 "sdt_last_hip_error", "sdt_empty_kernel"):
+                 "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
         getattr(L, name).restype = _int
     _lib = L
     return L
@@ -251,6 +253,20 @@ def gemv_f16_m1(x, B, y, stream=None, variant: int | None = None) -> None:
         rc = lib().gemv_f16_m1_ex(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), h, int(variant))
     if rc != SDT_OK:
         raise SdtError(rc, "gemv_f16_m1")
+
+
+def stream_read(buf, out, stream=None) -> None:
+    """Enqueue the library's read-only streaming kernel over the bytes of the
+    contiguous device tensor `buf` (a multiple of 8192 bytes); `out` is a
+    contiguous device tensor of at least numel(buf) * itemsize / 8192 int32
+    words."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or not out.is_contiguous() or \
+            out.numel() * out.element_size() < (nbytes // 8192) * 4:
+        raise ValueError("stream_read: contiguous buf, and out of one int32 word per 8 KB")
+    rc = lib().sdt_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_stream_read")
 
 
 def empty_kernel(stream=None) -> None:

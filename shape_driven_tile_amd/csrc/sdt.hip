@@ -269,6 +269,25 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
 // launch floor the small shapes are measured against.
 __global__ void empty_kernel() {}
 
+// Reads memory and nothing else: one wave per 8 KB run, eight non-temporal
+// 16-byte loads per lane (the decode GEMV's access pattern, without the
+// activations, the arithmetic or the output), folded into one word per run so
+// that no load is dead.  Timed over the decode shape's rotating weight buffers
+// it gives the streaming-read ceiling the GEMV is compared with.
+__global__ __launch_bounds__(64) void stream_read_kernel(const int4_t* buf, uint32_t* out) {
+    const int lane = threadIdx.x;
+    const int4_t* run = buf + (int64_t)blockIdx.x * 512;
+    int4_t v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(run + j * 64 + lane);
+    int x = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
+    if (lane == 0) out[blockIdx.x] = (uint32_t)x;
+}
+
 }  // namespace
 }  // namespace sdt
 
@@ -379,6 +398,21 @@ extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_ti
 }
 
 extern "C" int sdt_last_hip_error(void) { return sdt::g_last_hip_error; }
+
+extern "C" int sdt_stream_read(const void* buf, int64_t bytes, void* out, void* stream) {
+    if (bytes == 0) return SDT_OK;
+    if (bytes < 0 || !buf || !out) return SDT_ERR_INVALID_ARG;
+    if (bytes % 8192 != 0 || bytes / 8192 > INT_MAX ||
+        (reinterpret_cast<uintptr_t>(buf) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+        return SDT_ERR_UNSUPPORTED;
+    const sdt::int4_t* b = static_cast<const sdt::int4_t*>(buf);
+    uint32_t* o = static_cast<uint32_t*>(out);
+    void* args[] = {&b, &o};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sdt::stream_read_kernel),
+                                   dim3((unsigned)(bytes / 8192)), dim3(64), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);
+}
 
 extern "C" int sdt_empty_kernel(void* stream) {
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sdt::empty_kernel), dim3(1),

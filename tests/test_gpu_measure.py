@@ -1,0 +1,63 @@
+"""GPU tests of the library's measurement kernels (not part of the product's
+math): the empty kernel behind the launch floor and the read-only streaming
+kernel behind the decode shape's read ceiling.  The streaming kernel's output
+words are exact (XOR of each 8 KB run's 32-bit words), so the test checks that
+every byte was read, in bounds, and nothing else was written."""
+import numpy as np
+import pytest
+
+from gpu_helpers import say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _xor_words(buf_u8: np.ndarray) -> np.ndarray:
+    return np.bitwise_xor.reduce(buf_u8.view(np.int32).reshape(-1, 2048), axis=1)
+
+
+def test_empty_kernel_runs():
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    say("sdt_empty_kernel x 10")
+    for _ in range(10):
+        sdt.empty_kernel()
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("runs", [1, 3, 257, 12288])
+def test_stream_read_words_exact(runs):
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    rng = np.random.default_rng(7000 + runs)
+    host = rng.integers(0, 256, size=runs * 8192, dtype=np.uint8)
+    buf = to_dev(host)
+    out = torch.full((runs + 4,), -1, dtype=torch.int32, device=buf.device)   # 4 guard words
+    say(f"sdt_stream_read runs={runs}")
+    sdt.stream_read(buf, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[:runs], _xor_words(host))
+    assert (got[runs:] == -1).all(), "words past the last run were written"
+
+
+def test_stream_read_arguments():
+    import ctypes
+
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    L = sdt.lib()
+    buf = torch.zeros(2 * 8192, dtype=torch.uint8, device="cuda:0")
+    out = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    say("sdt_stream_read argument checks (nothing enqueued)")
+    assert L.sdt_stream_read(buf.data_ptr(), 0, out.data_ptr(), s) == sdt.SDT_OK
+    assert L.sdt_stream_read(buf.data_ptr(), -8192, out.data_ptr(), s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read(None, 8192, out.data_ptr(), s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read(buf.data_ptr(), 8192, None, s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read(buf.data_ptr(), 4096, out.data_ptr(), s) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_stream_read(buf.data_ptr() + 8, 8192, out.data_ptr(), s) == \
+        sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_stream_read(buf.data_ptr(), 8192, out.data_ptr() + 2, s) == \
+        sdt.SDT_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 0).all()
