@@ -115,8 +115,9 @@ def main():
     if args.profile:
         return profile_mode(args)
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; run with --gpus 1",
-                          "n_gpus": args.gpus}), flush=True)
+        print(json.dumps({"error": "one GPU only: the kernels are measured on a single MI355X "
+                                   "(a sharded run would split N across GPUs with no exchange); "
+                                   "run with --gpus 1", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
     import numpy as np

@@ -352,3 +352,23 @@ def test_capi_program_links_only_the_c_abi():
     needed = set(re.findall(r"NEEDED\)\s+Shared library: \[([^\]]+)\]", out))
     assert "libsdt.so" in needed and "libsdt_oracle.so" in needed
     assert not any("torch" in n or "python" in n for n in needed), needed
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import json
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    from shape_driven_tile_amd import binding
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libsdt.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()
