@@ -206,7 +206,8 @@ def test_overflow_rounds_to_inf():
 @pytest.mark.parametrize("M,N,K,pa,pb,pc", [
     (1, 1, 1, 7, 7, 7), (3, 5, 7, 1, 9, 3), (65, 129, 72, 8, 0, 8), (257, 511, 8, 0, 8, 0),
     (100, 90, 37, 3, 11, 6), (300, 200, 1000, 24, 0, 40), (129, 1025, 200, 64, 64, 64),
-    (520, 260, 4100, 0, 0, 0), (2, 3000, 300, 4, 4, 8)])
+    (520, 260, 4100, 0, 0, 0), (2, 3000, 300, 4, 4, 8), (300, 1, 520, 8, 8, 7),
+    (2, 1, 16384, 0, 0, 7), (3000, 3100, 1000, 8, 0, 8)])
 def test_ragged_and_padded(M, N, K, pa, pb, pc):
     """Ragged M, N, K with padded leading dimensions full of NaN: the padding
     never reaches C, and nothing past column N of C is written."""
