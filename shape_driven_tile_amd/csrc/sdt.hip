@@ -64,8 +64,7 @@ hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
         dim3(p.gm * p.gn), dim3(WM * WN * KS * 64), args, 0, stream);
 }
 
-// Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
-// pipeline with one k-group, or the deep pipeline with two.
+// The 256 x 256 ping-pong kernel: 8 waves, 160 KB of LDS, one workgroup per CU.
 template <typename Elt>
 hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
@@ -73,6 +72,9 @@ hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
                            dim3(p.gm * p.gn), dim3(512), args, 0, stream);
 }
 
+// Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
+// pipeline with one k-group, or the deep pipeline with two; rung 0's deep
+// pipeline is the ping-pong kernel.
 template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
@@ -118,8 +120,8 @@ int fill_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream
 
 // GEMV instantiations: rows per wave; the activations are held as 8 chunks
 // of 8 fp16 per lane (4096 k per pass).  One row per wave is the fastest on
-// the decode shape (cold, 8 rotating buffers): 16.2 us per launch against
-// 18.7 / 19.3 us for two / four.
+// the decode shape (cold, 8 rotating buffers), by 15-20% over two or four
+// rows per wave: more waves in flight beat more loads per wave.
 constexpr int kGemvRpw[] = {1, 2, 4, 8};
 constexpr int kGemvVariants = sizeof(kGemvRpw) / sizeof(kGemvRpw[0]);
 
