@@ -8,7 +8,8 @@
 // wave layout), re-designed for CDNA4:
 //   * wave64 and v_mfma_f32_32x32x16_f16 (v_mfma_f32_32x32x16_bf16 for the
 //     bf16 variant): each wave owns a (BM/WM) x (BN/WN) block of 32x32
-//     accumulator tiles;
+//     accumulator tiles (the 256 x 256 ping-pong kernel at the end of this
+//     file uses 16x16x32 MFMAs and its own schedule);
 //   * both operands are K-contiguous rows (A row-major, B "K-major"), staged
 //     the same way: a k-tile is BM (or BN) rows of 64 fp16 = 128 bytes, eight
 //     16-byte chunks per row; chunk c of row r is stored at chunk c ^ swz(r),
@@ -32,12 +33,14 @@
 //     the second group's partial sums are added to the first's through LDS
 //     (a fixed order: the result is deterministic) before the epilogue;
 //   * k-loop stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by
-//     choosing the tile from the shape", Changes): when the number of full
-//     k-tiles is a power of two, workgroup w visits them in the order
-//     (w + i) & (nfull - 1);
+//     choosing the tile from the shape", Changes), when a caller forces it:
+//     with a power-of-two number of full k-tiles, workgroup w visits them in
+//     the order (w + i) & (nfull - 1);
 //   * edges: operand rows come through buffer descriptors clipped to the
 //     valid rows, so rows past M or N read as zero; a partial last k-tile is
 //     loaded through registers with per-element masking; stores are masked;
+//     wave tiles 64 columns wide pass their output through LDS so that each
+//     lane stores 16 contiguous bytes;
 //   * MI355X deals workgroup ids round-robin over its XCDs, each with a
 //     private L2; ids are remapped so every XCD works through a contiguous,
 //     GROUP_M-grouped band of output tiles.
