@@ -236,9 +236,9 @@ __device__ __forceinline__ void store_block(const GemmParams& p, const floatx16_
 // chunk per 16 lanes) and the 16-byte reads (an even and an odd row x 8
 // chunks per 16 lanes served together) both fall on distinct banks.  Masked
 // at the M and N edges.
-template <typename Elt>
+template <typename Elt, int FM = 8>
 __device__ __forceinline__ void store_block_staged(const GemmParams& p,
-                                                   const floatx4_t (&acc)[4][8], int64_t mb,
+                                                   const floatx4_t (&acc)[4][FM], int64_t mb,
                                                    int64_t nb, int lane, int4_t* stage) {
     typedef typename Elt::vec4 vec4;
     typedef typename Elt::scalar scalar;
@@ -250,7 +250,7 @@ __device__ __forceinline__ void store_block_staged(const GemmParams& p,
     const int rr = 2 * ((lane >> 3) & 3) + (lane >> 5);
     const int rc = lane & 7;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {      // rows 32 q .. 32 q + 31: tiles j = 2 q, 2 q + 1
+    for (int q = 0; q < FM / 2; ++q) { // rows 32 q .. 32 q + 31: tiles j = 2 q, 2 q + 1
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
             const int r = 16 * jj + (lane & 15);
@@ -358,7 +358,7 @@ __device__ __forceinline__ void store_block_staged32(const GemmParams& p,
     }
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
     typedef typename Elt::vec4 vec4;
@@ -367,8 +367,12 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     constexpr int NMN = WM * WN;       // waves per k-group (one output block each)
     constexpr int NW = NMN * KS;       // waves per workgroup
     static_assert(KS == 1 || KS == 2, "k-groups: 1 or 2");
+    // MF = 32: v_mfma_f32_32x32x16 on 32 x 32 tiles, four 16-deep sub-steps per
+    // k-tile.  MF = 16: v_mfma_f32_16x16x32 on 16 x 16 tiles, two 32-deep
+    // sub-steps, one k-group and 64-column wave tiles only.
+    static_assert(MF == 32 || (MF == 16 && KS == 1 && BN / WN == 64), "MFMA shape");
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int FM = WTM / 32, FN = WTN / 32;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
     constexpr int STAGE = A_UNITS + B_UNITS;
     constexpr int A_DMA = A_UNITS / (64 * NW);         // 1 KB loads per wave per k-tile
@@ -426,13 +430,13 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
 #pragma unroll
     for (int j = 0; j < A_DMA; ++j) {
         const int row = (wave * A_DMA + j) * 8 + (lane >> 3);
-        chk_a[j] = (lane & 7) ^ swz(row);
+        chk_a[j] = (lane & 7) ^ (MF == 32 ? swz(row) : swz_pp(row));
         voff_a[j] = (uint32_t)(row * p.lda * 2 + chk_a[j] * 16);
     }
 #pragma unroll
     for (int j = 0; j < B_DMA; ++j) {
         const int row = (wave * B_DMA + j) * 8 + (lane >> 3);
-        chk_b[j] = (lane & 7) ^ swz(row);
+        chk_b[j] = (lane & 7) ^ (MF == 32 ? swz(row) : swz_pp(row));
         voff_b[j] = (uint32_t)(row * p.ldb * 2 + chk_b[j] * 16);
     }
 
@@ -469,37 +473,44 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     };
 
     // ---- accumulators and fragments ----------------------------------------------
-    floatx16_t acc[FN][FM];
+    typedef std::conditional_t<MF == 32, floatx16_t, floatx4_t> acc_t;
+    constexpr int ACC = MF == 32 ? 16 : 4;
+    acc_t acc[FN][FM];
 #pragma unroll
     for (int i = 0; i < FN; ++i)
 #pragma unroll
         for (int j = 0; j < FM; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+            for (int e = 0; e < ACC; ++e) acc[i][j][e] = 0.0f;
 
-    // Lane reads row (lane % 32) of a 32-row block, chunk 2*kk + lane/32.
-    const int frow = lane & 31;
-    const int fsw = swz(frow);
-    const int fhalf = lane >> 5;
+    // MF = 32: lane reads row (lane % 32) of a 32-row block, chunk 2*kk +
+    // lane/32.  MF = 16: row (lane % 16) of a 16-row block, chunk 4*kk +
+    // lane/16.  Rows of one lane differ by multiples of MF: same swizzle.
+    const int frow = lane & (MF - 1);
+    const int fsw = MF == 32 ? swz(frow) : swz_pp(frow);
+    const int fhalf = lane / MF;
     const int a_row0 = wave_m * WTM + frow;
     const int b_row0 = wave_n * WTN + frow;
     frag8 fa[2][FM], fb[2][FN];
     auto read_frags = [&](int stage, int kk, int set) {
         const int4_t* base = smem + stage * STAGE;
-        const int chunk = (2 * kk + fhalf) ^ fsw;
+        const int chunk = ((64 / MF) * kk + fhalf) ^ fsw;
 #pragma unroll
         for (int j = 0; j < FM; ++j)
-            fa[set][j] = __builtin_bit_cast(frag8, base[(a_row0 + j * 32) * 8 + chunk]);
+            fa[set][j] = __builtin_bit_cast(frag8, base[(a_row0 + j * MF) * 8 + chunk]);
 #pragma unroll
         for (int i = 0; i < FN; ++i)
-            fb[set][i] = __builtin_bit_cast(frag8, base[A_UNITS + (b_row0 + i * 32) * 8 + chunk]);
+            fb[set][i] = __builtin_bit_cast(frag8, base[A_UNITS + (b_row0 + i * MF) * 8 + chunk]);
     };
     auto mfmas = [&](int set) {
 #pragma unroll
         for (int i = 0; i < FN; ++i)
 #pragma unroll
             for (int j = 0; j < FM; ++j)
-                acc[i][j] = Elt::mfma(fb[set][i], fa[set][j], acc[i][j]);
+                if constexpr (MF == 32)
+                    acc[i][j] = Elt::mfma(fb[set][i], fa[set][j], acc[i][j]);
+                else
+                    acc[i][j] = Elt::mfma16(fb[set][i], fa[set][j], acc[i][j]);
     };
     // One MFMA, then one fragment read and one global load while any remain
     // (scheduling-group masks: 0x008 MFMA, 0x100 LDS read, 0x020 global read).
@@ -536,7 +547,12 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     int s = 0;                               // stage of tile i
     for (; i + NS < nfull; ++i) {
         const int sn = (s + 1 == NS) ? 0 : s + 1;
-        if constexpr (KS == 1) {
+        if constexpr (KS == 1 && MF == 16) {
+            read_frags(s, 1, 1);
+            mfmas(0);
+            interleave(Reads{}, None{});
+            __builtin_amdgcn_sched_barrier(0);
+        } else if constexpr (KS == 1) {
             read_frags(s, 1, 1);
             mfmas(0);
             interleave(Reads{}, None{});
@@ -567,7 +583,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     // ---- the last steps (every condition spelled out, full waits) -------------------
     for (; i < nseq; ++i) {
         const int sn = (s + 1 == NS) ? 0 : s + 1;
-        if constexpr (KS == 1) {
+        if constexpr (KS == 1 && MF == 16) {
+            read_frags(s, 1, 1);
+            mfmas(0);
+        } else if constexpr (KS == 1) {
             read_frags(s, 1, 1);
             mfmas(0);
             read_frags(s, 2, 0);
@@ -615,7 +634,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     // in the wave's own part of the partial-sum area (which only it reads),
     // otherwise at the start of the stages, which no wave reads any more
     // after the last k-step's barrier.
-    if constexpr (FN == 2) {
+    if constexpr (MF == 16) {
+        store_block_staged<Elt, FM>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
+                                    smem + wmn * 256);
+    } else if constexpr (FN == 2) {
         int4_t* stage = (KS > 1) ? smem + wmn * (FN * FM * 256) : smem + wmn * 256;
         store_block_staged32<Elt, FM>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, stage);
     } else {

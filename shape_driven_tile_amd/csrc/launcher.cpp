@@ -42,7 +42,14 @@ int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     if (num_cu <= 0) num_cu = 256;
     const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn);
     const int64_t nkt = ceil_div(K, kBK);
-    return (wgs <= num_cu && nkt >= kSplitMinKTiles) ? 2 : 1;
+    if (nkt < kSplitMinKTiles) return 1;
+    // A rung whose one-k-group pipeline runs 16x16x32 MFMAs keeps it once the
+    // grid fills every CU: there the part runs at its power limit and that
+    // MFMA's lower energy per FLOP wins (128x128 at 2048^3: 20.0 us against
+    // 21.5 with two k-groups); with CUs left idle the second k-group's
+    // shorter dependent chain wins (1536^3: 13.7 against 14.8).
+    if (d.deep16) return wgs < num_cu ? 2 : 1;
+    return wgs <= num_cu ? 2 : 1;
 }
 
 // The automatic plan on rung `id`: two k-groups always run the deep

@@ -22,6 +22,7 @@ struct TileDesc {
     int bm, bn, waves_m, waves_n, stages;
     int kgroups;    // 2: also built with two k-groups of waves (see kgroups_for)
     int pingpong;   // 1: the deep pipeline is the ping-pong kernel
+    int deep16;     // 1: the deep pipeline with one k-group runs 16x16x32 MFMAs
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
@@ -29,11 +30,11 @@ struct TileDesc {
 // occupancy, 3 measuring as fast as 4 or faster on every rung below the
 // largest, whose deep pipeline (2 A + 3 B stages) fills all 160 KB.
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 3, 1, 1},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 128, 2, 2, 3, 2, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3, 2, 0},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3, 2, 0},   // 4 waves, 64x32 per wave, 3 x 24 KB
-    {64, 64, 2, 2, 3, 2, 0},    // 4 waves, 32x32 per wave, 3 x 16 KB
+    {256, 256, 2, 4, 3, 1, 1, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
+    {256, 128, 2, 2, 3, 2, 0, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3, 2, 0, 0},   // 4 waves, 64x32 per wave, 3 x 24 KB
+    {64, 64, 2, 2, 3, 2, 0, 0},    // 4 waves, 32x32 per wave, 3 x 16 KB
 };
 
 // Operand bytes up to which a launch runs the shallow 2-stage pipeline: one

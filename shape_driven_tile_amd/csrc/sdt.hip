@@ -56,11 +56,11 @@ int device_info(DeviceInfo* out) {
     return SDT_OK;
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS>
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS>),
+        reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS, MF>),
         dim3(p.gm * p.gn), dim3(WM * WN * KS * 64), args, 0, stream);
 }
 
@@ -74,7 +74,8 @@ hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
 
 // Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
 // pipeline with one k-group, or the deep pipeline with two; rung 0's deep
-// pipeline is the ping-pong kernel.
+// pipeline is the ping-pong kernel, and a deep16 rung's deep pipeline with
+// one k-group runs 16x16x32 MFMAs.
 template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
@@ -91,7 +92,10 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
         }
         if (pl.stages == 2)
             return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
-        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1>(p, s);
+        if constexpr (d.deep16)
+            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16>(p, s);
+        else
+            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1>(p, s);
     }
 }
 

@@ -173,8 +173,10 @@ def test_ladder_is_well_formed():
 
 def test_launch_plan_rules():
     """k-groups: 2 on rungs built with them when the grid has at most num_cu
-    workgroups and K spans at least 12 k-tiles.  Stages: the deep count with
-    two k-groups; with one, 2 while A and B (2*K*(M+N) bytes) fit in 4 MiB."""
+    workgroups (fewer than num_cu on the 128x128 rung, whose one-k-group deep
+    pipeline runs 16x16x32 MFMAs) and K spans at least 12 k-tiles.  Stages:
+    the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
+    bytes) fit in 4 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
@@ -184,7 +186,8 @@ def test_launch_plan_rules():
             for (M, N, K) in shapes:
                 p = sdt.plan_tile(t["id"], M, N, K, num_cu)
                 wgs = -(-M // t["bm"]) * -(-N // t["bn"])
-                kg = 2 if (t["kgroups"] == 2 and wgs <= num_cu and -(-K // 64) >= 12) else 1
+                fits = wgs < num_cu if (t["bm"], t["bn"]) == (128, 128) else wgs <= num_cu
+                kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
                 st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
                                                   else t["stages"])
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
@@ -201,6 +204,8 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 2
     assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
+    assert sdt.pick_tile(1536, 1536, 1536, 256)["kgroups"] == 2   # 144 workgroups
+    assert sdt.pick_tile(2048, 2048, 2048, 256)["kgroups"] == 1   # 256: the 16x16x32 pipeline
 
 
 def test_gemm_cfg_rejects_kernels_that_do_not_exist():
