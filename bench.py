@@ -62,7 +62,7 @@ def parse():
     ap.add_argument("--launches", type=int, default=20)
     ap.add_argument("--tile", type=int, default=-1)
     ap.add_argument("--variant", type=int, default=-1, help="profile mode: GEMV variant")
-    ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 default (off), 0 off, 1 on")
+    ap.add_argument("--stagger", type=int, default=-1, help="profile mode: -1 the plan's choice, 0 off, 1 on")
     return ap.parse_args()
 
 
@@ -458,14 +458,15 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             "tile": sdt.pick_tile(n, n, n, 0)["id"],
         }
         log(f"square {n}: median {med:.2f} us {det['square'][str(n)]['tflops_median']} TFLOP/s")
-    # K sweep at M=N=2048: the default arm (plain k order) at every K, plus
-    # the forced stagger at K=2048, the one K whose k-tile count allows it
+    # K sweep at M=N=2048: the default arm at every K, plus both stagger arms
+    # forced at K=2048, the one K whose k-tile count allows a stagger
     for K in inputs.K_SWEEP_K:
         A, B = inputs.square_operands(inputs.K_SWEEP_MN, 3, k=K)
         dA, dB = dev_tensor(A), dev_tensor(B)
         C = torch.empty((2048, 2048), dtype=torch.float16, device=dev)
         arms = {"auto": (-1, -1)}
-        if K == 2048:
+        if sdt.stagger_eligible(K):
+            arms["stagger_off"] = (-1, 0)
             arms["stagger_on"] = (-1, 1)
         for name, (tile, st) in arms.items():
             f = (lambda j, tile=tile, st=st: sdt.gemm_f16_ex(dA, dB, C, tile_id=tile, stagger=st))
@@ -476,7 +477,7 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             det["k_sweep"][f"{K}_{name}"] = {
                 "us": _ranges(us),
                 "tflops_median": round(2.0 * 2048 * 2048 * K / (med * 1e-6) / 1e12, 1),
-                "stagger": st == 1,
+                "stagger": bool(st == 1 or (st == -1 and sdt.pick_tile(2048, 2048, K, 0)["stagger"])),
                 "tile": sdt.pick_tile(2048, 2048, K, 0)["id"],
             }
     # Cold-cache decode: 8 rotating 100.7 MB weight buffers (805 MB >> 256 MB

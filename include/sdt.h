@@ -68,6 +68,8 @@ typedef struct sdt_tile {
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
                         sub-steps (1 or 2; sdt_tile_info: the most the rung is
                         built with) */
+    int stagger;     /* 1: the automatic plan visits the k-tiles staggered,
+                        (workgroup + i) & (k-tiles - 1) (sdt_tile_info: 0) */
 } sdt_tile;
 
 /* A launch configuration; -1 in a field = the automatic choice. */
@@ -88,9 +90,12 @@ typedef struct sdt_launch {
  * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
  * definition).  The tile is chosen by sdt_pick_tile from the device's CU
- * count.  The k-loop runs in plain k order: the k-tile stagger of the
- * FlyDSL PR is available through gemm_f16_ex but measured no faster on
- * MI355X (sdt_stagger_eligible). */
+ * count.  The k-loop runs in plain k order except where the plan staggers it
+ * (FlyDSL PR, Changes: workgroup w starts at k-tile w and wraps): on rungs
+ * other than the ping-pong kernel, with a power-of-two count of at least 16
+ * full k-tiles, and A and B together within 16 MiB (2*K*(M+N) bytes), where
+ * it measured 2-5% faster on MI355X; larger operands lose up to 49% with it
+ * (sdt_plan_tile reports the choice). */
 int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
              const void* B, int64_t ldb,
@@ -139,8 +144,8 @@ int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x,
 
 /* gemm_f16 with the launcher's choices forced.  tile_id: -1 = automatic,
  * else a ladder index (SDT_ERR_INVALID_ARG if out of range).  stagger: -1 =
- * what gemm_f16 does (off), 0 = off, 1 = on (SDT_ERR_UNSUPPORTED unless
- * sdt_stagger_eligible(K)).  M == 1 is not rerouted to the GEMV here. */
+ * what gemm_f16 does (the plan's choice), 0 = off, 1 = on (SDT_ERR_UNSUPPORTED
+ * unless sdt_stagger_eligible(K)).  M == 1 is not rerouted to the GEMV here. */
 int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 const void* A, int64_t lda,
                 const void* B, int64_t ldb,
@@ -211,18 +216,18 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
  * else 1.  Stages: the deep count
  * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
  * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the
- * shorter prologue wins), else the deep count.  SDT_OK or
- * SDT_ERR_INVALID_ARG. */
+ * shorter prologue wins), else the deep count.  Stagger: as gemm_f16
+ * describes.  SDT_OK or SDT_ERR_INVALID_ARG. */
 int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
                   sdt_tile* out);
 
 /* Host-only: 1 if the k-loop of a product with inner size K can be staggered,
  * else 0: the number of full 64-deep k-tiles floor(K/64) must be a power of
  * two, since the wrap-around is a mask (FlyDSL PR, Changes; the PR enables
- * the stagger exactly then).  gemm_f16 does not stagger by itself on MI355X:
- * measured against plain k order it gains at most 2% (1536x1536x4096) and
- * loses up to 53% (2048x2048x8192), since workgroups that share operand rows
- * through one XCD's L2 stop reading the same k-tile at the same time. */
+ * the stagger exactly then).  On MI355X gemm_f16 staggers only the eligible
+ * products gemm_f16 describes: with larger operands it loses up to 49%
+ * (2048x2048x8192), since workgroups that share operand rows through one
+ * XCD's L2 stop reading the same k-tile at the same time. */
 int sdt_stagger_eligible(int64_t K);
 
 /* Host-only: the k-tile visited at step i by workgroup wg when staggered:

@@ -9,7 +9,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-sdt_tile describe(int id, int stages, int kgroups) {
+sdt_tile describe(int id, int stages, int kgroups, int stagger) {
     const TileDesc& d = kLadder[id];
     sdt_tile t;
     t.id = id;
@@ -24,6 +24,7 @@ sdt_tile describe(int id, int stages, int kgroups) {
     t.lds_bytes = (d.pingpong && stages == d.stages)
                       ? (2 * d.bm + d.stages * d.bn) * kBK * 2   // A in 2 stages, B in `stages`
                       : stages * (d.bm + d.bn) * kBK * 2;
+    t.stagger = stagger;
     return t;
 }
 
@@ -59,7 +60,14 @@ Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     p.tile = id;
     p.kgroups = kgroups_for(id, M, N, K, num_cu);
     p.stages = p.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
+    p.stagger = stagger_auto(id, M, N, K) ? 1 : 0;
     return p;
+}
+
+bool stagger_auto(int id, int64_t M, int64_t N, int64_t K) {
+    if (id < 0 || id >= kNumTiles || kLadder[id].pingpong) return false;
+    if (!stagger_eligible(K) || K / kBK < kStaggerMinKTiles) return false;
+    return 2 * K * (M + N) <= kStaggerMaxOperandBytes;
 }
 
 // A plan the library has a kernel for: stages 2 or the rung's deep count;
@@ -178,7 +186,7 @@ extern "C" int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int n
         return SDT_ERR_INVALID_ARG;
     if (num_cu <= 0) num_cu = 256;
     const sdt::Plan p = sdt::plan_for(tile_id, M, N, K, num_cu);
-    *out = sdt::describe(p.tile, p.stages, p.kgroups);
+    *out = sdt::describe(p.tile, p.stages, p.kgroups, p.stagger);
     return SDT_OK;
 }
 

@@ -53,9 +53,21 @@ constexpr int64_t kShallowOperandBytes = int64_t(4) << 20;
 // 8 k-tiles or fewer do not earn back (256^3: 3.69 -> 3.85 us).
 constexpr int kSplitMinKTiles = 12;
 
-// How one product is launched: rung, LDS stages, k-groups of waves.
+// Largest operand footprint, 2*K*(M+N) bytes, and fewest full k-tiles at
+// which the automatic plan staggers the k-loop (rungs other than the ping-pong
+// kernel, power-of-two k-tile count).  Fitted on MI355X: with A and B within
+// 16 MiB the stagger spreads the workgroups' concurrent row reads over
+// different k-offsets and buys 2-5% (2048^3 19.5 against 20.6 us,
+// 1024x1024x4096 17.5 against 18.2); past it it breaks the workgroups' shared
+// k-window in L2 and costs up to 49% (2048x2048x8192), and on the ping-pong
+// kernel 9% at 4096^3.  Below 16 k-tiles it measured neutral.
+constexpr int64_t kStaggerMaxOperandBytes = int64_t(16) << 20;
+constexpr int kStaggerMinKTiles = 16;
+
+// How one product is launched: rung, LDS stages, k-groups of waves, k-loop
+// stagger.
 struct Plan {
-    int tile, stages, kgroups;
+    int tile, stages, kgroups, stagger;
 };
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 
@@ -63,7 +75,8 @@ constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 // through one buffer descriptor with 32-bit byte offsets below 2^31.
 constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
-sdt_tile describe(int id, int stages, int kgroups);
+sdt_tile describe(int id, int stages, int kgroups, int stagger = 0);
+bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
 int stages_for(int id, int64_t M, int64_t N, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);

@@ -225,10 +225,7 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     } else if (cfg.stages >= 0 || cfg.kgroups >= 0) {
         if (cfg.stages > 4 || cfg.kgroups > 2) return SDT_ERR_INVALID_ARG;
     }
-    // Plain k order unless a caller forces the stagger (see
-    // sdt_stagger_eligible for why it is not used by default).
     if (stagger == 1 && !stagger_eligible(K)) return SDT_ERR_UNSUPPORTED;
-    const int use_stagger = stagger == 1 ? 1 : 0;
     if (M == 0 || N == 0) return SDT_OK;
     if (M > INT_MAX || N > INT_MAX) return SDT_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -246,6 +243,8 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
         if (cfg.stages < 0) pl.stages = pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
     }
     if (cfg.stages >= 0) pl.stages = cfg.stages;
+    // the plan's stagger (stagger_auto) unless the caller forces it on or off
+    const int use_stagger = stagger == -1 ? pl.stagger : stagger;
     st = check_plan(pl);
     if (st != SDT_OK) return st;
     const TileDesc& td = kLadder[id];
@@ -399,7 +398,7 @@ extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_ti
         num_cu = dev.num_cu;
     }
     const sdt::Plan p = sdt::plan_for(sdt::pick_tile(M, N, K, num_cu), M, N, K, num_cu);
-    *out = sdt::describe(p.tile, p.stages, p.kgroups);
+    *out = sdt::describe(p.tile, p.stages, p.kgroups, p.stagger);
     return SDT_OK;
 }
 

@@ -176,10 +176,12 @@ def test_launch_plan_rules():
     workgroups (fewer than num_cu on the 128x128 rung, whose one-k-group deep
     pipeline runs 16x16x32 MFMAs) and K spans at least 12 k-tiles.  Stages:
     the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
-    bytes) fit in 4 MiB."""
+    bytes) fit in 4 MiB.  Stagger: off the ping-pong rung, a power-of-two
+    count of at least 16 full k-tiles and A and B within 16 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
+              (2048, 2048, 4096), (1536, 1536, 2048), (1024, 1024, 4096),
               (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700)]
     for num_cu in (80, 256):
         for t in tiles:
@@ -191,6 +193,10 @@ def test_launch_plan_rules():
                 st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
                                                   else t["stages"])
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
+                nkt = K // 64
+                stg = int(t["id"] != 0 and nkt >= 16 and nkt & (nkt - 1) == 0
+                          and 2 * K * (M + N) <= 16 << 20)
+                assert p["stagger"] == stg, (num_cu, t["id"], M, N, K)
                 assert p["threads"] == 64 * t["waves_m"] * t["waves_n"] * kg
                 assert p["lds_bytes"] == lds_bytes(t, st)
     with pytest.raises(sdt.SdtError):
@@ -206,6 +212,13 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
     assert sdt.pick_tile(1536, 1536, 1536, 256)["kgroups"] == 2   # 144 workgroups
     assert sdt.pick_tile(2048, 2048, 2048, 256)["kgroups"] == 1   # 256: the 16x16x32 pipeline
+    # stagger: eligible, at least 16 k-tiles, operands within 16 MiB, not the ping-pong rung
+    assert sdt.pick_tile(2048, 2048, 2048, 256)["stagger"] == 1
+    assert sdt.pick_tile(2048, 2048, 4096, 256)["stagger"] == 0     # 32 MiB of operands
+    assert sdt.pick_tile(2048, 2048, 1984, 256)["stagger"] == 0     # 31 k-tiles
+    assert sdt.pick_tile(512, 512, 512, 256)["stagger"] == 0        # 8 k-tiles
+    assert sdt.pick_tile(4096, 4096, 1024, 256)["stagger"] == 0     # ping-pong rung
+    assert sdt.tile_info(2)["stagger"] == 0
 
 
 def test_gemm_cfg_rejects_kernels_that_do_not_exist():

@@ -159,7 +159,7 @@ def test_two_kgroups_auto_plan_matches_oracle():
         A = inputs.uniform_f16((M, K), 19)
         B = inputs.uniform_f16((N, K), 20)
         C, _ = run_gemm(A, B)
-        C2, _ = run_gemm(A, B, tile=p["id"], stagger=0, stages=p["stages"], kgroups=2)
+        C2, _ = run_gemm(A, B, tile=p["id"], stagger=p["stagger"], stages=p["stages"], kgroups=2)
         assert (C.view(np.uint16) == C2.view(np.uint16)).all()
         r, c = sample_positions(M, N, rows=8, cols=8, extra=2048, seed=M)
         assert_close(C[r, c], oracle.gemm_sample(A, B, r, c))
