@@ -60,9 +60,10 @@ typedef struct sdt_tile {
                         sdt_tile_info: the rung's deep pipeline).  On rung 0
                         the deep count (3) is the ping-pong kernel: two groups
                         of 4 waves one phase apart, A in 2 stages, B in 3.
-                        On rung 2 (128 x 128) the deep count with one k-group
-                        runs v_mfma_f32_16x16x32 (two 32-deep sub-steps per
-                        k-tile); every other launch runs v_mfma_f32_32x32x16 */
+                        On rungs 1 and 2 (256 x 128, 128 x 128) the deep count
+                        with one k-group runs v_mfma_f32_16x16x32 (two 32-deep
+                        sub-steps per k-tile); every other launch runs
+                        v_mfma_f32_32x32x16 */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16; rung 0 deep:
                         (2 bm + 3 bn) x bk fp16 = 160 KB */
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
@@ -212,7 +213,7 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
 /* Host-only: how a launch of rung tile_id on an M x N x K product on num_cu
  * CUs (num_cu <= 0: 256) is configured (stages, kgroups, threads, LDS).
  * k-groups: 2 on rungs built with them when the grid has at most num_cu
- * workgroups (on rung 2: fewer than num_cu) and K spans at least 12 k-tiles,
+ * workgroups (on rungs 1 and 2: fewer than num_cu) and K spans at least 12 k-tiles,
  * else 1.  Stages: the deep count
  * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
  * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the

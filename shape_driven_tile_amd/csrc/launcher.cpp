@@ -47,8 +47,9 @@ int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     // A rung whose one-k-group pipeline runs 16x16x32 MFMAs keeps it once the
     // grid fills every CU: there the part runs at its power limit and that
     // MFMA's lower energy per FLOP wins (128x128 at 2048^3: 20.0 us against
-    // 21.5 with two k-groups); with CUs left idle the second k-group's
-    // shorter dependent chain wins (1536^3: 13.7 against 14.8).
+    // 21.5 with two k-groups; 256x128 at 4096x2048x2048: 35.8 against 37.4);
+    // with CUs left idle the second k-group's shorter dependent chain wins
+    // (1536^3: 13.7 against 14.8; 256x128 at 2304^3: 31.8 against 34.6).
     if (d.deep16) return wgs < num_cu ? 2 : 1;
     return wgs <= num_cu ? 2 : 1;
 }

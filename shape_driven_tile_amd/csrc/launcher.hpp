@@ -31,7 +31,7 @@ struct TileDesc {
 // largest, whose deep pipeline (2 A + 3 B stages) fills all 160 KB.
 constexpr TileDesc kLadder[] = {
     {256, 256, 2, 4, 3, 1, 1, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 128, 2, 2, 3, 2, 0, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {256, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 128x64 per wave, 3 x 48 KB
     {128, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
     {128, 64, 2, 2, 3, 2, 0, 0},   // 4 waves, 64x32 per wave, 3 x 24 KB
     {64, 64, 2, 2, 3, 2, 0, 0},    // 4 waves, 32x32 per wave, 3 x 16 KB

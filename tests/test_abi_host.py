@@ -173,8 +173,9 @@ def test_ladder_is_well_formed():
 
 def test_launch_plan_rules():
     """k-groups: 2 on rungs built with them when the grid has at most num_cu
-    workgroups (fewer than num_cu on the 128x128 rung, whose one-k-group deep
-    pipeline runs 16x16x32 MFMAs) and K spans at least 12 k-tiles.  Stages:
+    workgroups (fewer than num_cu on the 256x128 and 128x128 rungs, whose
+    one-k-group deep pipelines run 16x16x32 MFMAs) and K spans at least 12
+    k-tiles.  Stages:
     the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
     bytes) fit in 4 MiB.  Stagger: off the ping-pong rung, a power-of-two
     count of at least 16 full k-tiles and A and B within 16 MiB."""
@@ -188,7 +189,7 @@ def test_launch_plan_rules():
             for (M, N, K) in shapes:
                 p = sdt.plan_tile(t["id"], M, N, K, num_cu)
                 wgs = -(-M // t["bm"]) * -(-N // t["bn"])
-                fits = wgs < num_cu if (t["bm"], t["bn"]) == (128, 128) else wgs <= num_cu
+                fits = wgs < num_cu if t["id"] in (1, 2) else wgs <= num_cu
                 kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
                 st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
                                                   else t["stages"])
