@@ -289,19 +289,30 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def code_sha16(path: str) -> str:
+    """sha256[:16] of a C/C++ source with its comments removed and whitespace
+    runs collapsed: it changes when the code does, not when a comment does."""
+    import hashlib
+    import re
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
 def counted_traffic(profile: str, source: str):
     """HBM bytes per launch from a committed counter summary under profiles/
-    (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the kernel source has
+    (FETCH_SIZE + WRITE_SIZE, copy-scaled), or None when the kernel code has
     changed since the counters were taken."""
-    import hashlib
     try:
         text = open(os.path.join(ROOT, "profiles", profile)).read()
-        src = open(os.path.join(ROOT, source), "rb").read()
+        code = code_sha16(os.path.join(ROOT, source))
     except OSError:
         return None
     fields = dict(line.split(": ", 1) for line in text.splitlines()
-                  if line.startswith(("kernel_source_sha256_16: ", "traffic_bytes_per_launch: ")))
-    if fields.get("kernel_source_sha256_16") != hashlib.sha256(src).hexdigest()[:16]:
+                  if line.startswith(("kernel_code_sha256_16: ", "traffic_bytes_per_launch: ")))
+    if fields.get("kernel_code_sha256_16") != code:
         return None
     return float(fields["traffic_bytes_per_launch"])
 

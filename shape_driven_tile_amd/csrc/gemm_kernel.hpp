@@ -542,7 +542,8 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     // under kk2; then tile i+1 must have landed (at most NS-2 younger tiles of
     // this wave still in flight) and every wave must be done with stage s:
     // wait, barrier; (D) tile i+NS's loads into stage s and the next stage's
-    // kk0 reads under the kk3 MFMAs.
+    // kk0 reads under the kk3 MFMAs.  MF = 16 has two sub-steps: (A), then the
+    // wait and barrier, then (D) under the kk1 MFMAs.
     int i = 0;
     int s = 0;                               // stage of tile i
     for (; i + NS < nfull; ++i) {
