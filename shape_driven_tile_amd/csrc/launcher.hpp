@@ -26,9 +26,11 @@ struct TileDesc {
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
-// deep pipeline of the rung: as many stages as fit next to a useful
-// occupancy, 3 measuring as fast as 4 or faster on every rung below the
-// largest, whose deep pipeline (2 A + 3 B stages) fills all 160 KB.
+// deep pipeline of the rung.  Below the largest rung, whose deep pipeline
+// (2 A + 3 B stages) fills all 160 KB, 3 stages measured 1-6% faster than 4 or
+// 6 on the squares up to 2048 (the longer prologue costs more than the deeper
+// prefetch gains); only long k-loops on the 64x64 rung gained from 4
+// (1024x1024x4096: 15.7 against 17.6 us), which the ladder does not build.
 constexpr TileDesc kLadder[] = {
     {256, 256, 2, 4, 3, 1, 1, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
     {256, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 128x64 per wave, 3 x 48 KB
