@@ -331,6 +331,63 @@ def test_nondefault_stream():
     assert_close(C, oracle.gemm(A, B))
 
 
+def test_concurrent_host_threads_own_streams():
+    """The entry points are reentrant: four host threads, each enqueueing on
+    its own stream (ctypes drops the GIL for the call), produce bit for bit
+    what the same calls give one after another on the default stream.  The
+    shapes differ per thread so different rungs, plans and the GEMV run at
+    the same time; every output is allocated before the threads start."""
+    import threading
+
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    cases = [(512, 512, 512), (1000, 1104, 520), (2048, 2048, 2048), (1, 12288, 4096)]
+    ops = []
+    for i, (M, N, K) in enumerate(cases):
+        A = to_dev(inputs.uniform_f16((M, K), 900 + i))
+        B = to_dev(inputs.uniform_f16((N, K), 950 + i))
+        ops.append((A, B, [torch.empty((M, N), dtype=torch.float16, device="cuda:0")
+                           for _ in range(5)]))
+
+    def call(A, B, C, stream=None):
+        if A.shape[0] == 1:
+            sdt.gemv_f16_m1(A[0], B, C[0], stream=stream)
+        else:
+            sdt.gemm_f16(A, B, C, stream=stream)
+
+    say("concurrent host threads: sequential reference")
+    refs = []
+    for A, B, outs in ops:
+        R = torch.empty_like(outs[0])
+        call(A, B, R)
+        refs.append(R)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in ops]
+    errors = []
+
+    def worker(j):
+        try:
+            A, B, outs = ops[j]
+            for C in outs:
+                call(A, B, C, stream=streams[j])
+        except Exception as e:          # reported after the join
+            errors.append((j, repr(e)))
+
+    say("concurrent host threads: 4 threads x 5 calls")
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(len(ops))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not any(t.is_alive() for t in threads), "a host thread did not return"
+    torch.cuda.synchronize()
+    assert not errors, errors
+    assert sdt.last_hip_error() == 0
+    for (A, B, outs), R in zip(ops, refs):
+        for C in outs:
+            assert torch.equal(C.view(torch.int16), R.view(torch.int16))
+
+
 def test_determinism_repeated_launches():
     """No atomics on the path: repeated launches are bit-identical (a missing
     barrier or an LDS race would show up as run-to-run differences)."""
