@@ -71,6 +71,11 @@ def lib():
         return _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built: run `python -m shape_driven_tile_amd.build`")
+    # torch first: it loads its own HIP and HSA runtimes, whose sonames then
+    # satisfy libsdt.so's dependencies, so the process holds one runtime.
+    # Loaded the other way round, libsdt.so pulls in the system runtime and
+    # torch adds its copy; the second to touch the GPU finds no device.
+    import torch  # noqa: F401
     L = ctypes.CDLL(LIB_PATH)
     L.gemm_f16.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
     L.gemm_f16_ex.argtypes = L.gemm_f16.argtypes + [_int, _int]

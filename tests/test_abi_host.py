@@ -391,3 +391,20 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libsdt.so"))
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+def test_one_hip_runtime_when_the_library_loads_first():
+    """Loading the library before anything has imported torch must not leave
+    two HIP runtimes in the process (libsdt.so's own dependency on the system
+    one, then torch's bundled copy): the second to open the GPU would find no
+    device.  The binding imports torch before it loads libsdt.so."""
+    import subprocess
+    import sys
+    code = ("from shape_driven_tile_amd import binding as b; b.lib(); import torch; "
+            "m = open('/proc/self/maps').read().splitlines(); "
+            "print(len({l.split()[-1] for l in m if 'libamdhip64' in l}), "
+            "len({l.split()[-1] for l in m if 'libhsa-runtime64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.split() == ["1", "1"], r.stdout
