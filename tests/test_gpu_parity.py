@@ -121,6 +121,60 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
             assert_bitexact(C, ref)
 
 
+@pytest.mark.parametrize("K", [8, 64, 104, 128, 192])
+def test_short_k_every_pipeline(K):
+    """k-loops of 0 to 3 full k-tiles (with and without a partial one) on every
+    rung's 2-stage and deep pipeline, two k-groups where built: the ping-pong
+    kernel's prologue, barrier pairing and tail then run with fewer tiles than
+    it has stages.  Exact integer sums, bit for bit, ragged M and N."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N = 300, 260
+    A = inputs.integer_f16((M, K), 40 + K)
+    B = inputs.integer_f16((N, K), 41 + K)
+    ref = oracle.gemm(A, B)
+    for tile in range(_ntiles()):
+        info = sdt.tile_info(tile)
+        plans = [(2, 1), (info["stages"], 1)] + ([(info["stages"], 2)] if info["kgroups"] == 2
+                                                 else [])
+        for stages, kg in plans:
+            say(f"short K={K} tile={tile} stages={stages} kgroups={kg}")
+            C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=stages, kgroups=kg)
+            assert pad_ok
+            assert_bitexact(C, ref)
+
+
+def test_offsets_past_4gib():
+    """Operand and output rows more than 4 GiB from their base pointers (lda =
+    ldc = 131072, M = 16448): every rung, both pipelines, reaches them with
+    64-bit row offsets and writes nothing past N.  Exact integer sums."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K, ld = 16448, 256, 64, 131072
+    assert (M - 1) * ld * 2 > (1 << 32)
+    A = inputs.integer_f16((M, K), 60)
+    B = inputs.integer_f16((N, K), 61)
+    ref = oracle.gemm(A, B)
+    say(f"offsets past 4 GiB: M={M} N={N} K={K} lda=ldb=ldc={ld}")
+    dA = torch.empty((M, ld), dtype=torch.float16, device="cuda:0")
+    dB = torch.empty((N, ld), dtype=torch.float16, device="cuda:0")
+    dA[:, :K].copy_(torch.from_numpy(A))
+    dB[:, :K].copy_(torch.from_numpy(B))
+    dC = torch.empty((M, ld), dtype=torch.float16, device="cuda:0")
+    for tile in range(_ntiles()):
+        info = sdt.tile_info(tile)
+        for stages in (2, info["stages"]):
+            say(f"offsets past 4 GiB tile={tile} stages={stages}")
+            dC.fill_(float("nan"))
+            sdt.gemm_f16_cfg(dA[:, :K], dB[:, :K], dC[:, :N], tile_id=tile, stages=stages,
+                             kgroups=1, stagger=0)
+            torch.cuda.synchronize()
+            assert bool(torch.isnan(dC[:, N:N + 64]).all().item())
+            assert bool(torch.isnan(dC[-1, -64:]).all().item())
+            assert_bitexact(dC[:, :N].cpu().numpy(), ref)
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("shape", [(200, 136, 136), (64, 64, 64), (513, 771, 520), (1, 700, 1000)])
 def test_two_kgroups_every_rung(shape):
     """Two k-groups of waves (the second takes sub-steps 1 and 3 of every
