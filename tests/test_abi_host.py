@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
 
 
 def test_library_exports_every_declared_symbol():
-    L = ctypes.CDLL(sdt.LIB_PATH)
+    L = sdt.lib()
     for name in declared_functions():
         assert hasattr(L, name), f"libsdt.so does not export {name}"
 
