@@ -94,9 +94,14 @@ def main(argv=None):
 
     results = []
     for (M, N, K) in shapes:
-        A = torch.from_numpy(inputs.uniform_f16((M, K), 11)).to(dev)
-        B = torch.from_numpy(inputs.uniform_f16((N, K), 12)).to(dev)
-        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        # Rows padded to a multiple of 8 elements (the library's 16-byte row
+        # alignment), so any M, N, K can be swept.
+        kp, np_ = -(-K // 8) * 8, -(-N // 8) * 8
+        A = torch.zeros((M, kp), dtype=torch.float16, device=dev)[:, :K]
+        B = torch.zeros((N, kp), dtype=torch.float16, device=dev)[:, :K]
+        A.copy_(torch.from_numpy(inputs.uniform_f16((M, K), 11)))
+        B.copy_(torch.from_numpy(inputs.uniform_f16((N, K), 12)))
+        C = torch.empty((M, np_), dtype=torch.float16, device=dev)[:, :N]
         flop = 2.0 * M * N * K
         chain = max(4, min(400, int(2e12 / max(flop, 1.0))))
         auto = sdt.pick_tile(M, N, K, num_cu)["id"]
