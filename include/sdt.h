@@ -63,7 +63,9 @@ typedef struct sdt_tile {
                         On rungs 1 and 2 (256 x 128, 128 x 128) the deep count
                         with one k-group runs v_mfma_f32_16x16x32 (two 32-deep
                         sub-steps per k-tile); every other launch runs
-                        v_mfma_f32_32x32x16 */
+                        v_mfma_f32_32x32x16.  The automatic plan takes the
+                        long count (long_stages) in place of the deep one on a
+                        rung that has it once K holds at least 48 full k-tiles */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16; rung 0 deep:
                         (2 bm + 3 bn) x bk fp16 = 160 KB */
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
@@ -71,13 +73,17 @@ typedef struct sdt_tile {
                         built with) */
     int stagger;     /* 1: the automatic plan visits the k-tiles staggered,
                         (workgroup + i) & (k-tiles - 1) (sdt_tile_info: 0) */
+    int long_stages; /* a deeper pipeline for long k-loops (4 on the 128 x 64
+                        and 64 x 64 rungs), 0 if the rung has none */
 } sdt_tile;
 
 /* A launch configuration; -1 in a field = the automatic choice. */
 typedef struct sdt_launch {
     int tile_id;     /* ladder rung */
-    int stages;      /* 2 or the rung's deep count (sdt_tile_info().stages) */
-    int kgroups;     /* 1, or 2 on rungs built with two (needs the deep count) */
+    int stages;      /* 2, the rung's deep count (sdt_tile_info().stages) or
+                        its long count (sdt_tile_info().long_stages, if any) */
+    int kgroups;     /* 1, or 2 on rungs built with two (needs the deep or long
+                        count) */
     int stagger;     /* 0 off, 1 on (power-of-two full k-tile count only) */
 } sdt_launch;
 

@@ -37,7 +37,7 @@ class SdtTile(ctypes.Structure):
                 ("bk", ctypes.c_int), ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
                 ("threads", ctypes.c_int), ("stages", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("kgroups", ctypes.c_int),
-                ("stagger", ctypes.c_int)]
+                ("stagger", ctypes.c_int), ("long_stages", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}

@@ -25,6 +25,7 @@ sdt_tile describe(int id, int stages, int kgroups, int stagger) {
                       ? (2 * d.bm + d.stages * d.bn) * kBK * 2   // A in 2 stages, B in `stages`
                       : stages * (d.bm + d.bn) * kBK * 2;
     t.stagger = stagger;
+    t.long_stages = d.long_stages;
     return t;
 }
 
@@ -54,13 +55,24 @@ int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     return wgs <= num_cu ? 2 : 1;
 }
 
+// The rung's long pipeline in place of its deep one when it has one and the
+// k-loop holds at least kLongMinKTiles full k-tiles; otherwise `stages`.
+int long_for(int id, int stages, int64_t K) {
+    const TileDesc& d = kLadder[id];
+    if (stages == d.stages && d.long_stages > 0 && K / kBK >= kLongMinKTiles)
+        return d.long_stages;
+    return stages;
+}
+
 // The automatic plan on rung `id`: two k-groups always run the deep
-// pipeline, one k-group the pipeline stages_for picks.
+// pipeline, one k-group the pipeline stages_for picks; long_for then swaps a
+// deep pipeline for the rung's long one on a long k-loop.
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
+    const TileDesc& d = kLadder[id];
     Plan p;
     p.tile = id;
     p.kgroups = kgroups_for(id, M, N, K, num_cu);
-    p.stages = p.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
+    p.stages = long_for(id, p.kgroups == 2 ? d.stages : stages_for(id, M, N, K), K);
     p.stagger = stagger_auto(id, M, N, K) ? 1 : 0;
     return p;
 }
@@ -71,14 +83,17 @@ bool stagger_auto(int id, int64_t M, int64_t N, int64_t K) {
     return 2 * K * (M + N) <= kStaggerMaxOperandBytes;
 }
 
-// A plan the library has a kernel for: stages 2 or the rung's deep count;
-// two k-groups only on rungs built with them, and with the deep pipeline.
+// A plan the library has a kernel for: stages 2, the rung's deep count or its
+// long count; two k-groups only on rungs built with them, and with the deep
+// or long pipeline.
 int check_plan(const Plan& p) {
     if (p.tile < 0 || p.tile >= kNumTiles) return SDT_ERR_INVALID_ARG;
     const TileDesc& d = kLadder[p.tile];
-    if (p.stages != 2 && p.stages != d.stages) return SDT_ERR_INVALID_ARG;
+    const bool is_long = d.long_stages > 0 && p.stages == d.long_stages;
+    if (p.stages != 2 && p.stages != d.stages && !is_long) return SDT_ERR_INVALID_ARG;
     if (p.kgroups != 1 && p.kgroups != 2) return SDT_ERR_INVALID_ARG;
-    if (p.kgroups == 2 && (d.kgroups < 2 || p.stages != d.stages)) return SDT_ERR_INVALID_ARG;
+    if (p.kgroups == 2 && (d.kgroups < 2 || (p.stages != d.stages && !is_long)))
+        return SDT_ERR_INVALID_ARG;
     return SDT_OK;
 }
 

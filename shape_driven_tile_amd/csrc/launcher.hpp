@@ -23,21 +23,31 @@ struct TileDesc {
     int kgroups;    // 2: also built with two k-groups of waves (see kgroups_for)
     int pingpong;   // 1: the deep pipeline is the ping-pong kernel
     int deep16;     // 1: the deep pipeline with one k-group runs 16x16x32 MFMAs
+    int long_stages;  // > 0: a deeper pipeline for long k-loops (see kLongMinKTiles)
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
 // deep pipeline of the rung.  Below the largest rung, whose deep pipeline
 // (2 A + 3 B stages) fills all 160 KB, 3 stages measured 1-6% faster than 4 or
 // 6 on the squares up to 2048 (the longer prologue costs more than the deeper
-// prefetch gains); only long k-loops on the 64x64 rung gained from 4
-// (1024x1024x4096: 15.7 against 17.6 us), which the ladder does not build.
+// prefetch gains).  The two smallest rungs also have a 4-stage pipeline for
+// long k-loops, where one k-tile's few MFMAs cannot cover the operand latency
+// two tiles ahead (64x64 with two k-groups: 512x512x8192 24.2 against 30.2 us,
+// 768x768x4096 14.5 against 17.5, 1024x1024x3072 13.2 against 15.2; 128x64:
+// 1280^3 x 4096 / 1280^2 22.1 against 23.1).
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 3, 1, 1, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3, 2, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3, 2, 0, 0},   // 4 waves, 64x32 per wave, 3 x 24 KB
-    {64, 64, 2, 2, 3, 2, 0, 0},    // 4 waves, 32x32 per wave, 3 x 16 KB
+    {256, 256, 2, 4, 3, 1, 1, 0, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
+    {256, 128, 2, 2, 3, 2, 0, 1, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3, 2, 0, 1, 0},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3, 2, 0, 0, 4},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
+    {64, 64, 2, 2, 3, 2, 0, 0, 4},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
 };
+
+// Fewest full k-tiles at which a rung with a long pipeline uses it in place
+// of its deep one.  Fitted on MI355X: 4 stages measured 1% slower than 3 at
+// 32 k-tiles (1024x1024x2048) and 7-20% faster from 48 (1024x1024x3072,
+// 512x512x4096, 768x768x4096, 1024x1024x8192).
+constexpr int kLongMinKTiles = 48;
 
 // Operand bytes up to which a launch runs the shallow 2-stage pipeline: one
 // MI355X XCD's L2.  While A and B together fit there, a k-tile arrives within
@@ -80,6 +90,7 @@ constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 sdt_tile describe(int id, int stages, int kgroups, int stagger = 0);
 bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
 int stages_for(int id, int64_t M, int64_t N, int64_t K);
+int long_for(int id, int stages, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 int check_plan(const Plan& p);

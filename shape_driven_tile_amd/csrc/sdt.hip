@@ -72,10 +72,10 @@ hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
                            dim3(p.gm * p.gn), dim3(512), args, 0, stream);
 }
 
-// Rung I with a plan check_plan accepted: its shallow (2-stage) or deep
-// pipeline with one k-group, or the deep pipeline with two; rung 0's deep
-// pipeline is the ping-pong kernel, and a deep16 rung's deep pipeline with
-// one k-group runs 16x16x32 MFMAs.
+// Rung I with a plan check_plan accepted: its shallow (2-stage), deep or long
+// pipeline with one k-group, or the deep or long pipeline with two; rung 0's
+// deep pipeline is the ping-pong kernel, and a deep16 rung's deep pipeline
+// with one k-group runs 16x16x32 MFMAs.
 template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
@@ -86,6 +86,14 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
         if (pl.stages != 2) return launch_gemm_pp<Elt>(p, s);
         return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
     } else {
+        if constexpr (d.long_stages > 0) {
+            static_assert(!d.deep16 && d.kgroups == 2, "long pipelines: 32x32x16, both k-group forms");
+            if (pl.stages == d.long_stages) {
+                if (pl.kgroups == 2)
+                    return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.long_stages, 2>(p, s);
+                return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.long_stages, 1>(p, s);
+            }
+        }
         if constexpr (d.kgroups == 2) {
             if (pl.kgroups == 2)
                 return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 2>(p, s);
@@ -218,7 +226,9 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
     if (tile_id >= 0) {   // a forced rung: its forced fields must name a kernel it has
         const TileDesc& d = kLadder[tile_id];
-        if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages) return SDT_ERR_INVALID_ARG;
+        if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages &&
+            !(d.long_stages > 0 && cfg.stages == d.long_stages))
+            return SDT_ERR_INVALID_ARG;
         if (cfg.kgroups >= 0 && cfg.kgroups != 1 && !(cfg.kgroups == 2 && d.kgroups == 2))
             return SDT_ERR_INVALID_ARG;
         if (cfg.kgroups == 2 && cfg.stages == 2 && d.stages != 2) return SDT_ERR_INVALID_ARG;
@@ -240,7 +250,8 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     Plan pl = plan_for(id, M, N, K, dev.num_cu);
     if (cfg.kgroups >= 0) {
         pl.kgroups = cfg.kgroups;
-        if (cfg.stages < 0) pl.stages = pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K);
+        if (cfg.stages < 0)
+            pl.stages = long_for(id, pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K), K);
     }
     if (cfg.stages >= 0) pl.stages = cfg.stages;
     // the plan's stagger (stagger_auto) unless the caller forces it on or off

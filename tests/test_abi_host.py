@@ -177,13 +177,16 @@ def test_launch_plan_rules():
     one-k-group deep pipelines run 16x16x32 MFMAs) and K spans at least 12
     k-tiles.  Stages:
     the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
-    bytes) fit in 4 MiB.  Stagger: off the ping-pong rung, a power-of-two
+    bytes) fit in 4 MiB; a deep pipeline becomes the rung's long one (if it
+    has one) from 48 full k-tiles.  Stagger: off the ping-pong rung, a power-of-two
     count of at least 16 full k-tiles and A and B within 16 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
               (2048, 2048, 4096), (1536, 1536, 2048), (1024, 1024, 4096),
-              (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700)]
+              (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700),
+              (512, 512, 3008), (512, 512, 3072), (1024, 1024, 8192), (64, 64, 8192),
+              (2048, 1024, 4096)]
     for num_cu in (80, 256):
         for t in tiles:
             for (M, N, K) in shapes:
@@ -193,6 +196,8 @@ def test_launch_plan_rules():
                 kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
                 st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
                                                   else t["stages"])
+                if st == t["stages"] and t["long_stages"] and K // 64 >= 48:
+                    st = t["long_stages"]
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
                 nkt = K // 64
                 stg = int(t["id"] != 0 and nkt >= 16 and nkt & (nkt - 1) == 0

@@ -103,7 +103,8 @@ def test_integer_exact_every_tile(shape):
 
 @pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
 def test_integer_exact_every_tile_deep_pipeline(shape):
-    """Operands past 4 MiB run every rung's deep pipeline (sdt_plan_tile);
+    """Operands past 4 MiB plan every rung's deep pipeline (the long one on the
+    rungs that have it, these k-loops being long; both are run here);
     exact integer sums, bit for bit, with a ragged last k-tile in the second
     shape and ragged M/N in both; one k-group and, where built, two."""
     from shape_driven_tile_amd import binding as sdt
@@ -113,7 +114,8 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
     ref = oracle.gemm(A, B)
     for tile in range(_ntiles()):
         info = sdt.tile_info(tile)
-        assert sdt.plan_tile(tile, M, N, K, 1 << 20)["stages"] == info["stages"]
+        want = info["long_stages"] if info["long_stages"] and K // 64 >= 48 else info["stages"]
+        assert sdt.plan_tile(tile, M, N, K, 1 << 20)["stages"] == want
         for kg in ((1, 2) if info["kgroups"] == 2 else (1,)):
             say(f"integer deep {shape} tile={tile} stages={info['stages']} kgroups={kg}")
             C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=info["stages"], kgroups=kg)
@@ -141,6 +143,51 @@ def test_short_k_every_pipeline(K):
             C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=stages, kgroups=kg)
             assert pad_ok
             assert_bitexact(C, ref)
+
+
+@pytest.mark.parametrize("shape", [(300, 260, 3136), (257, 129, 3112)])
+def test_long_pipeline_every_rung_with_one(shape):
+    """The 4-stage pipeline of the rungs that have one, with one and two
+    k-groups, on 49 and 48 full k-tiles (the second with a partial one after
+    them), bit for bit on integer inputs; then the automatic plan, which takes
+    it here."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    A = inputs.integer_f16((M, K), 70)
+    B = inputs.integer_f16((N, K), 71)
+    ref = oracle.gemm(A, B)
+    tried = 0
+    for tile in range(_ntiles()):
+        info = sdt.tile_info(tile)
+        if not info["long_stages"]:
+            continue
+        for kg in (1, 2):
+            say(f"long pipeline {shape} tile={tile} stages={info['long_stages']} kgroups={kg}")
+            C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=info["long_stages"], kgroups=kg)
+            assert pad_ok
+            assert_bitexact(C, ref)
+            tried += 1
+    assert tried >= 4
+    auto = sdt.pick_tile(M, N, K, 256)
+    assert auto["stages"] == sdt.tile_info(auto["id"])["long_stages"] > 0
+    say(f"long pipeline {shape} automatic plan")
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_bitexact(C, ref)
+
+
+def test_long_pipeline_uniform_512x512x8192():
+    """The automatic plan at 512 x 512 x 8192 (64 x 64, two k-groups, 4
+    stages) against the oracle within the stated tolerance."""
+    from shape_driven_tile_amd import binding as sdt
+    A = inputs.uniform_f16((512, 8192), 72)
+    B = inputs.uniform_f16((512, 8192), 73)
+    p = sdt.pick_tile(512, 512, 8192, 256)
+    assert (p["id"], p["kgroups"], p["stages"]) == (4, 2, 4)
+    say("long pipeline 512x512x8192 uniform, automatic plan")
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_close(C, oracle.gemm(A, B))
 
 
 def test_offsets_past_4gib():
