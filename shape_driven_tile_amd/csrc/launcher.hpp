@@ -33,8 +33,8 @@ struct TileDesc {
 // prefetch gains).  The two smallest rungs also have a 4-stage pipeline for
 // long k-loops, where one k-tile's few MFMAs cannot cover the operand latency
 // two tiles ahead (64x64 with two k-groups: 512x512x8192 24.2 against 30.2 us,
-// 768x768x4096 14.5 against 17.5, 1024x1024x3072 13.2 against 15.2; 128x64:
-// 1280^3 x 4096 / 1280^2 22.1 against 23.1).
+// 768x768x4096 14.5 against 17.5, 1024x1024x3072 13.2 against 15.2; 128x64
+// at 1280x1280x4096: 22.1 against 23.1).
 constexpr TileDesc kLadder[] = {
     {256, 256, 2, 4, 3, 1, 1, 0, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
     {256, 128, 2, 2, 3, 2, 0, 1, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
