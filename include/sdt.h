@@ -212,7 +212,7 @@ int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
                   int rungs, const int64_t* min_blocks);
 
 /* Host-only: number of ladder rungs, and the description of rung tile_id
- * (with its deep pipeline). */
+ * (with its deep pipeline; long_stages names its long one, if any). */
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 
@@ -223,8 +223,10 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
  * else 1.  Stages: the deep count
  * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
  * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the
- * shorter prologue wins), else the deep count.  Stagger: as gemm_f16
- * describes.  SDT_OK or SDT_ERR_INVALID_ARG. */
+ * shorter prologue wins), else the deep count; a deep count becomes the
+ * rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs) once K holds
+ * at least 48 full k-tiles.  Stagger: as gemm_f16 describes.  SDT_OK or
+ * SDT_ERR_INVALID_ARG. */
 int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
                   sdt_tile* out);
 
