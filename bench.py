@@ -8,8 +8,9 @@ N=12288 (routed to the streaming GEMV) on the next of 8 rotating weight
 buffers.  The printed value is the step's algorithmic fp16 FLOP rate.
 
 Before any number is printed the outputs are checked against the CPU oracle
-(sampled elements of every square product, every element of all 8 decode
-products); a failure prints no throughput.  The dominant kernel (8192^3) and
+(every element of every square product up to 4096^3, the whole rows of the
+8192^3 product that the CPU baseline computes, every element of all 8 decode
+products, each output NaN-filled first); a failure prints no throughput.  The dominant kernel (8192^3) and
 the GEMV are additionally timed launch by launch with HIP events inside the
 timed region, which feed the roofline object.  Per-size, K-sweep and
 cold-cache decode details follow the protocol of the pages: warm-up, then
@@ -174,28 +175,44 @@ def main():
             ev[3].record()
 
     # ---- parity gate ----------------------------------------------------------
+    # C starts NaN-filled, so an element the kernels never write cannot pass.
+    # Every element of every square product up to 4096^3 is compared with the
+    # oracle; at 8192^3 the whole rows the CPU baseline computes (or 512
+    # seeded rows with --no-cpu-baseline).
     import oracle
+    for n in SIZES:
+        ops[n][2].fill_(float("nan"))
+    y.fill_(float("nan"))
     step(0)
     torch.cuda.synchronize()
     gate = {}
     for n in SIZES:
+        if n == DOMINANT:
+            continue
         A, B = host[n]
         C = ops[n][2].cpu().numpy().astype(np.float64)
-        rng = np.random.default_rng(n)
-        r = rng.integers(0, n, 2048)
-        c = rng.integers(0, n, 2048)
-        ref = oracle.gemm_sample(A, B, r, c)
-        bad = int((~(np.abs(C[r, c] - ref) <= oracle.tolerance(ref))).sum())
-        gate[f"gemm_{n}"] = bad
+        ref = oracle.gemm(A, B)
+        gate[f"gemm_{n}_full"] = int((~(np.abs(C - ref) <= oracle.tolerance(ref))).sum())
+    A, B = host[DOMINANT]
+    if args.no_cpu_baseline:
+        base, rows, ref = None, gate_rows(DOMINANT, 512), None
+        ref = oracle.gemm(np.ascontiguousarray(A[rows]), B)
+    else:
+        base, rows, ref = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
+    C = ops[DOMINANT][2].cpu().numpy()[rows].astype(np.float64)
+    gate[f"gemm_{DOMINANT}_rows"] = int((~(np.abs(C - ref) <= oracle.tolerance(ref))).sum())
+    gate[f"gemm_{DOMINANT}_rows_checked"] = len(rows)
+    del C, ref
     bad_dec = 0
     for r in range(inputs.DECODE_BUFFERS):
+        y.fill_(float("nan"))
         sdt.gemm_f16(x2, Ws[r], y2)
         torch.cuda.synchronize()
         ref = oracle.gemv_m1(x_h, W_h[r])
         got = y.cpu().numpy().astype(np.float64)
         bad_dec += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
     gate["gemv_8_buffers"] = bad_dec
-    if any(gate.values()):
+    if any(v for k, v in gate.items() if not k.endswith("_checked")):
         print(json.dumps({"metric": METRIC, "value": None, "error": "parity gate failed",
                           "gate": gate}), flush=True)
         sys.exit(1)
@@ -264,13 +281,19 @@ def main():
                                        "shape_driven_tile_amd/csrc/gemm_kernel.hpp"),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-scaled)",
             "avg_launch_us": round(dom_avg_us, 2),
+            "time_source": (f"HIP events recorded on the launch stream around each {DOMINANT}^3 "
+                            "launch of the timed region, averaged over its steps"),
         },
         "decode": {
             "avg_launch_us_in_step": round(dec_avg_us, 3),
             "GBps_in_step": round(bytes_gemv / (dec_avg_us * 1e-6) / 1e9, 1),
             "hbm_frac_in_step": round(bytes_gemv / (dec_avg_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         },
-        "gate": "pass",
+        "gate": {"result": "pass",
+                 "checked": (f"every element of C at {', '.join(str(n) for n in SIZES if n != DOMINANT)}"
+                             f"^3 (C NaN-filled first); {gate[f'gemm_{DOMINANT}_rows_checked']} "
+                             f"whole rows of the {DOMINANT}^3 product; every element of the 8 "
+                             "decode products")},
     }
 
     if not args.no_detail:
@@ -283,8 +306,8 @@ def main():
             clk["timed_region_frac_of_clock_ceiling"] = round(
                 achieved / clk["mfma_ceiling_at_clock_tflops"], 4)
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
+    if base is not None:
+        result["cpu_baseline"] = base
 
     print(json.dumps(result), flush=True)
 
@@ -470,7 +493,9 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         }
         log(f"square {n}: median {med:.2f} us {det['square'][str(n)]['tflops_median']} TFLOP/s")
     # K sweep at M=N=2048: the default arm at every K, plus both stagger arms
-    # forced at K=2048, the one K whose k-tile count allows a stagger
+    # forced at K=2048, the one K whose k-tile count allows a stagger; every
+    # arm graph-replayed (200 launches per graph, 10 replays), as the squares
+    # above, so host launch cost does not blur the per-K differences.
     for K in inputs.K_SWEEP_K:
         A, B = inputs.square_operands(inputs.K_SWEEP_MN, 3, k=K)
         dA, dB = dev_tensor(A), dev_tensor(B)
@@ -481,16 +506,15 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             arms["stagger_on"] = (-1, 1)
         for name, (tile, st) in arms.items():
             f = (lambda j, tile=tile, st=st: sdt.gemm_f16_ex(dA, dB, C, tile_id=tile, stagger=st))
-            for j in range(50):
-                f(j)
-            us = time_launches(torch, f, 200)
+            us, _ = graph_launches(torch, f, 200)
             med = sorted(us)[len(us) // 2]
             det["k_sweep"][f"{K}_{name}"] = {
-                "us": _ranges(us),
+                "us": _ranges(us), "timing": "graph replay, 200 launches x 10",
                 "tflops_median": round(2.0 * 2048 * 2048 * K / (med * 1e-6) / 1e12, 1),
                 "stagger": bool(st == 1 or (st == -1 and sdt.pick_tile(2048, 2048, K, 0)["stagger"])),
                 "tile": sdt.pick_tile(2048, 2048, K, 0)["id"],
             }
+            log(f"K sweep {K} {name}: median {med:.2f} us")
     # Cold-cache decode: 8 rotating 100.7 MB weight buffers (805 MB >> 256 MB
     # Infinity Cache), ~1 s warm-up, 200 launches x 10 repeats.
     x2, y2 = x.view(1, -1), y.view(1, -1)
@@ -658,9 +682,27 @@ def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):
     return out
 
 
+def gate_rows(n, count, seed=8192):
+    """`count` distinct sorted row indices of an n-row product: the first and
+    last row of every 256-row tile band, the rest drawn from a seeded
+    generator."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    pick = {0, n - 1}
+    if count >= 2 * (n // 256):
+        for b in range(0, n, 256):
+            pick.update((b, b + 255))
+    while len(pick) < min(count, n):
+        pick.update(int(v) for v in rng.integers(0, n, count - len(pick)))
+    return np.array(sorted(pick)[:count], dtype=np.int64)
+
+
 def cpu_baseline(oracle, AB, target_s):
     """The oracle, untuned, on a bounded sample of the dominant product: whole
-    output rows of the 8192^3 GEMM, as many as take about target_s seconds."""
+    output rows of the 8192^3 GEMM (gate_rows: every tile band's edges plus
+    seeded rows), as many as take about target_s seconds.  Returns the
+    baseline record, the row indices and the oracle's rows, which the parity
+    gate compares with the GPU's."""
     import numpy as np
     A, B = AB
     n = A.shape[0]
@@ -668,11 +710,13 @@ def cpu_baseline(oracle, AB, target_s):
     # rate estimate on enough rows to occupy every thread
     est = min(n, 8 * threads)
     t = time.time()
-    oracle.gemm(A[:est], B)
+    oracle.gemm(np.ascontiguousarray(A[:est]), B)
     per_row = max((time.time() - t) / est, 1e-6)
-    rows = int(min(n, max(est, target_s / per_row)))
+    rows = int(min(n, max(512, est, target_s / per_row)))
+    idx = gate_rows(n, rows)
+    a_rows = np.ascontiguousarray(A[idx])
     t = time.time()
-    oracle.gemm(A[:rows], B)
+    ref = oracle.gemm(a_rows, B)
     dt = time.time() - t
     flop = 2.0 * rows * n * n
     # one thread at two small squares, for scale
@@ -693,12 +737,14 @@ def cpu_baseline(oracle, AB, target_s):
                     break
     except OSError:
         pass
-    return {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{rows} full output rows of the {n}^3 product ({flop:.3g} FLOP) in "
-                      f"{dt:.2f} s, fp64 accumulation, {threads} OpenMP threads",
-            "GFLOP_s": round(flop / dt / 1e9, 3), "cpu_model": model,
-            "one_thread": one_thread}
+    rec = {"value": round(flop / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{rows} whole output rows of the {n}^3 product ({flop:.3g} FLOP) in "
+                     f"{dt:.2f} s, fp64 accumulation, {threads} OpenMP threads; the same rows "
+                     "are the parity gate's check of the GPU's {n}^3 result".replace("{n}", str(n)),
+           "GFLOP_s": round(flop / dt / 1e9, 3), "cpu_model": model,
+           "one_thread": one_thread}
+    return rec, idx, ref
 
 
 if __name__ == "__main__":

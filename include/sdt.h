@@ -65,7 +65,8 @@ typedef struct sdt_tile {
                         sub-steps per k-tile); every other launch runs
                         v_mfma_f32_32x32x16.  The automatic plan takes the
                         long count (long_stages) in place of the deep one on a
-                        rung that has it once K holds at least 48 full k-tiles */
+                        rung that has it when the launch runs two k-groups and
+                        K holds at least 48 full k-tiles */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16; rung 0 deep:
                         (2 bm + 3 bn) x bk fp16 = 160 KB */
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
@@ -223,9 +224,9 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
  * else 1.  Stages: the deep count
  * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
  * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the
- * shorter prologue wins), else the deep count; a deep count becomes the
- * rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs) once K holds
- * at least 48 full k-tiles.  Stagger: as gemm_f16 describes.  SDT_OK or
+ * shorter prologue wins), else the deep count; with two k-groups a deep count
+ * becomes the rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs)
+ * once K holds at least 48 full k-tiles.  Stagger: as gemm_f16 describes.  SDT_OK or
  * SDT_ERR_INVALID_ARG. */
 int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
                   sdt_tile* out);

@@ -1,9 +1,12 @@
 """Build libsdt.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
     python -m shape_driven_tile_amd.build [--resource-usage]
+    python -m shape_driven_tile_amd.build --resource-summary PATH
 
 Writes ``shape_driven_tile_amd/libsdt.so``.  With ``--resource-usage`` the
-compiler's per-kernel register/LDS/spill report is printed as well.
+compiler's per-kernel register/LDS/spill report is printed as well;
+``--resource-summary PATH`` writes that report as a markdown table instead of
+building the library.
 """
 from __future__ import annotations
 
@@ -68,6 +71,56 @@ def build_capi_check() -> str:
     return CAPI_BIN
 
 
+def resource_summary(path: str) -> str:
+    """Compile the library with the compiler's per-kernel resource remarks and
+    write them as a markdown table (one row per kernel instantiation:
+    registers, spills, LDS, occupancy) to `path`."""
+    import re
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-I", INCLUDE, "-I", CSRC] + DEVICE_FLAGS + [
+           "-Rpass-analysis=kernel-resource-usage", "--cuda-device-only", "-c",
+           os.path.join(CSRC, "sdt.hip"), "-o", os.devnull]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stderr}")
+    rows, cur = [], None
+    for line in res.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"mangled": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^]]*\])?: (\S+) \[-Rpass", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = m.group(2)
+    names = subprocess.run(["c++filt"], input="\n".join(r["mangled"] for r in rows),
+                           capture_output=True, text=True).stdout.splitlines()
+    out = ["# Kernel resources: every instantiation in libsdt.so (gfx950)", "",
+           "The compiler's own report (`-Rpass-analysis=kernel-resource-usage`) for the",
+           "device code of `shape_driven_tile_amd/csrc/sdt.hip`, written by", "",
+           "    python -m shape_driven_tile_amd.build --resource-summary "
+           "profiles/kernel_resource_usage.md", "",
+           "VGPRs and AGPRs are per lane (the two files are allocated together on",
+           "gfx950: 512 per SIMD lane in all, so a wave using V + A registers leaves",
+           "room for floor(512 / (V + A)) waves per SIMD, at most 8); LDS is per workgroup",
+           "(160 KB per CU).", "",
+           "| kernel | VGPRs | AGPRs | SGPRs | VGPR spill | SGPR spill | scratch B/lane | LDS bytes | waves/SIMD |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for r, n in zip(rows, names):
+        n = n.replace("void ", "").replace("sdt::(anonymous namespace)::", "sdt::")
+        n = re.sub(r"\(.*\)$", "", n)
+        out.append(f"| `{n}` | {r.get('VGPRs', '?')} | {r.get('AGPRs', '?')} | "
+                   f"{r.get('TotalSGPRs', '?')} | {r.get('VGPRs Spill', '?')} | "
+                   f"{r.get('SGPRs Spill', '?')} | {r.get('ScratchSize', '?')} | "
+                   f"{r.get('LDS Size', '?')} | {r.get('Occupancy', '?')} |")
+    with open(path, "w") as f:
+        f.write("\n".join(out) + "\n")
+    return path
+
+
 if __name__ == "__main__":
+    if "--resource-summary" in sys.argv:
+        print(resource_summary(sys.argv[sys.argv.index("--resource-summary") + 1]))
+        sys.exit(0)
     build(resource_usage="--resource-usage" in sys.argv, verbose="-v" in sys.argv)
     print(LIB)

@@ -33,7 +33,9 @@
 //     the second group's partial sums are added to the first's through LDS
 //     (a fixed order: the result is deterministic) before the epilogue;
 //   * k-loop stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by
-//     choosing the tile from the shape", Changes), when a caller forces it:
+//     choosing the tile from the shape", Changes), when the launch plan
+//     enables it (the automatic plan on every rung except the ping-pong one,
+//     for the shapes launcher.cpp's stagger_auto names) or a caller forces it:
 //     with a power-of-two number of full k-tiles, workgroup w visits them in
 //     the order (w + i) & (nfull - 1);
 //   * edges: operand rows come through buffer descriptors clipped to the

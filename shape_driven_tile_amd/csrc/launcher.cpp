@@ -55,24 +55,28 @@ int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     return wgs <= num_cu ? 2 : 1;
 }
 
-// The rung's long pipeline in place of its deep one when it has one and the
-// k-loop holds at least kLongMinKTiles full k-tiles; otherwise `stages`.
-int long_for(int id, int stages, int64_t K) {
+// The rung's long pipeline in place of its deep one when it has one, the
+// launch runs two k-groups and the k-loop holds at least kLongMinKTiles full
+// k-tiles; otherwise `stages`.  Only the two-k-group form was measured
+// faster: one k-group is planned when the grid exceeds the CU count, where the
+// fourth stage's LDS costs a co-resident workgroup per CU (128 x 64: 72 ->
+// 96 KB, two workgroups per CU -> one).
+int long_for(int id, int stages, int kgroups, int64_t K) {
     const TileDesc& d = kLadder[id];
-    if (stages == d.stages && d.long_stages > 0 && K / kBK >= kLongMinKTiles)
+    if (kgroups == 2 && stages == d.stages && d.long_stages > 0 && K / kBK >= kLongMinKTiles)
         return d.long_stages;
     return stages;
 }
 
 // The automatic plan on rung `id`: two k-groups always run the deep
 // pipeline, one k-group the pipeline stages_for picks; long_for then swaps a
-// deep pipeline for the rung's long one on a long k-loop.
+// two-k-group deep pipeline for the rung's long one on a long k-loop.
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     const TileDesc& d = kLadder[id];
     Plan p;
     p.tile = id;
     p.kgroups = kgroups_for(id, M, N, K, num_cu);
-    p.stages = long_for(id, p.kgroups == 2 ? d.stages : stages_for(id, M, N, K), K);
+    p.stages = long_for(id, p.kgroups == 2 ? d.stages : stages_for(id, M, N, K), p.kgroups, K);
     p.stagger = stagger_auto(id, M, N, K) ? 1 : 0;
     return p;
 }

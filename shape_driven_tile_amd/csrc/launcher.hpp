@@ -90,7 +90,7 @@ constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 sdt_tile describe(int id, int stages, int kgroups, int stagger = 0);
 bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
 int stages_for(int id, int64_t M, int64_t N, int64_t K);
-int long_for(int id, int stages, int64_t K);
+int long_for(int id, int stages, int kgroups, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 int check_plan(const Plan& p);

@@ -251,7 +251,8 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     if (cfg.kgroups >= 0) {
         pl.kgroups = cfg.kgroups;
         if (cfg.stages < 0)
-            pl.stages = long_for(id, pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K), K);
+            pl.stages = long_for(id, pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K),
+                                 pl.kgroups, K);
     }
     if (cfg.stages >= 0) pl.stages = cfg.stages;
     // the plan's stagger (stagger_auto) unless the caller forces it on or off

@@ -98,6 +98,20 @@ def sample_positions(M, N, rows=32, cols=32, extra=4096, seed=0):
     return np.concatenate(r).astype(np.int64), np.concatenate(c).astype(np.int64)
 
 
+def seeded_rows(n, count, seed, band=256):
+    """`count` distinct sorted indices in [0, n): 0 and n - 1, the first and
+    last index of every `band`-wide tile band when count covers them all, the
+    rest drawn from a seeded generator."""
+    rng = np.random.default_rng(seed)
+    pick = {0, n - 1}
+    if count >= 2 * (-(-n // band)):
+        for b in range(0, n, band):
+            pick.update((b, min(b + band, n) - 1))
+    while len(pick) < min(count, n):
+        pick.update(int(v) for v in rng.integers(0, n, count - len(pick)))
+    return np.array(sorted(pick)[:count], dtype=np.int64)
+
+
 def run_gemv_kn(x, W, N=None, variant=None, y_pad=8):
     """x: (K,) float16; W: (K, ldb) float16 host buffer, the N of a row
     contiguous.  Returns y (N,) and whether the y_pad elements past N stayed

@@ -177,8 +177,8 @@ def test_launch_plan_rules():
     one-k-group deep pipelines run 16x16x32 MFMAs) and K spans at least 12
     k-tiles.  Stages:
     the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
-    bytes) fit in 4 MiB; a deep pipeline becomes the rung's long one (if it
-    has one) from 48 full k-tiles.  Stagger: off the ping-pong rung, a power-of-two
+    bytes) fit in 4 MiB; a two-k-group deep pipeline becomes the rung's long
+    one (if it has one) from 48 full k-tiles.  Stagger: off the ping-pong rung, a power-of-two
     count of at least 16 full k-tiles and A and B within 16 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
@@ -196,7 +196,7 @@ def test_launch_plan_rules():
                 kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
                 st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
                                                   else t["stages"])
-                if st == t["stages"] and t["long_stages"] and K // 64 >= 48:
+                if kg == 2 and st == t["stages"] and t["long_stages"] and K // 64 >= 48:
                     st = t["long_stages"]
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
                 nkt = K // 64
@@ -413,3 +413,36 @@ def test_one_hip_runtime_when_the_library_loads_first():
                        timeout=300)
     assert r.returncode == 0, r.stderr[-2000:]
     assert r.stdout.split() == ["1", "1"], r.stdout
+
+
+_REFUSAL_PROBE = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+from shape_driven_tile_amd import binding as sdt
+A, B, C = 0x10000, 0x20000, 0x30000   # never dereferenced: the runtime refuses first
+out = []
+out.append(sdt.gemm_f16_raw(64, 64, 64, A, 64, B, 64, C, 64))
+out.append(sdt.last_hip_error())
+out.append(sdt.gemm_f16_raw(64, 64, 0, A, 64, B, 64, C, 64))      # K = 0: the zero fill
+out.append(sdt.gemv_f16_m1_raw(128, 64, A, B, 64, C))
+out.append(sdt.lib().sdt_empty_kernel(None))
+out.append(sdt.last_hip_error())
+print(" ".join(str(v) for v in out))
+"""
+
+
+def test_runtime_refusal_maps_to_sdt_err_hip():
+    """A launch the HIP runtime refuses before any GPU work (here: a process
+    in which no device is visible, so the runtime reports hipErrorNoDevice,
+    100) comes back as SDT_ERR_HIP from every launching entry point, with the
+    runtime's code kept for sdt_last_hip_error().  Run in a child process with
+    every device hidden, so the outcome does not depend on the machine."""
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1")
+    res = subprocess.run([sys.executable, "-c", _REFUSAL_PROBE, ROOT], env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    vals = [int(v) for v in res.stdout.split()[-6:]]
+    hip_err = sdt.SDT_ERR_HIP
+    assert vals == [hip_err, 100, hip_err, hip_err, hip_err, 100], vals

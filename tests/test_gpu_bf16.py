@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 from gpu_helpers import (assert_bitexact_bf16, assert_close_bf16, bits_to_dev_bf16,
-                         dev_bf16_to_bits, run_gemm_bf16, sample_positions, say)
+                         dev_bf16_to_bits, run_gemm_bf16, say, seeded_rows)
 from shape_driven_tile_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -27,14 +27,38 @@ def test_bf16_square_full(n):
     assert_close_bf16(C, oracle.gemm(A, B, dtype="bf16"))
 
 
-@pytest.mark.parametrize("n", [4096, 8192])
-def test_bf16_square_large_sampled(n):
-    say(f"bf16 square {n}^3, sampled oracle")
+def test_bf16_square_4096_full():
+    say("bf16 square 4096^3, full oracle")
+    A, B = inputs.square_operands_bf16(4096, 2)
+    C, _ = run_gemm_bf16(A, B)
+    assert_close_bf16(C, oracle.gemm(A, B, dtype="bf16"))
+
+
+def test_bf16_square_8192_rows():
+    """512 seeded whole rows (both edges of every 256-row band) and 16 whole
+    columns of the 8192^3 product."""
+    n = 8192
+    say("bf16 square 8192^3, 512 full rows + 16 full columns")
     A, B = inputs.square_operands_bf16(n, 2)
     C, _ = run_gemm_bf16(A, B)
-    r, c = sample_positions(n, n, rows=16, cols=16, extra=4096, seed=n)
-    ref = oracle.gemm_sample(A, B, r, c, dtype="bf16")
-    assert_close_bf16(C[r, c], ref)
+    rows = seeded_rows(n, 512, seed=n)
+    assert_close_bf16(C[rows], oracle.gemm(np.ascontiguousarray(A[rows]), B, dtype="bf16"))
+    cols = seeded_rows(n, 16, seed=n + 1)
+    r = np.repeat(np.arange(n), len(cols))
+    c = np.tile(cols, n)
+    assert_close_bf16(C[r, c], oracle.gemm_sample(A, B, r, c, dtype="bf16"))
+
+
+def test_bf16_integer_exact_4096_auto():
+    """Integer inputs through gemm_bf16's automatic plan at 4096^3 (the
+    ping-pong kernel and its 16 x 16-block tile order), every element bit for
+    bit."""
+    A = inputs.integer_bf16((4096, 4096), 103)
+    B = inputs.integer_bf16((4096, 4096), 104)
+    say("bf16 integer 4096^3 automatic plan, full C")
+    C, pad_ok = run_gemm_bf16(A, B)
+    assert pad_ok
+    assert_bitexact_bf16(C, oracle.gemm(A, B, dtype="bf16"))
 
 
 @pytest.mark.parametrize("shape", [(200, 136, 136), (257, 129, 200), (64, 64, 4096),

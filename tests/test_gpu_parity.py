@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 from gpu_helpers import (assert_bitexact, assert_close, run_gemm, run_gemv, sample_positions,
-                         say, to_dev)
+                         say, seeded_rows, to_dev)
 from shape_driven_tile_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -38,15 +38,77 @@ def test_square_sweep(n):
     assert_close(C, oracle.gemm(A, B))
 
 
-@pytest.mark.parametrize("n", inputs.SQUARE_LARGE)
-def test_square_large_sampled(n):
-    say(f"square {n}^3 uniform, auto tile, sampled oracle")
+def test_square_4096_full():
+    """4096^3 (the automatic plan: the 256 x 256 ping-pong kernel with its 16 x
+    16-block XCD order on a 256-CU part): every element of C against the oracle."""
+    say("square 4096^3 uniform, auto tile, full oracle")
+    A, B = inputs.square_operands(4096, 2)
+    C, _ = run_gemm(A, B)
+    assert_close(C, oracle.gemm(A, B))
+
+
+def test_square_8192_rows():
+    """8192^3: 512 seeded whole rows (every 256-row tile band is hit, with its
+    first and last rows) and 16 whole columns of C against the oracle, the
+    rest of C checked finite."""
+    say("square 8192^3 uniform, auto tile, 512 full rows + 16 full columns")
+    n = 8192
     A, B = inputs.square_operands(n, 2)
     C, _ = run_gemm(A, B)
-    r, c = sample_positions(n, n, rows=24, cols=24, extra=8192, seed=n)
-    ref = oracle.gemm_sample(A, B, r, c)
-    assert_close(C[r, c], ref)
+    rows = seeded_rows(n, 512, seed=n)
+    assert_close(C[rows], oracle.gemm(np.ascontiguousarray(A[rows]), B))
+    cols = seeded_rows(n, 16, seed=n + 1)
+    r = np.repeat(np.arange(n), len(cols))
+    c = np.tile(cols, n)
+    assert_close(C[r, c], oracle.gemm_sample(A, B, r, c))
     assert np.isfinite(C.astype(np.float32)).all()
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 1024), (8192, 8192, 512), (4096, 4096, 4096)])
+def test_integer_exact_large_auto(shape):
+    """Integer inputs in [-2, 2] (every fp32 partial sum exact, so any order
+    gives the same bits) through gemm_f16's automatic plan at the large-square
+    grids: the ping-pong kernel and, on a part with 8 XCDs, its 16 x 16-block
+    tile order.  Every element of C, bit for bit against the oracle's RNE
+    rounding."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    p = sdt.pick_tile(M, N, K, 0)
+    assert (p["id"], p["stages"]) == (0, 3), p   # the ping-pong kernel
+    A = inputs.integer_f16((M, K), 21)
+    B = inputs.integer_f16((N, K), 22)
+    say(f"integer {shape} automatic plan (ping-pong), full C")
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_bitexact(C, oracle.gemm(A, B))
+
+
+def test_integer_exact_8192_rows_auto():
+    """8192^3 on integer inputs through the automatic plan: 512 seeded whole
+    rows and 16 whole columns bit for bit."""
+    n = 8192
+    A = inputs.integer_f16((n, n), 23)
+    B = inputs.integer_f16((n, n), 24)
+    say("integer 8192^3 automatic plan, 512 full rows + 16 full columns")
+    C, _ = run_gemm(A, B)
+    rows = seeded_rows(n, 512, seed=5)
+    assert_bitexact(C[rows], oracle.gemm(np.ascontiguousarray(A[rows]), B))
+    cols = seeded_rows(n, 16, seed=6)
+    r = np.repeat(np.arange(n), len(cols))
+    c = np.tile(cols, n)
+    assert_bitexact(C[r, c], oracle.gemm_sample(A, B, r, c))
+
+
+def test_integer_exact_pingpong_short_k_block_order():
+    """The ping-pong kernel forced at 4096 x 4096 x 128 (its automatic plan
+    there is the 2-stage kernel): two k-tiles, the 16 x 16-block tile order,
+    every element bit for bit."""
+    A = inputs.integer_f16((4096, 128), 25)
+    B = inputs.integer_f16((4096, 128), 26)
+    say("integer 4096x4096x128 ping-pong forced, full C")
+    C, pad_ok = run_gemm(A, B, tile=0, stagger=0, stages=3, kgroups=1)
+    assert pad_ok
+    assert_bitexact(C, oracle.gemm(A, B))
 
 
 @pytest.mark.parametrize("K", inputs.K_SWEEP_K)
@@ -103,10 +165,13 @@ def test_integer_exact_every_tile(shape):
 
 @pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
 def test_integer_exact_every_tile_deep_pipeline(shape):
-    """Operands past 4 MiB plan every rung's deep pipeline (the long one on the
-    rungs that have it, these k-loops being long; both are run here);
-    exact integer sums, bit for bit, with a ragged last k-tile in the second
-    shape and ragged M/N in both; one k-group and, where built, two."""
+    """Operands past 4 MiB plan every rung's deep pipeline (on the rungs with
+    a long pipeline the plan takes that one at these k-loop lengths, which
+    the assertion checks; the long pipelines themselves run in
+    test_long_pipeline_every_rung_with_one).  Here each rung's deep pipeline
+    is forced: exact integer sums, bit for bit, with a ragged last k-tile in
+    the second shape and ragged M/N in both; one k-group and, where built,
+    two."""
     from shape_driven_tile_amd import binding as sdt
     M, N, K = shape
     A = inputs.integer_f16((M, K), 13)
