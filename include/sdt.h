@@ -32,6 +32,12 @@
 
 #include <stdint.h>
 
+/* Version of the structures and signatures below; bumped whenever sdt_tile,
+ * sdt_launch or an entry point's arguments change.  sdt_abi_version() reports
+ * the version the library was built with: a caller compiled against another
+ * header must not pass these structures to it. */
+#define SDT_ABI_VERSION 3
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -76,6 +82,14 @@ typedef struct sdt_tile {
                         (workgroup + i) & (k-tiles - 1) (sdt_tile_info: 0) */
     int long_stages; /* a deeper pipeline for long k-loops (4 on the 128 x 64
                         and 64 x 64 rungs), 0 if the rung has none */
+    int splits;      /* workgroups each output tile's k-loop is split over
+                        (1: none).  Only the workspace entry points split */
+    int split_algo;  /* splits > 1: how the fp32 partial sums are reduced, in
+                        split order: 0 by a second kernel, 1 by the last
+                        workgroup of each tile in the same kernel */
+    int persistent;  /* 0: one workgroup per tile; P > 0: P workgroups loop
+                        over the tiles (ping-pong kernel only) */
+    int ksplit;      /* 1: the rung is built to split K across workgroups */
 } sdt_tile;
 
 /* A launch configuration; -1 in a field = the automatic choice. */
@@ -86,6 +100,17 @@ typedef struct sdt_launch {
     int kgroups;     /* 1, or 2 on rungs built with two (needs the deep or long
                         count) */
     int stagger;     /* 0 off, 1 on (power-of-two full k-tile count only) */
+    int splits;      /* 1 none; s in [2, 16] on a ksplit rung: K split over s
+                        workgroups per tile (at most one per full k-tile, no
+                        stagger), needs the workspace sdt_launch_workspace_size
+                        reports */
+    int split_algo;  /* 0 a second kernel sums the partials, 1 the last
+                        workgroup of each tile does */
+    int persistent;  /* 0 off; P in [1, tiles]: the ping-pong kernel (rung 0's
+                        deep pipeline) runs P workgroups, workgroup w taking
+                        tiles w, w + P, w + 2P, ... (the FlyDSL PR, Changes:
+                        persistent workgroups, where only 0 or the tile count
+                        is accepted; any P in between is accepted here) */
 } sdt_launch;
 
 /* ---- main entry points ---------------------------------------------------- */
@@ -108,6 +133,45 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
              const void* B, int64_t ldb,
              void* C, int64_t ldc, void* stream);
+
+/* gemm_f16 with a workspace, which lets the plan split the k-loop across
+ * workgroups ("Iteratively Tuning hipBLASLt TensileLite Kernels", The Six
+ * Rounds, 2: splitting K is how shapes that cannot fill the device get work).
+ * When the grid of gemm_f16's tile leaves CUs idle and K is long enough, each
+ * output tile's k-tiles are divided into `splits` contiguous runs, one
+ * workgroup each; their fp32 partial sums go to the workspace and are added
+ * in split order, ((P_0 + P_1) + P_2) + ..., before the single rounding to
+ * fp16, so the result is deterministic (no atomics on the data).
+ * workspace: device memory owned by the caller, 16-byte aligned, at least
+ * sdt_gemm_workspace_size(M, N, K, 0) bytes for the split plan (smaller, or
+ * NULL with 0: the call runs gemm_f16's plan, unsplit, and touches no
+ * workspace).  Its leading counter bytes must be zero before the first call
+ * that uses it (sdt_workspace_init); every call leaves them zero again.  One
+ * workspace serves one call at a time: calls that share it must be ordered
+ * on one stream (concurrent calls on other streams need their own).
+ * Everything else as gemm_f16 (same requirements, statuses and
+ * degenerate-size behaviour; M == 1 runs the decode GEMV). */
+int gemm_f16_ws(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda,
+                const void* B, int64_t ldb,
+                void* C, int64_t ldc,
+                void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_f16_ws's automatic plan uses for this product on a
+ * device with num_cu compute units (num_cu <= 0 reads the current device);
+ * 0 when it does not split.  Negative sizes: -1. */
+int64_t sdt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int num_cu);
+
+/* Bytes of workspace a launch configuration (as gemm_f16_cfg takes it, every
+ * field given) needs for an M x N product: 0 without a split; -1 for an
+ * invalid configuration. */
+int64_t sdt_launch_workspace_size(int64_t M, int64_t N, int64_t K, const sdt_launch* cfg);
+
+/* Enqueue on `stream` the zero fill of a workspace's `bytes` bytes (a kernel,
+ * so it may be captured into a graph).  workspace 16-byte aligned, bytes a
+ * multiple of 4.  SDT_OK, SDT_ERR_INVALID_ARG, SDT_ERR_UNSUPPORTED or
+ * SDT_ERR_HIP. */
+int sdt_workspace_init(void* workspace, int64_t bytes, void* stream);
 
 /* y(n) = sum_k x(k) * B(k,n), n < N: the M=1 decode product (mojo-baro page,
  * "Four rounds on the decode shape"), with B stored K-major as above (column n
@@ -143,6 +207,11 @@ int gemm_bf16(int64_t M, int64_t N, int64_t K,
               const void* A, int64_t lda,
               const void* B, int64_t ldb,
               void* C, int64_t ldc, void* stream);
+int gemm_bf16_ws(int64_t M, int64_t N, int64_t K,
+                 const void* A, int64_t lda,
+                 const void* B, int64_t ldb,
+                 void* C, int64_t ldc,
+                 void* workspace, int64_t workspace_bytes, void* stream);
 int gemv_bf16_m1(int64_t N, int64_t K, const void* x,
                  const void* B, int64_t ldb, void* y, void* stream);
 int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x,
@@ -160,18 +229,25 @@ int gemm_f16_ex(int64_t M, int64_t N, int64_t K,
                 void* C, int64_t ldc, void* stream,
                 int tile_id, int stagger);
 
-/* gemm_f16 / gemm_bf16 with any part of the launch configuration forced
- * (NULL cfg, an index out of range, or a combination the library has no
- * kernel for: SDT_ERR_INVALID_ARG; a forced stagger on an ineligible K:
- * SDT_ERR_UNSUPPORTED).  M == 1 is not rerouted to the GEMV here. */
+/* gemm_f16_ws / gemm_bf16_ws with any part of the launch configuration
+ * forced (NULL cfg, an index out of range, a combination the library has no
+ * kernel for, or a split whose workspace is missing or smaller than
+ * sdt_launch_workspace_size: SDT_ERR_INVALID_ARG; a forced stagger on an
+ * ineligible K: SDT_ERR_UNSUPPORTED).  splits == -1 lets the plan split when
+ * the workspace allows, as gemm_f16_ws does.  M == 1 is not rerouted to the
+ * GEMV here. */
 int gemm_f16_cfg(int64_t M, int64_t N, int64_t K,
                  const void* A, int64_t lda,
                  const void* B, int64_t ldb,
-                 void* C, int64_t ldc, void* stream, const sdt_launch* cfg);
+                 void* C, int64_t ldc,
+                 void* workspace, int64_t workspace_bytes, void* stream,
+                 const sdt_launch* cfg);
 int gemm_bf16_cfg(int64_t M, int64_t N, int64_t K,
                   const void* A, int64_t lda,
                   const void* B, int64_t ldb,
-                  void* C, int64_t ldc, void* stream, const sdt_launch* cfg);
+                  void* C, int64_t ldc,
+                  void* workspace, int64_t workspace_bytes, void* stream,
+                  const sdt_launch* cfg);
 
 /* gemm_bf16 with the launcher's choices forced (as gemm_f16_ex). */
 int gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
@@ -204,6 +280,12 @@ int sdt_gemv_kn_num_variants(void);
  * mattered"; ladder constants fitted on MI355X).  Touches no device when
  * num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
+
+/* Host-only: the plan gemm_f16_ws makes with a workspace of workspace_bytes
+ * bytes (the k-split is taken only when it fits); otherwise as
+ * sdt_pick_tile. */
+int sdt_pick_tile_ws(int64_t M, int64_t N, int64_t K, int num_cu, int64_t workspace_bytes,
+                     sdt_tile* out);
 
 /* Host-only, the mechanism of the rule above: given `rungs` thresholds in
  * units of ref_bm x ref_bn output blocks (largest tile first, non-increasing),
@@ -276,6 +358,9 @@ int sdt_check_gemm_args(int64_t M, int64_t N, int64_t K,
                         const void* A, int64_t lda,
                         const void* B, int64_t ldb,
                         const void* C, int64_t ldc);
+
+/* SDT_ABI_VERSION as the library was built. */
+int sdt_abi_version(void);
 
 /* Human-readable name of a status code (static storage). */
 const char* sdt_status_string(int status);

@@ -29,7 +29,12 @@ EXPORTS = (
     "sdt_status_string", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read",
     "sdt_plan_tile",
     "gemm_f16_cfg", "gemm_bf16_cfg",
+    "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
+    "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
 )
+
+# The include/sdt.h version these structures and signatures follow.
+ABI_VERSION = 3
 
 
 class SdtTile(ctypes.Structure):
@@ -37,7 +42,9 @@ class SdtTile(ctypes.Structure):
                 ("bk", ctypes.c_int), ("waves_m", ctypes.c_int), ("waves_n", ctypes.c_int),
                 ("threads", ctypes.c_int), ("stages", ctypes.c_int),
                 ("lds_bytes", ctypes.c_int), ("kgroups", ctypes.c_int),
-                ("stagger", ctypes.c_int), ("long_stages", ctypes.c_int)]
+                ("stagger", ctypes.c_int), ("long_stages", ctypes.c_int),
+                ("splits", ctypes.c_int), ("split_algo", ctypes.c_int),
+                ("persistent", ctypes.c_int), ("ksplit", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -46,7 +53,9 @@ class SdtTile(ctypes.Structure):
 class SdtLaunch(ctypes.Structure):
     """sdt_launch: -1 in a field = the automatic choice."""
     _fields_ = [("tile_id", ctypes.c_int), ("stages", ctypes.c_int),
-                ("kgroups", ctypes.c_int), ("stagger", ctypes.c_int)]
+                ("kgroups", ctypes.c_int), ("stagger", ctypes.c_int),
+                ("splits", ctypes.c_int), ("split_algo", ctypes.c_int),
+                ("persistent", ctypes.c_int)]
 
 
 class SdtError(RuntimeError):
@@ -95,8 +104,17 @@ def lib():
     L.sdt_num_tiles.argtypes = []
     L.sdt_tile_info.argtypes = [_int, ctypes.POINTER(SdtTile)]
     L.sdt_plan_tile.argtypes = [_int, _i64, _i64, _i64, _int, ctypes.POINTER(SdtTile)]
-    L.gemm_f16_cfg.argtypes = L.gemm_f16.argtypes + [ctypes.POINTER(SdtLaunch)]
+    L.gemm_f16_ws.argtypes = [_i64, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp]
+    L.gemm_bf16_ws.argtypes = L.gemm_f16_ws.argtypes
+    L.gemm_f16_cfg.argtypes = L.gemm_f16_ws.argtypes + [ctypes.POINTER(SdtLaunch)]
     L.gemm_bf16_cfg.argtypes = L.gemm_f16_cfg.argtypes
+    L.sdt_gemm_workspace_size.argtypes = [_i64, _i64, _i64, _int]
+    L.sdt_gemm_workspace_size.restype = _i64
+    L.sdt_launch_workspace_size.argtypes = [_i64, _i64, _i64, ctypes.POINTER(SdtLaunch)]
+    L.sdt_launch_workspace_size.restype = _i64
+    L.sdt_workspace_init.argtypes = [_vp, _i64, _vp]
+    L.sdt_pick_tile_ws.argtypes = [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(SdtTile)]
+    L.sdt_abi_version.argtypes = []
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -112,9 +130,13 @@ def lib():
                  "sdt_check_gemv_kn_args",
                  "sdt_gemv_num_variants", "sdt_pick_tile", "sdt_pick_rung", "sdt_num_tiles",
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
-                 "gemm_f16_cfg", "gemm_bf16_cfg",
+                 "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
+                 "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
                  "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
         getattr(L, name).restype = _int
+    if L.sdt_abi_version() != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
+                           f"expects {ABI_VERSION}: rebuild the library")
     _lib = L
     return L
 
@@ -150,8 +172,62 @@ def plan_tile(tile_id: int, M: int, N: int, K: int, num_cu: int = 256) -> dict:
     return t.as_dict()
 
 
-def launch_cfg(tile_id=-1, stages=-1, kgroups=-1, stagger=-1) -> SdtLaunch:
-    return SdtLaunch(int(tile_id), int(stages), int(kgroups), int(stagger))
+def launch_cfg(tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1, split_algo=-1,
+               persistent=-1) -> SdtLaunch:
+    return SdtLaunch(int(tile_id), int(stages), int(kgroups), int(stagger), int(splits),
+                     int(split_algo), int(persistent))
+
+
+def pick_tile_ws(M: int, N: int, K: int, num_cu: int, workspace_bytes: int) -> dict:
+    """The plan gemm_f16_ws makes with a workspace of that many bytes."""
+    t = SdtTile()
+    rc = lib().sdt_pick_tile_ws(int(M), int(N), int(K), int(num_cu), int(workspace_bytes),
+                                ctypes.byref(t))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_pick_tile_ws")
+    return t.as_dict()
+
+
+def gemm_workspace_size(M: int, N: int, K: int, num_cu: int = 0) -> int:
+    """Workspace bytes gemm_f16_ws's automatic plan uses (0: no split)."""
+    v = int(lib().sdt_gemm_workspace_size(int(M), int(N), int(K), int(num_cu)))
+    if v < 0:
+        raise SdtError(SDT_ERR_INVALID_ARG, "sdt_gemm_workspace_size")
+    return v
+
+
+def launch_workspace_size(M: int, N: int, K: int, **cfg) -> int:
+    """Workspace bytes a forced launch configuration needs (0: no split)."""
+    c = launch_cfg(**cfg)
+    v = int(lib().sdt_launch_workspace_size(int(M), int(N), int(K), ctypes.byref(c)))
+    if v < 0:
+        raise SdtError(SDT_ERR_INVALID_ARG, "sdt_launch_workspace_size")
+    return v
+
+
+class Workspace:
+    """A device workspace for the k-split entry points: `nbytes` bytes of a
+    torch uint8 tensor (16-byte aligned by torch's allocator), its counters
+    zeroed once by sdt_workspace_init on the current stream."""
+
+    def __init__(self, nbytes: int, device="cuda", stream=None):
+        import torch
+        self.nbytes = (int(nbytes) + 15) // 16 * 16
+        self.tensor = torch.empty(max(self.nbytes, 16), dtype=torch.uint8, device=device)
+        if self.nbytes:
+            rc = lib().sdt_workspace_init(self.tensor.data_ptr(), self.nbytes,
+                                          _stream_handle(stream))
+            if rc != SDT_OK:
+                raise SdtError(rc, "sdt_workspace_init")
+
+    def ptr(self):
+        return self.tensor.data_ptr() if self.nbytes else None
+
+
+def _ws_args(workspace):
+    if workspace is None:
+        return None, 0
+    return workspace.ptr(), workspace.nbytes
 
 
 def pick_tile(M: int, N: int, K: int, num_cu: int) -> dict:
@@ -317,17 +393,45 @@ def _gemm_16(entry, A, B, C, stream, dtype, extra=()):
         raise SdtError(rc, entry)
 
 
-def gemm_f16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, stream=None) -> None:
-    """gemm_f16 with any part of the launch configuration forced (-1 = automatic)."""
-    import torch
-    cfg = launch_cfg(tile_id, stages, kgroups, stagger)
-    _gemm_16("gemm_f16_cfg", A, B, C, stream, torch.float16, (ctypes.byref(cfg),))
+def _gemm_16_ws(entry, A, B, C, workspace, stream, dtype, extra=()):
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch A{tuple(A.shape)} B{tuple(B.shape)} C{tuple(C.shape)}")
+    pa, lda = _rows(A, "A", dtype)
+    pb, ldb = _rows(B, "B", dtype)
+    pc, ldc = _rows(C, "C", dtype)
+    wp, wn = _ws_args(workspace)
+    rc = getattr(lib(), entry)(M, N, K, pa, lda, pb, ldb, pc, ldc, wp, wn,
+                               _stream_handle(stream), *extra)
+    if rc != SDT_OK:
+        raise SdtError(rc, entry)
 
 
-def gemm_bf16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, stream=None) -> None:
+def gemm_f16_ws(A, B, C, workspace=None, stream=None) -> None:
+    """gemm_f16 with a Workspace: the plan may split K across workgroups."""
     import torch
-    cfg = launch_cfg(tile_id, stages, kgroups, stagger)
-    _gemm_16("gemm_bf16_cfg", A, B, C, stream, torch.bfloat16, (ctypes.byref(cfg),))
+    _gemm_16_ws("gemm_f16_ws", A, B, C, workspace, stream, torch.float16)
+
+
+def gemm_bf16_ws(A, B, C, workspace=None, stream=None) -> None:
+    import torch
+    _gemm_16_ws("gemm_bf16_ws", A, B, C, workspace, stream, torch.bfloat16)
+
+
+def gemm_f16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1,
+                 split_algo=-1, persistent=-1, workspace=None, stream=None) -> None:
+    """gemm_f16_ws with any part of the launch configuration forced (-1 = automatic)."""
+    import torch
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent)
+    _gemm_16_ws("gemm_f16_cfg", A, B, C, workspace, stream, torch.float16, (ctypes.byref(cfg),))
+
+
+def gemm_bf16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1,
+                  split_algo=-1, persistent=-1, workspace=None, stream=None) -> None:
+    import torch
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent)
+    _gemm_16_ws("gemm_bf16_cfg", A, B, C, workspace, stream, torch.bfloat16, (ctypes.byref(cfg),))
 
 
 def gemm_bf16(A, B, C, stream=None) -> None:

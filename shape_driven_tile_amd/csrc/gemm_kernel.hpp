@@ -71,6 +71,7 @@ typedef float floatx16_t __attribute__((ext_vector_type(16)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef int int4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int uint2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int uint4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 // Raw-buffer descriptor word 3 for gfx9-family parts (32-bit data format).
@@ -86,7 +87,35 @@ struct GemmParams {
     int gm, gn;    // output tiles along M and N
     int stagger;   // 1: full k-tiles in (w + i) & (K/64 - 1) order
     int nxcd;      // XCDs the dispatcher deals workgroups over
+    int splits;    // workgroups per output tile along K (1: none; see gemm_kernel)
+    int split_algo;  // splits > 1: 0 a second kernel reduces, 1 the tile's last workgroup does
+    float* ws;     // splits > 1: fp32 partial sums, tiles x splits slots of BM x BN
+    int* cnt;      // split_algo 1: one arrival counter per (tile, wave), zero between launches
+    int persistent;  // ping-pong kernel: 0 one workgroup per tile, else the grid size
 };
+
+// Dealing order of workgroup ids over the XCDs: MI355X hands workgroup w to
+// XCD w % nxcd.  Returns a logical index such that every XCD works through a
+// contiguous range of [0, nwg) (a bijection for any nwg).
+__device__ __forceinline__ int xcd_remap(int w, int nwg, int nxcd) {
+    if (nxcd <= 1) return w;
+    const int xcd = w % nxcd, q = nwg / nxcd, r = nwg % nxcd;
+    return xcd * q + min(xcd, r) + w / nxcd;
+}
+
+// Output tile `tile` (a logical index in [0, gm * gn)) in the grouped order:
+// kGroupM tile rows at a time, column by column inside a group, so that
+// consecutive tiles share B rows and a group shares A rows.
+__device__ __forceinline__ void grouped_origin(const GemmParams& p, int tile, int BM, int BN,
+                                               int64_t& m0, int64_t& n0) {
+    const int group_span = kGroupM * p.gn;
+    const int g = tile / group_span;
+    const int first_m = g * kGroupM;
+    const int gsz = min(p.gm - first_m, kGroupM);
+    const int within = tile - g * group_span;
+    m0 = (int64_t)(first_m + within % gsz) * BM;
+    n0 = (int64_t)(within / gsz) * BN;
+}
 
 // Element types.  Each names its vector types, the 32x32x16 and 16x16x32 MFMAs, the
 // two-term dot product into fp32 used by the GEMV kernels, and (through
@@ -360,11 +389,135 @@ __device__ __forceinline__ void store_block_staged32(const GemmParams& p,
     }
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32>
+// ---- k-split partial sums -------------------------------------------------------
+// A wave's fp32 accumulators (FN x FM tiles of ACC values per lane) leave and
+// return in 16-byte pieces: piece q = (i * FM + j) * (ACC / 4) + e of the
+// wave's slot holds accumulator elements 4e .. 4e + 3 of tile (i, j) for all
+// 64 lanes, lane l at byte 16 (64 q + l), so every store or load instruction
+// of a wave covers 1 KB of consecutive memory.  AUX is the buffer
+// instruction's cache-policy field: 0, or kScopeDevice for the single-kernel
+// reduction (see splitk_arrive).
+constexpr int kScopeDevice = 16;   // sc1: coherent at device scope, across XCDs
+
+template <int AUX, int FN, int FM, typename acc_t>
+__device__ __forceinline__ void store_partial(const acc_t (&acc)[FN][FM], __amdgpu_buffer_rsrc_t r,
+                                              int lane) {
+    constexpr int E = sizeof(acc_t) / 16;
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                uint4_t v;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) v[d] = __builtin_bit_cast(uint32_t, acc[i][j][4 * e + d]);
+                __builtin_amdgcn_raw_buffer_store_b128(v, r, (((i * FM + j) * E + e) * 64 + lane) * 16,
+                                                       0, AUX);
+            }
+}
+
+// acc = partial (ADD false) or acc += partial (ADD true), element by element.
+template <int AUX, bool ADD, int FN, int FM, typename acc_t>
+__device__ __forceinline__ void load_partial(acc_t (&acc)[FN][FM], __amdgpu_buffer_rsrc_t r, int lane) {
+    constexpr int E = sizeof(acc_t) / 16;
+    uint4_t v[FN][FM][E];
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                v[i][j][e] = __builtin_amdgcn_raw_buffer_load_b128(
+                    r, (((i * FM + j) * E + e) * 64 + lane) * 16, 0, AUX);
+#pragma unroll
+    for (int i = 0; i < FN; ++i)
+#pragma unroll
+        for (int j = 0; j < FM; ++j)
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const float x = __builtin_bit_cast(float, v[i][j][e][d]);
+                    if constexpr (ADD)
+                        acc[i][j][4 * e + d] += x;
+                    else
+                        acc[i][j][4 * e + d] = x;
+                }
+}
+
+// Slot of (tile, split, wave) in the partial-sum area: tiles x splits x
+// waves slots of `slot_floats` each.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_slot(const GemmParams& p, int tile, int split,
+                                                               int wave, int nwaves, int slot_floats) {
+    const int64_t idx = ((int64_t)tile * p.splits + split) * nwaves + wave;
+    return make_rsrc(p.ws + idx * slot_floats, (uint32_t)slot_floats * 4);
+}
+
+// The single-kernel k-split reduction, per wave: store this split's partial
+// sums at device scope, wait until they are complete, then count the arrival
+// on the (tile, wave) counter.  The wave that arrives last returns true and
+// owns the block: it clears the counter for the next launch and forms
+//   acc = ((P_0 + P_1) + P_2) + ... + P_{splits-1}
+// in that order, whichever split it holds (fp32 addition is commutative, so
+// adding its own P_split to the running sum of P_0 .. P_{split-1} gives the
+// same bits as the opposite operand order): the result does not depend on
+// the order of arrival.  The others return false and are done.  Every store
+// and load of a partial carries the device-scope bit (written through to,
+// and read from, the level shared by all XCDs); the counter is an agent-scope
+// atomic issued only after vmcnt(0), i.e. after this wave's stores have
+// completed at that scope, and the last wave issues its loads only after the
+// atomic has returned.  No wave waits for another: nothing spins.
+template <int FN, int FM, typename acc_t>
+__device__ __forceinline__ bool splitk_arrive(const GemmParams& p, acc_t (&acc)[FN][FM], int tile,
+                                              int split, int wave, int nwaves, int lane) {
+    constexpr int SLOT = FN * FM * (int)(sizeof(acc_t) / 4) * 64;
+    store_partial<kScopeDevice>(acc, partial_slot(p, tile, split, wave, nwaves, SLOT), lane);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    wait_global_loads<0>();              // vmcnt counts stores too on this target
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int* counter = p.cnt + (int64_t)tile * nwaves + wave;
+    int old = 0;
+    if (lane == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != p.splits - 1) return false;
+    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (split == 0) {
+        for (int s = 1; s < p.splits; ++s)
+            load_partial<kScopeDevice, true>(acc, partial_slot(p, tile, s, wave, nwaves, SLOT), lane);
+    } else {
+        acc_t run[FN][FM];
+        load_partial<kScopeDevice, false>(run, partial_slot(p, tile, 0, wave, nwaves, SLOT), lane);
+        for (int s = 1; s < split; ++s)
+            load_partial<kScopeDevice, true>(run, partial_slot(p, tile, s, wave, nwaves, SLOT), lane);
+#pragma unroll
+        for (int i = 0; i < FN; ++i)
+#pragma unroll
+            for (int j = 0; j < FM; ++j) acc[i][j] = run[i][j] + acc[i][j];
+        for (int s = split + 1; s < p.splits; ++s)
+            load_partial<kScopeDevice, true>(acc, partial_slot(p, tile, s, wave, nwaves, SLOT), lane);
+    }
+    return true;
+}
+
+// Epilogue of one wave of gemm_kernel (and of the k-split reduction kernel):
+// rounds the accumulators to the output type and stores them, through the
+// wave's 4 KB of LDS at `stage` when its tile is 64 columns wide.
+template <typename Elt, int MF, int FN, int FM, typename acc_t>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const acc_t (&acc)[FN][FM],
+                                              int64_t mb, int64_t nb, int lane, int4_t* stage) {
+    if constexpr (MF == 16) {
+        store_block_staged<Elt, FM>(p, acc, mb, nb, lane, stage);
+    } else if constexpr (FN == 2) {
+        store_block_staged32<Elt, FM>(p, acc, mb, nb, lane, stage);
+    } else {
+        store_block<Elt, FM, FN>(p, acc, mb, nb, lane & 31, lane >> 5);
+    }
+}
+
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32, bool SK = false>
 __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
-    typedef typename Elt::vec4 vec4;
-    typedef typename Elt::scalar scalar;
     constexpr int BK = kBK;
     constexpr int NMN = WM * WN;       // waves per k-group (one output block each)
     constexpr int NW = NMN * KS;       // waves per workgroup
@@ -399,21 +552,17 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     const int wave_m = wmn % WM;
     const int wave_n = wmn / WM;
 
-    // ---- workgroup -> output tile (XCD-aware, grouped) -----------------------
-    const int nwg = p.gm * p.gn;
+    // ---- workgroup -> (k-split, output tile), XCD-aware and grouped ----------
+    // With splits > 1 the grid holds `splits` workgroups per tile; logical
+    // index l takes split l / tiles of tile l % tiles, so each XCD's range is
+    // neighbouring tiles over one k-range (shared A and B rows in its L2).
+    const int ntile = p.gm * p.gn;
     const int w = blockIdx.x;
-    int logical = w;
-    if (p.nxcd > 1) {
-        const int xcd = w % p.nxcd, q = nwg / p.nxcd, r = nwg % p.nxcd;
-        logical = xcd * q + min(xcd, r) + w / p.nxcd;
-    }
-    const int group_span = kGroupM * p.gn;
-    const int g = logical / group_span;
-    const int first_m = g * kGroupM;
-    const int gsz = min(p.gm - first_m, kGroupM);
-    const int within = logical - g * group_span;
-    const int64_t m0 = (int64_t)(first_m + within % gsz) * BM;
-    const int64_t n0 = (int64_t)(within / gsz) * BN;
+    const int logical = xcd_remap(w, SK ? ntile * p.splits : ntile, p.nxcd);
+    const int split = SK ? logical / ntile : 0;
+    const int tile = logical - split * ntile;
+    int64_t m0, n0;
+    grouped_origin(p, tile, BM, BN, m0, n0);
 
     // ---- operand descriptors: only this tile's valid rows are addressable ----
     const int rows_a = (int)min((int64_t)BM, (int64_t)p.M - m0);
@@ -443,14 +592,23 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     }
 
     // ---- k-tile sequence: the full tiles (staggered), then a partial one ------
-    const int nfull = p.K / BK;
-    const int ktail = p.K - nfull * BK;
+    // A k-split takes a contiguous run of the full k-tiles (the first
+    // nfull % splits splits one more than the others); the last split also
+    // takes the partial one.  Splits are never staggered.
+    const int nfull_all = p.K / BK;
+    int kbeg = 0, nfull = nfull_all, ktail = p.K - nfull_all * BK;
+    if (SK && p.splits > 1) {
+        const int q = nfull_all / p.splits, r = nfull_all % p.splits;
+        kbeg = split * q + min(split, r);
+        nfull = q + (split < r ? 1 : 0);
+        if (split != p.splits - 1) ktail = 0;
+    }
     const int nseq = nfull + (ktail > 0 ? 1 : 0);
     const int kmask = p.stagger ? (nfull - 1) : 0x7fffffff;
     const int k0 = p.stagger ? (w & (nfull - 1)) : 0;
 
     auto dma_tile = [&](int step, int stage) {   // a full k-tile, straight into LDS
-        const int soff = ((k0 + step) & kmask) * (BK * 2);
+        const int soff = (kbeg + ((k0 + step) & kmask)) * (BK * 2);
         int4_t* base = smem + stage * STAGE;
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j) dma16(ra, base + (wave * A_DMA + j) * 64, voff_a[j], soff);
@@ -459,7 +617,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
             dma16(rb, base + A_UNITS + (wave * B_DMA + j) * 64, voff_b[j], soff);
     };
     auto tail_tile = [&](int stage) {            // the partial k-tile, masked
-        const int soff = nfull * (BK * 2);
+        const int soff = nfull_all * (BK * 2);
         int4_t* base = smem + stage * STAGE;
 #pragma unroll
         for (int j = 0; j < A_DMA; ++j)
@@ -632,20 +790,51 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
                     acc[i2][j][e] += red[((wmn * FN * FM + i2 * FM + j) * 16 + e) * 64 + lane];
     }
 
+    // ---- k-split: partial sums out; the split that completes a block sums them --------
+    if constexpr (SK) {
+        if (p.splits > 1) {
+            constexpr int SLOT = FN * FM * ACC * 64;
+            if (p.split_algo == 0) {   // a second kernel sums the partials
+                store_partial<0>(acc, partial_slot(p, tile, split, wmn, NMN, SLOT), lane);
+                return;
+            }
+            if (!splitk_arrive(p, acc, tile, split, wmn, NMN, lane)) return;
+        }
+    }
+
     // ---- epilogue: fp32 -> fp16 / bf16 (RNE), masked stores ---------------------------
     // A 64-column wave tile goes through 4 KB of LDS per wave: with k-groups
     // in the wave's own part of the partial-sum area (which only it reads),
     // otherwise at the start of the stages, which no wave reads any more
     // after the last k-step's barrier.
-    if constexpr (MF == 16) {
-        store_block_staged<Elt, FM>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
-                                    smem + wmn * 256);
-    } else if constexpr (FN == 2) {
-        int4_t* stage = (KS > 1) ? smem + wmn * (FN * FM * 256) : smem + wmn * 256;
-        store_block_staged32<Elt, FM>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, stage);
-    } else {
-        store_block<Elt, FM, FN>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, frow, fhalf);
-    }
+    int4_t* stage = (KS > 1 && MF == 32) ? smem + wmn * (FN * FM * 256) : smem + wmn * 256;
+    gemm_epilogue<Elt, MF>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, stage);
+}
+
+// The second kernel of a k-split launch with split_algo 0: one workgroup per
+// output tile, laid out as gemm_kernel's k-group 0 (WM x WN waves), sums the
+// tile's `splits` partials in split order, ((P_0 + P_1) + P_2) + ..., and
+// stores the block with gemm_kernel's epilogue.
+template <typename Elt, int BM, int BN, int WM, int WN, int MF>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_splitk_reduce_kernel(GemmParams p) {
+    constexpr int NMN = WM * WN;
+    constexpr int WTM = BM / WM, WTN = BN / WN;
+    constexpr int FM = WTM / MF, FN = WTN / MF;
+    constexpr int ACC = MF == 32 ? 16 : 4;
+    constexpr int SLOT = FN * FM * ACC * 64;
+    typedef std::conditional_t<MF == 32, floatx16_t, floatx4_t> acc_t;
+    __shared__ int4_t smem[NMN * 256];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_m = wave % WM, wave_n = wave / WM;
+    const int tile = blockIdx.x;
+    int64_t m0, n0;
+    grouped_origin(p, tile, BM, BN, m0, n0);
+    acc_t acc[FN][FM];
+    load_partial<0, false>(acc, partial_slot(p, tile, 0, wave, NMN, SLOT), lane);
+    for (int s = 1; s < p.splits; ++s)
+        load_partial<0, true>(acc, partial_slot(p, tile, s, wave, NMN, SLOT), lane);
+    gemm_epilogue<Elt, MF>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, smem + wave * 256);
 }
 
 // The 256 x 256 rung with a ping-pong schedule (8 waves, 2 per SIMD).
@@ -752,7 +941,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
 
     const int nfull = p.K / BK;
     const int ktail = p.K - nfull * BK;
-    const int nseq = nfull + (ktail > 0 ? 1 : 0);
     const int kmask = p.stagger ? (nfull - 1) : 0x7fffffff;
     const int k0 = p.stagger ? (w & (nfull - 1)) : 0;
 

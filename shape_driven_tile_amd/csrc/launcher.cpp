@@ -9,24 +9,71 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
-sdt_tile describe(int id, int stages, int kgroups, int stagger) {
-    const TileDesc& d = kLadder[id];
+sdt_tile describe(const Plan& p) {
+    const TileDesc& d = kLadder[p.tile];
     sdt_tile t;
-    t.id = id;
+    t.id = p.tile;
     t.bm = d.bm;
     t.bn = d.bn;
     t.bk = kBK;
     t.waves_m = d.waves_m;
     t.waves_n = d.waves_n;
-    t.threads = 64 * d.waves_m * d.waves_n * kgroups;
-    t.kgroups = kgroups;
-    t.stages = stages;
-    t.lds_bytes = (d.pingpong && stages == d.stages)
+    t.threads = 64 * d.waves_m * d.waves_n * p.kgroups;
+    t.kgroups = p.kgroups;
+    t.stages = p.stages;
+    t.lds_bytes = (d.pingpong && p.stages == d.stages)
                       ? (2 * d.bm + d.stages * d.bn) * kBK * 2   // A in 2 stages, B in `stages`
-                      : stages * (d.bm + d.bn) * kBK * 2;
-    t.stagger = stagger;
+                      : p.stages * (d.bm + d.bn) * kBK * 2;
+    t.stagger = p.stagger;
     t.long_stages = d.long_stages;
+    t.splits = p.splits;
+    t.split_algo = p.splits > 1 ? p.split_algo : 0;
+    t.persistent = p.persistent;
+    t.ksplit = d.ksplit;
     return t;
+}
+
+// The rung as built: its deep pipeline and the most k-groups it has.
+sdt_tile describe_rung(int id) {
+    Plan p;
+    p.tile = id;
+    p.stages = kLadder[id].stages;
+    p.kgroups = kLadder[id].kgroups;
+    p.stagger = 0;
+    return describe(p);
+}
+
+// Workspace of a k-split launch: the arrival counters (one int per tile and
+// wave of a k-group, rounded up to 256 bytes), then the fp32 partial sums
+// (splits slots of bm x bn per tile).  Zero without a split.
+int64_t counter_bytes(const Plan& p, int64_t M, int64_t N) {
+    if (p.splits <= 1) return 0;
+    const TileDesc& d = kLadder[p.tile];
+    const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    return (tiles * d.waves_m * d.waves_n * 4 + 255) / 256 * 256;
+}
+
+int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
+    if (p.splits <= 1) return 0;
+    const TileDesc& d = kLadder[p.tile];
+    const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    return counter_bytes(p, M, N) + tiles * p.splits * int64_t(d.bm) * d.bn * 4;
+}
+
+// k-split of the automatic plan when a workspace is available: on a rung
+// built for it, while the grid leaves CUs idle, as many splits as keep the
+// grid within the CU count, each with at least kSplitMinKTilesPerSplit full
+// k-tiles (at most kMaxSplits).  1 = no split.
+int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
+    const TileDesc& d = kLadder[p.tile];
+    if (!d.ksplit || p.stagger) return 1;
+    if (num_cu <= 0) num_cu = 256;
+    const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    const int64_t nfull = K / kBK;
+    int64_t s = num_cu / tiles;
+    if (s > nfull / kSplitMinKTilesPerSplit) s = nfull / kSplitMinKTilesPerSplit;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s >= 2 ? (int)s : 1;
 }
 
 // 2 stages while A and B (2 bytes per element) fit in one XCD's L2, else the
@@ -40,10 +87,14 @@ int stages_for(int id, int64_t M, int64_t N, int64_t K) {
 // once (at most one workgroup per CU) and the k-loop is long enough.
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     const TileDesc& d = kLadder[id];
+    return kgroups_for_grid(id, ceil_div(M, d.bm) * ceil_div(N, d.bn), ceil_div(K, kBK), num_cu);
+}
+
+// The same rule for a grid of `wgs` workgroups each running `nkt` k-tiles.
+int kgroups_for_grid(int id, int64_t wgs, int64_t nkt, int num_cu) {
+    const TileDesc& d = kLadder[id];
     if (d.kgroups < 2) return 1;
     if (num_cu <= 0) num_cu = 256;
-    const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn);
-    const int64_t nkt = ceil_div(K, kBK);
     if (nkt < kSplitMinKTiles) return 1;
     // A rung whose one-k-group pipeline runs 16x16x32 MFMAs keeps it once the
     // grid fills every CU: there the part runs at its power limit and that
@@ -90,7 +141,7 @@ bool stagger_auto(int id, int64_t M, int64_t N, int64_t K) {
 // A plan the library has a kernel for: stages 2, the rung's deep count or its
 // long count; two k-groups only on rungs built with them, and with the deep
 // or long pipeline.
-int check_plan(const Plan& p) {
+int check_plan(const Plan& p, int64_t K) {
     if (p.tile < 0 || p.tile >= kNumTiles) return SDT_ERR_INVALID_ARG;
     const TileDesc& d = kLadder[p.tile];
     const bool is_long = d.long_stages > 0 && p.stages == d.long_stages;
@@ -98,6 +149,80 @@ int check_plan(const Plan& p) {
     if (p.kgroups != 1 && p.kgroups != 2) return SDT_ERR_INVALID_ARG;
     if (p.kgroups == 2 && (d.kgroups < 2 || (p.stages != d.stages && !is_long)))
         return SDT_ERR_INVALID_ARG;
+    // k-split: rungs built for it, at most one split per full k-tile, never
+    // with the stagger
+    if (p.splits < 1 || p.splits > kMaxSplits) return SDT_ERR_INVALID_ARG;
+    if (p.splits > 1 && (!d.ksplit || p.splits > K / kBK || p.stagger)) return SDT_ERR_INVALID_ARG;
+    if (p.split_algo != 0 && p.split_algo != 1) return SDT_ERR_INVALID_ARG;
+    // persistent workgroups: the ping-pong kernel only
+    if (p.persistent < 0 || (p.persistent > 0 && (!d.pingpong || p.stages != d.stages)))
+        return SDT_ERR_INVALID_ARG;
+    return SDT_OK;
+}
+
+// The plan a launch runs: gemm_f16's automatic plan (pick_tile, plan_for),
+// with every field of cfg that is not -1 forced, and a k-split (splits_for)
+// when the caller offers ws_bytes >= 0 bytes of workspace and it fits.
+int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num_cu,
+                 int64_t ws_bytes, Plan* out) {
+    if (cfg.tile_id < -1 || cfg.tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
+    if (cfg.stagger < -1 || cfg.stagger > 1) return SDT_ERR_INVALID_ARG;
+    if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
+    if (cfg.splits < -1 || cfg.splits == 0 || cfg.splits > kMaxSplits) return SDT_ERR_INVALID_ARG;
+    if (cfg.split_algo < -1 || cfg.split_algo > 1 || cfg.persistent < -1) return SDT_ERR_INVALID_ARG;
+    if (cfg.tile_id >= 0) {   // a forced rung: its forced fields must name a kernel it has
+        const TileDesc& d = kLadder[cfg.tile_id];
+        if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages &&
+            !(d.long_stages > 0 && cfg.stages == d.long_stages))
+            return SDT_ERR_INVALID_ARG;
+        if (cfg.kgroups >= 0 && cfg.kgroups != 1 && !(cfg.kgroups == 2 && d.kgroups == 2))
+            return SDT_ERR_INVALID_ARG;
+        if (cfg.kgroups == 2 && cfg.stages == 2 && d.stages != 2) return SDT_ERR_INVALID_ARG;
+    } else if (cfg.stages >= 0 || cfg.kgroups >= 0) {
+        if (cfg.stages > 4 || cfg.kgroups > 2) return SDT_ERR_INVALID_ARG;
+    }
+    if (cfg.stagger == 1 && !stagger_eligible(K)) return SDT_ERR_UNSUPPORTED;
+    if (num_cu <= 0) num_cu = 256;
+    const int id = cfg.tile_id >= 0 ? cfg.tile_id : pick_tile(M, N, K, num_cu);
+    const TileDesc& d = kLadder[id];
+    Plan pl = plan_for(id, M, N, K, num_cu);
+    if (cfg.stagger != -1) pl.stagger = cfg.stagger;
+
+    // k-split: forced, or taken by the automatic plan when the workspace holds it
+    if (cfg.splits >= 1) {
+        pl.splits = cfg.splits;
+    } else if (ws_bytes > 0 && cfg.stagger != 1) {
+        Plan t = pl;
+        t.stagger = 0;
+        t.splits = splits_for(t, M, N, K, num_cu);
+        if (t.splits > 1 && workspace_bytes(t, M, N) <= ws_bytes) pl = t;
+    }
+    if (pl.splits > 1) {
+        pl.stagger = cfg.stagger == 1 ? 1 : 0;
+        // the split grid decides the k-groups and stages, as for any grid
+        const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn) * pl.splits;
+        const int64_t nkt = (K / kBK) / pl.splits;   // full k-tiles of the shortest split
+        pl.kgroups = kgroups_for_grid(id, wgs, nkt, num_cu);
+        pl.stages = pl.kgroups == 2 ? d.stages
+                                    : (2 * K * (M + N) <= kShallowOperandBytes ? 2 : d.stages);
+        pl.stages = long_for(id, pl.stages, pl.kgroups, K / pl.splits);
+        pl.split_algo = cfg.split_algo >= 0 ? cfg.split_algo : kSplitAlgoAuto;
+    }
+    if (cfg.kgroups >= 0) {
+        pl.kgroups = cfg.kgroups;
+        if (cfg.stages < 0)
+            pl.stages = long_for(id, pl.kgroups == 2 ? d.stages : stages_for(id, M, N, K),
+                                 pl.kgroups, pl.splits > 1 ? K / pl.splits : K);
+    }
+    if (cfg.stages >= 0) pl.stages = cfg.stages;
+    if (cfg.split_algo >= 0) pl.split_algo = cfg.split_algo;
+    if (cfg.persistent >= 0) pl.persistent = cfg.persistent;
+    int st = check_plan(pl, K);
+    if (st != SDT_OK) return st;
+    if (pl.persistent > ceil_div(M, d.bm) * ceil_div(N, d.bn)) return SDT_ERR_INVALID_ARG;
+    if (pl.splits > 1 && workspace_bytes(pl, M, N) > (ws_bytes < 0 ? 0 : ws_bytes))
+        return SDT_ERR_INVALID_ARG;
+    *out = pl;
     return SDT_OK;
 }
 
@@ -194,9 +319,11 @@ extern "C" int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int r
 
 extern "C" int sdt_num_tiles(void) { return sdt::kNumTiles; }
 
+extern "C" int sdt_abi_version(void) { return SDT_ABI_VERSION; }
+
 extern "C" int sdt_tile_info(int tile_id, sdt_tile* out) {
     if (tile_id < 0 || tile_id >= sdt::kNumTiles || !out) return SDT_ERR_INVALID_ARG;
-    *out = sdt::describe(tile_id, sdt::kLadder[tile_id].stages, sdt::kLadder[tile_id].kgroups);
+    *out = sdt::describe_rung(tile_id);
     return SDT_OK;
 }
 
@@ -205,8 +332,7 @@ extern "C" int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int n
     if (tile_id < 0 || tile_id >= sdt::kNumTiles || M < 0 || N < 0 || K < 0 || !out)
         return SDT_ERR_INVALID_ARG;
     if (num_cu <= 0) num_cu = 256;
-    const sdt::Plan p = sdt::plan_for(tile_id, M, N, K, num_cu);
-    *out = sdt::describe(p.tile, p.stages, p.kgroups, p.stagger);
+    *out = sdt::describe(sdt::plan_for(tile_id, M, N, K, num_cu));
     return SDT_OK;
 }
 

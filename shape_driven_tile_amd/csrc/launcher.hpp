@@ -24,6 +24,7 @@ struct TileDesc {
     int pingpong;   // 1: the deep pipeline is the ping-pong kernel
     int deep16;     // 1: the deep pipeline with one k-group runs 16x16x32 MFMAs
     int long_stages;  // > 0: a deeper pipeline for long k-loops (see kLongMinKTiles)
+    int ksplit;     // 1: every pipeline also built to split K across workgroups
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
@@ -35,12 +36,15 @@ struct TileDesc {
 // two tiles ahead (64x64 with two k-groups: 512x512x8192 24.2 against 30.2 us,
 // 768x768x4096 14.5 against 17.5, 1024x1024x3072 13.2 against 15.2; 128x64
 // at 1280x1280x4096: 22.1 against 23.1).
+// The three smallest rungs can also split K across workgroups (the larger
+// ones are picked when the grid already fills the CUs, and the 256 x 128
+// wave tile has no registers left for the k-split sum).
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 3, 1, 1, 0, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 128, 2, 2, 3, 2, 0, 1, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3, 2, 0, 1, 0},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3, 2, 0, 0, 4},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
-    {64, 64, 2, 2, 3, 2, 0, 0, 4},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
+    {256, 256, 2, 4, 3, 1, 1, 0, 0, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
+    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
+    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 64, 2, 2, 3, 2, 0, 0, 4, 1},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
+    {64, 64, 2, 2, 3, 2, 0, 0, 4, 1},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place
@@ -76,10 +80,21 @@ constexpr int kSplitMinKTiles = 12;
 constexpr int64_t kStaggerMaxOperandBytes = int64_t(16) << 20;
 constexpr int kStaggerMinKTiles = 16;
 
+// Most workgroups one output tile's k-loop is split over, and the fewest
+// full k-tiles each split keeps.
+constexpr int kMaxSplits = 16;
+constexpr int kSplitMinKTilesPerSplit = 2;
+// How the automatic plan reduces a k-split: 1, the last workgroup of each
+// tile (one launch).
+constexpr int kSplitAlgoAuto = 1;
+
 // How one product is launched: rung, LDS stages, k-groups of waves, k-loop
-// stagger.
+// stagger; k-split across workgroups (splits per tile and how the partial
+// sums are reduced: 0 a second kernel, 1 the last workgroup of each tile);
+// persistent workgroups (ping-pong rung: 0 off, else the grid size).
 struct Plan {
     int tile, stages, kgroups, stagger;
+    int splits = 1, split_algo = 0, persistent = 0;
 };
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 
@@ -87,13 +102,20 @@ constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 // through one buffer descriptor with 32-bit byte offsets below 2^31.
 constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
-sdt_tile describe(int id, int stages, int kgroups, int stagger = 0);
+sdt_tile describe(const Plan& p);
+sdt_tile describe_rung(int id);
+int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N);
+int64_t counter_bytes(const Plan& p, int64_t M, int64_t N);
+int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu);
 bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
 int stages_for(int id, int64_t M, int64_t N, int64_t K);
 int long_for(int id, int stages, int kgroups, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
+int kgroups_for_grid(int id, int64_t wgs, int64_t nkt, int num_cu);
+int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num_cu,
+                 int64_t ws_bytes, Plan* out);
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
-int check_plan(const Plan& p);
+int check_plan(const Plan& p, int64_t K);
 int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks);
 int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu);

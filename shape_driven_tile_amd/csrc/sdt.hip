@@ -4,6 +4,7 @@
 // enqueues it on the caller's stream.  Allocates nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdint>
 #include <mutex>
@@ -16,9 +17,18 @@
 namespace sdt {
 namespace {
 
+// Whether the ladder rung with this tile is built to split K across
+// workgroups (only those rungs instantiate the k-split kernels).
+template <int BM, int BN>
+constexpr bool kLadderHasSplit() {
+    for (const TileDesc& d : kLadder)
+        if (d.bm == BM && d.bn == BN) return d.ksplit != 0;
+    return false;
+}
+
 thread_local int g_last_hip_error = 0;
 
-constexpr sdt_launch kAuto = {-1, -1, -1, -1};
+constexpr sdt_launch kAuto = {-1, -1, -1, -1, -1, -1, -1};
 
 struct DeviceInfo {
     int num_cu = 0;
@@ -56,12 +66,27 @@ int device_info(DeviceInfo* out) {
     return SDT_OK;
 }
 
+// One launch of gemm_kernel; a k-split launch (splits > 1) runs the
+// instantiation built for it, `splits` workgroups per tile, followed (with
+// split_algo 0) by the kernel that sums the partials.
 template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
+    const int tiles = p.gm * p.gn;
+    if constexpr (kLadderHasSplit<BM, BN>()) {
+        if (p.splits > 1) {
+            hipError_t e = hipLaunchKernel(
+                reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS, MF, true>),
+                dim3(tiles * p.splits), dim3(WM * WN * KS * 64), args, 0, stream);
+            if (e != hipSuccess || p.split_algo != 0) return e;
+            return hipLaunchKernel(
+                reinterpret_cast<const void*>(&gemm_splitk_reduce_kernel<Elt, BM, BN, WM, WN, MF>),
+                dim3(tiles), dim3(WM * WN * 64), args, 0, stream);
+        }
+    }
     return hipLaunchKernel(
         reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS, MF>),
-        dim3(p.gm * p.gn), dim3(WM * WN * KS * 64), args, 0, stream);
+        dim3(tiles), dim3(WM * WN * KS * 64), args, 0, stream);
 }
 
 // The 256 x 256 ping-pong kernel: 8 waves, 160 KB of LDS, one workgroup per CU.
@@ -117,6 +142,22 @@ hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
         case 3: return launch_rung<Elt, 3>(p, pl, s);
         default: return launch_rung<Elt, 4>(p, pl, s);
     }
+}
+
+// Zero `words` 32-bit words at `w` (the workspace's counters).
+__global__ void fill_words_kernel(uint32_t* w, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        w[i] = 0u;
+}
+
+int fill_words(uint32_t* w, int64_t words, hipStream_t stream) {
+    int64_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    void* args[] = {&w, &words};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&fill_words_kernel),
+                                   dim3((unsigned)blocks), dim3(256), args, 0, stream);
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
 int fill_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream) {
@@ -214,28 +255,21 @@ int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void*
 }
 
 // cfg fields: -1 = the automatic choice.  route_m1: M == 1 runs the GEMV.
+// ws / ws_bytes: the caller's workspace (NULL and 0: none; the plan then
+// never splits K across workgroups).
 template <typename Elt>
 int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B,
               int64_t ldb, void* C, int64_t ldc, void* stream, const sdt_launch& cfg,
-              bool route_m1) {
+              bool route_m1, void* ws, int64_t ws_bytes) {
     int st = check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != SDT_OK) return st;
-    const int tile_id = cfg.tile_id, stagger = cfg.stagger;
-    if (tile_id < -1 || tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
-    if (stagger < -1 || stagger > 1) return SDT_ERR_INVALID_ARG;
-    if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
-    if (tile_id >= 0) {   // a forced rung: its forced fields must name a kernel it has
-        const TileDesc& d = kLadder[tile_id];
-        if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages &&
-            !(d.long_stages > 0 && cfg.stages == d.long_stages))
-            return SDT_ERR_INVALID_ARG;
-        if (cfg.kgroups >= 0 && cfg.kgroups != 1 && !(cfg.kgroups == 2 && d.kgroups == 2))
-            return SDT_ERR_INVALID_ARG;
-        if (cfg.kgroups == 2 && cfg.stages == 2 && d.stages != 2) return SDT_ERR_INVALID_ARG;
-    } else if (cfg.stages >= 0 || cfg.kgroups >= 0) {
-        if (cfg.stages > 4 || cfg.kgroups > 2) return SDT_ERR_INVALID_ARG;
-    }
-    if (stagger == 1 && !stagger_eligible(K)) return SDT_ERR_UNSUPPORTED;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return SDT_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return SDT_ERR_UNSUPPORTED;
+    // the configuration is checked before the sizes short-circuit
+    Plan pl;
+    st = resolve_plan(cfg, std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), K, 256,
+                      ws ? ws_bytes : 0, &pl);
+    if (st != SDT_OK) return st;
     if (M == 0 || N == 0) return SDT_OK;
     if (M > INT_MAX || N > INT_MAX) return SDT_ERR_UNSUPPORTED;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,24 +279,12 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     DeviceInfo dev;
     st = device_info(&dev);
     if (st != SDT_OK) return st;
-
-    const int id = tile_id >= 0 ? tile_id : pick_tile(M, N, K, dev.num_cu);
-    Plan pl = plan_for(id, M, N, K, dev.num_cu);
-    if (cfg.kgroups >= 0) {
-        pl.kgroups = cfg.kgroups;
-        if (cfg.stages < 0)
-            pl.stages = long_for(id, pl.kgroups == 2 ? kLadder[id].stages : stages_for(id, M, N, K),
-                                 pl.kgroups, K);
-    }
-    if (cfg.stages >= 0) pl.stages = cfg.stages;
-    // the plan's stagger (stagger_auto) unless the caller forces it on or off
-    const int use_stagger = stagger == -1 ? pl.stagger : stagger;
-    st = check_plan(pl);
+    st = resolve_plan(cfg, M, N, K, dev.num_cu, ws ? ws_bytes : 0, &pl);
     if (st != SDT_OK) return st;
-    const TileDesc& td = kLadder[id];
+    const TileDesc& td = kLadder[pl.tile];
     const int64_t gm = ceil_div(M, td.bm);
     const int64_t gn = ceil_div(N, td.bn);
-    if (gm * gn > INT_MAX) return SDT_ERR_UNSUPPORTED;
+    if (gm * gn * pl.splits > INT_MAX) return SDT_ERR_UNSUPPORTED;
 
     GemmParams p;
     p.A = static_cast<const uint16_t*>(A);
@@ -276,8 +298,15 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     p.K = (int)K;
     p.gm = (int)gm;
     p.gn = (int)gn;
-    p.stagger = use_stagger;
+    p.stagger = pl.stagger;
     p.nxcd = dev.nxcd;
+    p.splits = pl.splits;
+    p.split_algo = pl.split_algo;
+    p.cnt = static_cast<int*>(ws);
+    p.ws = pl.splits > 1
+               ? reinterpret_cast<float*>(static_cast<char*>(ws) + counter_bytes(pl, M, N))
+               : nullptr;
+    p.persistent = pl.persistent;
     hipError_t e = launch_gemm<Elt>(pl, p, s);
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
@@ -310,40 +339,92 @@ __global__ __launch_bounds__(64) void stream_read_kernel(const int4_t* buf, uint
 
 extern "C" int gemm_f16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                         const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true,
+                                    nullptr, 0);
+}
+
+extern "C" int gemm_f16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                           const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                           int64_t workspace_bytes, void* stream) {
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true,
+                                    workspace, workspace_bytes);
 }
 
 extern "C" int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                            int tile_id, int stagger) {
     return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                                    sdt_launch{tile_id, -1, -1, stagger}, false);
+                                    sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1}, false,
+                                    nullptr, 0);
 }
 
 extern "C" int gemm_bf16(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                          const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
-    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true);
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true,
+                                     nullptr, 0);
+}
+
+extern "C" int gemm_bf16_ws(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                            const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                            int64_t workspace_bytes, void* stream) {
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true,
+                                     workspace, workspace_bytes);
 }
 
 extern "C" int gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                             int tile_id, int stagger) {
     return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                                     sdt_launch{tile_id, -1, -1, stagger}, false);
+                                     sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1}, false,
+                                     nullptr, 0);
 }
 
 extern "C" int gemm_f16_cfg(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
-                            const sdt_launch* cfg) {
+                            const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                            int64_t workspace_bytes, void* stream, const sdt_launch* cfg) {
     if (!cfg) return SDT_ERR_INVALID_ARG;
-    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false);
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false,
+                                    workspace, workspace_bytes);
 }
 
 extern "C" int gemm_bf16_cfg(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
-                             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
-                             const sdt_launch* cfg) {
+                             const void* B, int64_t ldb, void* C, int64_t ldc, void* workspace,
+                             int64_t workspace_bytes, void* stream, const sdt_launch* cfg) {
     if (!cfg) return SDT_ERR_INVALID_ARG;
-    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false);
+    return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false,
+                                     workspace, workspace_bytes);
+}
+
+extern "C" int64_t sdt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int num_cu) {
+    if (M < 0 || N < 0 || K < 0) return -1;
+    if (M <= 1 || N == 0 || K == 0) return 0;   // routed to the GEMV, a no-op or a fill
+    if (num_cu <= 0) {
+        sdt::DeviceInfo dev;
+        if (sdt::device_info(&dev) != SDT_OK) return -1;
+        num_cu = dev.num_cu;
+    }
+    sdt::Plan p;
+    if (sdt::resolve_plan(sdt::kAuto, M, N, K, num_cu, INT64_MAX, &p) != SDT_OK) return -1;
+    return sdt::workspace_bytes(p, M, N);
+}
+
+extern "C" int64_t sdt_launch_workspace_size(int64_t M, int64_t N, int64_t K,
+                                             const sdt_launch* cfg) {
+    if (!cfg || M < 0 || N < 0 || K < 0) return -1;
+    sdt::Plan p;
+    if (sdt::resolve_plan(*cfg, std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), K, 256,
+                          INT64_MAX, &p) != SDT_OK)
+        return -1;
+    return (M == 0 || N == 0) ? 0 : sdt::workspace_bytes(p, M, N);
+}
+
+extern "C" int sdt_workspace_init(void* workspace, int64_t bytes, void* stream) {
+    if (bytes == 0) return SDT_OK;
+    if (bytes < 0 || !workspace) return SDT_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 || bytes % 4 != 0)
+        return SDT_ERR_UNSUPPORTED;
+    return sdt::fill_words(static_cast<uint32_t*>(workspace), bytes / 4,
+                           static_cast<hipStream_t>(stream));
 }
 
 extern "C" int gemv_f16_m1(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
@@ -410,7 +491,24 @@ extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_ti
         num_cu = dev.num_cu;
     }
     const sdt::Plan p = sdt::plan_for(sdt::pick_tile(M, N, K, num_cu), M, N, K, num_cu);
-    *out = sdt::describe(p.tile, p.stages, p.kgroups, p.stagger);
+    *out = sdt::describe(p);
+    return SDT_OK;
+}
+
+extern "C" int sdt_pick_tile_ws(int64_t M, int64_t N, int64_t K, int num_cu,
+                                int64_t workspace_bytes, sdt_tile* out) {
+    if (M < 0 || N < 0 || K < 0 || workspace_bytes < 0 || !out) return SDT_ERR_INVALID_ARG;
+    if (num_cu <= 0) {
+        sdt::DeviceInfo dev;
+        int st = sdt::device_info(&dev);
+        if (st != SDT_OK) return st;
+        num_cu = dev.num_cu;
+    }
+    sdt::Plan p;
+    int st = sdt::resolve_plan(sdt::kAuto, std::max<int64_t>(M, 1), std::max<int64_t>(N, 1), K,
+                               num_cu, workspace_bytes, &p);
+    if (st != SDT_OK) return st;
+    *out = sdt::describe(p);
     return SDT_OK;
 }
 

@@ -11,6 +11,7 @@ replayed `--repeats` times back to back; one more replay into a cleared C is
 compared bit for bit with an eager launch of the same rung.
 
     python -m shape_driven_tile_amd.sweep [--shapes 512,1024,...] [--out file.json]
+    python -m shape_driven_tile_amd.sweep --splits 2,3,4,6,8 [--shapes ...]
 """
 from __future__ import annotations
 
@@ -23,12 +24,14 @@ DEFAULT_SQUARES = (256, 512, 768, 1024, 1280, 1536, 1792, 2048, 2560, 3072, 3584
                    6144, 8192)
 
 
-def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats, kgroups=-1):
+def time_rung(sdt, torch, A, B, C, tile, stagger, chain, repeats, kgroups=-1, ws=None, **cfg):
     """Median microseconds per launch of rung `tile` over `repeats` back-to-back
     graph replays, all of them, and whether a replay into a cleared C
-    reproduced the eager result bit for bit."""
+    reproduced the eager result bit for bit.  cfg: further sdt_launch fields
+    (splits, split_algo, stages, persistent); ws: a binding.Workspace."""
     def launch():
-        sdt.gemm_f16_cfg(A, B, C, tile_id=tile, kgroups=kgroups, stagger=stagger)
+        sdt.gemm_f16_cfg(A, B, C, tile_id=tile, kgroups=kgroups, stagger=stagger, workspace=ws,
+                         **cfg)
     launch()
     torch.cuda.synchronize()
     eager = C.clone()
@@ -66,6 +69,9 @@ def main(argv=None):
                     help="comma list of M=N=K squares, or MxNxK entries")
     ap.add_argument("--repeats", type=int, default=7)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--splits", default=None,
+                    help="comma list of k-split counts: instead of the rung sweep, time every "
+                         "k-split rung with each count (both reductions, one and two k-groups)")
     args = ap.parse_args(argv)
 
     import torch
@@ -91,6 +97,10 @@ def main(argv=None):
     for _ in range(200):
         sdt.gemm_f16_ex(WA, WB, WC)
     torch.cuda.synchronize()
+
+    if args.splits:
+        return split_sweep(sdt, torch, inputs, dev, num_cu, shapes,
+                           [int(v) for v in args.splits.split(",")], args)
 
     results = []
     for (M, N, K) in shapes:
@@ -149,6 +159,66 @@ def main(argv=None):
     ok = all(v["replays_match_eager"] for r in results
              for v in (list(r["rungs"].values()) + list(r.get("stagger_arms", {}).values())
                        + list(r.get("kgroup_arms", {}).values())))
+    return 0 if ok else 1
+
+
+def split_sweep(sdt, torch, inputs, dev, num_cu, shapes, split_counts, args):
+    """The k-split arms: on every rung built to split K, each count in
+    split_counts that leaves at least two full k-tiles per split, with the
+    partials reduced by a second kernel (algo 0) or by each tile's last
+    workgroup (algo 1), one k-group (2-stage and deep pipelines) and two;
+    beside them the rung unsplit and the automatic plans of gemm_f16 and
+    gemm_f16_ws."""
+    ws = sdt.Workspace(256 << 20, device=dev)
+    results = []
+    for (M, N, K) in shapes:
+        kp, np_ = -(-K // 8) * 8, -(-N // 8) * 8
+        A = torch.zeros((M, kp), dtype=torch.float16, device=dev)[:, :K]
+        B = torch.zeros((N, kp), dtype=torch.float16, device=dev)[:, :K]
+        A.copy_(torch.from_numpy(inputs.uniform_f16((M, K), 11)))
+        B.copy_(torch.from_numpy(inputs.uniform_f16((N, K), 12)))
+        C = torch.empty((M, np_), dtype=torch.float16, device=dev)[:, :N]
+        flop = 2.0 * M * N * K
+        chain = max(4, min(400, int(2e12 / max(flop, 1.0))))
+        row = {"M": M, "N": N, "K": K, "arms": {}}
+        plain = sdt.pick_tile(M, N, K, num_cu)
+        wsplan = sdt.pick_tile_ws(M, N, K, num_cu, ws.nbytes)
+        med, allv, same = time_rung(sdt, torch, A, B, C, -1, -1, chain, args.repeats)
+        row["arms"]["gemm_f16"] = {"us": round(med, 3), "min_us": round(allv[0], 3),
+                                   "max_us": round(allv[-1], 3), "replays_match_eager": same,
+                                   "plan": plain}
+        med, allv, same = time_rung(sdt, torch, A, B, C, -1, -1, chain, args.repeats, ws=ws)
+        row["arms"]["gemm_f16_ws"] = {"us": round(med, 3), "min_us": round(allv[0], 3),
+                                      "max_us": round(allv[-1], 3), "replays_match_eager": same,
+                                      "plan": wsplan}
+        print(f"{M}x{N}x{K}: gemm_f16 {row['arms']['gemm_f16']['us']:.2f} "
+              f"(t{plain['id']} s{plain['stages']} kg{plain['kgroups']})  gemm_f16_ws "
+              f"{row['arms']['gemm_f16_ws']['us']:.2f} (t{wsplan['id']} splits {wsplan['splits']}"
+              f" algo {wsplan['split_algo']} s{wsplan['stages']} kg{wsplan['kgroups']})", flush=True)
+        for tile in range(sdt.num_tiles()):
+            info = sdt.tile_info(tile)
+            if not info["ksplit"]:
+                continue
+            pipes = [(2, 1), (info["stages"], 1), (info["stages"], 2)]
+            for sp in [1] + [v for v in split_counts if v > 1 and (K // 64) // v >= 2]:
+                for (stages, kg) in pipes:
+                    for algo in ((0, 1) if sp > 1 else (0,)):
+                        key = f"t{tile}_s{sp}_a{algo}_st{stages}_kg{kg}"
+                        med, allv, same = time_rung(sdt, torch, A, B, C, tile, 0, chain,
+                                                    args.repeats, kgroups=kg, ws=ws, splits=sp,
+                                                    split_algo=algo, stages=stages)
+                        row["arms"][key] = {"us": round(med, 3), "min_us": round(allv[0], 3),
+                                            "max_us": round(allv[-1], 3),
+                                            "replays_match_eager": same}
+        best = sorted(row["arms"].items(), key=lambda kv: kv[1]["us"])[:6]
+        print("    best: " + "  ".join(f"{k} {v['us']:.2f}" for k, v in best), flush=True)
+        results.append(row)
+    out = {"num_cu": num_cu, "device": torch.cuda.get_device_properties(dev).name,
+           "shapes": results}
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump(out, f, indent=1)
+    ok = all(v["replays_match_eager"] for r in results for v in r["arms"].values())
     return 0 if ok else 1
 
 

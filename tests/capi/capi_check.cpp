@@ -97,8 +97,11 @@ static std::vector<uint16_t> host_copy(const void* p, size_t n) {
     return h;
 }
 
-// C = A.B on a ragged shape with padded strides, on an explicit stream.
-static void check_gemm(int dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+// C = A.B on a ragged shape with padded strides, on an explicit stream;
+// use_ws: through the workspace entry point, with the workspace the library
+// asks for (hipMalloc, counters zeroed by sdt_workspace_init).
+static void check_gemm(int dtype, int64_t M, int64_t N, int64_t K, hipStream_t stream,
+                       bool use_ws = false) {
     const int64_t lda = (K + 7) / 8 * 8 + 8, ldb = (K + 7) / 8 * 8 + 16, ldc = (N + 7) / 8 * 8;
     std::vector<uint16_t> A = draw((size_t)(M * lda), 11 + dtype, dtype);
     std::vector<uint16_t> B = draw((size_t)(N * ldb), 12 + dtype, dtype);
@@ -106,8 +109,24 @@ static void check_gemm(int dtype, int64_t M, int64_t N, int64_t K, hipStream_t s
     void* dB = dev_copy(B);
     void* dC = nullptr;
     HIP_OK(hipMalloc(&dC, (size_t)(M * ldc) * 2));
-    const int rc = dtype == 1 ? gemm_bf16(M, N, K, dA, lda, dB, ldb, dC, ldc, stream)
-                              : gemm_f16(M, N, K, dA, lda, dB, ldb, dC, ldc, stream);
+    void* ws = nullptr;
+    int64_t ws_bytes = 0;
+    if (use_ws) {
+        ws_bytes = sdt_gemm_workspace_size(M, N, K, 0);
+        CHECK(ws_bytes > 0, "%lldx%lldx%lld: no k-split planned", (long long)M, (long long)N,
+              (long long)K);
+        if (ws_bytes > 0) {
+            HIP_OK(hipMalloc(&ws, (size_t)ws_bytes));
+            CHECK(sdt_workspace_init(ws, ws_bytes, stream) == SDT_OK, "workspace init");
+        }
+    }
+    int rc;
+    if (use_ws)
+        rc = dtype == 1 ? gemm_bf16_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, ws_bytes, stream)
+                        : gemm_f16_ws(M, N, K, dA, lda, dB, ldb, dC, ldc, ws, ws_bytes, stream);
+    else
+        rc = dtype == 1 ? gemm_bf16(M, N, K, dA, lda, dB, ldb, dC, ldc, stream)
+                        : gemm_f16(M, N, K, dA, lda, dB, ldb, dC, ldc, stream);
     CHECK(rc == SDT_OK, "gemm dtype %d %lldx%lldx%lld: %s", dtype, (long long)M, (long long)N,
           (long long)K, sdt_status_string(rc));
     HIP_OK(hipStreamSynchronize(stream));
@@ -124,6 +143,7 @@ static void check_gemm(int dtype, int64_t M, int64_t N, int64_t K, hipStream_t s
     HIP_OK(hipFree(dA));
     HIP_OK(hipFree(dB));
     HIP_OK(hipFree(dC));
+    if (ws) HIP_OK(hipFree(ws));
 }
 
 static void check_gemv(int dtype, bool kn, int64_t N, int64_t K) {
@@ -170,6 +190,8 @@ int main() {
         check_gemm(dtype, 300, 260, 1000, s);     // several tiles, ragged edges, partial k-tile
         check_gemm(dtype, 1024, 1024, 1024, s);   // two k-groups of waves
         check_gemm(dtype, 1, 500, 777 / 8 * 8, s);   // M = 1 -> the streaming GEMV
+        check_gemm(dtype, 300, 260, 1000, s, true);   // K split across workgroups
+        check_gemm(dtype, 512, 512, 2048, s, true);
         check_gemv(dtype, false, 12288, 4096);
         check_gemv(dtype, true, 12288, 4096);
         check_gemv(dtype, true, 1001, 1003);
@@ -185,9 +207,11 @@ int main() {
               SDT_ERR_UNSUPPORTED, "misaligned A");
     CHECK(gemm_f16(64, 64, 64, b, 60, b + 8192, 64, b + 65536, 64, nullptr) == SDT_ERR_INVALID_ARG,
           "lda < K");
-    sdt_launch cfg = {0, 5, -1, -1};
-    CHECK(gemm_f16_cfg(64, 64, 64, b, 64, b + 8192, 64, b + 65536, 64, nullptr, &cfg) ==
-              SDT_ERR_INVALID_ARG, "stage count without a kernel");
+    sdt_launch cfg = {0, 5, -1, -1, -1, -1, -1};
+    CHECK(gemm_f16_cfg(64, 64, 64, b, 64, b + 8192, 64, b + 65536, 64, nullptr, 0, nullptr,
+                       &cfg) == SDT_ERR_INVALID_ARG, "stage count without a kernel");
+    CHECK(sdt_abi_version() == SDT_ABI_VERSION, "ABI version %d, header %d", sdt_abi_version(),
+          SDT_ABI_VERSION);
     // K = 0 writes zeros (the empty sum)
     HIP_OK(hipMemset(b + 65536, 0x55, 64 * 64 * 2));
     CHECK(gemm_f16(64, 64, 0, nullptr, 0, nullptr, 0, b + 65536, 64, nullptr) == SDT_OK, "K = 0");

@@ -231,7 +231,7 @@ def test_gemm_cfg_rejects_kernels_that_do_not_exist():
     """Forced combinations without a kernel are refused before any device
     call (fake aligned pointers, null stream)."""
     L = sdt.lib()
-    args = (512, 512, 512, 0x10000, 512, 0x20000, 512, 0x30000, 512, None)
+    args = (512, 512, 512, 0x10000, 512, 0x20000, 512, 0x30000, 512, None, 0, None)
     tiles = ladder()
     def cfg(*v):
         return ctypes.byref(sdt.launch_cfg(*v))
@@ -446,3 +446,76 @@ def test_runtime_refusal_maps_to_sdt_err_hip():
     vals = [int(v) for v in res.stdout.split()[-6:]]
     hip_err = sdt.SDT_ERR_HIP
     assert vals == [hip_err, 100, hip_err, hip_err, hip_err, 100], vals
+
+
+def test_abi_version():
+    assert sdt.lib().sdt_abi_version() == sdt.ABI_VERSION
+    text = open(HEADER).read()
+    assert f"#define SDT_ABI_VERSION {sdt.ABI_VERSION}" in text
+
+
+def test_ksplit_plan_rules():
+    """gemm_f16_ws's plan: without a workspace (or one too small) it is
+    gemm_f16's; with room it splits K on the rungs built for it while the
+    grid leaves CUs idle: the most splits that keep tiles x splits within the
+    CU count, each with at least two full k-tiles, at most 16; the stagger is
+    then off.  The workspace it reports is the counters (one int per tile and
+    wave, rounded up to 256 bytes) plus the fp32 partial tiles."""
+    tiles = ladder()
+    shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
+              (1536, 1536, 1536), (2048, 2048, 2048), (4096, 4096, 4096), (300, 260, 1000),
+              (64, 64, 64), (100, 3000, 700), (512, 512, 8192), (128, 128, 65536)]
+    for num_cu in (80, 256):
+        for (M, N, K) in shapes:
+            plain = sdt.pick_tile(M, N, K, num_cu)
+            assert sdt.pick_tile_ws(M, N, K, num_cu, 0) == plain
+            big = sdt.pick_tile_ws(M, N, K, num_cu, 1 << 40)
+            t = tiles[plain["id"]]
+            ntile = -(-M // t["bm"]) * -(-N // t["bn"])
+            s = min(num_cu // ntile, (K // 64) // 2, 16) if t["ksplit"] else 1
+            s = s if s >= 2 else 1
+            assert big["id"] == plain["id"] and big["splits"] == s, (num_cu, M, N, K, big)
+            need = sdt.gemm_workspace_size(M, N, K, num_cu)
+            if s == 1:
+                assert need == 0 and big == plain
+                continue
+            assert big["stagger"] == 0 and big["split_algo"] == 1
+            counters = -(-(ntile * t["waves_m"] * t["waves_n"] * 4) // 256) * 256
+            assert need == counters + ntile * s * t["bm"] * t["bn"] * 4
+            assert sdt.pick_tile_ws(M, N, K, num_cu, need) == big
+            assert sdt.pick_tile_ws(M, N, K, num_cu, need - 1)["splits"] == 1
+
+
+def test_ksplit_and_persistent_cfg_refusals():
+    """Forced k-split and persistent configurations the library has no kernel
+    for, or without the workspace they need, are refused before any device
+    call (fake aligned pointers)."""
+    L = sdt.lib()
+    ws, big = 0x40000, 1 << 40
+    def call(M, N, K, w, wbytes, **kw):
+        c = sdt.launch_cfg(**kw)
+        return L.gemm_f16_cfg(M, N, K, 0x10000, K, 0x20000, K, 0x30000, N, w, wbytes, None,
+                              ctypes.byref(c))
+    bad = sdt.SDT_ERR_INVALID_ARG
+    assert call(512, 512, 1024, None, 0, tile_id=4, splits=2) == bad            # no workspace
+    need = sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=2)
+    assert need > 0
+    assert call(512, 512, 1024, ws, need - 16, tile_id=4, splits=2) == bad      # too small
+    assert call(512, 512, 1024, ws, big, tile_id=0, splits=2) == bad            # rung 0: no split
+    assert call(512, 512, 1024, ws, big, tile_id=1, splits=2) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=17) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=0) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=-2) == bad
+    assert call(512, 512, 960, ws, big, tile_id=4, splits=16) == bad            # 15 full k-tiles
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=2, stagger=1) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=2, split_algo=2) == bad
+    assert call(512, 512, 1024, ws + 8, big, tile_id=4, splits=2) == sdt.SDT_ERR_UNSUPPORTED
+    assert call(512, 512, 1024, None, 8, tile_id=4) == bad                      # bytes, no pointer
+    assert call(512, 512, 1024, None, -1, tile_id=4) == bad
+    # persistent workgroups: the ping-pong kernel only, at most one per tile
+    assert call(4096, 4096, 4096, None, 0, tile_id=2, persistent=64) == bad
+    assert call(4096, 4096, 4096, None, 0, tile_id=0, stages=2, persistent=64) == bad
+    assert call(4096, 4096, 4096, None, 0, tile_id=0, persistent=257) == bad    # 256 tiles
+    assert call(4096, 4096, 4096, None, 0, tile_id=0, persistent=-2) == bad
+    with pytest.raises(sdt.SdtError):
+        sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=17)
