@@ -409,9 +409,14 @@ __device__ __forceinline__ void store_partial(const acc_t (&acc)[FN][FM], __amdg
         for (int j = 0; j < FM; ++j)
 #pragma unroll
             for (int e = 0; e < E; ++e) {
+                // element first, then reinterpret: a bit cast applied to a
+                // vector-element expression reads element 0 of the vector
                 uint4_t v;
 #pragma unroll
-                for (int d = 0; d < 4; ++d) v[d] = __builtin_bit_cast(uint32_t, acc[i][j][4 * e + d]);
+                for (int d = 0; d < 4; ++d) {
+                    const float x = acc[i][j][4 * e + d];
+                    v[d] = __builtin_bit_cast(uint32_t, x);
+                }
                 __builtin_amdgcn_raw_buffer_store_b128(v, r, (((i * FM + j) * E + e) * 64 + lane) * 16,
                                                        0, AUX);
             }
@@ -438,7 +443,8 @@ __device__ __forceinline__ void load_partial(acc_t (&acc)[FN][FM], __amdgpu_buff
             for (int e = 0; e < E; ++e)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const float x = __builtin_bit_cast(float, v[i][j][e][d]);
+                    const uint32_t u = v[i][j][e][d];   // element first (see store_partial)
+                    const float x = __builtin_bit_cast(float, u);
                     if constexpr (ADD)
                         acc[i][j][4 * e + d] += x;
                     else
