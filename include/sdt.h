@@ -145,10 +145,13 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
  * workspace: device memory owned by the caller, 16-byte aligned, at least
  * sdt_gemm_workspace_size(M, N, K, 0) bytes for the split plan (smaller, or
  * NULL with 0: the call runs gemm_f16's plan, unsplit, and touches no
- * workspace).  Its leading counter bytes must be zero before the first call
- * that uses it (sdt_workspace_init); every call leaves them zero again.  One
- * workspace serves one call at a time: calls that share it must be ordered
- * on one stream (concurrent calls on other streams need their own).
+ * workspace).  Layout: the first 64 KiB hold arrival counters (one int per
+ * output tile and wave, so a split launch has at most 16384 / waves tiles),
+ * the fp32 partial sums follow.  The counter area must be zero before the
+ * first call that uses the workspace (sdt_workspace_init); every call leaves
+ * it zero again, whatever its shape.  One workspace serves one call at a
+ * time: calls that share it must be ordered on one stream (concurrent calls
+ * on other streams need their own).
  * Everything else as gemm_f16 (same requirements, statuses and
  * degenerate-size behaviour; M == 1 runs the decode GEMV). */
 int gemm_f16_ws(int64_t M, int64_t N, int64_t K,

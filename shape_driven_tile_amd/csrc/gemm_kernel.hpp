@@ -461,32 +461,33 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_slot(const GemmParams&
 }
 
 // The single-kernel k-split reduction, per wave: store this split's partial
-// sums at device scope, wait until they are complete, then count the arrival
-// on the (tile, wave) counter.  The wave that arrives last returns true and
-// owns the block: it clears the counter for the next launch and forms
+// sums, make them visible at agent scope (a release fence: the XCDs' L2s are
+// separate caches, so the wave's dirty lines are written back and its stores
+// waited for), then count the arrival on the (tile, wave) counter with an
+// agent-scope atomic.  The wave that arrives last returns true and owns the
+// block: an acquire fence (which invalidates what its L2 may hold of the
+// other splits' slots), then it clears the counter for the next launch and
+// forms
 //   acc = ((P_0 + P_1) + P_2) + ... + P_{splits-1}
 // in that order, whichever split it holds (fp32 addition is commutative, so
 // adding its own P_split to the running sum of P_0 .. P_{split-1} gives the
 // same bits as the opposite operand order): the result does not depend on
-// the order of arrival.  The others return false and are done.  Every store
-// and load of a partial carries the device-scope bit (written through to,
-// and read from, the level shared by all XCDs); the counter is an agent-scope
-// atomic issued only after vmcnt(0), i.e. after this wave's stores have
-// completed at that scope, and the last wave issues its loads only after the
-// atomic has returned.  No wave waits for another: nothing spins.
+// the order of arrival.  The others return false and are done.  The
+// partials are also stored and loaded with the device-scope bit (written
+// through to memory, so the release has little to write back).  No wave
+// waits for another: nothing spins.
 template <int FN, int FM, typename acc_t>
 __device__ __forceinline__ bool splitk_arrive(const GemmParams& p, acc_t (&acc)[FN][FM], int tile,
                                               int split, int wave, int nwaves, int lane) {
     constexpr int SLOT = FN * FM * (int)(sizeof(acc_t) / 4) * 64;
     store_partial<kScopeDevice>(acc, partial_slot(p, tile, split, wave, nwaves, SLOT), lane);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    wait_global_loads<0>();              // vmcnt counts stores too on this target
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     int* counter = p.cnt + (int64_t)tile * nwaves + wave;
     int old = 0;
     if (lane == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __builtin_amdgcn_readfirstlane(old);
     if (old != p.splits - 1) return false;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (split == 0) {
         for (int s = 1; s < p.splits; ++s)
@@ -871,8 +872,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_splitk_reduce_kernel(GemmPa
 // reads tile t+1 in P 2t+2.  Group 1 takes one extra barrier before its loop
 // and group 0 one after it, so every wave executes the same number of
 // barriers.
+constexpr int kPpLdsUnits = 2 * 256 * 8 + 3 * 256 * 8;   // 160 KB of 16-byte units
+
+// One 256 x 256 output tile of the ping-pong kernel: w is the tile's
+// workgroup index in a one-workgroup-per-tile launch (the persistent form
+// passes each tile it visits in turn).
 template <typename Elt>
-__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_pp_tile(const GemmParams& p, const int w, int4_t* smem) {
     typedef typename Elt::frag8 frag8;
     constexpr int BM = 256, BN = 256, BK = kBK;
     constexpr int WTM = 128, WTN = 64;          // per wave: 2 x 4 waves
@@ -880,8 +886,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
     constexpr int B_BASE = 2 * A_UNITS;                 // A stages first, then B stages
     constexpr int DMA = 8;                      // loads per operand k-tile per wave: 64 rows
-
-    __shared__ int4_t smem[2 * A_UNITS + 3 * B_UNITS];   // 160 KB
+    static_assert(2 * A_UNITS + 3 * B_UNITS == kPpLdsUnits, "LDS layout");
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -900,7 +905,6 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     // XCDs through the Infinity Cache; blocks are visited row by row.  Other
     // grids use the grouped order of gemm_kernel.
     const int nwg = p.gm * p.gn;
-    const int w = blockIdx.x;
     int64_t m0, n0;
     if (p.nxcd == 8 && (p.gm & 15) == 0 && (p.gn & 15) == 0) {
         const int x = w & 7, idx = w >> 3;      // idx-th workgroup of XCD x
@@ -1094,6 +1098,27 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
     store_block_staged<Elt>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane,
                             smem + A_UNITS + wave * 256);
     if (grp == 0 && ktail == 0) __syncthreads();   // matches group 1's extra barrier
+}
+
+// The ping-pong kernel.  PERSIST = false: one workgroup per output tile.
+// PERSIST = true (persistent workgroups, the FlyDSL PR's Changes): a grid of
+// p.persistent workgroups, workgroup w taking tiles w, w + grid, w + 2 grid,
+// ... in turn.  Each tile's barriers pair up between the two wave groups
+// (above); a barrier between tiles lets every wave finish the previous
+// tile's epilogue (in A stage 1) before group 1's prologue loads and group
+// 0's first A load of the next tile go into the stages.
+template <typename Elt, bool PERSIST = false>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
+    __shared__ int4_t smem[kPpLdsUnits];   // 160 KB
+    if constexpr (PERSIST) {
+        const int ntile = p.gm * p.gn;
+        for (int v = blockIdx.x; v < ntile; v += gridDim.x) {
+            if (v != (int)blockIdx.x) __syncthreads();
+            gemm_pp_tile<Elt>(p, v, smem);
+        }
+    } else {
+        gemm_pp_tile<Elt>(p, blockIdx.x, smem);
+    }
 }
 
 // C = 0 for K == 0 (the empty sum), M x N with stride ldc.

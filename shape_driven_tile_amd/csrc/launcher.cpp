@@ -43,21 +43,20 @@ sdt_tile describe_rung(int id) {
     return describe(p);
 }
 
-// Workspace of a k-split launch: the arrival counters (one int per tile and
-// wave of a k-group, rounded up to 256 bytes), then the fp32 partial sums
-// (splits slots of bm x bn per tile).  Zero without a split.
-int64_t counter_bytes(const Plan& p, int64_t M, int64_t N) {
-    if (p.splits <= 1) return 0;
-    const TileDesc& d = kLadder[p.tile];
-    const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
-    return (tiles * d.waves_m * d.waves_n * 4 + 255) / 256 * 256;
+// Workspace of a k-split launch: the arrival-counter area (a fixed
+// kCounterBytes at the start, whatever the shape, so that no launch's partial
+// sums ever land where another keeps counters: counters stay zero between
+// launches), then the fp32 partial sums (splits slots of bm x bn per tile).
+// Zero without a split.
+int64_t counter_bytes(const Plan& p, int64_t, int64_t) {
+    return p.splits <= 1 ? 0 : kCounterBytes;
 }
 
 int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
     if (p.splits <= 1) return 0;
     const TileDesc& d = kLadder[p.tile];
     const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
-    return counter_bytes(p, M, N) + tiles * p.splits * int64_t(d.bm) * d.bn * 4;
+    return kCounterBytes + tiles * p.splits * int64_t(d.bm) * d.bn * 4;
 }
 
 // k-split of the automatic plan when a workspace is available: on a rung
@@ -195,7 +194,9 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
         Plan t = pl;
         t.stagger = 0;
         t.splits = splits_for(t, M, N, K, num_cu);
-        if (t.splits > 1 && workspace_bytes(t, M, N) <= ws_bytes) pl = t;
+        const int64_t counters = ceil_div(M, d.bm) * ceil_div(N, d.bn) * d.waves_m * d.waves_n;
+        if (t.splits > 1 && workspace_bytes(t, M, N) <= ws_bytes && counters <= kCounterBytes / 4)
+            pl = t;
     }
     if (pl.splits > 1) {
         pl.stagger = cfg.stagger == 1 ? 1 : 0;
@@ -220,6 +221,10 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
     int st = check_plan(pl, K);
     if (st != SDT_OK) return st;
     if (pl.persistent > ceil_div(M, d.bm) * ceil_div(N, d.bn)) return SDT_ERR_INVALID_ARG;
+    // one arrival counter per tile and wave of a k-group must fit the counter area
+    if (pl.splits > 1 &&
+        ceil_div(M, d.bm) * ceil_div(N, d.bn) * d.waves_m * d.waves_n > kCounterBytes / 4)
+        return SDT_ERR_UNSUPPORTED;
     if (pl.splits > 1 && workspace_bytes(pl, M, N) > (ws_bytes < 0 ? 0 : ws_bytes))
         return SDT_ERR_INVALID_ARG;
     *out = pl;

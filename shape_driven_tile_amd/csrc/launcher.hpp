@@ -87,6 +87,9 @@ constexpr int kSplitMinKTilesPerSplit = 2;
 // How the automatic plan reduces a k-split: 1, the last workgroup of each
 // tile (one launch).
 constexpr int kSplitAlgoAuto = 1;
+// Bytes at the start of a k-split workspace that hold the arrival counters
+// (one int per output tile and wave of a k-group: at most 16384).
+constexpr int64_t kCounterBytes = 64 * 1024;
 
 // How one product is launched: rung, LDS stages, k-groups of waves, k-loop
 // stagger; k-split across workgroups (splits per tile and how the partial

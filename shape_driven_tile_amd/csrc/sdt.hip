@@ -89,10 +89,14 @@ hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
         dim3(tiles), dim3(WM * WN * KS * 64), args, 0, stream);
 }
 
-// The 256 x 256 ping-pong kernel: 8 waves, 160 KB of LDS, one workgroup per CU.
+// The 256 x 256 ping-pong kernel: 8 waves, 160 KB of LDS, one workgroup per
+// CU; with p.persistent > 0 a grid of that many workgroups loops over the tiles.
 template <typename Elt>
 hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
+    if (p.persistent > 0)
+        return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_pp_kernel<Elt, true>),
+                               dim3(p.persistent), dim3(512), args, 0, stream);
     return hipLaunchKernel(reinterpret_cast<const void*>(&gemm_pp_kernel<Elt>),
                            dim3(p.gm * p.gn), dim3(512), args, 0, stream);
 }

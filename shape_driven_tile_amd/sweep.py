@@ -69,6 +69,9 @@ def main(argv=None):
                     help="comma list of M=N=K squares, or MxNxK entries")
     ap.add_argument("--repeats", type=int, default=7)
     ap.add_argument("--out", default=None)
+    ap.add_argument("--persistent", default=None,
+                    help="comma list of persistent grid sizes (0 = one workgroup per tile): "
+                         "instead of the rung sweep, time the ping-pong kernel with each")
     ap.add_argument("--splits", default=None,
                     help="comma list of k-split counts: instead of the rung sweep, time every "
                          "k-split rung with each count (both reductions, one and two k-groups)")
@@ -101,6 +104,9 @@ def main(argv=None):
     if args.splits:
         return split_sweep(sdt, torch, inputs, dev, num_cu, shapes,
                            [int(v) for v in args.splits.split(",")], args)
+    if args.persistent:
+        return persistent_sweep(sdt, torch, inputs, dev, num_cu, shapes,
+                                [int(v) for v in args.persistent.split(",")], args)
 
     results = []
     for (M, N, K) in shapes:
@@ -220,6 +226,47 @@ def split_sweep(sdt, torch, inputs, dev, num_cu, shapes, split_counts, args):
             json.dump(out, f, indent=1)
     ok = all(v["replays_match_eager"] for r in results for v in r["arms"].values())
     return 0 if ok else 1
+
+
+def persistent_sweep(sdt, torch, inputs, dev, num_cu, shapes, grids, args):
+    """The ping-pong kernel (rung 0's deep pipeline) with each persistent grid
+    size that does not exceed the tile count (0: one workgroup per tile),
+    graph-timed, in alternating rounds so that clock drift spreads over the
+    arms alike."""
+    results = []
+    for (M, N, K) in shapes:
+        kp, np_ = -(-K // 8) * 8, -(-N // 8) * 8
+        A = torch.zeros((M, kp), dtype=torch.float16, device=dev)[:, :K]
+        B = torch.zeros((N, kp), dtype=torch.float16, device=dev)[:, :K]
+        A.copy_(torch.from_numpy(inputs.uniform_f16((M, K), 11)))
+        B.copy_(torch.from_numpy(inputs.uniform_f16((N, K), 12)))
+        C = torch.empty((M, np_), dtype=torch.float16, device=dev)[:, :N]
+        flop = 2.0 * M * N * K
+        chain = max(4, min(400, int(2e12 / max(flop, 1.0))))
+        tiles = -(-M // 256) * -(-N // 256)
+        arms = [g for g in grids if g <= tiles]
+        row = {"M": M, "N": N, "K": K, "tiles": tiles, "arms": {}}
+        samples = {g: [] for g in arms}
+        same = True
+        for _ in range(3):
+            for g in arms:
+                med, allv, ok = time_rung(sdt, torch, A, B, C, 0, -1, chain, args.repeats,
+                                          kgroups=1, stages=3, persistent=g)
+                samples[g] += allv
+                same = same and ok
+        for g in arms:
+            v = sorted(samples[g])
+            row["arms"][g] = {"us": round(v[len(v) // 2], 3), "min_us": round(v[0], 3),
+                              "max_us": round(v[-1], 3)}
+        row["replays_match_eager"] = same
+        print(f"{M}x{N}x{K} ({tiles} tiles): " + "  ".join(
+            f"P={g}: {row['arms'][g]['us']:.2f} [{row['arms'][g]['min_us']:.2f}, "
+            f"{row['arms'][g]['max_us']:.2f}]" for g in arms), flush=True)
+        results.append(row)
+    if args.out:
+        with open(args.out, "w") as f:
+            json.dump({"num_cu": num_cu, "shapes": results}, f, indent=1)
+    return 0 if all(r["replays_match_eager"] for r in results) else 1
 
 
 if __name__ == "__main__":

@@ -84,7 +84,13 @@ def assert_bitexact(gpu16, ref):
     want = oracle.f16_encode_rne(ref)
     got = np.ascontiguousarray(gpu16).view(np.uint16)
     diff = got != want
-    assert not diff.any(), f"{int(diff.sum())} of {got.size} differ from the RNE oracle"
+    if diff.any():
+        g = np.ascontiguousarray(gpu16).astype(np.float64)
+        nan = int(np.isnan(g[diff]).sum())
+        idx = np.argwhere(diff)
+        raise AssertionError(f"{int(diff.sum())} of {got.size} differ from the RNE oracle "
+                             f"({nan} NaN, i.e. never written); first at {idx[0].tolist()}, "
+                             f"last at {idx[-1].tolist()}")
 
 
 def sample_positions(M, N, rows=32, cols=32, extra=4096, seed=0):

@@ -459,8 +459,8 @@ def test_ksplit_plan_rules():
     gemm_f16's; with room it splits K on the rungs built for it while the
     grid leaves CUs idle: the most splits that keep tiles x splits within the
     CU count, each with at least two full k-tiles, at most 16; the stagger is
-    then off.  The workspace it reports is the counters (one int per tile and
-    wave, rounded up to 256 bytes) plus the fp32 partial tiles."""
+    then off.  The workspace it reports is the fixed 64 KiB counter area plus
+    the fp32 partial tiles."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (1536, 1536, 1536), (2048, 2048, 2048), (4096, 4096, 4096), (300, 260, 1000),
@@ -480,8 +480,7 @@ def test_ksplit_plan_rules():
                 assert need == 0 and big == plain
                 continue
             assert big["stagger"] == 0 and big["split_algo"] == 1
-            counters = -(-(ntile * t["waves_m"] * t["waves_n"] * 4) // 256) * 256
-            assert need == counters + ntile * s * t["bm"] * t["bn"] * 4
+            assert need == 65536 + ntile * s * t["bm"] * t["bn"] * 4
             assert sdt.pick_tile_ws(M, N, K, num_cu, need) == big
             assert sdt.pick_tile_ws(M, N, K, num_cu, need - 1)["splits"] == 1
 

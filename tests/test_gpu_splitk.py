@@ -158,7 +158,7 @@ def test_forced_split_needs_workspace_and_a_split_rung():
     C = torch.zeros((512, 512), dtype=torch.float16, device=DEV)
     need = sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=4, split_algo=1,
                                      stages=-1, kgroups=-1, stagger=0, persistent=-1)
-    assert need == 64 * 4 * 4 + 64 * 4 * 64 * 64 * 4   # counters (64 tiles x 4 waves) + partials
+    assert need == 65536 + 64 * 4 * 64 * 64 * 4   # the counter area + 64 tiles x 4 splits
     bad = [dict(tile_id=4, splits=4, workspace=None),
            dict(tile_id=4, splits=4, workspace=_ws(need - 16)),
            dict(tile_id=0, splits=2, workspace=_ws(64 << 20)),
@@ -263,3 +263,22 @@ def test_bf16_split_integer_and_uniform():
     got = oracle.bf16_decode(dev_bf16_to_bits(C))
     refu = oracle.gemm(Au, Bu, dtype="bf16")
     assert (np.abs(got - refu) <= oracle.tolerance(refu, "bf16")).all()
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace serving k-split launches of different shapes in turn
+    (few tiles, then many, then few): the partial sums of one launch never
+    land in the counter area another relies on, so every launch is bit for
+    bit right and the counters end at zero."""
+    sdt = _sdt()
+    ws = _ws(64 << 20)
+    for (M, N, K, tile, sp) in [(128, 128, 1024, 3, 8), (700, 650, 1000, 4, 7),
+                                (256, 128, 2048, 2, 16), (900, 1000, 768, 4, 3),
+                                (64, 64, 512, 4, 8)]:
+        A = inputs.integer_f16((M, K), 351 + M)
+        B = inputs.integer_f16((N, K), 352 + N)
+        say(f"workspace reuse {M}x{N}x{K} tile={tile} splits={sp}")
+        C, pad_ok = _launch(to_dev(A), to_dev(B), ws, tile_id=tile, splits=sp, split_algo=1)
+        assert pad_ok
+        assert_bitexact(C, oracle.gemm(A, B))
+    assert _counters_zero(ws, 65536)
