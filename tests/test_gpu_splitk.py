@@ -92,7 +92,7 @@ def test_integer_exact_every_split(shape):
                     assert_bitexact(C, ref)
                     tried += 1
     assert tried >= 24
-    assert _counters_zero(ws, 1 << 20), "arrival counters not left at zero"
+    assert _counters_zero(ws, 65536), "arrival counters not left at zero"
 
 
 @pytest.mark.parametrize("n", [256, 512, 768, 1024, 1536, 2048])
