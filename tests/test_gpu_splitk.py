@@ -91,7 +91,7 @@ def test_integer_exact_every_split(shape):
                     assert pad_ok
                     assert_bitexact(C, ref)
                     tried += 1
-    assert tried >= 24
+    assert tried >= 3 * 3 * 2 * len(_split_counts(K))   # 3 rungs x 3+ pipelines x 2 reductions
     assert _counters_zero(ws, 65536), "arrival counters not left at zero"
 
 
