@@ -146,7 +146,7 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
  * sdt_gemm_workspace_size(M, N, K, 0) bytes for the split plan (smaller, or
  * NULL with 0: the call runs gemm_f16's plan, unsplit, and touches no
  * workspace).  Layout: the first 64 KiB hold arrival counters (one int per
- * output tile and wave, so a split launch has at most 16384 / waves tiles),
+ * output tile, so a split launch has at most 16384 tiles),
  * the fp32 partial sums follow.  The counter area must be zero before the
  * first call that uses the workspace (sdt_workspace_init); every call leaves
  * it zero again, whatever its shape.  One workspace serves one call at a

@@ -460,35 +460,45 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_slot(const GemmParams&
     return make_rsrc(p.ws + idx * slot_floats, (uint32_t)slot_floats * 4);
 }
 
-// The single-kernel k-split reduction, per wave: store this split's partial
-// sums, make them visible at agent scope (a release fence: the XCDs' L2s are
-// separate caches, so the wave's dirty lines are written back and its stores
-// waited for), then count the arrival on the (tile, wave) counter with an
-// agent-scope atomic.  The wave that arrives last returns true and owns the
-// block: an acquire fence (which invalidates what its L2 may hold of the
-// other splits' slots), then it clears the counter for the next launch and
-// forms
+// The single-kernel k-split reduction, per workgroup.  Every wave of the
+// workgroup has stored its part of this split's partial sums (with the
+// device-scope bit: written through to memory).  A workgroup barrier (each
+// wave waits for its stores first), then one thread makes them visible at
+// agent scope (a release fence: the XCDs' L2s are separate caches, so the
+// XCD's dirty lines are written back) and counts the arrival on the tile's
+// counter with an agent-scope atomic.  The workgroup that arrives last owns
+// the tile: its counting thread takes an acquire fence (which invalidates
+// what the CU and XCD caches hold of the other splits' slots) and clears the
+// counter for the next launch; after a second barrier its waves form
 //   acc = ((P_0 + P_1) + P_2) + ... + P_{splits-1}
-// in that order, whichever split it holds (fp32 addition is commutative, so
-// adding its own P_split to the running sum of P_0 .. P_{split-1} gives the
-// same bits as the opposite operand order): the result does not depend on
-// the order of arrival.  The others return false and are done.  The
-// partials are also stored and loaded with the device-scope bit (written
-// through to memory, so the release has little to write back).  No wave
-// waits for another: nothing spins.
+// in that order, whichever split they hold (fp32 addition is commutative, so
+// adding their own P_split to the running sum of P_0 .. P_{split-1} gives
+// the same bits as the opposite operand order): the result does not depend
+// on the order of arrival.  The other workgroups are done.  No workgroup
+// waits for another: nothing spins.  `active` = false for waves that hold
+// no accumulators (a second k-group): they take the two barriers only.
+// Returns whether the calling wave owns its block.
 template <int FN, int FM, typename acc_t>
 __device__ __forceinline__ bool splitk_arrive(const GemmParams& p, acc_t (&acc)[FN][FM], int tile,
-                                              int split, int wave, int nwaves, int lane) {
+                                              int split, int wave, int nwaves, int lane,
+                                              bool active, int* flag) {
     constexpr int SLOT = FN * FM * (int)(sizeof(acc_t) / 4) * 64;
-    store_partial<kScopeDevice>(acc, partial_slot(p, tile, split, wave, nwaves, SLOT), lane);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    int* counter = p.cnt + (int64_t)tile * nwaves + wave;
-    int old = 0;
-    if (lane == 0) old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __builtin_amdgcn_readfirstlane(old);
-    if (old != p.splits - 1) return false;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (lane == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (active)
+        store_partial<kScopeDevice>(acc, partial_slot(p, tile, split, wave, nwaves, SLOT), lane);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        int* counter = p.cnt + tile;
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = old == p.splits - 1;
+        if (last) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *flag = last;
+    }
+    __syncthreads();
+    if (!active || !*flag) return false;
     if (split == 0) {
         for (int s = 1; s < p.splits; ++s)
             load_partial<kScopeDevice, true>(acc, partial_slot(p, tile, s, wave, nwaves, SLOT), lane);
@@ -544,9 +554,16 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
                   "each wave loads whole 8-row slabs");
     static_assert(NS >= 2 && NS * STAGE * 16 <= 160 * 1024, "stages must fit the LDS");
     static_assert(KS == 1 || BM * BN * 4 <= NS * STAGE * 16, "k-group partials fit the LDS");
+    static_assert(WM * WN * (KS > 1 && MF == 32 ? (BM / WM / MF) * (BN / WN / MF) : 1) * 256 <
+                      NS * STAGE && (KS == 1 || BM * BN / 4 < NS * STAGE),
+                  "the last LDS unit is free after the k-loop");
     constexpr int L = A_DMA + B_DMA;   // global loads per wave per k-tile
 
     __shared__ int4_t smem[NS * STAGE];
+    // The k-split arrival's verdict for the workgroup, in the last LDS unit:
+    // by then every k-step's reads are done, and neither the k-group sums nor
+    // the staged epilogue reach that far.
+    int* const splitk_flag = reinterpret_cast<int*>(smem + NS * STAGE - 1);
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -787,7 +804,14 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
                         red[((wmn * FN * FM + i2 * FM + j) * 16 + e) * 64 + lane] = acc[i2][j][e];
         }
         __syncthreads();
-        if (kg == 1) return;
+        if (kg == 1) {
+            // the single-kernel k-split reduction's barriers are taken by every wave
+            if constexpr (SK) {
+                if (p.splits > 1 && p.split_algo != 0)
+                    splitk_arrive(p, acc, 0, 0, 0, NMN, lane, false, splitk_flag);
+            }
+            return;
+        }
 #pragma unroll
         for (int i2 = 0; i2 < FN; ++i2)
 #pragma unroll
@@ -805,7 +829,7 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
                 store_partial<0>(acc, partial_slot(p, tile, split, wmn, NMN, SLOT), lane);
                 return;
             }
-            if (!splitk_arrive(p, acc, tile, split, wmn, NMN, lane)) return;
+            if (!splitk_arrive(p, acc, tile, split, wmn, NMN, lane, true, splitk_flag)) return;
         }
     }
 

@@ -194,7 +194,7 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
         Plan t = pl;
         t.stagger = 0;
         t.splits = splits_for(t, M, N, K, num_cu);
-        const int64_t counters = ceil_div(M, d.bm) * ceil_div(N, d.bn) * d.waves_m * d.waves_n;
+        const int64_t counters = ceil_div(M, d.bm) * ceil_div(N, d.bn);
         if (t.splits > 1 && workspace_bytes(t, M, N) <= ws_bytes && counters <= kCounterBytes / 4)
             pl = t;
     }
@@ -221,9 +221,8 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
     int st = check_plan(pl, K);
     if (st != SDT_OK) return st;
     if (pl.persistent > ceil_div(M, d.bm) * ceil_div(N, d.bn)) return SDT_ERR_INVALID_ARG;
-    // one arrival counter per tile and wave of a k-group must fit the counter area
-    if (pl.splits > 1 &&
-        ceil_div(M, d.bm) * ceil_div(N, d.bn) * d.waves_m * d.waves_n > kCounterBytes / 4)
+    // one arrival counter per tile must fit the counter area
+    if (pl.splits > 1 && ceil_div(M, d.bm) * ceil_div(N, d.bn) > kCounterBytes / 4)
         return SDT_ERR_UNSUPPORTED;
     if (pl.splits > 1 && workspace_bytes(pl, M, N) > (ws_bytes < 0 ? 0 : ws_bytes))
         return SDT_ERR_INVALID_ARG;

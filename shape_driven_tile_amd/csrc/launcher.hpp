@@ -88,7 +88,7 @@ constexpr int kSplitMinKTilesPerSplit = 2;
 // tile (one launch).
 constexpr int kSplitAlgoAuto = 1;
 // Bytes at the start of a k-split workspace that hold the arrival counters
-// (one int per output tile and wave of a k-group: at most 16384).
+// (one int per output tile: at most 16384 tiles).
 constexpr int64_t kCounterBytes = 64 * 1024;
 
 // How one product is launched: rung, LDS stages, k-groups of waves, k-loop

@@ -210,21 +210,29 @@ def split_sweep(sdt, torch, inputs, dev, num_cu, shapes, split_counts, args):
                 for (stages, kg) in pipes:
                     for algo in ((0, 1) if sp > 1 else (0,)):
                         key = f"t{tile}_s{sp}_a{algo}_st{stages}_kg{kg}"
-                        med, allv, same = time_rung(sdt, torch, A, B, C, tile, 0, chain,
-                                                    args.repeats, kgroups=kg, ws=ws, splits=sp,
-                                                    split_algo=algo, stages=stages)
+                        try:
+                            med, allv, same = time_rung(sdt, torch, A, B, C, tile, 0, chain,
+                                                        args.repeats, kgroups=kg, ws=ws,
+                                                        splits=sp, split_algo=algo, stages=stages)
+                        except sdt.SdtError as e:
+                            row["arms"][key] = {"refused": str(e)}
+                            continue
                         row["arms"][key] = {"us": round(med, 3), "min_us": round(allv[0], 3),
                                             "max_us": round(allv[-1], 3),
                                             "replays_match_eager": same}
-        best = sorted(row["arms"].items(), key=lambda kv: kv[1]["us"])[:6]
-        print("    best: " + "  ".join(f"{k} {v['us']:.2f}" for k, v in best), flush=True)
+        timed = [(k, v) for k, v in row["arms"].items() if "us" in v]
+        for k, v in sorted(timed, key=lambda kv: kv[1]["us"]):
+            print(f"    {k:28s} {v['us']:8.2f} [{v['min_us']:.2f}, {v['max_us']:.2f}]", flush=True)
         results.append(row)
+        if args.out:
+            with open(args.out, "w") as f:
+                json.dump({"num_cu": num_cu, "shapes": results}, f, indent=1)
     out = {"num_cu": num_cu, "device": torch.cuda.get_device_properties(dev).name,
            "shapes": results}
     if args.out:
         with open(args.out, "w") as f:
             json.dump(out, f, indent=1)
-    ok = all(v["replays_match_eager"] for r in results for v in r["arms"].values())
+    ok = all(v.get("replays_match_eager", True) for r in results for v in r["arms"].values())
     return 0 if ok else 1
 
 
