@@ -563,6 +563,34 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     log(f"decode read ceiling: median {med_r:.2f} us = "
         f"{det['decode_read_ceiling']['GBps_median']} GB/s; the GEMV reaches "
         f"{100 * med_r / med:.1f}% of it")
+    # An independent streaming-read reference: a grid-stride read (a plain
+    # bandwidth-test pattern, not either GEMV's) over the same rotation, with
+    # 32 workgroups of 256 threads per CU.
+    nwg = 32 * props_cus(torch, dev)
+    words_g = torch.empty(nwg, dtype=torch.int32, device=dev)
+    rg = (lambda j: sdt.stream_read_grid(Ws[j % len(Ws)], words_g, nwg))
+    t0 = time.time()
+    j = 0
+    while time.time() - t0 < 1.0:
+        rg(j)
+        j += 1
+        if j % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    us_g = time_launches(torch, rg, 200)
+    med_g = sorted(us_g)[len(us_g) // 2]
+    det["decode_read_ceiling_grid"] = {
+        "us": _ranges(us_g),
+        "GBps_median": round(bytes_gemv / (med_g * 1e-6) / 1e9, 1),
+        "hbm_frac_median": round(bytes_gemv / (med_g * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "gemv_frac_of_ceiling_median": round(med_g / med, 4),
+        "kernel": f"sdt_stream_read_grid: {nwg} workgroups of 256 threads, grid-stride, four "
+                  "non-temporal 16-byte loads per lane per pass",
+        "protocol": "the same 8 rotating weight buffers, 1 s warm, 200 launches x 10 repeats",
+    }
+    log(f"decode grid-stride read ceiling: median {med_g:.2f} us = "
+        f"{det['decode_read_ceiling_grid']['GBps_median']} GB/s; the GEMV reaches "
+        f"{100 * med_g / med:.1f}% of it")
 
     # The same decode product with the weights stored as K rows of N (the
     # pages' B-layout): gated against the oracle, then the same cold protocol
@@ -606,7 +634,61 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
                                          "200 launches x 10 repeats, event-timed")
     det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)
+    det["ksplit"] = detail_ksplit(sdt, torch, np, inputs, oracle, dev)
     return det
+
+
+def props_cus(torch, dev):
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
+# shapes of the k-split detail: long k-loops over few output tiles, where the
+# workspace entry point splits K, and two of the benchmarked squares, where
+# it does not (its plan is gemm_f16's)
+KSPLIT_SHAPES = ((256, 256, 16384), (128, 128, 65536), (512, 512, 8192), (384, 384, 12288),
+                 (1024, 1024, 1024), (1536, 1536, 1536))
+
+
+def detail_ksplit(sdt, torch, np, inputs, oracle, dev):
+    """gemm_f16 against gemm_f16_ws (k-split across workgroups where its plan
+    takes one) on the same inputs: every element gated against the oracle,
+    then both graph-timed."""
+    out = {}
+    for (M, N, K) in KSPLIT_SHAPES:
+        A = inputs.uniform_f16((M, K), 61)
+        B = inputs.uniform_f16((N, K), 62)
+        dA = torch.from_numpy(A).to(dev)
+        dB = torch.from_numpy(B).to(dev)
+        C = torch.empty((M, N), dtype=torch.float16, device=dev)
+        need = sdt.gemm_workspace_size(M, N, K)
+        ws = sdt.Workspace(max(need, 16), device=dev)
+        plan = sdt.pick_tile_ws(M, N, K, 0, ws.nbytes)
+        C.fill_(float("nan"))
+        sdt.gemm_f16_ws(dA, dB, C, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.gemm(A, B)
+        bad = int((~(np.abs(C.cpu().numpy().astype(np.float64) - ref) <=
+                     oracle.tolerance(ref))).sum())
+        key = f"{M}x{N}x{K}"
+        if bad:
+            out[key] = {"gate": f"{bad} outside tolerance"}
+            log(f"k-split {key}: PARITY FAILED ({bad}), not timed")
+            continue
+        flop = 2.0 * M * N * K
+        chain = max(4, min(200, int(2e12 / flop)))
+        us_p, _ = graph_launches(torch, (lambda j: sdt.gemm_f16(dA, dB, C)), chain)
+        us_w, _ = graph_launches(torch, (lambda j: sdt.gemm_f16_ws(dA, dB, C, workspace=ws)), chain)
+        mp, mw = sorted(us_p)[len(us_p) // 2], sorted(us_w)[len(us_w) // 2]
+        out[key] = {"gate": "pass (every element)", "gemm_f16_us": _ranges(us_p),
+                    "gemm_f16_ws_us": _ranges(us_w),
+                    "plan_ws": {k: plan[k] for k in ("id", "splits", "split_algo", "stages",
+                                                     "kgroups")},
+                    "workspace_bytes": need, "speedup_median": round(mp / mw, 3),
+                    "timing": f"graph replay, {chain} launches x 10"}
+        log(f"k-split {key}: gemm_f16 {mp:.2f} us, gemm_f16_ws {mw:.2f} us "
+            f"(splits {plan['splits']})")
+        del dA, dB, C, ws
+    return out
 
 
 def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):

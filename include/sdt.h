@@ -100,7 +100,7 @@ typedef struct sdt_launch {
     int kgroups;     /* 1, or 2 on rungs built with two (needs the deep or long
                         count) */
     int stagger;     /* 0 off, 1 on (power-of-two full k-tile count only) */
-    int splits;      /* 1 none; s in [2, 16] on a ksplit rung: K split over s
+    int splits;      /* 1 none; s in [2, 64] on a ksplit rung: K split over s
                         workgroups per tile (at most one per full k-tile, no
                         stagger), needs the workspace sdt_launch_workspace_size
                         reports */
@@ -137,11 +137,14 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
 /* gemm_f16 with a workspace, which lets the plan split the k-loop across
  * workgroups ("Iteratively Tuning hipBLASLt TensileLite Kernels", The Six
  * Rounds, 2: splitting K is how shapes that cannot fill the device get work).
- * When the grid of gemm_f16's tile leaves CUs idle and K is long enough, each
- * output tile's k-tiles are divided into `splits` contiguous runs, one
- * workgroup each; their fp32 partial sums go to the workspace and are added
- * in split order, ((P_0 + P_1) + P_2) + ..., before the single rounding to
- * fp16, so the result is deterministic (no atomics on the data).
+ * When the grid of gemm_f16's tile leaves CUs idle and the k-loop is long
+ * (each split keeps at least 16 full k-tiles: on MI355X shorter loops ran
+ * slower split), each output tile's k-tiles are divided into `splits`
+ * contiguous runs, one workgroup each, with splits = min(CUs / tiles,
+ * full k-tiles / 16, 64); their fp32 partial sums go to the workspace and a
+ * second kernel adds them in split order, ((P_0 + P_1) + P_2) + ..., before
+ * the single rounding to fp16, so the result is deterministic (no atomics on
+ * the data).  Example: 256 x 256 x 16384 runs 16 splits of 64 x 64 tiles.
  * workspace: device memory owned by the caller, 16-byte aligned, at least
  * sdt_gemm_workspace_size(M, N, K, 0) bytes for the split plan (smaller, or
  * NULL with 0: the call runs gemm_f16's plan, unsplit, and touches no
@@ -260,8 +263,11 @@ int gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
                  int tile_id, int stagger);
 
 /* gemv_f16_m1 with the kernel instantiation forced: variant in
- * [0, sdt_gemv_num_variants()) selects how many output columns one wave
- * streams (variant 0 is what gemv_f16_m1 uses).  Same result definition. */
+ * [0, sdt_gemv_num_variants()).  Variant 0, what gemv_f16_m1 uses: one column
+ * per workgroup of four waves splitting K.  Variants 1-4: one wave streams 1,
+ * 2, 4 or 8 whole columns (these four add in the same order and agree bit
+ * for bit; variant 0 adds the same products in another order).  Same result
+ * definition. */
 int gemv_f16_m1_ex(int64_t N, int64_t K, const void* x,
                    const void* B, int64_t ldb, void* y, void* stream,
                    int variant);
@@ -348,6 +354,20 @@ int sdt_empty_kernel(void* stream);
  * runs), buf not 16-byte aligned or out not 4-byte aligned.  SDT_ERR_HIP: the
  * launch failed. */
 int sdt_stream_read(const void* buf, int64_t bytes, void* out, void* stream);
+
+/* Measurement: enqueue a grid-stride read-only kernel over `bytes` bytes at
+ * `buf`: `workgroups` workgroups of 256 threads, each pass reading 4 KB per
+ * workgroup with four non-temporal 16-byte loads per lane, striding by the
+ * whole grid (a plain bandwidth-test pattern, unlike either GEMV's).  Writes
+ * one 32-bit word per workgroup to out[0 .. workgroups) (device,
+ * caller-owned), with no meaning beyond keeping the loads live.  It gives a
+ * streaming-read ceiling independent of the GEMV kernels' own access pattern.
+ * bytes == 0: SDT_OK, nothing enqueued.  SDT_ERR_INVALID_ARG: bytes < 0, a
+ * null pointer or workgroups <= 0.  SDT_ERR_UNSUPPORTED: bytes not a
+ * multiple of 16, buf not 16-byte or out not 4-byte aligned.  SDT_ERR_HIP:
+ * the launch failed. */
+int sdt_stream_read_grid(const void* buf, int64_t bytes, void* out, int workgroups,
+                         void* stream);
 
 /* Host-only argument check used by gemv_f16_m1_kn before anything is
  * enqueued (the status it would return for these arguments). */

@@ -30,7 +30,7 @@ EXPORTS = (
     "sdt_plan_tile",
     "gemm_f16_cfg", "gemm_bf16_cfg",
     "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
-    "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
+    "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version", "sdt_stream_read_grid",
 )
 
 # The include/sdt.h version these structures and signatures follow.
@@ -115,6 +115,7 @@ def lib():
     L.sdt_workspace_init.argtypes = [_vp, _i64, _vp]
     L.sdt_pick_tile_ws.argtypes = [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(SdtTile)]
     L.sdt_abi_version.argtypes = []
+    L.sdt_stream_read_grid.argtypes = [_vp, _i64, _vp, _int, _vp]
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -132,7 +133,7 @@ def lib():
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
                  "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
                  "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
-                 "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
+                 "sdt_stream_read_grid", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
         getattr(L, name).restype = _int
     if L.sdt_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
@@ -349,6 +350,20 @@ def stream_read(buf, out, stream=None) -> None:
     rc = lib().sdt_stream_read(buf.data_ptr(), nbytes, out.data_ptr(), _stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, "sdt_stream_read")
+
+
+def stream_read_grid(buf, out, workgroups: int, stream=None) -> None:
+    """Enqueue the library's grid-stride read-only kernel over the bytes of the
+    contiguous device tensor `buf`; `out` holds at least `workgroups` int32
+    words."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or not out.is_contiguous() or \
+            out.numel() * out.element_size() < 4 * int(workgroups):
+        raise ValueError("stream_read_grid: contiguous buf, and out of one int32 word per workgroup")
+    rc = lib().sdt_stream_read_grid(buf.data_ptr(), nbytes, out.data_ptr(), int(workgroups),
+                                    _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_stream_read_grid")
 
 
 def empty_kernel(stream=None) -> None:

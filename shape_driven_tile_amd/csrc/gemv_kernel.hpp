@@ -170,6 +170,61 @@ __global__ __launch_bounds__(WPB * 64) void gemv_m1_kernel(GemvParams p) {
     }
 }
 
+// One output column per workgroup of WPC waves.  The column's 512-element
+// chunks (64 lanes x 8 fp16, 1 KB) are dealt round-robin over the waves, wave
+// q taking chunks q, q + WPC, ..., XCH of them in flight per trip; each wave
+// adds its chunks per lane, reduces across its lanes, and the WPC wave sums
+// are added in wave order through LDS (a fixed order: deterministic).  On
+// the decode shape (K = 4096) a workgroup of 4 waves reads its column's 8 KB
+// as 2 KB per wave, two 16-byte loads per lane: measured against one wave
+// per column (8 KB, eight loads per lane), 15.55-15.62 against 15.73-15.85 us
+// on one box (cold, 8 rotating buffers), the finer workgroups keeping more
+// CUs streaming while the last columns drain.
+template <typename Elt, int WPC, int XCH>
+__global__ __launch_bounds__(WPC * 64) void gemv_m1_wsplit_kernel(GemvParams p) {
+    const int lane = threadIdx.x & 63;
+    const int q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t n = blockIdx.x;
+    const uint16_t* row = p.B + n * p.ldb;
+    const int nch = p.K >> 9;                 // full chunks
+    float acc = 0.0f;
+    for (int c0 = q; c0 < nch; c0 += WPC * XCH) {
+        int4_t w[XCH], xr[XCH];
+        if (c0 + (XCH - 1) * WPC < nch) {     // a whole trip (uniform): plain loads
+#pragma unroll
+            for (int j = 0; j < XCH; ++j)
+                w[j] = __builtin_nontemporal_load(
+                    reinterpret_cast<const int4_t*>(row + (c0 + j * WPC) * 512 + lane * 8));
+#pragma unroll
+            for (int j = 0; j < XCH; ++j)
+                xr[j] = *reinterpret_cast<const int4_t*>(p.x + (c0 + j * WPC) * 512 + lane * 8);
+#pragma unroll
+            for (int j = 0; j < XCH; ++j) acc = dot8<Elt>(w[j], xr[j], acc);
+        } else {
+            for (int c = c0; c < nch; c += WPC)
+                acc = dot8<Elt>(__builtin_nontemporal_load(
+                                    reinterpret_cast<const int4_t*>(row + c * 512 + lane * 8)),
+                                *reinterpret_cast<const int4_t*>(p.x + c * 512 + lane * 8), acc);
+        }
+    }
+    if ((p.K & 511) && q == nch % WPC) {     // the ragged last chunk, element-exact
+        const int k = nch * 512 + lane * 8;
+        acc = dot8<Elt>(gemv_chunk(row, k, p.K, true), gemv_chunk(p.x, k, p.K, false), acc);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    __shared__ float part[WPC];
+    if (lane == 0) part[q] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float v = part[0];
+#pragma unroll
+        for (int r = 1; r < WPC; ++r) v += part[r];
+        const typename Elt::scalar h = (typename Elt::scalar)v;
+        p.y[n] = __builtin_bit_cast(uint16_t, h);
+    }
+}
+
 // ---- the same product with the weights as K rows of N ("B-layout") ---------
 //
 // y(n) = sum_k x(k) * B[k*ldb + n].  This is the layout the mojo-baro page

@@ -61,7 +61,7 @@ int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 
 // k-split of the automatic plan when a workspace is available: on a rung
 // built for it, while the grid leaves CUs idle, as many splits as keep the
-// grid within the CU count, each with at least kSplitMinKTilesPerSplit full
+// grid within the CU count, each with at least kSplitAutoMinKTiles full
 // k-tiles (at most kMaxSplits).  1 = no split.
 int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     const TileDesc& d = kLadder[p.tile];
@@ -70,7 +70,7 @@ int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
     const int64_t nfull = K / kBK;
     int64_t s = num_cu / tiles;
-    if (s > nfull / kSplitMinKTilesPerSplit) s = nfull / kSplitMinKTilesPerSplit;
+    if (s > nfull / kSplitAutoMinKTiles) s = nfull / kSplitAutoMinKTiles;
     if (s > kMaxSplits) s = kMaxSplits;
     return s >= 2 ? (int)s : 1;
 }
@@ -148,8 +148,8 @@ int check_plan(const Plan& p, int64_t K) {
     if (p.kgroups != 1 && p.kgroups != 2) return SDT_ERR_INVALID_ARG;
     if (p.kgroups == 2 && (d.kgroups < 2 || (p.stages != d.stages && !is_long)))
         return SDT_ERR_INVALID_ARG;
-    // k-split: rungs built for it, at most one split per full k-tile, never
-    // with the stagger
+    // k-split: rungs built for it, at most one split per full k-tile (and
+    // kMaxSplits), never with the stagger
     if (p.splits < 1 || p.splits > kMaxSplits) return SDT_ERR_INVALID_ARG;
     if (p.splits > 1 && (!d.ksplit || p.splits > K / kBK || p.stagger)) return SDT_ERR_INVALID_ARG;
     if (p.split_algo != 0 && p.split_algo != 1) return SDT_ERR_INVALID_ARG;

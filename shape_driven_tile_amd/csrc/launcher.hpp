@@ -80,13 +80,23 @@ constexpr int kSplitMinKTiles = 12;
 constexpr int64_t kStaggerMaxOperandBytes = int64_t(16) << 20;
 constexpr int kStaggerMinKTiles = 16;
 
-// Most workgroups one output tile's k-loop is split over, and the fewest
-// full k-tiles each split keeps.
-constexpr int kMaxSplits = 16;
-constexpr int kSplitMinKTilesPerSplit = 2;
-// How the automatic plan reduces a k-split: 1, the last workgroup of each
-// tile (one launch).
-constexpr int kSplitAlgoAuto = 1;
+// Most workgroups one output tile's k-loop is split over.
+constexpr int kMaxSplits = 64;
+// Fewest full k-tiles per split the automatic plan keeps.  Fitted on MI355X
+// (graph-timed sweep of every k-split rung, count, reduction and pipeline):
+// a split pays only where each workgroup's k-loop is long -- 128x128x65536
+// 162 -> 20 us, 256x256x16384 43.8 -> 13-16, 384x384x12288 36.8 -> 15.5,
+// 512x512x8192 24.5 -> 13.3 -- and loses everywhere with shorter loops
+// (1024^3 6.0 -> 11.6 at best, 1536^3 13.8 -> 22.6, 512^3 4.5 -> 6.9): the
+// partial sums make a second round trip through memory and the reduction
+// a second launch or a fence, which only a long k-loop earns back.
+constexpr int kSplitAutoMinKTiles = 16;
+// How the automatic plan reduces a k-split: 0, a second kernel.  The
+// single-kernel reduction (1) measured slower at the grid sizes the plan
+// makes (512x512x8192 split 4: 16.0 against 13.3 us; 256x256x16384 split 16:
+// 16.2 against 14.3): its agent-scope release fence writes back the XCD's L2
+// once per workgroup.
+constexpr int kSplitAlgoAuto = 0;
 // Bytes at the start of a k-split workspace that hold the arrival counters
 // (one int per output tile: at most 16384 tiles).
 constexpr int64_t kCounterBytes = 64 * 1024;

@@ -175,11 +175,13 @@ int fill_zero(uint16_t* C, int64_t ldc, int64_t M, int64_t N, hipStream_t stream
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
-// GEMV instantiations: rows per wave; the activations are held as 8 chunks
-// of 8 fp16 per lane (4096 k per pass).  One row per wave is the fastest on
-// the decode shape (cold, 8 rotating buffers), by 15-20% over two or four
-// rows per wave: more waves in flight beat more loads per wave.
-constexpr int kGemvRpw[] = {1, 2, 4, 8};
+// GEMV instantiations.  Variant 0 (gemv_f16_m1's): four waves per column
+// (gemv_m1_wsplit_kernel).  Variants 1-4: one wave streams 1, 2, 4 or 8
+// columns (gemv_m1_kernel; the activations held as 8 chunks of 8 fp16 per
+// lane, 4096 k per pass); among those one column per wave is the fastest on
+// the decode shape (cold, 8 rotating buffers), by 15-20% over two or four:
+// more waves in flight beat more loads per wave.
+constexpr int kGemvRpw[] = {0, 1, 2, 4, 8};
 constexpr int kGemvVariants = sizeof(kGemvRpw) / sizeof(kGemvRpw[0]);
 
 template <typename Elt, int RPW>
@@ -211,6 +213,12 @@ int launch_gemv(int variant, int64_t N, int64_t K, const void* x, const void* B,
     p.K = (int)K;
     hipError_t e;
     switch (kGemvRpw[variant]) {
+        case 0: {
+            void* args[] = {&p};
+            e = hipLaunchKernel(reinterpret_cast<const void*>(&gemv_m1_wsplit_kernel<Elt, 4, 2>),
+                                dim3((unsigned)N), dim3(256), args, 0, stream);
+            break;
+        }
         case 1: e = launch_gemv_rpw<Elt, 1>(p, stream); break;
         case 2: e = launch_gemv_rpw<Elt, 2>(p, stream); break;
         case 8: e = launch_gemv_rpw<Elt, 8>(p, stream); break;
@@ -336,6 +344,33 @@ __global__ __launch_bounds__(64) void stream_read_kernel(const int4_t* buf, uint
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
     if (lane == 0) out[blockIdx.x] = (uint32_t)x;
+}
+
+// Reads memory with a grid-stride loop, the access pattern of a plain
+// bandwidth test rather than of any GEMV here: a fixed grid of 256-thread
+// workgroups, each pass reading 4 KB per workgroup per load slot with four
+// non-temporal 16-byte loads per lane in flight, striding by the whole grid.
+// Folded into one word per workgroup so that no load is dead.
+__global__ __launch_bounds__(256) void stream_read_grid_kernel(const int4_t* buf, int64_t n16,
+                                                               uint32_t* out) {
+    int x = 0;
+    const int64_t stride = (int64_t)gridDim.x * 1024;
+    for (int64_t base = (int64_t)blockIdx.x * 1024; base < n16; base += stride) {
+        int4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = base + u * 256 + threadIdx.x;
+            v[u] = i < n16 ? __builtin_nontemporal_load(buf + i) : int4_t{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
+    __shared__ int wx[4];
+    if ((threadIdx.x & 63) == 0) wx[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)(wx[0] ^ wx[1] ^ wx[2] ^ wx[3]);
 }
 
 }  // namespace
@@ -529,6 +564,23 @@ extern "C" int sdt_stream_read(const void* buf, int64_t bytes, void* out, void* 
     void* args[] = {&b, &o};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sdt::stream_read_kernel),
                                    dim3((unsigned)(bytes / 8192)), dim3(64), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);
+}
+
+extern "C" int sdt_stream_read_grid(const void* buf, int64_t bytes, void* out, int workgroups,
+                                    void* stream) {
+    if (bytes == 0) return SDT_OK;
+    if (bytes < 0 || !buf || !out || workgroups <= 0) return SDT_ERR_INVALID_ARG;
+    if (bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(buf) & 15) != 0 ||
+        (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+        return SDT_ERR_UNSUPPORTED;
+    const sdt::int4_t* b = static_cast<const sdt::int4_t*>(buf);
+    int64_t n16 = bytes / 16;
+    uint32_t* o = static_cast<uint32_t*>(out);
+    void* args[] = {&b, &n16, &o};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sdt::stream_read_grid_kernel),
+                                   dim3((unsigned)workgroups), dim3(256), args, 0,
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);
 }

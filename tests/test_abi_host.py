@@ -458,13 +458,14 @@ def test_ksplit_plan_rules():
     """gemm_f16_ws's plan: without a workspace (or one too small) it is
     gemm_f16's; with room it splits K on the rungs built for it while the
     grid leaves CUs idle: the most splits that keep tiles x splits within the
-    CU count, each with at least two full k-tiles, at most 16; the stagger is
-    then off.  The workspace it reports is the fixed 64 KiB counter area plus
+    CU count, each with at least 16 full k-tiles, at most 64, reduced by a
+    second kernel; the stagger is then off.  The workspace it reports is the fixed 64 KiB counter area plus
     the fp32 partial tiles."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (1536, 1536, 1536), (2048, 2048, 2048), (4096, 4096, 4096), (300, 260, 1000),
-              (64, 64, 64), (100, 3000, 700), (512, 512, 8192), (128, 128, 65536)]
+              (64, 64, 64), (100, 3000, 700), (512, 512, 8192), (128, 128, 65536),
+              (256, 256, 16384), (384, 384, 12288), (768, 768, 8192), (64, 128, 1 << 20)]
     for num_cu in (80, 256):
         for (M, N, K) in shapes:
             plain = sdt.pick_tile(M, N, K, num_cu)
@@ -472,14 +473,14 @@ def test_ksplit_plan_rules():
             big = sdt.pick_tile_ws(M, N, K, num_cu, 1 << 40)
             t = tiles[plain["id"]]
             ntile = -(-M // t["bm"]) * -(-N // t["bn"])
-            s = min(num_cu // ntile, (K // 64) // 2, 16) if t["ksplit"] else 1
+            s = min(num_cu // ntile, (K // 64) // 16, 64) if t["ksplit"] else 1
             s = s if s >= 2 else 1
             assert big["id"] == plain["id"] and big["splits"] == s, (num_cu, M, N, K, big)
             need = sdt.gemm_workspace_size(M, N, K, num_cu)
             if s == 1:
                 assert need == 0 and big == plain
                 continue
-            assert big["stagger"] == 0 and big["split_algo"] == 1
+            assert big["stagger"] == 0 and big["split_algo"] == 0
             assert need == 65536 + ntile * s * t["bm"] * t["bn"] * 4
             assert sdt.pick_tile_ws(M, N, K, num_cu, need) == big
             assert sdt.pick_tile_ws(M, N, K, num_cu, need - 1)["splits"] == 1
@@ -502,7 +503,8 @@ def test_ksplit_and_persistent_cfg_refusals():
     assert call(512, 512, 1024, ws, need - 16, tile_id=4, splits=2) == bad      # too small
     assert call(512, 512, 1024, ws, big, tile_id=0, splits=2) == bad            # rung 0: no split
     assert call(512, 512, 1024, ws, big, tile_id=1, splits=2) == bad
-    assert call(512, 512, 1024, ws, big, tile_id=4, splits=17) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=65) == bad
+    assert call(512, 512, 1024, ws, big, tile_id=4, splits=17) == bad          # 16 full k-tiles
     assert call(512, 512, 1024, ws, big, tile_id=4, splits=0) == bad
     assert call(512, 512, 1024, ws, big, tile_id=4, splits=-2) == bad
     assert call(512, 512, 960, ws, big, tile_id=4, splits=16) == bad            # 15 full k-tiles
@@ -517,4 +519,4 @@ def test_ksplit_and_persistent_cfg_refusals():
     assert call(4096, 4096, 4096, None, 0, tile_id=0, persistent=257) == bad    # 256 tiles
     assert call(4096, 4096, 4096, None, 0, tile_id=0, persistent=-2) == bad
     with pytest.raises(sdt.SdtError):
-        sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=17)
+        sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=65)

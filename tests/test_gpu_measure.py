@@ -1,6 +1,6 @@
 """GPU tests of the library's measurement kernels (not part of the product's
-math): the empty kernel behind the launch floor and the read-only streaming
-kernel behind the decode shape's read ceiling.  The streaming kernel's output
+math): the empty kernel behind the launch floor and the two read-only streaming
+kernels behind the decode shape's read ceilings.  The streaming kernel's output
 words are exact (XOR of each 8 KB run's 32-bit words), so the test checks that
 every byte was read, in bounds, and nothing else was written."""
 import numpy as np
@@ -59,5 +59,49 @@ def test_stream_read_arguments():
         sdt.SDT_ERR_UNSUPPORTED
     assert L.sdt_stream_read(buf.data_ptr(), 8192, out.data_ptr() + 2, s) == \
         sdt.SDT_ERR_UNSUPPORTED
+    torch.cuda.synchronize()
+    assert (out.cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("nbytes,wgs", [(16, 1), (4096 * 16 + 48, 3), (8192 * 12288, 8192),
+                                        (1 << 20, 4096)])
+def test_stream_read_grid_words_exact(nbytes, wgs):
+    """The grid-stride read: the XOR of its per-workgroup words is the XOR of
+    every 32-bit word of the buffer (every byte read once, none past the
+    end: a 16-byte tail past a whole pass included), and nothing past the
+    last workgroup's word is written."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    rng = np.random.default_rng(7100 + wgs)
+    host = rng.integers(0, 256, size=nbytes, dtype=np.uint8)
+    buf = to_dev(host)
+    out = torch.full((wgs + 4,), -1, dtype=torch.int32, device=buf.device)
+    say(f"sdt_stream_read_grid bytes={nbytes} workgroups={wgs}")
+    sdt.stream_read_grid(buf, out, wgs)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.bitwise_xor.reduce(got[:wgs]) == np.bitwise_xor.reduce(host.view(np.int32))
+    assert (got[wgs:] == -1).all()
+
+
+def test_stream_read_grid_arguments():
+    import ctypes
+
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    L = sdt.lib()
+    buf = torch.zeros(4096, dtype=torch.uint8, device="cuda:0")
+    out = torch.zeros(4, dtype=torch.int32, device="cuda:0")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    p, o = buf.data_ptr(), out.data_ptr()
+    say("sdt_stream_read_grid argument checks (nothing enqueued)")
+    assert L.sdt_stream_read_grid(p, 0, o, 1, s) == sdt.SDT_OK
+    assert L.sdt_stream_read_grid(p, -16, o, 1, s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_grid(None, 16, o, 1, s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_grid(p, 16, None, 1, s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_grid(p, 16, o, 0, s) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_grid(p, 24, o, 1, s) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_stream_read_grid(p + 8, 16, o, 1, s) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_stream_read_grid(p, 16, o + 2, 1, s) == sdt.SDT_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert (out.cpu().numpy() == 0).all()

@@ -95,28 +95,34 @@ def test_integer_exact_every_split(shape):
     assert _counters_zero(ws, 65536), "arrival counters not left at zero"
 
 
-@pytest.mark.parametrize("n", [256, 512, 768, 1024, 1536, 2048])
-def test_uniform_automatic_plan(n):
-    """gemm_f16_ws's automatic plan on the square workloads (uniform [-1, 1]),
-    every element against the oracle; with a workspace too small for its
-    split it runs gemm_f16's plan, bit for bit."""
+@pytest.mark.parametrize("shape", [(256, 256, 256), (512, 512, 512), (1024, 1024, 1024),
+                                   (1536, 1536, 1536), (256, 256, 16384), (128, 128, 65536),
+                                   (512, 512, 8192), (384, 384, 12288), (200, 300, 20000)])
+def test_uniform_automatic_plan(shape):
+    """gemm_f16_ws's automatic plan (uniform [-1, 1]) on square workloads,
+    where it does not split, and on long-K ones, where it does: every element
+    against the oracle; with a workspace too small for its split it runs
+    gemm_f16's plan, bit for bit."""
     import torch
     sdt = _sdt()
-    A, B = inputs.square_operands(n, 1 if n > 256 else 0)
+    M, N, K = shape
+    A = inputs.uniform_f16((M, K), 361)
+    B = inputs.uniform_f16((N, K), 362)
     dA, dB = to_dev(A), to_dev(B)
-    need = sdt.gemm_workspace_size(n, n, n)
-    plan = sdt.pick_tile_ws(n, n, n, 0, 1 << 40)
+    need = sdt.gemm_workspace_size(M, N, K)
+    plan = sdt.pick_tile_ws(M, N, K, 0, 1 << 40)
     assert (need > 0) == (plan["splits"] > 1)
+    assert (plan["splits"] > 1) == (K >= 8192), plan
     ws = _ws(max(need, 16))
-    say(f"k-split automatic plan {n}^3 (splits={plan['splits']} algo={plan['split_algo']})")
+    say(f"k-split automatic plan {shape} (splits={plan['splits']} algo={plan['split_algo']})")
     C, pad_ok = _launch(dA, dB, ws)
     assert pad_ok
     assert_close(C, oracle.gemm(A, B))
     # no workspace (or too small): the unsplit plan, the same bits as gemm_f16
     small = _ws(16)
     C2, _ = _launch(dA, dB, small)
-    ldc = -(-n // 8) * 8
-    C3 = torch.empty((n, ldc), dtype=torch.float16, device=DEV)[:, :n]
+    ldc = -(-N // 8) * 8
+    C3 = torch.empty((M, ldc), dtype=torch.float16, device=DEV)[:, :N]
     sdt.gemm_f16(dA, dB, C3)
     torch.cuda.synchronize()
     assert np.array_equal(C2.view(np.uint16), C3.cpu().numpy().view(np.uint16))
@@ -163,7 +169,8 @@ def test_forced_split_needs_workspace_and_a_split_rung():
            dict(tile_id=4, splits=4, workspace=_ws(need - 16)),
            dict(tile_id=0, splits=2, workspace=_ws(64 << 20)),
            dict(tile_id=1, splits=2, workspace=_ws(64 << 20)),
-           dict(tile_id=4, splits=17, workspace=_ws(64 << 20)),
+           dict(tile_id=4, splits=17, workspace=_ws(64 << 20)),   # 16 full k-tiles
+           dict(tile_id=4, splits=65, workspace=_ws(64 << 20)),
            dict(tile_id=4, splits=16, stagger=1, workspace=_ws(64 << 20))]
     for kw in bad:
         with pytest.raises(sdt.SdtError) as e:
