@@ -190,8 +190,8 @@ int main() {
         check_gemm(dtype, 300, 260, 1000, s);     // several tiles, ragged edges, partial k-tile
         check_gemm(dtype, 1024, 1024, 1024, s);   // two k-groups of waves
         check_gemm(dtype, 1, 500, 777 / 8 * 8, s);   // M = 1 -> the streaming GEMV
-        check_gemm(dtype, 300, 260, 1000, s, true);   // K split across workgroups
-        check_gemm(dtype, 512, 512, 2048, s, true);
+        check_gemm(dtype, 300, 260, 8200, s, true);   // K split across workgroups (ragged)
+        check_gemm(dtype, 256, 256, 16384, s, true);
         check_gemv(dtype, false, 12288, 4096);
         check_gemv(dtype, true, 12288, 4096);
         check_gemv(dtype, true, 1001, 1003);
