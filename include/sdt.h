@@ -141,7 +141,7 @@ int gemm_f16(int64_t M, int64_t N, int64_t K,
  * (each split keeps at least 16 full k-tiles: on MI355X shorter loops ran
  * slower split), each output tile's k-tiles are divided into `splits`
  * contiguous runs, one workgroup each, with splits = min(CUs / tiles,
- * full k-tiles / 16, 64); their fp32 partial sums go to the workspace and a
+ * full k-tiles / 16, 16); their fp32 partial sums go to the workspace and a
  * second kernel adds them in split order, ((P_0 + P_1) + P_2) + ..., before
  * the single rounding to fp16, so the result is deterministic (no atomics on
  * the data).  Example: 256 x 256 x 16384 runs 16 splits of 64 x 64 tiles.

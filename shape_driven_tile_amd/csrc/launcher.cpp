@@ -62,7 +62,7 @@ int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N) {
 // k-split of the automatic plan when a workspace is available: on a rung
 // built for it, while the grid leaves CUs idle, as many splits as keep the
 // grid within the CU count, each with at least kSplitAutoMinKTiles full
-// k-tiles (at most kMaxSplits).  1 = no split.
+// k-tiles (at most kMaxSplitsAuto).  1 = no split.
 int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     const TileDesc& d = kLadder[p.tile];
     if (!d.ksplit || p.stagger) return 1;
@@ -71,7 +71,7 @@ int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     const int64_t nfull = K / kBK;
     int64_t s = num_cu / tiles;
     if (s > nfull / kSplitAutoMinKTiles) s = nfull / kSplitAutoMinKTiles;
-    if (s > kMaxSplits) s = kMaxSplits;
+    if (s > kMaxSplitsAuto) s = kMaxSplitsAuto;
     return s >= 2 ? (int)s : 1;
 }
 

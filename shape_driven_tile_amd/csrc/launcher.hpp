@@ -91,6 +91,10 @@ constexpr int kMaxSplits = 64;
 // partial sums make a second round trip through memory and the reduction
 // a second launch or a fence, which only a long k-loop earns back.
 constexpr int kSplitAutoMinKTiles = 16;
+// Most splits the automatic plan takes: the second kernel sums a tile's
+// partials in one workgroup, so its time grows with the count
+// (128x128x65536: 16 splits 24 us, 64 splits 32 us).
+constexpr int kMaxSplitsAuto = 16;
 // How the automatic plan reduces a k-split: 0, a second kernel.  The
 // single-kernel reduction (1) measured slower at the grid sizes the plan
 // makes (512x512x8192 split 4: 16.0 against 13.3 us; 256x256x16384 split 16:

@@ -458,7 +458,7 @@ def test_ksplit_plan_rules():
     """gemm_f16_ws's plan: without a workspace (or one too small) it is
     gemm_f16's; with room it splits K on the rungs built for it while the
     grid leaves CUs idle: the most splits that keep tiles x splits within the
-    CU count, each with at least 16 full k-tiles, at most 64, reduced by a
+    CU count, each with at least 16 full k-tiles, at most 16, reduced by a
     second kernel; the stagger is then off.  The workspace it reports is the fixed 64 KiB counter area plus
     the fp32 partial tiles."""
     tiles = ladder()
@@ -473,7 +473,7 @@ def test_ksplit_plan_rules():
             big = sdt.pick_tile_ws(M, N, K, num_cu, 1 << 40)
             t = tiles[plain["id"]]
             ntile = -(-M // t["bm"]) * -(-N // t["bn"])
-            s = min(num_cu // ntile, (K // 64) // 16, 64) if t["ksplit"] else 1
+            s = min(num_cu // ntile, (K // 64) // 16, 16) if t["ksplit"] else 1
             s = s if s >= 2 else 1
             assert big["id"] == plain["id"] and big["splits"] == s, (num_cu, M, N, K, big)
             need = sdt.gemm_workspace_size(M, N, K, num_cu)
