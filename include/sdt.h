@@ -163,6 +163,23 @@ int gemm_f16_ws(int64_t M, int64_t N, int64_t K,
                 void* C, int64_t ldc,
                 void* workspace, int64_t workspace_bytes, void* stream);
 
+/* gemm_f16_ws for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same plan and the same result bits as gemm_f16_ws with a workspace of
+ * sdt_gemm_workspace_size bytes, with the k-split workspace taken from a
+ * library-owned array of 16 MiB + 64 KiB per device (static device memory,
+ * held until the process ends; its address is looked up, and its counter
+ * area cleared by a kernel on `stream`, on the first call on each device).
+ * Calls no allocating routine.  A product whose plan needs more workspace
+ * than that array holds (only on a device with more than 256 CUs) returns
+ * SDT_ERR_UNSUPPORTED and enqueues nothing.  All calls on one device share
+ * the array: calls that overlap on one GPU (other streams, concurrent graph
+ * replays) race and must be ordered by the caller.  Otherwise as gemm_f16. */
+int gemm_f16_noalloc(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb,
+                     void* C, int64_t ldc, void* stream);
+
 /* Bytes of workspace gemm_f16_ws's automatic plan uses for this product on a
  * device with num_cu compute units (num_cu <= 0 reads the current device);
  * 0 when it does not split.  Negative sizes: -1. */

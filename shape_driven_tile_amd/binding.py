@@ -31,6 +31,7 @@ EXPORTS = (
     "gemm_f16_cfg", "gemm_bf16_cfg",
     "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
     "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version", "sdt_stream_read_grid",
+    "gemm_f16_noalloc",
 )
 
 # The include/sdt.h version these structures and signatures follow.
@@ -115,6 +116,7 @@ def lib():
     L.sdt_workspace_init.argtypes = [_vp, _i64, _vp]
     L.sdt_pick_tile_ws.argtypes = [_i64, _i64, _i64, _int, _i64, ctypes.POINTER(SdtTile)]
     L.sdt_abi_version.argtypes = []
+    L.gemm_f16_noalloc.argtypes = L.gemm_f16.argtypes
     L.sdt_stream_read_grid.argtypes = [_vp, _i64, _vp, _int, _vp]
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
@@ -133,7 +135,7 @@ def lib():
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
                  "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
                  "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
-                 "sdt_stream_read_grid", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
+                 "sdt_stream_read_grid", "gemm_f16_noalloc", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
         getattr(L, name).restype = _int
     if L.sdt_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
@@ -421,6 +423,13 @@ def _gemm_16_ws(entry, A, B, C, workspace, stream, dtype, extra=()):
                                _stream_handle(stream), *extra)
     if rc != SDT_OK:
         raise SdtError(rc, entry)
+
+
+def gemm_f16_noalloc(A, B, C, stream=None) -> None:
+    """gemm_f16_ws with the library's own per-device scratch as the workspace
+    (no allocation; calls overlapping on one GPU race)."""
+    import torch
+    _gemm_16("gemm_f16_noalloc", A, B, C, stream, torch.float16)
 
 
 def gemm_f16_ws(A, B, C, workspace=None, stream=None) -> None:

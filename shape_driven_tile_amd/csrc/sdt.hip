@@ -323,6 +323,48 @@ int gemm_impl(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
+// ---- the allocation-free k-split workspace ------------------------------------
+// gemm_f16_noalloc takes its k-split workspace from this array instead of the
+// caller: the 64 KiB counter area and the fp32 partial sums of the automatic
+// plan, which splits only grids of at most one workgroup per CU, i.e. at most
+// 256 x 64 KiB of partials on a 256-CU part.  Each device holds its own copy
+// (zero-filled when the code object is loaded) at its own address, taken once
+// per device by hipGetSymbolAddress; host code uses that address only (the
+// array's name is a host-side stand-in).
+constexpr int64_t kScratchBytes = kCounterBytes + (int64_t(16) << 20);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+struct ScratchSlot {
+    std::once_flag once;
+    void* ptr = nullptr;
+    hipError_t err = hipSuccess;
+    int st = SDT_OK;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// The current device's scratch address, set up on the first call on that
+// device (the device current): its address, then its counter area cleared by
+// a fill kernel on `stream` (the array starts zero-filled and every call
+// leaves the counters zero; the clear makes that independent of the load).
+int scratch_for_current_device(void** out, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail_hip(e);
+    if (dev < 0 || dev >= kMaxDevices) return SDT_ERR_UNSUPPORTED;
+    ScratchSlot& sl = g_scratch[dev];
+    std::call_once(sl.once, [&sl, stream] {
+        void* ptr = nullptr;
+        sl.err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (sl.err != hipSuccess) return;
+        sl.ptr = ptr;
+        sl.st = fill_words(static_cast<uint32_t*>(ptr), kCounterBytes / 4, stream);
+    });
+    if (sl.err != hipSuccess) return fail_hip(sl.err);
+    if (sl.st != SDT_OK) return sl.st;
+    *out = sl.ptr;
+    return SDT_OK;
+}
+
 // Does nothing: one workgroup, no memory access.  Timing it gives the
 // launch floor the small shapes are measured against.
 __global__ void empty_kernel() {}
@@ -432,6 +474,24 @@ extern "C" int gemm_bf16_cfg(int64_t M, int64_t N, int64_t K, const void* A, int
     if (!cfg) return SDT_ERR_INVALID_ARG;
     return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream, *cfg, false,
                                      workspace, workspace_bytes);
+}
+
+extern "C" int gemm_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
+                                const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
+    int st = sdt::check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
+    if (st != SDT_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    // the plan gemm_f16_ws makes with a workspace as large as it asks for
+    const int64_t need = (M <= 1 || N == 0 || K == 0) ? 0 : sdt_gemm_workspace_size(M, N, K, 0);
+    if (need < 0) return SDT_ERR_INVALID_ARG;
+    if (need > sdt::kScratchBytes) return SDT_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = sdt::scratch_for_current_device(&ws, s);
+        if (st != SDT_OK) return st;
+    }
+    return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream, sdt::kAuto, true, ws,
+                                    need > 0 ? sdt::kScratchBytes : 0);
 }
 
 extern "C" int64_t sdt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int num_cu) {
