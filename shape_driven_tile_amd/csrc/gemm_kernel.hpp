@@ -1138,7 +1138,14 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmParams p) {
         const int ntile = p.gm * p.gn;
         for (int v = blockIdx.x; v < ntile; v += gridDim.x) {
             if (v != (int)blockIdx.x) __syncthreads();
-            gemm_pp_tile<Elt>(p, v, smem);
+            // The strides pass through an empty asm each tile, so the tile's
+            // stride-derived load offsets are recomputed per tile instead of
+            // hoisted out of the loop and held across it: 27 spilled VGPRs
+            // instead of 34 (the per-tile code alone takes 250 of the 256 a
+            // wave has at two waves per SIMD, so the loop's state spills).
+            GemmParams q = p;
+            asm volatile("" : "+s"(q.lda), "+s"(q.ldb));
+            gemm_pp_tile<Elt>(q, v, smem);
         }
     } else {
         gemm_pp_tile<Elt>(p, blockIdx.x, smem);
