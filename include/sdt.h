@@ -57,7 +57,9 @@ typedef enum sdt_status {
  * section "The part that actually mattered" (tile shape as a compile-time
  * kernel parameter, each with its own warp layout). */
 typedef struct sdt_tile {
-    int id;          /* index in the ladder, 0 = largest tile */
+    int id;          /* rung index: 0-4 the ladder, largest tile first (256 x 256,
+                        256 x 128, 128 x 128, 128 x 64, 64 x 64); 5 the off-ladder
+                        96 x 96 tile (see sdt_pick_tile) */
     int bm, bn, bk;
     int waves_m, waves_n;
     int threads;     /* 64 * waves_m * waves_n * kgroups */
@@ -68,8 +70,9 @@ typedef struct sdt_tile {
                         of 4 waves one phase apart, A in 2 stages, B in 3.
                         On rungs 1 and 2 (256 x 128, 128 x 128) the deep count
                         with one k-group runs v_mfma_f32_16x16x32 (two 32-deep
-                        sub-steps per k-tile); every other launch runs
-                        v_mfma_f32_32x32x16.  The automatic plan takes the
+                        sub-steps per k-tile), and so does every pipeline
+                        of rung 5 (96 x 96, 48 x 48 per wave); every other
+                        launch runs v_mfma_f32_32x32x16.  The automatic plan takes the
                         long count (long_stages) in place of the deep one on a
                         rung that has it when the launch runs two k-groups and
                         K holds at least 48 full k-tiles */
@@ -124,8 +127,8 @@ typedef struct sdt_launch {
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
  * definition).  The tile is chosen by sdt_pick_tile from the device's CU
  * count.  The k-loop runs in plain k order except where the plan staggers it
- * (FlyDSL PR, Changes: workgroup w starts at k-tile w and wraps): on rungs
- * other than the ping-pong kernel, with a power-of-two count of at least 16
+ * (FlyDSL PR, Changes: workgroup w starts at k-tile w and wraps): on ladder
+ * rungs 1-4 (not the ping-pong kernel), with a power-of-two count of at least 16
  * full k-tiles, and A and B together within 16 MiB (2*K*(M+N) bytes), where
  * it measured 2-5% faster on MI355X; larger operands lose up to 49% with it
  * (sdt_plan_tile reports the choice). */
@@ -303,8 +306,13 @@ int sdt_gemv_kn_num_variants(void);
  * device with num_cu compute units (num_cu <= 0 reads the current device).
  * The rule compares the number of output blocks the grid produces with the
  * CU count ("Beating hipBLASLt on a Gaming GPU", "The part that actually
- * mattered"; ladder constants fitted on MI355X).  Touches no device when
- * num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
+ * mattered"; ladder constants fitted on MI355X): the ladder's pick is
+ * sdt_pick_rung over rungs 0-4 with rung r taken from
+ * (bm/64)(bn/64)(num_cu/2 + 1) 64 x 64 blocks up (the last rung below that).
+ * An off-ladder rung with a smaller tile replaces the pick when its grid has
+ * more workgroups than the pick's and at most num_cu: on MI355X the 96 x 96
+ * rung in place of 128 x 128 (e.g. 1536^3: 144 workgroups -> 256).
+ * Touches no device when num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
 
 /* Host-only: the plan gemm_f16_ws makes with a workspace of workspace_bytes
@@ -320,8 +328,9 @@ int sdt_pick_tile_ws(int64_t M, int64_t N, int64_t K, int num_cu, int64_t worksp
 int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
                   int rungs, const int64_t* min_blocks);
 
-/* Host-only: number of ladder rungs, and the description of rung tile_id
- * (with its deep pipeline; long_stages names its long one, if any). */
+/* Host-only: number of rungs (the ladder's and the off-ladder ones), and
+ * the description of rung tile_id (with its deep pipeline; long_stages names
+ * its long one, if any). */
 int sdt_num_tiles(void);
 int sdt_tile_info(int tile_id, sdt_tile* out);
 

@@ -517,14 +517,68 @@ __device__ __forceinline__ bool splitk_arrive(const GemmParams& p, acc_t (&acc)[
     return true;
 }
 
+// Epilogue of one wave whose 16 x 16 accumulator tiles (FN column tiles x FM
+// row tiles, MF = 16) span a width other than 64 columns: 16 rows at a time
+// through the wave's LDS (rows FN * 32 bytes, padded by 16 so consecutive rows
+// start on different banks), then 16 contiguous bytes per lane, a row's FN * 32
+// bytes stored by 2 FN lanes side by side.  Masked at the M and N edges.
+template <typename Elt, int FN, int FM>
+__device__ __forceinline__ void store_block_staged16(const GemmParams& p,
+                                                     const floatx4_t (&acc)[FN][FM], int64_t mb,
+                                                     int64_t nb, int lane, int4_t* stage) {
+    typedef typename Elt::vec4 vec4;
+    typedef typename Elt::scalar scalar;
+    constexpr int RB = FN * 32 + 16;   // staged row stride, bytes
+    constexpr int CPR = 2 * FN;        // 16-byte chunks per row
+    static_assert(16 * RB <= 4096, "16 staged rows fit the wave's 4 KB");
+    char* lds = reinterpret_cast<char*>(stage);
+    const int wr = lane & 15, wq = lane >> 4;
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {     // rows 16 j .. 16 j + 15
+#pragma unroll
+        for (int i = 0; i < FN; ++i) {
+            const floatx4_t& a = acc[i][j];
+            vec4 h;
+            h[0] = (scalar)a[0];
+            h[1] = (scalar)a[1];
+            h[2] = (scalar)a[2];
+            h[3] = (scalar)a[3];
+            *reinterpret_cast<uint2_t*>(lds + wr * RB + i * 32 + wq * 8) =
+                __builtin_bit_cast(uint2_t, h);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+        for (int c = lane; c < 16 * CPR; c += 64) {
+            const int r = c / CPR, cc = c - (c / CPR) * CPR;
+            const int4_t v = *reinterpret_cast<const int4_t*>(lds + r * RB + cc * 16);
+            const int64_t m = mb + j * 16 + r;
+            const int64_t n = nb + 8 * cc;
+            if (m < p.M) {
+                uint16_t* dst = p.C + m * p.ldc + n;
+                if (n + 7 < p.N) {
+                    *reinterpret_cast<int4_t*>(dst) = v;
+                } else {
+                    const uint16_t* e16 = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (n + e < p.N) dst[e] = e16[e];
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+}
+
 // Epilogue of one wave of gemm_kernel (and of the k-split reduction kernel):
 // rounds the accumulators to the output type and stores them, through the
 // wave's 4 KB of LDS at `stage` when its tile is 64 columns wide.
 template <typename Elt, int MF, int FN, int FM, typename acc_t>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const acc_t (&acc)[FN][FM],
                                               int64_t mb, int64_t nb, int lane, int4_t* stage) {
-    if constexpr (MF == 16) {
+    if constexpr (MF == 16 && FN == 4) {
         store_block_staged<Elt, FM>(p, acc, mb, nb, lane, stage);
+    } else if constexpr (MF == 16) {
+        store_block_staged16<Elt, FN, FM>(p, acc, mb, nb, lane, stage);
     } else if constexpr (FN == 2) {
         store_block_staged32<Elt, FM>(p, acc, mb, nb, lane, stage);
     } else {
@@ -541,15 +595,15 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     static_assert(KS == 1 || KS == 2, "k-groups: 1 or 2");
     // MF = 32: v_mfma_f32_32x32x16 on 32 x 32 tiles, four 16-deep sub-steps per
     // k-tile.  MF = 16: v_mfma_f32_16x16x32 on 16 x 16 tiles, two 32-deep
-    // sub-steps, one k-group and 64-column wave tiles only.
-    static_assert(MF == 32 || (MF == 16 && KS == 1 && BN / WN == 64), "MFMA shape");
+    // sub-steps, one k-group.
+    static_assert(MF == 32 || (MF == 16 && KS == 1), "MFMA shape");
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int A_UNITS = BM * 8, B_UNITS = BN * 8;   // 16-byte LDS units per stage
     constexpr int STAGE = A_UNITS + B_UNITS;
     constexpr int A_DMA = A_UNITS / (64 * NW);         // 1 KB loads per wave per k-tile
     constexpr int B_DMA = B_UNITS / (64 * NW);
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be 32-aligned");
+    static_assert(WTM % MF == 0 && WTN % MF == 0, "wave tile must be whole MFMA tiles");
     static_assert(A_UNITS % (64 * NW) == 0 && B_UNITS % (64 * NW) == 0,
                   "each wave loads whole 8-row slabs");
     static_assert(NS >= 2 && NS * STAGE * 16 <= 160 * 1024, "stages must fit the LDS");

@@ -132,7 +132,9 @@ Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
 }
 
 bool stagger_auto(int id, int64_t M, int64_t N, int64_t K) {
-    if (id < 0 || id >= kNumTiles || kLadder[id].pingpong) return false;
+    // the ladder's rungs other than the ping-pong kernel (the off-ladder rungs
+    // were measured without it)
+    if (id < 0 || id >= kNumLadder || kLadder[id].pingpong) return false;
     if (!stagger_eligible(K) || K / kBK < kStaggerMinKTiles) return false;
     return 2 * K * (M + N) <= kStaggerMaxOperandBytes;
 }
@@ -257,13 +259,30 @@ int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
 // larger would leave half the CUs or more idle.
 int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     if (num_cu <= 0) num_cu = 256;
-    int64_t thresholds[kNumTiles];
-    for (int r = 0; r < kNumTiles; ++r) {
+    int64_t thresholds[kNumLadder];
+    for (int r = 0; r < kNumLadder; ++r) {
         const int64_t area = int64_t(kLadder[r].bm / 64) * (kLadder[r].bn / 64);
         thresholds[r] = area * (num_cu / 2 + 1);
     }
-    thresholds[kNumTiles - 1] = 0;
-    return pick_rung(M, N, 64, 64, kNumTiles, thresholds);
+    thresholds[kNumLadder - 1] = 0;
+    const int r = pick_rung(M, N, 64, 64, kNumLadder, thresholds);
+    // An off-ladder rung with a smaller tile whose grid is larger than the
+    // pick's but still at most one workgroup per CU: every CU then runs one
+    // smaller tile instead of some CUs idling while the others run a larger
+    // one.  Fitted on MI355X, where only the 96 x 96 rung in place of
+    // 128 x 128 qualifies: 1536^3 14.5 -> 11.0 us, 1440^3 15.9 -> 13.7,
+    // 1152x1920x2048 16.3 -> 13.8, 768x3072x4096 26.6 -> 23.4,
+    // 1536x1536x12288 74.7 -> 62.2; with more workgroups than CUs it lost
+    // (1664^3: 17.7 against 14.9, 1536x2048x1536: 17.0 against 14.9), and
+    // in place of 128 x 64 (a smaller tile already) it did not pay.
+    const int64_t br = ceil_div(M, kLadder[r].bm) * ceil_div(N, kLadder[r].bn);
+    for (int c = kNumLadder; c < kNumTiles; ++c) {
+        const int64_t bc = ceil_div(M, kLadder[c].bm) * ceil_div(N, kLadder[c].bn);
+        if (kLadder[c].bm * kLadder[c].bn < kLadder[r].bm * kLadder[r].bn && br < bc &&
+            bc <= num_cu)
+            return c;
+    }
+    return r;
 }
 
 // FlyDSL PR, Changes: the k-loop stagger wraps with a mask over the full

@@ -45,6 +45,9 @@ constexpr TileDesc kLadder[] = {
     {128, 128, 2, 2, 3, 2, 0, 1, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
     {128, 64, 2, 2, 3, 2, 0, 0, 4, 1},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
     {64, 64, 2, 2, 3, 2, 0, 0, 4, 1},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
+    // Off the ladder (see kNumLadder): 4 waves, 48x48 per wave, 16x16x32 MFMAs
+    // on every pipeline (48 is no multiple of 32), 3 x 24 KB.
+    {96, 96, 2, 2, 3, 1, 0, 1, 0, 0},
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place
@@ -114,6 +117,11 @@ struct Plan {
     int splits = 1, split_algo = 0, persistent = 0;
 };
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
+// Rungs 0 .. kNumLadder-1 form the ladder pick_rung walks (largest first).
+// The rungs after them are off the ladder: pick_tile takes one in place of the
+// ladder's pick when its smaller tile turns a grid that leaves CUs idle into
+// more workgroups that still fit one per CU (see pick_tile).
+constexpr int kNumLadder = 5;
 
 // Largest leading dimension accepted: a workgroup addresses its operand rows
 // through one buffer descriptor with 32-bit byte offsets below 2^31.

@@ -108,7 +108,15 @@ hipError_t launch_gemm_pp(GemmParams p, hipStream_t stream) {
 template <typename Elt, int I>
 hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
     constexpr TileDesc d = kLadder[I];
-    if constexpr (d.pingpong) {
+    // wave tiles that are not whole 32 x 32 MFMA tiles: 16x16x32 on every pipeline
+    constexpr bool only16 = (d.bm / d.waves_m) % 32 != 0 || (d.bn / d.waves_n) % 32 != 0;
+    if constexpr (only16) {
+        static_assert(d.kgroups == 1 && d.long_stages == 0 && !d.pingpong && !d.ksplit,
+                      "16x16x32-only rungs: one k-group, no long pipeline, no k-split");
+        if (pl.stages == 2)
+            return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1, 16>(p, s);
+        return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16>(p, s);
+    } else if constexpr (d.pingpong) {
         static_assert(d.bm == 256 && d.bn == 256 && d.waves_m == 2 && d.waves_n == 4 &&
                           d.stages == 3 && d.kgroups == 1,
                       "the ping-pong kernel's tile");
@@ -138,13 +146,14 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
 
 template <typename Elt>
 hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
-    static_assert(kNumTiles == 5, "dispatch table below lists every rung");
+    static_assert(kNumTiles == 6, "dispatch table below lists every rung");
     switch (pl.tile) {
         case 0: return launch_rung<Elt, 0>(p, pl, s);
         case 1: return launch_rung<Elt, 1>(p, pl, s);
         case 2: return launch_rung<Elt, 2>(p, pl, s);
         case 3: return launch_rung<Elt, 3>(p, pl, s);
-        default: return launch_rung<Elt, 4>(p, pl, s);
+        case 4: return launch_rung<Elt, 4>(p, pl, s);
+        default: return launch_rung<Elt, 5>(p, pl, s);
     }
 }
 

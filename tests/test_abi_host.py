@@ -143,8 +143,33 @@ def test_gemv_rejects_before_launch():
 
 # ---- the tile ladder and pick_tile -------------------------------------------
 
+# Rungs 0-4 are the ladder pick_rung walks; the rungs after them are taken
+# only in place of the ladder's pick (the header's sdt_pick_tile rule).
+NUM_LADDER = 5
+
+
 def ladder():
     return [sdt.tile_info(i) for i in range(sdt.num_tiles())]
+
+
+def blocks(t, M, N):
+    return -(-M // t["bm"]) * -(-N // t["bn"])
+
+
+def expected_pick(M, N, num_cu):
+    """The header's rule, restated: the ladder's pick from the 64 x 64 block
+    count, then an off-ladder rung with a smaller tile whose grid is larger
+    than the pick's and at most num_cu."""
+    tiles = ladder()
+    b64 = -(-M // 64) * -(-N // 64)
+    area = [(r["bm"] // 64) * (r["bn"] // 64) for r in tiles[:NUM_LADDER]]
+    r = next((i for i, a in enumerate(area[:-1]) if b64 >= a * (num_cu // 2 + 1)),
+             NUM_LADDER - 1)
+    for c in tiles[NUM_LADDER:]:
+        if (c["bm"] * c["bn"] < tiles[r]["bm"] * tiles[r]["bn"]
+                and blocks(tiles[r], M, N) < blocks(c, M, N) <= num_cu):
+            return c["id"]
+    return r
 
 
 def lds_bytes(t, stages):
@@ -157,13 +182,19 @@ def lds_bytes(t, stages):
 
 def test_ladder_is_well_formed():
     tiles = ladder()
-    areas = [t["bm"] * t["bn"] for t in tiles]
+    assert len(tiles) == NUM_LADDER + 1
+    areas = [t["bm"] * t["bn"] for t in tiles[:NUM_LADDER]]
     assert areas == sorted(areas, reverse=True), "largest tile first"
+    # the off-ladder 96 x 96 rung: 16x16x32 MFMAs only, one k-group, no k-split
+    off = tiles[NUM_LADDER]
+    assert (off["bm"], off["bn"], off["waves_m"], off["waves_n"]) == (96, 96, 2, 2)
+    assert off["kgroups"] == 1 and off["ksplit"] == 0 and off["long_stages"] == 0
     for t in tiles:
         assert t["bk"] == 64
         assert t["kgroups"] in (1, 2)
         assert t["threads"] == 64 * t["waves_m"] * t["waves_n"] * t["kgroups"]
-        assert t["bm"] % (32 * t["waves_m"]) == 0 and t["bn"] % (32 * t["waves_n"]) == 0
+        mf = 32 if t["id"] < NUM_LADDER else 16
+        assert t["bm"] % (mf * t["waves_m"]) == 0 and t["bn"] % (mf * t["waves_n"]) == 0
         assert 2 <= t["stages"] <= 4
         assert t["lds_bytes"] == lds_bytes(t, t["stages"])
         assert t["lds_bytes"] <= 160 * 1024, "fits MI355X LDS"
@@ -200,7 +231,7 @@ def test_launch_plan_rules():
                     st = t["long_stages"]
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
                 nkt = K // 64
-                stg = int(t["id"] != 0 and nkt >= 16 and nkt & (nkt - 1) == 0
+                stg = int(0 < t["id"] < NUM_LADDER and nkt >= 16 and nkt & (nkt - 1) == 0
                           and 2 * K * (M + N) <= 16 << 20)
                 assert p["stagger"] == stg, (num_cu, t["id"], M, N, K)
                 assert p["threads"] == 64 * t["waves_m"] * t["waves_n"] * kg
@@ -216,7 +247,10 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 2
     assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
-    assert sdt.pick_tile(1536, 1536, 1536, 256)["kgroups"] == 2   # 144 workgroups
+    assert sdt.pick_tile(1664, 1664, 1664, 256)["kgroups"] == 2   # 169 workgroups
+    # 1536^3: 96 x 96 in place of 128 x 128 (256 workgroups instead of 144)
+    p = sdt.pick_tile(1536, 1536, 1536, 256)
+    assert (p["id"], p["bm"], p["kgroups"], p["stages"], p["stagger"]) == (5, 96, 1, 3, 0)
     assert sdt.pick_tile(2048, 2048, 2048, 256)["kgroups"] == 1   # 256: the 16x16x32 pipeline
     # stagger: eligible, at least 16 k-tiles, operands within 16 MiB, not the ping-pong rung
     assert sdt.pick_tile(2048, 2048, 2048, 256)["stagger"] == 1
@@ -287,20 +321,24 @@ def test_pick_tile_properties():
             big = tiles[0]
             if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
                 assert t["id"] == 0
-    # the largest rung whose grid, counted in 64x64 blocks scaled by the
-    # rung's area, exceeds half the CUs (exactly its workgroup count when the
-    # tile divides the shape)
+    # the largest ladder rung whose grid, counted in 64x64 blocks scaled by
+    # the rung's area, exceeds half the CUs (exactly its workgroup count when
+    # the tile divides the shape), or the off-ladder rung in its place
     for num_cu in (80, 256, 304):
         for n in [64 * i for i in range(1, 200)]:
             t = sdt.pick_tile(n, n, n, num_cu)
-            blocks = (n // 64) ** 2
-            area = [(r["bm"] // 64) * (r["bn"] // 64) for r in tiles]
-            want = next((i for i, a in enumerate(area[:-1]) if blocks >= a * (num_cu // 2 + 1)),
-                        len(tiles) - 1)
-            assert t["id"] == want, (num_cu, n)
-            if n % 256 == 0:
+            assert t["id"] == expected_pick(n, n, num_cu), (num_cu, n)
+            if n % 256 == 0 and t["id"] < NUM_LADDER:
                 wgs = (n // t["bm"]) * (n // t["bn"])
-                assert t["id"] == len(tiles) - 1 or wgs > num_cu // 2
+                assert t["id"] == NUM_LADDER - 1 or wgs > num_cu // 2
+            if t["id"] >= NUM_LADDER:   # more workgroups than the ladder's pick, one per CU
+                assert blocks(t, n, n) <= num_cu
+    for (M, N) in [(1536, 1536), (1440, 1440), (1152, 1920), (768, 3072), (1664, 1664),
+                   (1536, 2048), (1280, 1280), (100, 30000), (30000, 100)]:
+        for num_cu in (80, 256, 304):
+            assert sdt.pick_tile(M, N, 4096, num_cu)["id"] == expected_pick(M, N, num_cu)
+    assert sdt.pick_tile(1536, 2048, 1536, 256)["id"] == 2      # 352 > 256 workgroups of 96 x 96
+    assert sdt.pick_tile(1152, 1920, 2048, 256)["id"] == 5      # 135 -> 240 workgroups
     # any shape, even degenerate ones, gets a valid rung
     for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
         assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
@@ -310,7 +348,7 @@ def test_pick_tile_on_mi355x_square_sweep():
     """The rungs a sweep of every rung over square shapes measured fastest on
     MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
     want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
-            1536: (128, 128), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
+            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
             3072: (256, 256), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
             8192: (256, 256)}
     for n, (bm, bn) in want.items():

@@ -318,7 +318,7 @@ def test_two_kgroups_auto_plan_matches_oracle():
     """Shapes whose automatic plan uses two k-groups (resident grid, >= 12
     k-tiles) against the oracle, and bit-identical to the forced plan."""
     from shape_driven_tile_amd import binding as sdt
-    for (M, N, K) in [(1024, 1024, 1024), (768, 768, 768), (1536, 1536, 1536)]:
+    for (M, N, K) in [(1024, 1024, 1024), (768, 768, 768), (1664, 1664, 1664)]:
         p = sdt.pick_tile(M, N, K, 256)
         assert p["kgroups"] == 2, (M, N, K)
         say(f"auto two k-groups {M}x{N}x{K} tile={p['id']}")
