@@ -75,7 +75,7 @@ typedef struct sdt_tile {
                         launch runs v_mfma_f32_32x32x16.  The automatic plan takes the
                         long count (long_stages) in place of the deep one on a
                         rung that has it when the launch runs two k-groups and
-                        K holds at least 48 full k-tiles */
+                        K holds at least 12 full k-tiles */
     int lds_bytes;   /* stages x (bm + bn) x bk fp16; rung 0 deep:
                         (2 bm + 3 bn) x bk fp16 = 160 KB */
     int kgroups;     /* groups of waves splitting each k-tile's four 16-deep
@@ -338,13 +338,11 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
  * CUs (num_cu <= 0: 256) is configured (stages, kgroups, threads, LDS).
  * k-groups: 2 on rungs built with them when the grid has at most num_cu
  * workgroups (on rungs 1 and 2: fewer than num_cu) and K spans at least 12 k-tiles,
- * else 1.  Stages: the deep count
- * with two k-groups; with one, 2 while the operands, 2*K*(M+N) bytes, fit in
- * one MI355X XCD's 4 MiB L2 (tiles arrive within a one-tile prefetch and the
- * shorter prologue wins), else the deep count; with two k-groups a deep count
- * becomes the rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs)
- * once K holds at least 48 full k-tiles.  Stagger: as gemm_f16 describes.  SDT_OK or
- * SDT_ERR_INVALID_ARG. */
+ * else 1.  Stages: the rung's deep count, which with two k-groups becomes
+ * the rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs) once K
+ * holds at least 12 full k-tiles; the 2-stage pipeline is never planned (it
+ * lost with the operands in HBM and tied with them in L2).  Stagger: as
+ * gemm_f16 describes.  SDT_OK or SDT_ERR_INVALID_ARG. */
 int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
                   sdt_tile* out);
 

@@ -77,11 +77,6 @@ int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
 
 // 2 stages while A and B (2 bytes per element) fit in one XCD's L2, else the
 // rung's deep pipeline.
-int stages_for(int id, int64_t M, int64_t N, int64_t K) {
-    const int64_t operand_bytes = 2 * K * (M + N);
-    return operand_bytes <= kShallowOperandBytes ? 2 : kLadder[id].stages;
-}
-
 // Two k-groups on a rung built with them, when its grid is resident all at
 // once (at most one workgroup per CU) and the k-loop is long enough.
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
@@ -118,15 +113,21 @@ int long_for(int id, int stages, int kgroups, int64_t K) {
     return stages;
 }
 
-// The automatic plan on rung `id`: two k-groups always run the deep
-// pipeline, one k-group the pipeline stages_for picks; long_for then swaps a
-// two-k-group deep pipeline for the rung's long one on a long k-loop.
+// The automatic plan on rung `id`: the rung's deep pipeline, which long_for
+// swaps for its long one when two k-groups run a long k-loop.  The 2-stage
+// pipeline is never planned: it never measured faster by more than 2% (256^3
+// on operands in L2), and with the operands in HBM it lost by up to 38% even
+// where they fit in one XCD's L2 (kernel-trace medians with caches flushed
+// before each launch, 2 against 3 stages: 512^3 7.92 / 6.48 us, 640^3
+// 9.36 / 7.34, 2048x2048x512 11.84 / 10.24, 4096x4096x256 16.76 / 14.68 with
+// the ping-pong kernel; on operands in L2 5.44 / 5.44, 5.92 / 6.00,
+// 9.68 / 9.20, 16.12 / 14.00).
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     const TileDesc& d = kLadder[id];
     Plan p;
     p.tile = id;
     p.kgroups = kgroups_for(id, M, N, K, num_cu);
-    p.stages = long_for(id, p.kgroups == 2 ? d.stages : stages_for(id, M, N, K), p.kgroups, K);
+    p.stages = long_for(id, d.stages, p.kgroups, K);
     p.stagger = stagger_auto(id, M, N, K) ? 1 : 0;
     return p;
 }
@@ -206,16 +207,13 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
         const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn) * pl.splits;
         const int64_t nkt = (K / kBK) / pl.splits;   // full k-tiles of the shortest split
         pl.kgroups = kgroups_for_grid(id, wgs, nkt, num_cu);
-        pl.stages = pl.kgroups == 2 ? d.stages
-                                    : (2 * K * (M + N) <= kShallowOperandBytes ? 2 : d.stages);
-        pl.stages = long_for(id, pl.stages, pl.kgroups, K / pl.splits);
+        pl.stages = long_for(id, d.stages, pl.kgroups, K / pl.splits);
         pl.split_algo = cfg.split_algo >= 0 ? cfg.split_algo : kSplitAlgoAuto;
     }
     if (cfg.kgroups >= 0) {
         pl.kgroups = cfg.kgroups;
         if (cfg.stages < 0)
-            pl.stages = long_for(id, pl.kgroups == 2 ? d.stages : stages_for(id, M, N, K),
-                                 pl.kgroups, pl.splits > 1 ? K / pl.splits : K);
+            pl.stages = long_for(id, d.stages, pl.kgroups, pl.splits > 1 ? K / pl.splits : K);
     }
     if (cfg.stages >= 0) pl.stages = cfg.stages;
     if (cfg.split_algo >= 0) pl.split_algo = cfg.split_algo;

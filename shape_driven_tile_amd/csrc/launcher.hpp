@@ -14,8 +14,9 @@ constexpr int kBK = 64;
 
 // A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
 // each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
-// A launch uses 2 or `stages` LDS stages of (bm + bn) x 64 elements each (see
-// stages_for); the global prefetch runs stages - 1 k-tiles deep.  A ping-pong
+// A launch uses 2 (forced plans only), `stages` or `long_stages` LDS stages
+// of (bm + bn) x 64 elements each (see plan_for); the global prefetch runs
+// stages - 1 k-tiles deep.  A ping-pong
 // rung's deep pipeline is its own kernel (gemm_pp_kernel): two wave groups
 // one phase apart, A in two LDS stages and B in `stages` (three).
 struct TileDesc {
@@ -51,18 +52,15 @@ constexpr TileDesc kLadder[] = {
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place
-// of its deep one.  Fitted on MI355X: 4 stages measured 1% slower than 3 at
-// 32 k-tiles (1024x1024x2048) and 7-20% faster from 48 (1024x1024x3072,
-// 512x512x4096, 768x768x4096, 1024x1024x8192).
-constexpr int kLongMinKTiles = 48;
-
-// Operand bytes up to which a launch runs the shallow 2-stage pipeline: one
-// MI355X XCD's L2.  While A and B together fit there, a k-tile arrives within
-// the one-tile prefetch and the shorter prologue wins (about 1% at 256^3 ..
-// 1024^3); past it the tiles stream from the Infinity Cache or HBM and the
-// deeper prefetch wins by up to 40% (64x64 at 512x512x4096: 29.3 us with 2
-// stages, 18.0 us with 3).
-constexpr int64_t kShallowOperandBytes = int64_t(4) << 20;
+// of its deep one (with two k-groups, which themselves need 12).  Fitted on
+// MI355X with the operands in HBM (caches flushed before each launch, as in a
+// benchmark step that streams other products in between, or for weights read
+// once): 4 stages against 3, kernel-trace medians, 384x384x768 (12 k-tiles)
+// 7.50 against 7.78 us, 768^3 7.56 / 8.12, 1024^3 8.72 / 9.24,
+// 1024x1024x2048 13.28 / 14.92, 128x8192x1024 10.02 / 10.84.  Repeated on
+// operands already in L2 the two tie within 4% either way (768^3 6.32 /
+// 6.32, 1024^3 7.64 / 7.50, 384x384x768 6.12 / 5.88).
+constexpr int kLongMinKTiles = 12;
 
 // Shortest k-loop (in 64-deep k-tiles) that a second k-group of waves pays
 // on: a grid resident all at once spends each k-tile on one chain of
@@ -133,7 +131,6 @@ int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N);
 int64_t counter_bytes(const Plan& p, int64_t M, int64_t N);
 int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu);
 bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
-int stages_for(int id, int64_t M, int64_t N, int64_t K);
 int long_for(int id, int stages, int kgroups, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 int kgroups_for_grid(int id, int64_t wgs, int64_t nkt, int num_cu);

@@ -206,18 +206,17 @@ def test_launch_plan_rules():
     """k-groups: 2 on rungs built with them when the grid has at most num_cu
     workgroups (fewer than num_cu on the 256x128 and 128x128 rungs, whose
     one-k-group deep pipelines run 16x16x32 MFMAs) and K spans at least 12
-    k-tiles.  Stages:
-    the deep count with two k-groups; with one, 2 while A and B (2*K*(M+N)
-    bytes) fit in 4 MiB; a two-k-group deep pipeline becomes the rung's long
-    one (if it has one) from 48 full k-tiles.  Stagger: off the ping-pong rung, a power-of-two
-    count of at least 16 full k-tiles and A and B within 16 MiB."""
+    k-tiles.  Stages: the deep count, never the 2-stage pipeline; a
+    two-k-group deep pipeline becomes the rung's long one (if it has one) from
+    12 full k-tiles.  Stagger: on ladder rungs 1-4, a power-of-two count of at
+    least 16 full k-tiles and A and B within 16 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
               (2048, 2048, 4096), (1536, 1536, 2048), (1024, 1024, 4096),
               (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700),
               (512, 512, 3008), (512, 512, 3072), (1024, 1024, 8192), (64, 64, 8192),
-              (2048, 1024, 4096)]
+              (2048, 1024, 4096), (384, 384, 768), (384, 384, 704), (640, 640, 640)]
     for num_cu in (80, 256):
         for t in tiles:
             for (M, N, K) in shapes:
@@ -225,9 +224,8 @@ def test_launch_plan_rules():
                 wgs = -(-M // t["bm"]) * -(-N // t["bn"])
                 fits = wgs < num_cu if t["id"] in (1, 2) else wgs <= num_cu
                 kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
-                st = t["stages"] if kg == 2 else (2 if 2 * K * (M + N) <= 4 * 1024 * 1024
-                                                  else t["stages"])
-                if kg == 2 and st == t["stages"] and t["long_stages"] and K // 64 >= 48:
+                st = t["stages"]
+                if kg == 2 and t["long_stages"] and K // 64 >= 12:
                     st = t["long_stages"]
                 assert (p["kgroups"], p["stages"]) == (kg, st), (num_cu, t["id"], M, N, K)
                 nkt = K // 64

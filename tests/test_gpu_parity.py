@@ -100,9 +100,12 @@ def test_integer_exact_8192_rows_auto():
 
 
 def test_integer_exact_pingpong_short_k_block_order():
-    """The ping-pong kernel forced at 4096 x 4096 x 128 (its automatic plan
-    there is the 2-stage kernel): two k-tiles, the 16 x 16-block tile order,
+    """The ping-pong kernel (forced, and the automatic plan) at 4096 x 4096 x
+    128: two k-tiles, fewer than its stages, the 16 x 16-block tile order,
     every element bit for bit."""
+    from shape_driven_tile_amd import binding as sdt
+    p = sdt.pick_tile(4096, 4096, 128, 256)
+    assert (p["id"], p["stages"]) == (0, 3), p
     A = inputs.integer_f16((4096, 128), 25)
     B = inputs.integer_f16((4096, 128), 26)
     say("integer 4096x4096x128 ping-pong forced, full C")
@@ -165,7 +168,7 @@ def test_integer_exact_every_tile(shape):
 
 @pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
 def test_integer_exact_every_tile_deep_pipeline(shape):
-    """Operands past 4 MiB plan every rung's deep pipeline (on the rungs with
+    """The automatic plan is every rung's deep pipeline (on the rungs with
     a long pipeline the plan takes that one at these k-loop lengths, which
     the assertion checks; the long pipelines themselves run in
     test_long_pipeline_every_rung_with_one).  Here each rung's deep pipeline
@@ -179,7 +182,7 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
     ref = oracle.gemm(A, B)
     for tile in range(_ntiles()):
         info = sdt.tile_info(tile)
-        want = info["long_stages"] if info["long_stages"] and K // 64 >= 48 else info["stages"]
+        want = info["long_stages"] if info["long_stages"] and K // 64 >= 12 else info["stages"]
         assert sdt.plan_tile(tile, M, N, K, 1 << 20)["stages"] == want
         for kg in ((1, 2) if info["kgroups"] == 2 else (1,)):
             say(f"integer deep {shape} tile={tile} stages={info['stages']} kgroups={kg}")
@@ -619,8 +622,11 @@ def test_graph_capture_replays_match_eager():
     y2 = torch.empty_like(y1)
 
     def work():
-        for A, B, C in ops:
-            sdt.gemm_f16(A, B, C)
+        for i, (A, B, C) in enumerate(ops):
+            if i == 0:   # the automatic plan never takes the 2-stage pipeline: forced
+                sdt.gemm_f16_cfg(A, B, C, stages=2)
+            else:
+                sdt.gemm_f16(A, B, C)
         sdt.gemv_f16_m1(x, W, y1)
         sdt.gemv_f16_m1_kn(x, Wkn, y2)
 
