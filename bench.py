@@ -99,6 +99,15 @@ def profile_mode(args):
         v = None if args.variant < 0 else args.variant
         for j in range(args.launches):
             sdt.gemv_f16_m1_kn(x, Ws[j % len(Ws)], y, variant=v)
+    elif name == "gemvknws":
+        x = torch.from_numpy(inputs.decode_activations()).to(dev)
+        Ws = [torch.from_numpy(inputs.decode_weights_kn(r)).to(dev)
+              for r in range(inputs.DECODE_BUFFERS)]
+        y = torch.empty((inputs.DECODE_N,), dtype=torch.float16, device=dev)
+        ws = sdt.Workspace(sdt.gemv_kn_workspace_size(inputs.DECODE_N, inputs.DECODE_K),
+                           device=dev)
+        for j in range(args.launches):
+            sdt.gemv_f16_m1_kn_ws(x, Ws[j % len(Ws)], y, workspace=ws)
     elif name.startswith("copy"):
         mb = int(name[4:])
         src = torch.ones((mb * 1024 * 1024 // 2,), dtype=torch.float16, device=dev)
@@ -631,6 +640,41 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         }
         log(f"decode [K][N] variant {v}: median {med:.2f} us = "
             f"{det['decode_kn_cold']['variants'][str(v)]['GBps_weights_median']} GB/s")
+    # the same product split over K through a workspace (gemv_f16_m1_kn_ws)
+    ws_kn = sdt.Workspace(sdt.gemv_kn_workspace_size(inputs.DECODE_N, inputs.DECODE_K), device=dev)
+    bad = 0
+    for r in range(inputs.DECODE_BUFFERS):
+        sdt.gemv_f16_m1_kn_ws(x, Wkn[r], y, workspace=ws_kn)
+        torch.cuda.synchronize()
+        ref = oracle.gemv_kn(x_h, Wkn_h[r])
+        got = y.cpu().numpy().astype(np.float64)
+        bad += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+    if bad:
+        det["decode_kn_cold"]["split_ws"] = {"gate": f"{bad} outside tolerance"}
+        log(f"decode [K][N] split over K: PARITY FAILED ({bad}), not timed")
+    else:
+        h = (lambda j: sdt.gemv_f16_m1_kn_ws(x, Wkn[j % len(Wkn)], y, workspace=ws_kn))
+        t0 = time.time()
+        j = 0
+        while time.time() - t0 < 1.0:
+            h(j)
+            j += 1
+            if j % 200 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        us = time_launches(torch, h, 200)
+        med = sorted(us)[len(us) // 2]
+        det["decode_kn_cold"]["split_ws"] = {
+            "us": _ranges(us),
+            "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
+            "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "workspace_bytes": ws_kn.nbytes,
+            "gate": "pass (all 8 buffers)",
+            "what": "gemv_f16_m1_kn_ws: 256-column bands, K split so ~768 workgroups stream, "
+                    "then a second kernel adds the splits in order (both kernels timed)",
+        }
+        log(f"decode [K][N] split over K: median {med:.2f} us = "
+            f"{det['decode_kn_cold']['split_ws']['GBps_weights_median']} GB/s")
     det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
                                          "200 launches x 10 repeats, event-timed")
     det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)

@@ -33,10 +33,11 @@
 #include <stdint.h>
 
 /* Version of the structures and signatures below; bumped whenever sdt_tile,
- * sdt_launch or an entry point's arguments change.  sdt_abi_version() reports
- * the version the library was built with: a caller compiled against another
- * header must not pass these structures to it. */
-#define SDT_ABI_VERSION 3
+ * sdt_launch or an entry point's arguments change, or entry points are added
+ * (4: the off-ladder rung 5 and the [K][N] workspace entry points).
+ * sdt_abi_version() reports the version the library was built with: a caller
+ * compiled against another header must not pass these structures to it. */
+#define SDT_ABI_VERSION 4
 
 #ifdef __cplusplus
 extern "C" {
@@ -220,6 +221,28 @@ int gemv_f16_m1(int64_t N, int64_t K, const void* x,
 int gemv_f16_m1_kn(int64_t N, int64_t K, const void* x,
                    const void* B, int64_t ldb, void* y, void* stream);
 
+/* gemv_f16_m1_kn with a workspace, which lets the product split K across
+ * workgroups: bands of 256 columns (512-byte runs of every weight row, where
+ * the one-launch kernel reads 128-byte runs: on MI355X such runs stream at
+ * most 5.46 TB/s, 512-byte ones 6.29) with K cut into `splits` ranges so that
+ * about 768 workgroups stream at once; each writes its fp32 column sums to
+ * the workspace and a second kernel adds the splits in split order, then
+ * rounds once.  Deterministic; the bits differ from gemv_f16_m1_kn's (another
+ * summation order), within the same error bound.  workspace: device memory
+ * owned by the caller, 16-byte aligned, at least sdt_gemv_kn_workspace_size(N,
+ * K) bytes for the split (smaller, or NULL with 0: the call runs
+ * gemv_f16_m1_kn); needs no initialisation; one workspace serves one call at a
+ * time (calls that share it must be ordered on one stream).  Errors as
+ * gemv_f16_m1_kn, plus SDT_ERR_INVALID_ARG for workspace_bytes < 0 or a NULL
+ * workspace with bytes > 0, SDT_ERR_UNSUPPORTED for a misaligned one. */
+int gemv_f16_m1_kn_ws(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                      void* y, void* workspace, int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemv_f16_m1_kn_ws splits with for an N x K product: 0
+ * when it does not split (K < 16, or a grid of 768 band workgroups without
+ * one); -1 for negative sizes.  Host-only. */
+int64_t sdt_gemv_kn_workspace_size(int64_t N, int64_t K);
+
 /* ---- bfloat16 variants ------------------------------------------------------
  * The same products with bfloat16 operands and output (1 sign, 8 exponent,
  * 7 fraction bits; fp32 accumulation on v_mfma_f32_32x32x16_bf16 /
@@ -242,6 +265,8 @@ int gemv_bf16_m1(int64_t N, int64_t K, const void* x,
                  const void* B, int64_t ldb, void* y, void* stream);
 int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x,
                     const void* B, int64_t ldb, void* y, void* stream);
+int gemv_bf16_m1_kn_ws(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
+                       void* y, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* ---- test / benchmark extras ---------------------------------------------- */
 

@@ -31,11 +31,11 @@ EXPORTS = (
     "gemm_f16_cfg", "gemm_bf16_cfg",
     "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
     "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version", "sdt_stream_read_grid",
-    "gemm_f16_noalloc",
+    "gemm_f16_noalloc", "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_gemv_kn_workspace_size",
 )
 
 # The include/sdt.h version these structures and signatures follow.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class SdtTile(ctypes.Structure):
@@ -118,6 +118,10 @@ def lib():
     L.sdt_abi_version.argtypes = []
     L.gemm_f16_noalloc.argtypes = L.gemm_f16.argtypes
     L.sdt_stream_read_grid.argtypes = [_vp, _i64, _vp, _int, _vp]
+    L.gemv_f16_m1_kn_ws.argtypes = [_i64, _i64, _vp, _vp, _i64, _vp, _vp, _i64, _vp]
+    L.gemv_bf16_m1_kn_ws.argtypes = L.gemv_f16_m1_kn_ws.argtypes
+    L.sdt_gemv_kn_workspace_size.argtypes = [_i64, _i64]
+    L.sdt_gemv_kn_workspace_size.restype = _i64
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -135,7 +139,8 @@ def lib():
                  "sdt_tile_info", "sdt_stagger_eligible", "sdt_plan_tile", "sdt_check_gemm_args",
                  "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
                  "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
-                 "sdt_stream_read_grid", "gemm_f16_noalloc", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read"):
+                 "sdt_stream_read_grid", "gemm_f16_noalloc", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read",
+                 "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws"):
         getattr(L, name).restype = _int
     if L.sdt_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
@@ -485,6 +490,39 @@ def _gemv_16(entry, x, B, y, stream, dtype, kn):
     rc = getattr(lib(), entry)(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), _stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, entry)
+
+
+def gemv_kn_workspace_size(N: int, K: int) -> int:
+    """Bytes of workspace gemv_f16_m1_kn_ws splits with (0: no split)."""
+    return int(lib().sdt_gemv_kn_workspace_size(int(N), int(K)))
+
+
+def _gemv_kn_ws(entry, x, B, y, workspace, stream, dtype):
+    if x.dtype != dtype or y.dtype != dtype:
+        raise TypeError(f"x and y must be {dtype}")
+    if x.dim() != 1 or y.dim() != 1 or x.stride(0) != 1 or y.stride(0) != 1:
+        raise ValueError("x and y must be contiguous vectors")
+    K, N = B.shape
+    if x.shape[0] != K or y.shape[0] != N:
+        raise ValueError(f"shape mismatch x{tuple(x.shape)} B{tuple(B.shape)} y{tuple(y.shape)}")
+    pb, ldb = _rows(B, "B", dtype)
+    wp, wb = _ws_args(workspace)
+    rc = getattr(lib(), entry)(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), wp, wb,
+                               _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, entry)
+
+
+def gemv_f16_m1_kn_ws(x, B, y, workspace=None, stream=None) -> None:
+    """gemv_f16_m1_kn split over K through `workspace` (a Workspace of at least
+    gemv_kn_workspace_size(N, K) bytes; smaller or None: the one-launch kernel)."""
+    import torch
+    _gemv_kn_ws("gemv_f16_m1_kn_ws", x, B, y, workspace, stream, torch.float16)
+
+
+def gemv_bf16_m1_kn_ws(x, B, y, workspace=None, stream=None) -> None:
+    import torch
+    _gemv_kn_ws("gemv_bf16_m1_kn_ws", x, B, y, workspace, stream, torch.bfloat16)
 
 
 def gemv_bf16_m1(x, B, y, stream=None) -> None:

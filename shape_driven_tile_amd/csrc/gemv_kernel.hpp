@@ -257,6 +257,12 @@ struct GemvKnParams {
     uint16_t* y;
     int64_t ldb;
     int N, K;
+    // K split over workgroups (gemv_kn_kernel with SPLIT): workgroup
+    // (band, blockIdx.y) sums rows [blockIdx.y * kc, +kc) (kc a multiple of 8)
+    // into part[blockIdx.y * pstride + n] (fp32, pstride >= N).
+    float* part;
+    int64_t pstride;
+    int kc;
 };
 
 // acc[c] += x(r) * w(r, c) for the first `rows` of eight rows.  The chunks are
@@ -276,7 +282,11 @@ __device__ __forceinline__ void kn_block(int4_t xv, const int4_t* w, int rows, f
     }
 }
 
-template <typename Elt, int SEG, int NW>
+// One workgroup per band of SEG * 8 columns.  Without SPLIT it sums every
+// row and writes y; with SPLIT the grid's second dimension splits the rows
+// (see GemvKnParams) and the workgroup writes its fp32 column sums for the
+// second kernel, gemv_kn_reduce_kernel.
+template <typename Elt, int SEG, int NW, bool SPLIT = false, int UB = 2>
 __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
     constexpr int BW = SEG * 8;          // columns per workgroup
     constexpr int RGW = 64 / SEG;        // row groups per wave
@@ -285,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
     constexpr int PARTS = NT / BW;       // first-level partial sums per column
     static_assert(64 % SEG == 0 && NT % BW == 0 && RG % PARTS == 0, "reduction shape");
     __shared__ float red[RG * BW];
-    __shared__ float part[PARTS * BW];
+    __shared__ float colsum[PARTS * BW];
 
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -294,8 +304,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
     const int rg = wave * RGW + lane / SEG;
     const int nb = blockIdx.x * BW;
     const int n0 = nb + seg * 8;
-    const int nblk = p.K / 8;            // blocks of eight rows wholly below K
-    const int krem = p.K - nblk * 8;
+    // rows [kbeg, kend): blocks of eight rows b0 .. b1-1, then krem more
+    const int kbeg = SPLIT ? (int)blockIdx.y * p.kc : 0;
+    const int kend = SPLIT ? min(p.K, kbeg + p.kc) : p.K;
+    const int b0 = kbeg / 8;
+    const int b1 = kend / 8;
+    const int krem = kend - b1 * 8;
 
     float acc[8];
 #pragma unroll
@@ -303,24 +317,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
 
     const uint16_t* col = p.B + n0;
     if (nb + BW <= p.N) {                // whole band below N (uniform)
-        int b = rg;
-        for (; b + RG < nblk; b += 2 * RG) {
-            const int k0 = 8 * b, k1 = 8 * (b + RG);
-            const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
-            const int4_t x1 = *reinterpret_cast<const int4_t*>(p.x + k1);
-            int4_t w0[8], w1[8];
+        // UB blocks of eight rows per trip (UB * 8 loads per lane in flight),
+        // the row group's blocks in increasing order
+        int b = b0 + rg;
+        for (; b + (UB - 1) * RG < b1; b += UB * RG) {
+            int4_t xv[UB], w[UB][8];
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                w0[r] = __builtin_nontemporal_load(
-                    reinterpret_cast<const int4_t*>(col + (int64_t)(k0 + r) * p.ldb));
+            for (int u = 0; u < UB; ++u)
+                xv[u] = *reinterpret_cast<const int4_t*>(p.x + 8 * (b + u * RG));
 #pragma unroll
-            for (int r = 0; r < 8; ++r)
-                w1[r] = __builtin_nontemporal_load(
-                    reinterpret_cast<const int4_t*>(col + (int64_t)(k1 + r) * p.ldb));
-            kn_block<Elt>(x0, w0, 8, acc);
-            kn_block<Elt>(x1, w1, 8, acc);
+            for (int u = 0; u < UB; ++u)
+#pragma unroll
+                for (int r = 0; r < 8; ++r)
+                    w[u][r] = __builtin_nontemporal_load(reinterpret_cast<const int4_t*>(
+                        col + (int64_t)(8 * (b + u * RG) + r) * p.ldb));
+#pragma unroll
+            for (int u = 0; u < UB; ++u) kn_block<Elt>(xv[u], w[u], 8, acc);
         }
-        if (b < nblk) {
+        for (; b < b1; b += RG) {
             const int k0 = 8 * b;
             const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
             int4_t w0[8];
@@ -331,7 +345,7 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
             kn_block<Elt>(x0, w0, 8, acc);
         }
     } else {                             // ragged last band: masked columns
-        for (int b = rg; b < nblk; b += RG) {
+        for (int b = b0 + rg; b < b1; b += RG) {
             const int k0 = 8 * b;
             const int4_t x0 = *reinterpret_cast<const int4_t*>(p.x + k0);
             int4_t w0[8];
@@ -341,8 +355,8 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
             kn_block<Elt>(x0, w0, 8, acc);
         }
     }
-    if (krem > 0 && rg == nblk % RG) {   // ragged last block of rows
-        const int k0 = 8 * nblk;
+    if (krem > 0 && rg == (b1 - b0) % RG) {   // ragged last block of rows
+        const int k0 = 8 * b1;
         const int4_t x0 = gemv_chunk(p.x, k0, p.K, false);
         int4_t w0[8];
 #pragma unroll
@@ -362,18 +376,34 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
         float s = 0.0f;
 #pragma unroll
         for (int j = 0; j < PER; ++j) s += red[(q * PER + j) * BW + c];
-        part[q * BW + c] = s;
+        colsum[q * BW + c] = s;
     }
     __syncthreads();
     if (t < BW) {
         float s = 0.0f;
 #pragma unroll
-        for (int q = 0; q < PARTS; ++q) s += part[q * BW + t];
+        for (int q = 0; q < PARTS; ++q) s += colsum[q * BW + t];
         if (nb + t < p.N) {
-            const typename Elt::scalar h = (typename Elt::scalar)s;
-            p.y[nb + t] = __builtin_bit_cast(uint16_t, h);
+            if constexpr (SPLIT) {
+                p.part[(int64_t)blockIdx.y * p.pstride + nb + t] = s;
+            } else {
+                const typename Elt::scalar h = (typename Elt::scalar)s;
+                p.y[nb + t] = __builtin_bit_cast(uint16_t, h);
+            }
         }
     }
+}
+
+// Second kernel of a split [K][N] product: y(n) = the `splits` partial sums of
+// column n added in split order, rounded once to the element type.
+template <typename Elt>
+__global__ __launch_bounds__(256) void gemv_kn_reduce_kernel(GemvKnParams p, int splits) {
+    const int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= p.N) return;
+    float s = p.part[n];
+    for (int q = 1; q < splits; ++q) s += p.part[(int64_t)q * p.pstride + n];
+    const typename Elt::scalar h = (typename Elt::scalar)s;
+    p.y[n] = __builtin_bit_cast(uint16_t, h);
 }
 
 }  // namespace sdt

@@ -1,6 +1,8 @@
 // Host-side launch decisions (see launcher.hpp).  No HIP dependency.
 #include "launcher.hpp"
 
+#include <algorithm>
+#include <climits>
 #include <cstdint>
 
 namespace sdt {
@@ -314,6 +316,24 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // 16-byte loads at column offsets that are multiples of 8, so B must be
 // 16-byte aligned with ldb a multiple of 8 whenever there is a second row;
 // the activations are read 8 at a time from a 16-byte aligned x.
+KnSplit kn_split_plan(int64_t N, int64_t K) {
+    KnSplit s{1, 0, 0, 0, 0};
+    if (N <= 0 || K < 16 || N > INT_MAX || K > INT_MAX) return s;
+    const int64_t bw = int64_t(kKnSplitSeg) * 8;
+    const int64_t bands = ceil_div(N, bw);
+    int64_t splits = std::min(ceil_div(kKnSplitTargetWgs, bands), K / 8);
+    if (splits < 2) return s;
+    const int64_t kc = ceil_div(ceil_div(K, splits), 8) * 8;
+    splits = ceil_div(K, kc);
+    if (splits < 2) return s;
+    s.splits = (int)splits;
+    s.kc = (int)kc;
+    s.bands = bands;
+    s.pstride = bands * bw;
+    s.bytes = splits * s.pstride * 4;
+    return s;
+}
+
 int check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb,
                        const void* y) {
     if (N < 0 || K < 0) return SDT_ERR_INVALID_ARG;
@@ -364,6 +384,11 @@ extern "C" int sdt_stagger_eligible(int64_t K) { return sdt::stagger_eligible(K)
 extern "C" int64_t sdt_stagger_ktile(int64_t wg, int64_t i, int64_t nkt) {
     if (!sdt::is_pow2(nkt) || wg < 0 || i < 0) return -1;
     return (wg + i) & (nkt - 1);
+}
+
+extern "C" int64_t sdt_gemv_kn_workspace_size(int64_t N, int64_t K) {
+    if (N < 0 || K < 0) return -1;
+    return sdt::kn_split_plan(N, K).bytes;
 }
 
 extern "C" int sdt_check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B,

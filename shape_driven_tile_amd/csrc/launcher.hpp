@@ -125,6 +125,27 @@ constexpr int kNumLadder = 5;
 // through one buffer descriptor with 32-bit byte offsets below 2^31.
 constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 
+// The [K][N] decode GEMV split over K (gemv_f16_m1_kn_ws): bands of
+// kKnSplitSeg * 8 columns (512-byte runs of every weight row) read by
+// workgroups of kKnSplitWaves waves, each over kc rows, until about
+// kKnSplitTargetWgs workgroups stream at once; a second kernel adds the
+// splits' fp32 column sums in split order.  Fitted on MI355X at the decode
+// shape (K = 4096, N = 12288, weights in HBM): runs of 128 bytes per row, the
+// one-launch kernel's, read at most 5.46 TB/s however many workgroups read
+// them, runs of 512 bytes 6.29 TB/s; the split kernel alone streams in
+// 16.2 us with 768 workgroups (384: 17.9, 1536: 20.9), 19.3 us with the sum.
+constexpr int kKnSplitSeg = 32;
+constexpr int kKnSplitWaves = 8;
+constexpr int kKnSplitTargetWgs = 768;
+struct KnSplit {
+    int splits;        // 1: no split (the one-launch kernel)
+    int kc;            // rows per split, a multiple of 8
+    int64_t bands;     // workgroups along N
+    int64_t pstride;   // floats per split in the workspace (bands * band width)
+    int64_t bytes;     // workspace bytes (0 without a split)
+};
+KnSplit kn_split_plan(int64_t N, int64_t K);
+
 sdt_tile describe(const Plan& p);
 sdt_tile describe_rung(int id);
 int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N);

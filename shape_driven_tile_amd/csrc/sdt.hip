@@ -275,6 +275,48 @@ int launch_gemv_kn(int variant, int64_t N, int64_t K, const void* x, const void*
     return e == hipSuccess ? SDT_OK : fail_hip(e);
 }
 
+// The [K][N] GEMV split over K with the plan kn_split_plan made: the band
+// kernel into the workspace's fp32 column sums, then their sum in split order.
+template <typename Elt>
+int launch_gemv_kn_split(const KnSplit& sp, int64_t N, int64_t K, const void* x, const void* B,
+                         int64_t ldb, void* y, void* ws, hipStream_t stream) {
+    GemvKnParams p;
+    p.x = static_cast<const uint16_t*>(x);
+    p.B = static_cast<const uint16_t*>(B);
+    p.y = static_cast<uint16_t*>(y);
+    p.ldb = ldb;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.part = static_cast<float*>(ws);
+    p.pstride = sp.pstride;
+    p.kc = sp.kc;
+    int splits = sp.splits;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(
+        reinterpret_cast<const void*>(&gemv_kn_kernel<Elt, kKnSplitSeg, kKnSplitWaves, true>),
+        dim3((unsigned)sp.bands, (unsigned)sp.splits), dim3(kKnSplitWaves * 64), args, 0, stream);
+    if (e != hipSuccess) return fail_hip(e);
+    void* rargs[] = {&p, &splits};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&gemv_kn_reduce_kernel<Elt>),
+                        dim3((unsigned)((N + 255) / 256)), dim3(256), rargs, 0, stream);
+    return e == hipSuccess ? SDT_OK : fail_hip(e);
+}
+
+template <typename Elt>
+int gemv_kn_ws_impl(int64_t N, int64_t K, const void* x, const void* B, int64_t ldb, void* y,
+                    void* ws, int64_t ws_bytes, void* stream) {
+    int st = check_gemv_kn_args(N, K, x, B, ldb, y);
+    if (st != SDT_OK) return st;
+    if (ws_bytes < 0 || (ws_bytes > 0 && !ws)) return SDT_ERR_INVALID_ARG;
+    if (ws && (reinterpret_cast<uintptr_t>(ws) & 15u) != 0) return SDT_ERR_UNSUPPORTED;
+    if (N == 0) return SDT_OK;
+    const KnSplit sp = kn_split_plan(N, K);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (sp.splits < 2 || ws_bytes < sp.bytes)
+        return launch_gemv_kn<Elt>(0, N, K, x, B, ldb, y, s);
+    return launch_gemv_kn_split<Elt>(sp, N, K, x, B, ldb, y, ws, s);
+}
+
 // cfg fields: -1 = the automatic choice.  route_m1: M == 1 runs the GEMV.
 // ws / ws_bytes: the caller's workspace (NULL and 0: none; the plan then
 // never splits K across workgroups).
@@ -577,6 +619,20 @@ extern "C" int gemv_bf16_m1_kn(int64_t N, int64_t K, const void* x, const void* 
     if (st != SDT_OK || N == 0) return st;
     return sdt::launch_gemv_kn<sdt::BF16>(0, N, K, x, B, ldb, y,
                                           static_cast<hipStream_t>(stream));
+}
+
+extern "C" int gemv_f16_m1_kn_ws(int64_t N, int64_t K, const void* x, const void* B,
+                                 int64_t ldb, void* y, void* workspace,
+                                 int64_t workspace_bytes, void* stream) {
+    return sdt::gemv_kn_ws_impl<sdt::F16>(N, K, x, B, ldb, y, workspace, workspace_bytes,
+                                          stream);
+}
+
+extern "C" int gemv_bf16_m1_kn_ws(int64_t N, int64_t K, const void* x, const void* B,
+                                  int64_t ldb, void* y, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+    return sdt::gemv_kn_ws_impl<sdt::BF16>(N, K, x, B, ldb, y, workspace, workspace_bytes,
+                                           stream);
 }
 
 extern "C" int gemv_f16_m1_kn_ex(int64_t N, int64_t K, const void* x, const void* B,

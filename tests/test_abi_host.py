@@ -556,3 +556,42 @@ def test_ksplit_and_persistent_cfg_refusals():
     assert call(4096, 4096, 4096, None, 0, tile_id=0, persistent=-2) == bad
     with pytest.raises(sdt.SdtError):
         sdt.launch_workspace_size(512, 512, 1024, tile_id=4, splits=65)
+
+
+# ---- the [K][N] GEMV split over K ------------------------------------------------
+
+def test_gemv_kn_split_plan():
+    """gemv_f16_m1_kn_ws's split: 256-column bands, K cut into ranges of a
+    multiple of 8 rows so that about 768 workgroups stream at once (at least
+    2 ranges, each of at least 8 rows); the workspace holds one fp32 row of
+    bands * 256 column sums per range.  No split below 16 rows or when the
+    bands alone make 768 workgroups."""
+    def plan(N, K):
+        if N <= 0 or K < 16:
+            return 0
+        bands = -(-N // 256)
+        s = min(-(-768 // bands), K // 8)
+        if s < 2:
+            return 0
+        kc = -(-(-(-K // s)) // 8) * 8
+        s = -(-K // kc)
+        return 0 if s < 2 else s * bands * 256 * 4
+    for N in (1, 8, 255, 256, 257, 1000, 4096, 12288, 65536, 196608, 196609, 1 << 20):
+        for K in (0, 1, 15, 16, 17, 20, 64, 1000, 4096, 4100, 65536):
+            assert sdt.gemv_kn_workspace_size(N, K) == plan(N, K), (N, K)
+    assert sdt.gemv_kn_workspace_size(12288, 4096) == 16 * 48 * 256 * 4
+    assert sdt.gemv_kn_workspace_size(-1, 5) == -1 and sdt.gemv_kn_workspace_size(5, -1) == -1
+
+
+def test_gemv_kn_ws_argument_checks():
+    """Refusals before any device call (fake aligned pointers, null stream)."""
+    L = sdt.lib()
+    x, B, y, ws = 0x10000, 0x20000, 0x30000, 0x40000
+    assert L.gemv_f16_m1_kn_ws(-1, 8, x, B, 16, y, None, 0, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_kn_ws(16, 8, x, B, 8, y, None, 0, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_kn_ws(16, 8, x, B, 16, y, None, 64, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_kn_ws(16, 8, x, B, 16, y, ws, -1, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.gemv_f16_m1_kn_ws(16, 8, x, B, 16, y, ws + 4, 64, None) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.gemv_f16_m1_kn_ws(16, 8, x, B + 2, 16, y, ws, 64, None) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.gemv_bf16_m1_kn_ws(16, 8, x + 2, B, 16, y, ws, 64, None) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.gemv_f16_m1_kn_ws(0, 8, x, B, 16, y, ws, 64, None) == sdt.SDT_OK   # N == 0: no-op
