@@ -675,6 +675,28 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         }
         log(f"decode [K][N] split over K: median {med:.2f} us = "
             f"{det['decode_kn_cold']['split_ws']['GBps_weights_median']} GB/s")
+    # read ceilings of the [K][N] access pattern: the same 8 weight buffers read
+    # in runs of 128 bytes per row (the one-launch kernel's bands) and 512 bytes
+    # (the split kernel's), with one workgroup per band or K cut into chunks
+    row_bytes = inputs.DECODE_N * 2
+    runs = {}
+    out_w = torch.empty((1 << 16,), dtype=torch.int32, device=dev)
+    for run, rpw in ((128, inputs.DECODE_K), (128, 256), (512, 256), (512, 64)):
+        h = (lambda j, run=run, rpw=rpw: sdt.stream_read_runs(
+            Wkn[j % len(Wkn)], inputs.DECODE_K, row_bytes, run, rpw, out_w))
+        for j in range(400):
+            h(j)
+        torch.cuda.synchronize()
+        us = time_launches(torch, h, 200)
+        med = sorted(us)[len(us) // 2]
+        runs[f"{run}B_rows_per_wg_{rpw}"] = {
+            "workgroups": (row_bytes // run) * (inputs.DECODE_K // rpw),
+            "us": _ranges(us),
+            "GBps_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
+        }
+        log(f"[K][N] read in {run}-byte runs, {rpw} rows per workgroup: median {med:.2f} us = "
+            f"{runs[f'{run}B_rows_per_wg_{rpw}']['GBps_median']} GB/s")
+    det["decode_kn_cold"]["read_runs"] = runs
     det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
                                          "200 launches x 10 repeats, event-timed")
     det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)

@@ -34,7 +34,8 @@
 
 /* Version of the structures and signatures below; bumped whenever sdt_tile,
  * sdt_launch or an entry point's arguments change, or entry points are added
- * (4: the off-ladder rung 5 and the [K][N] workspace entry points).
+ * (4: the off-ladder rung 5, the [K][N] workspace entry points and
+ * sdt_stream_read_runs).
  * sdt_abi_version() reports the version the library was built with: a caller
  * compiled against another header must not pass these structures to it. */
 #define SDT_ABI_VERSION 4
@@ -417,6 +418,23 @@ int sdt_stream_read(const void* buf, int64_t bytes, void* out, void* stream);
  * the launch failed. */
 int sdt_stream_read_grid(const void* buf, int64_t bytes, void* out, int workgroups,
                          void* stream);
+
+/* Measurement: enqueue a read-only kernel over `rows` rows of row_bytes bytes
+ * at `buf`, read in runs of run_bytes contiguous bytes per row, the access
+ * pattern of a [K][N] decode GEMV whose workgroups own column bands:
+ * workgroup w (256 threads) reads band w % (row_bytes / run_bytes) of rows
+ * [c * rows_per_wg, (c + 1) * rows_per_wg), c = w / (row_bytes / run_bytes),
+ * with 16-byte non-temporal loads, 8 per lane in flight.  Grid: (row_bytes /
+ * run_bytes) * (rows / rows_per_wg) workgroups, each writing one 32-bit word
+ * (the XOR of every 32-bit word it read) to out[w].  rows == 0: SDT_OK,
+ * nothing enqueued.  SDT_ERR_INVALID_ARG: negative rows, row_bytes <= 0, a
+ * null pointer, run_bytes not 64, 128, 256, 512 or 1024, row_bytes not a
+ * multiple of run_bytes, rows_per_wg not a positive multiple of 8 * 4096 /
+ * run_bytes, or rows not a multiple of rows_per_wg.  SDT_ERR_UNSUPPORTED: buf
+ * not 16-byte or out not 4-byte aligned, or a grid past 2^31 - 1.
+ * SDT_ERR_HIP: the launch failed. */
+int sdt_stream_read_runs(const void* buf, int64_t rows, int64_t row_bytes, int run_bytes,
+                         int rows_per_wg, void* out, void* stream);
 
 /* Host-only argument check used by gemv_f16_m1_kn before anything is
  * enqueued (the status it would return for these arguments). */

@@ -32,6 +32,7 @@ EXPORTS = (
     "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
     "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version", "sdt_stream_read_grid",
     "gemm_f16_noalloc", "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_gemv_kn_workspace_size",
+    "sdt_stream_read_runs",
 )
 
 # The include/sdt.h version these structures and signatures follow.
@@ -122,6 +123,7 @@ def lib():
     L.gemv_bf16_m1_kn_ws.argtypes = L.gemv_f16_m1_kn_ws.argtypes
     L.sdt_gemv_kn_workspace_size.argtypes = [_i64, _i64]
     L.sdt_gemv_kn_workspace_size.restype = _i64
+    L.sdt_stream_read_runs.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp]
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -140,7 +142,7 @@ def lib():
                  "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
                  "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
                  "sdt_stream_read_grid", "gemm_f16_noalloc", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read",
-                 "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws"):
+                 "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_stream_read_runs"):
         getattr(L, name).restype = _int
     if L.sdt_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
@@ -490,6 +492,17 @@ def _gemv_16(entry, x, B, y, stream, dtype, kn):
     rc = getattr(lib(), entry)(N, K, x.data_ptr(), pb, ldb, y.data_ptr(), _stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, entry)
+
+
+def stream_read_runs(buf, rows: int, row_bytes: int, run_bytes: int, rows_per_wg: int, out,
+                     stream=None) -> None:
+    """Enqueue the run-length read measurement kernel over a device buffer
+    (rows x row_bytes bytes); out: an int32 device tensor of at least
+    (row_bytes // run_bytes) * (rows // rows_per_wg) elements."""
+    rc = lib().sdt_stream_read_runs(buf.data_ptr(), int(rows), int(row_bytes), int(run_bytes),
+                                    int(rows_per_wg), out.data_ptr(), _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_stream_read_runs")
 
 
 def gemv_kn_workspace_size(N: int, K: int) -> int:

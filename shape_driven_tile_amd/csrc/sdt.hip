@@ -466,6 +466,38 @@ __global__ __launch_bounds__(256) void stream_read_grid_kernel(const int4_t* buf
     if (threadIdx.x == 0) out[blockIdx.x] = (uint32_t)(wx[0] ^ wx[1] ^ wx[2] ^ wx[3]);
 }
 
+// Rows of row_bytes read in runs of RUN bytes: workgroup w reads band
+// w % nbands (RUN bytes at RUN * band) of rows [chunk * rpw, +rpw), chunk =
+// w / nbands; RUN / 16 lanes per row, 16 bytes each, 8 loads per lane in flight.
+template <int RUN>
+__global__ __launch_bounds__(256) void stream_read_runs_kernel(const char* buf, int64_t row_bytes,
+                                                               int nbands, int rpw,
+                                                               uint32_t* out) {
+    constexpr int LPR = RUN / 16;       // lanes per row
+    constexpr int RPI = 256 / LPR;      // rows per workgroup-wide load
+    const int band = blockIdx.x % nbands;
+    const int chunk = blockIdx.x / nbands;
+    const int t = threadIdx.x;
+    const char* p = buf + ((int64_t)chunk * rpw + t / LPR) * row_bytes + (int64_t)band * RUN +
+                    (t % LPR) * 16;
+    int x = 0;
+    for (int i = 0; i < rpw; i += 8 * RPI) {
+        int4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            v[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const int4_t*>(p + (int64_t)(i + u * RPI) * row_bytes));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, 64);
+    __shared__ int wx[4];
+    if ((t & 63) == 0) wx[t >> 6] = x;
+    __syncthreads();
+    if (t == 0) out[blockIdx.x] = (uint32_t)(wx[0] ^ wx[1] ^ wx[2] ^ wx[3]);
+}
+
 }  // namespace
 }  // namespace sdt
 
@@ -706,6 +738,38 @@ extern "C" int sdt_stream_read_grid(const void* buf, int64_t bytes, void* out, i
     void* args[] = {&b, &n16, &o};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&sdt::stream_read_grid_kernel),
                                    dim3((unsigned)workgroups), dim3(256), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);
+}
+
+extern "C" int sdt_stream_read_runs(const void* buf, int64_t rows, int64_t row_bytes,
+                                    int run_bytes, int rows_per_wg, void* out, void* stream) {
+    if (rows == 0) return SDT_OK;
+    if (rows < 0 || row_bytes <= 0 || !buf || !out || rows_per_wg <= 0) return SDT_ERR_INVALID_ARG;
+    if (run_bytes != 64 && run_bytes != 128 && run_bytes != 256 && run_bytes != 512 &&
+        run_bytes != 1024)
+        return SDT_ERR_INVALID_ARG;
+    const int rpi = 4096 / run_bytes;   // rows per workgroup-wide load (256 lanes x 16 bytes)
+    if (row_bytes % run_bytes != 0 || rows_per_wg % (8 * rpi) != 0 || rows % rows_per_wg != 0)
+        return SDT_ERR_INVALID_ARG;
+    if ((reinterpret_cast<uintptr_t>(buf) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+        return SDT_ERR_UNSUPPORTED;
+    const int64_t nbands = row_bytes / run_bytes;
+    const int64_t grid = nbands * (rows / rows_per_wg);
+    if (grid > INT_MAX) return SDT_ERR_UNSUPPORTED;
+    const char* b = static_cast<const char*>(buf);
+    int nb = (int)nbands, rpw = rows_per_wg;
+    uint32_t* o = static_cast<uint32_t*>(out);
+    void* args[] = {&b, &row_bytes, &nb, &rpw, &o};
+    const void* k;
+    switch (run_bytes) {
+        case 64: k = reinterpret_cast<const void*>(&sdt::stream_read_runs_kernel<64>); break;
+        case 128: k = reinterpret_cast<const void*>(&sdt::stream_read_runs_kernel<128>); break;
+        case 256: k = reinterpret_cast<const void*>(&sdt::stream_read_runs_kernel<256>); break;
+        case 512: k = reinterpret_cast<const void*>(&sdt::stream_read_runs_kernel<512>); break;
+        default: k = reinterpret_cast<const void*>(&sdt::stream_read_runs_kernel<1024>); break;
+    }
+    hipError_t e = hipLaunchKernel(k, dim3((unsigned)grid), dim3(256), args, 0,
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);
 }

@@ -595,3 +595,20 @@ def test_gemv_kn_ws_argument_checks():
     assert L.gemv_f16_m1_kn_ws(16, 8, x, B + 2, 16, y, ws, 64, None) == sdt.SDT_ERR_UNSUPPORTED
     assert L.gemv_bf16_m1_kn_ws(16, 8, x + 2, B, 16, y, ws, 64, None) == sdt.SDT_ERR_UNSUPPORTED
     assert L.gemv_f16_m1_kn_ws(0, 8, x, B, 16, y, ws, 64, None) == sdt.SDT_OK   # N == 0: no-op
+
+
+def test_stream_read_runs_argument_checks():
+    """Refusals of the run-length read kernel before any device call."""
+    L = sdt.lib()
+    b, o = 0x10000, 0x20000
+    ok_args = (1024, 4096, 128, 256)
+    assert L.sdt_stream_read_runs(b, 0, 4096, 128, 256, o, None) == sdt.SDT_OK
+    assert L.sdt_stream_read_runs(None, *ok_args, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, *ok_args, None, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, -1, 4096, 128, 256, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, 1024, 4096, 96, 256, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, 1024, 4000, 128, 256, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, 1024, 4096, 128, 128, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b, 1000, 4096, 512, 64, o, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_stream_read_runs(b + 8, *ok_args, o, None) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_stream_read_runs(b, *ok_args, o + 2, None) == sdt.SDT_ERR_UNSUPPORTED

@@ -105,3 +105,31 @@ def test_stream_read_grid_arguments():
     assert L.sdt_stream_read_grid(p, 16, o + 2, 1, s) == sdt.SDT_ERR_UNSUPPORTED
     torch.cuda.synchronize()
     assert (out.cpu().numpy() == 0).all()
+
+
+@pytest.mark.parametrize("run,rpw", [(64, 512), (128, 256), (256, 128), (512, 64), (1024, 32),
+                                     (128, 1024)])
+def test_stream_read_runs_words_exact(run, rpw):
+    """The run-length read kernel: workgroup w's word is the XOR of every
+    32-bit word of its band of its rows, so every byte was read, in bounds."""
+    import torch
+    from shape_driven_tile_amd import binding as sdt
+    rows, row_bytes = 1024, 4096
+    rng = np.random.default_rng(7100 + run)
+    host = rng.integers(0, 256, size=rows * row_bytes, dtype=np.uint8)
+    buf = to_dev(host)
+    nbands = row_bytes // run
+    grid = nbands * (rows // rpw)
+    out = torch.full((grid + 4,), -1, dtype=torch.int32, device=buf.device)   # 4 guard words
+    say(f"sdt_stream_read_runs run={run} rows_per_wg={rpw} grid={grid}")
+    sdt.stream_read_runs(buf, rows, row_bytes, run, rpw, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    words = host.view(np.int32).reshape(rows, row_bytes // 4)
+    want = np.empty(grid, np.int32)
+    for w in range(grid):
+        band, chunk = w % nbands, w // nbands
+        blk = words[chunk * rpw:(chunk + 1) * rpw, band * run // 4:(band + 1) * run // 4]
+        want[w] = np.bitwise_xor.reduce(blk.ravel())
+    np.testing.assert_array_equal(got[:grid], want)
+    assert (got[grid:] == -1).all(), "words past the grid were written"
