@@ -369,6 +369,31 @@ def time_launches(torch, fn, launches, repeats=10):
     return out
 
 
+PROTOCOL_COLD = ("8 rotating weight buffers (805 MB, past the 256 MB Infinity Cache), ~1 s of "
+                 "eager launches to warm up; 200 launches captured in a HIP graph and replayed "
+                 "10 times back to back (us: no host launch cost); the same 200 launches issued "
+                 "eagerly from Python and event-timed (us_events)")
+
+
+def cold_times(torch, fn, launches=200):
+    """Per-launch microseconds of a rotating-buffer launch fn(j): ~1 s of eager
+    launches to warm up, then `launches` calls captured in a HIP graph and
+    replayed 10 times back to back (no host launch cost: the reported figure),
+    and the same calls issued eagerly from this process, event-timed (beside
+    it, for the dispatch gaps)."""
+    t0 = time.time()
+    j = 0
+    while time.time() - t0 < 1.0:
+        fn(j)
+        j += 1
+        if j % 200 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    graph, _ = graph_launches(torch, fn, launches)
+    eager = time_launches(torch, fn, launches)
+    return graph, eager
+
+
 def graph_launches(torch, fn, chain, repeats=10):
     """Per-launch microseconds of `chain` calls captured in one HIP graph and
     replayed `repeats` times back to back (graph edges serialize the launches;
@@ -528,46 +553,32 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     # Infinity Cache), ~1 s warm-up, 200 launches x 10 repeats.
     x2, y2 = x.view(1, -1), y.view(1, -1)
     g = (lambda j: sdt.gemm_f16(x2, Ws[j % len(Ws)], y2))
-    t0 = time.time()
-    j = 0
-    while time.time() - t0 < 1.0:
-        g(j)
-        j += 1
-        if j % 200 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    us = time_launches(torch, g, 200)
+    us, us_ev = cold_times(torch, g)
     med = sorted(us)[len(us) // 2]
     det["decode_cold"] = {
         "us": _ranges(us),
+        "us_events": _ranges(us_ev),
         "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
         "GBps_all_median": round(bytes_gemv_all / (med * 1e-6) / 1e9, 1),
         "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-        "protocol": "8 rotating buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
+        "protocol": PROTOCOL_COLD,
     }
     log(f"decode cold: median {med:.2f} us = {det['decode_cold']['GBps_weights_median']} GB/s")
     # The streaming-read ceiling for the same rotation: the library's read-only
     # kernel (the GEMV's load pattern and nothing else), same protocol.
     words = torch.empty(int(bytes_gemv) // 8192, dtype=torch.int32, device=dev)
     r = (lambda j: sdt.stream_read(Ws[j % len(Ws)], words))
-    t0 = time.time()
-    j = 0
-    while time.time() - t0 < 1.0:
-        r(j)
-        j += 1
-        if j % 200 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    us_r = time_launches(torch, r, 200)
+    us_r, us_r_ev = cold_times(torch, r)
     med_r = sorted(us_r)[len(us_r) // 2]
     det["decode_read_ceiling"] = {
         "us": _ranges(us_r),
+        "us_events": _ranges(us_r_ev),
         "GBps_median": round(bytes_gemv / (med_r * 1e-6) / 1e9, 1),
         "hbm_frac_median": round(bytes_gemv / (med_r * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "gemv_frac_of_ceiling_median": round(med_r / med, 4),
         "kernel": "sdt_stream_read: 8 KB per wave, 8 non-temporal 16-byte loads per lane, "
                   "no arithmetic or output beyond one word per 8 KB",
-        "protocol": "the same 8 rotating weight buffers, 1 s warm, 200 launches x 10 repeats",
+        "protocol": PROTOCOL_COLD,
     }
     log(f"decode read ceiling: median {med_r:.2f} us = "
         f"{det['decode_read_ceiling']['GBps_median']} GB/s; the GEMV reaches "
@@ -578,24 +589,17 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     nwg = 32 * props_cus(torch, dev)
     words_g = torch.empty(nwg, dtype=torch.int32, device=dev)
     rg = (lambda j: sdt.stream_read_grid(Ws[j % len(Ws)], words_g, nwg))
-    t0 = time.time()
-    j = 0
-    while time.time() - t0 < 1.0:
-        rg(j)
-        j += 1
-        if j % 200 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    us_g = time_launches(torch, rg, 200)
+    us_g, us_g_ev = cold_times(torch, rg)
     med_g = sorted(us_g)[len(us_g) // 2]
     det["decode_read_ceiling_grid"] = {
         "us": _ranges(us_g),
+        "us_events": _ranges(us_g_ev),
         "GBps_median": round(bytes_gemv / (med_g * 1e-6) / 1e9, 1),
         "hbm_frac_median": round(bytes_gemv / (med_g * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "gemv_frac_of_ceiling_median": round(med_g / med, 4),
         "kernel": f"sdt_stream_read_grid: {nwg} workgroups of 256 threads, grid-stride, four "
                   "non-temporal 16-byte loads per lane per pass",
-        "protocol": "the same 8 rotating weight buffers, 1 s warm, 200 launches x 10 repeats",
+        "protocol": PROTOCOL_COLD,
     }
     log(f"decode grid-stride read ceiling: median {med_g:.2f} us = "
         f"{det['decode_read_ceiling_grid']['GBps_median']} GB/s; the GEMV reaches "
@@ -622,18 +626,11 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             log(f"decode [K][N] variant {v}: PARITY FAILED ({bad}), not timed")
             continue
         h = (lambda j, v=v: sdt.gemv_f16_m1_kn(x, Wkn[j % len(Wkn)], y, variant=v))
-        t0 = time.time()
-        j = 0
-        while time.time() - t0 < 1.0:
-            h(j)
-            j += 1
-            if j % 200 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        us = time_launches(torch, h, 200)
+        us, us_ev = cold_times(torch, h)
         med = sorted(us)[len(us) // 2]
         det["decode_kn_cold"]["variants"][str(v)] = {
             "us": _ranges(us),
+            "us_events": _ranges(us_ev),
             "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
             "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "gate": "pass",
@@ -654,18 +651,11 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         log(f"decode [K][N] split over K: PARITY FAILED ({bad}), not timed")
     else:
         h = (lambda j: sdt.gemv_f16_m1_kn_ws(x, Wkn[j % len(Wkn)], y, workspace=ws_kn))
-        t0 = time.time()
-        j = 0
-        while time.time() - t0 < 1.0:
-            h(j)
-            j += 1
-            if j % 200 == 0:
-                torch.cuda.synchronize()
-        torch.cuda.synchronize()
-        us = time_launches(torch, h, 200)
+        us, us_ev = cold_times(torch, h)
         med = sorted(us)[len(us) // 2]
         det["decode_kn_cold"]["split_ws"] = {
             "us": _ranges(us),
+            "us_events": _ranges(us_ev),
             "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
             "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "workspace_bytes": ws_kn.nbytes,
@@ -684,21 +674,18 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     for run, rpw in ((128, inputs.DECODE_K), (128, 256), (512, 256), (512, 64)):
         h = (lambda j, run=run, rpw=rpw: sdt.stream_read_runs(
             Wkn[j % len(Wkn)], inputs.DECODE_K, row_bytes, run, rpw, out_w))
-        for j in range(400):
-            h(j)
-        torch.cuda.synchronize()
-        us = time_launches(torch, h, 200)
+        us, us_ev = cold_times(torch, h)
         med = sorted(us)[len(us) // 2]
         runs[f"{run}B_rows_per_wg_{rpw}"] = {
             "workgroups": (row_bytes // run) * (inputs.DECODE_K // rpw),
             "us": _ranges(us),
+            "us_events": _ranges(us_ev),
             "GBps_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
         }
         log(f"[K][N] read in {run}-byte runs, {rpw} rows per workgroup: median {med:.2f} us = "
             f"{runs[f'{run}B_rows_per_wg_{rpw}']['GBps_median']} GB/s")
     det["decode_kn_cold"]["read_runs"] = runs
-    det["decode_kn_cold"]["protocol"] = ("weights as K rows of N; 8 rotating buffers, 1 s warm, "
-                                         "200 launches x 10 repeats, event-timed")
+    det["decode_kn_cold"]["protocol"] = "weights as K rows of N; " + PROTOCOL_COLD
     det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)
     det["ksplit"] = detail_ksplit(sdt, torch, np, inputs, oracle, dev)
     return det
@@ -810,21 +797,13 @@ def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):
         log(f"bf16 decode: PARITY FAILED ({bad}), not timed")
         return out
     g = (lambda j: sdt.gemv_bf16_m1(x, Ws[j % len(Ws)], y))
-    t0 = time.time()
-    j = 0
-    while time.time() - t0 < 1.0:
-        g(j)
-        j += 1
-        if j % 200 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-    us = time_launches(torch, g, 200)
+    us, us_ev = cold_times(torch, g)
     med = sorted(us)[len(us) // 2]
     out["decode_cold"] = {
-        "us": _ranges(us), "gate": "pass",
+        "us": _ranges(us), "us_events": _ranges(us_ev), "gate": "pass",
         "GBps_weights_median": round(bytes_gemv / (med * 1e-6) / 1e9, 1),
         "hbm_frac_median": round(bytes_gemv / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-        "protocol": "8 rotating bf16 buffers, 1 s warm, 200 launches x 10 repeats, event-timed",
+        "protocol": "bf16 weights; " + PROTOCOL_COLD,
     }
     log(f"bf16 decode cold: median {med:.2f} us = {out['decode_cold']['GBps_weights_median']} GB/s")
     return out
