@@ -47,21 +47,15 @@ def test_square_4096_full():
     assert_close(C, oracle.gemm(A, B))
 
 
-def test_square_8192_rows():
-    """8192^3: 512 seeded whole rows (every 256-row tile band is hit, with its
-    first and last rows) and 16 whole columns of C against the oracle, the
-    rest of C checked finite."""
-    say("square 8192^3 uniform, auto tile, 512 full rows + 16 full columns")
+def test_square_8192_full():
+    """8192^3: every element of C against the oracle (1.1e12 fp64
+    multiply-adds on the host's cores, about 15 s with 16 threads)."""
+    say("square 8192^3 uniform, auto tile, full C")
     n = 8192
     A, B = inputs.square_operands(n, 2)
-    C, _ = run_gemm(A, B)
-    rows = seeded_rows(n, 512, seed=n)
-    assert_close(C[rows], oracle.gemm(np.ascontiguousarray(A[rows]), B))
-    cols = seeded_rows(n, 16, seed=n + 1)
-    r = np.repeat(np.arange(n), len(cols))
-    c = np.tile(cols, n)
-    assert_close(C[r, c], oracle.gemm_sample(A, B, r, c))
-    assert np.isfinite(C.astype(np.float32)).all()
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_close(C, oracle.gemm(A, B))
 
 
 @pytest.mark.parametrize("shape", [(4096, 4096, 1024), (8192, 8192, 512), (4096, 4096, 4096)])
