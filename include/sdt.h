@@ -240,8 +240,8 @@ int gemv_f16_m1_kn_ws(int64_t N, int64_t K, const void* x, const void* B, int64_
                       void* y, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Bytes of workspace gemv_f16_m1_kn_ws splits with for an N x K product: 0
- * when it does not split (K < 16, or a grid of 768 band workgroups without
- * one); -1 for negative sizes.  Host-only. */
+ * when it does not split (K < 16 or K > 2^30 - 1, N > 2^31 - 1, or a grid of
+ * 768 band workgroups without a split); -1 for negative sizes.  Host-only. */
 int64_t sdt_gemv_kn_workspace_size(int64_t N, int64_t K);
 
 /* ---- bfloat16 variants ------------------------------------------------------

@@ -318,7 +318,8 @@ int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
 // the activations are read 8 at a time from a 16-byte aligned x.
 KnSplit kn_split_plan(int64_t N, int64_t K) {
     KnSplit s{1, 0, 0, 0, 0};
-    if (N <= 0 || K < 16 || N > INT_MAX || K > INT_MAX) return s;
+    // (K at most INT_MAX / 2: a range's end, start + kc, stays an int)
+    if (N <= 0 || K < 16 || N > INT_MAX || K > INT_MAX / 2) return s;
     const int64_t bw = int64_t(kKnSplitSeg) * 8;
     const int64_t bands = ceil_div(N, bw);
     int64_t splits = std::min(ceil_div(kKnSplitTargetWgs, bands), K / 8);

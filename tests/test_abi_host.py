@@ -567,7 +567,7 @@ def test_gemv_kn_split_plan():
     bands * 256 column sums per range.  No split below 16 rows or when the
     bands alone make 768 workgroups."""
     def plan(N, K):
-        if N <= 0 or K < 16:
+        if N <= 0 or K < 16 or N > 2 ** 31 - 1 or K > (2 ** 31 - 1) // 2:
             return 0
         bands = -(-N // 256)
         s = min(-(-768 // bands), K // 8)
@@ -580,6 +580,9 @@ def test_gemv_kn_split_plan():
         for K in (0, 1, 15, 16, 17, 20, 64, 1000, 4096, 4100, 65536):
             assert sdt.gemv_kn_workspace_size(N, K) == plan(N, K), (N, K)
     assert sdt.gemv_kn_workspace_size(12288, 4096) == 16 * 48 * 256 * 4
+    assert sdt.gemv_kn_workspace_size(1024, 2 ** 30 - 8) > 0
+    assert sdt.gemv_kn_workspace_size(1024, 2 ** 30) == 0     # past INT_MAX / 2 rows
+    assert sdt.gemv_kn_workspace_size(2 ** 31, 4096) == 0
     assert sdt.gemv_kn_workspace_size(-1, 5) == -1 and sdt.gemv_kn_workspace_size(5, -1) == -1
 
 
