@@ -146,7 +146,7 @@ static void check_gemm(int dtype, int64_t M, int64_t N, int64_t K, hipStream_t s
     if (ws) HIP_OK(hipFree(ws));
 }
 
-static void check_gemv(int dtype, bool kn, int64_t N, int64_t K) {
+static void check_gemv(int dtype, bool kn, int64_t N, int64_t K, bool split = false) {
     const int64_t ldb = kn ? (N + 7) / 8 * 8 : (K + 7) / 8 * 8;
     std::vector<uint16_t> x = draw((size_t)K, 21 + dtype, dtype);
     std::vector<uint16_t> B = draw((size_t)((kn ? K : N) * ldb), 22 + dtype, dtype);
@@ -154,8 +154,17 @@ static void check_gemv(int dtype, bool kn, int64_t N, int64_t K) {
     void* dB = dev_copy(B);
     void* dy = nullptr;
     HIP_OK(hipMalloc(&dy, (size_t)N * 2));
+    void* ws = nullptr;
+    const int64_t ws_bytes = split ? sdt_gemv_kn_workspace_size(N, K) : 0;
+    if (split) {
+        CHECK(ws_bytes > 0, "[K][N] N=%lld K=%lld: no split planned", (long long)N, (long long)K);
+        HIP_OK(hipMalloc(&ws, (size_t)ws_bytes));   // needs no initialisation
+    }
     int rc;
-    if (kn)
+    if (kn && split)
+        rc = dtype == 1 ? gemv_bf16_m1_kn_ws(N, K, dx, dB, ldb, dy, ws, ws_bytes, nullptr)
+                        : gemv_f16_m1_kn_ws(N, K, dx, dB, ldb, dy, ws, ws_bytes, nullptr);
+    else if (kn)
         rc = dtype == 1 ? gemv_bf16_m1_kn(N, K, dx, dB, ldb, dy, nullptr)
                         : gemv_f16_m1_kn(N, K, dx, dB, ldb, dy, nullptr);
     else
@@ -174,6 +183,7 @@ static void check_gemv(int dtype, bool kn, int64_t N, int64_t K) {
     HIP_OK(hipFree(dx));
     HIP_OK(hipFree(dB));
     HIP_OK(hipFree(dy));
+    if (ws) HIP_OK(hipFree(ws));
 }
 
 int main() {
@@ -195,6 +205,8 @@ int main() {
         check_gemv(dtype, false, 12288, 4096);
         check_gemv(dtype, true, 12288, 4096);
         check_gemv(dtype, true, 1001, 1003);
+        check_gemv(dtype, true, 12288, 4096, true);   // [K][N] split over K (workspace)
+        check_gemv(dtype, true, 1001, 1003, true);
     }
 
     // error paths: nothing is launched, the status names the cause
