@@ -269,12 +269,16 @@ int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     // An off-ladder rung with a smaller tile whose grid is larger than the
     // pick's but still at most one workgroup per CU: every CU then runs one
     // smaller tile instead of some CUs idling while the others run a larger
-    // one.  Fitted on MI355X, where only the 96 x 96 rung in place of
-    // 128 x 128 qualifies: 1536^3 14.5 -> 11.0 us, 1440^3 15.9 -> 13.7,
-    // 1152x1920x2048 16.3 -> 13.8, 768x3072x4096 26.6 -> 23.4,
+    // one (the first such rung in id order).  Fitted on MI355X: the 96 x 96
+    // rung in place of 128 x 128 at 1536^3 14.5 -> 11.0 us, 1440^3 15.9 ->
+    // 13.7, 1152x1920x2048 16.3 -> 13.8, 768x3072x4096 26.6 -> 23.4,
     // 1536x1536x12288 74.7 -> 62.2; with more workgroups than CUs it lost
     // (1664^3: 17.7 against 14.9, 1536x2048x1536: 17.0 against 14.9), and
-    // in place of 128 x 64 (a smaller tile already) it did not pay.
+    // in place of 128 x 64 (a smaller tile already) it did not pay.  The
+    // 192 x 192 rung in place of the 256 x 256 ping-pong kernel: 3072^3
+    // 54.2 -> 48.6, 2944^3 53.9 -> 46.8, 3072x3072x1024 23.4 -> 21.0,
+    // 3072x3072x8192 131.9 -> 121.2, 3072x2816x4096 69.9 -> 61.3; with
+    // 272 workgroups (3000x3104x1000) 41.2 against 28.1.
     const int64_t br = ceil_div(M, kLadder[r].bm) * ceil_div(N, kLadder[r].bn);
     for (int c = kNumLadder; c < kNumTiles; ++c) {
         const int64_t bc = ceil_div(M, kLadder[c].bm) * ceil_div(N, kLadder[c].bn);

@@ -146,14 +146,15 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
 
 template <typename Elt>
 hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
-    static_assert(kNumTiles == 6, "dispatch table below lists every rung");
+    static_assert(kNumTiles == 7, "dispatch table below lists every rung");
     switch (pl.tile) {
         case 0: return launch_rung<Elt, 0>(p, pl, s);
         case 1: return launch_rung<Elt, 1>(p, pl, s);
         case 2: return launch_rung<Elt, 2>(p, pl, s);
         case 3: return launch_rung<Elt, 3>(p, pl, s);
         case 4: return launch_rung<Elt, 4>(p, pl, s);
-        default: return launch_rung<Elt, 5>(p, pl, s);
+        case 5: return launch_rung<Elt, 5>(p, pl, s);
+        default: return launch_rung<Elt, 6>(p, pl, s);
     }
 }
 

@@ -182,13 +182,15 @@ def lds_bytes(t, stages):
 
 def test_ladder_is_well_formed():
     tiles = ladder()
-    assert len(tiles) == NUM_LADDER + 1
+    assert len(tiles) == NUM_LADDER + 2
     areas = [t["bm"] * t["bn"] for t in tiles[:NUM_LADDER]]
     assert areas == sorted(areas, reverse=True), "largest tile first"
-    # the off-ladder 96 x 96 rung: 16x16x32 MFMAs only, one k-group, no k-split
-    off = tiles[NUM_LADDER]
-    assert (off["bm"], off["bn"], off["waves_m"], off["waves_n"]) == (96, 96, 2, 2)
-    assert off["kgroups"] == 1 and off["ksplit"] == 0 and off["long_stages"] == 0
+    # the off-ladder 96 x 96 and 192 x 192 rungs: 16x16x32 MFMAs only, one
+    # k-group, no k-split
+    shapes = [(t["bm"], t["bn"], t["waves_m"], t["waves_n"]) for t in tiles[NUM_LADDER:]]
+    assert shapes == [(96, 96, 2, 2), (192, 192, 2, 4)]
+    for off in tiles[NUM_LADDER:]:
+        assert off["kgroups"] == 1 and off["ksplit"] == 0 and off["long_stages"] == 0
     for t in tiles:
         assert t["bk"] == 64
         assert t["kgroups"] in (1, 2)
@@ -337,6 +339,9 @@ def test_pick_tile_properties():
             assert sdt.pick_tile(M, N, 4096, num_cu)["id"] == expected_pick(M, N, num_cu)
     assert sdt.pick_tile(1536, 2048, 1536, 256)["id"] == 2      # 352 > 256 workgroups of 96 x 96
     assert sdt.pick_tile(1152, 1920, 2048, 256)["id"] == 5      # 135 -> 240 workgroups
+    assert sdt.pick_tile(3072, 3072, 3072, 256)["id"] == 6      # 144 -> 256 workgroups
+    assert sdt.pick_tile(3000, 3104, 1000, 256)["id"] == 0      # 272 > 256 of 192 x 192
+    assert sdt.pick_tile(2816, 2816, 2816, 256)["id"] == 1      # 225 < 242 of 256 x 128
     # any shape, even degenerate ones, gets a valid rung
     for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
         assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
@@ -347,7 +352,7 @@ def test_pick_tile_on_mi355x_square_sweep():
     MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
     want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
             1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
-            3072: (256, 256), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
+            3072: (192, 192), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
             8192: (256, 256)}
     for n, (bm, bn) in want.items():
         t = sdt.pick_tile(n, n, n, 256)
