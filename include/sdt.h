@@ -34,7 +34,7 @@
 
 /* Version of the structures and signatures below; bumped whenever sdt_tile,
  * sdt_launch or an entry point's arguments change, or entry points are added
- * (4: the off-ladder rungs 5 and 6, the [K][N] workspace entry points and
+ * (4: the off-ladder rungs 5-7, the [K][N] workspace entry points and
  * sdt_stream_read_runs).
  * sdt_abi_version() reports the version the library was built with: a caller
  * compiled against another header must not pass these structures to it. */
@@ -60,9 +60,9 @@ typedef enum sdt_status {
  * kernel parameter, each with its own warp layout). */
 typedef struct sdt_tile {
     int id;          /* rung index: 0-4 the ladder, largest tile first (256 x 256,
-                        256 x 128, 128 x 128, 128 x 64, 64 x 64); 5 and 6 the
-                        off-ladder 96 x 96 and 192 x 192 tiles (see
-                        sdt_pick_tile) */
+                        256 x 128, 128 x 128, 128 x 64, 64 x 64); 5, 6 and 7
+                        the off-ladder 96 x 96, 192 x 192 and 160 x 160
+                        tiles (see sdt_pick_tile) */
     int bm, bn, bk;
     int waves_m, waves_n;
     int threads;     /* 64 * waves_m * waves_n * kgroups */
@@ -74,9 +74,9 @@ typedef struct sdt_tile {
                         On rungs 1 and 2 (256 x 128, 128 x 128) the deep count
                         with one k-group runs v_mfma_f32_16x16x32 (two 32-deep
                         sub-steps per k-tile), and so does every pipeline
-                        of rungs 5 and 6 (96 x 96 with 48 x 48 per wave,
-                        192 x 192 with 96 x 48); every other launch runs
-                        v_mfma_f32_32x32x16.  The automatic plan takes the
+                        of rungs 5-7 (96 x 96 with 48 x 48 per wave,
+                        192 x 192 with 96 x 48, 160 x 160 with 80 x 80);
+                        every other launch runs v_mfma_f32_32x32x16.  The automatic plan takes the
                         long count (long_stages) in place of the deep one on a
                         rung that has it when the launch runs two k-groups and
                         K holds at least 12 full k-tiles */
@@ -340,8 +340,9 @@ int sdt_gemv_kn_num_variants(void);
  * An off-ladder rung with a smaller tile replaces the pick when its grid has
  * more workgroups than the pick's and at most num_cu (the first such rung in
  * id order): on MI355X the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3:
- * 144 workgroups -> 256) and the 192 x 192 rung in place of 256 x 256 (e.g.
- * 3072^3: 144 -> 256).
+ * 144 workgroups -> 256), the 192 x 192 rung in place of 256 x 256 (e.g.
+ * 3072^3: 144 -> 256) and the 160 x 160 rung in place of 256 x 128 (e.g.
+ * 2560^3: 200 -> 256).
  * Touches no device when num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
 

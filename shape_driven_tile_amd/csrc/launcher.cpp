@@ -278,7 +278,13 @@ int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     // 192 x 192 rung in place of the 256 x 256 ping-pong kernel: 3072^3
     // 54.2 -> 48.6, 2944^3 53.9 -> 46.8, 3072x3072x1024 23.4 -> 21.0,
     // 3072x3072x8192 131.9 -> 121.2, 3072x2816x4096 69.9 -> 61.3; with
-    // 272 workgroups (3000x3104x1000) 41.2 against 28.1.
+    // 272 workgroups (3000x3104x1000) 41.2 against 28.1.  The 160 x 160 rung
+    // in place of 256 x 128: 2560^3 36.7 -> 33.7, 2496^3 37.2 -> 33.8,
+    // 2240^3 31.3 -> 27.7, 2560x2560x1024 19.5 -> 17.1, 2560x2560x8192
+    // 101.3 -> 94.5, 1920x2560x4096 47.0 -> 45.2; it lost 2-4% where the
+    // 256 x 128 grid has no ragged edge and the 160 x 160 one does (2304^3
+    // 30.3 -> 31.5, 2176^3 28.2 -> 28.9): at the power limit the extra
+    // padded work costs clock.
     const int64_t br = ceil_div(M, kLadder[r].bm) * ceil_div(N, kLadder[r].bn);
     for (int c = kNumLadder; c < kNumTiles; ++c) {
         const int64_t bc = ceil_div(M, kLadder[c].bm) * ceil_div(N, kLadder[c].bn);

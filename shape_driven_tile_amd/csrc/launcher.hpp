@@ -46,11 +46,12 @@ constexpr TileDesc kLadder[] = {
     {128, 128, 2, 2, 3, 2, 0, 1, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
     {128, 64, 2, 2, 3, 2, 0, 0, 4, 1},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
     {64, 64, 2, 2, 3, 2, 0, 0, 4, 1},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
-    // Off the ladder (see kNumLadder), 16x16x32 MFMAs on every pipeline (48 is
-    // no multiple of 32): 4 waves of 48x48, 3 x 24 KB; 8 waves of 96x48,
-    // 3 x 48 KB.
+    // Off the ladder (see kNumLadder), 16x16x32 MFMAs on every pipeline (48
+    // and 80 are no multiples of 32): 4 waves of 48x48, 3 x 24 KB; 8 waves of
+    // 96x48, 3 x 48 KB; 4 waves of 80x80, 3 x 40 KB.
     {96, 96, 2, 2, 3, 1, 0, 1, 0, 0},
     {192, 192, 2, 4, 3, 1, 0, 1, 0, 0},
+    {160, 160, 2, 2, 3, 1, 0, 1, 0, 0},
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place

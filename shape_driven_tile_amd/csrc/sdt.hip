@@ -146,7 +146,7 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
 
 template <typename Elt>
 hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
-    static_assert(kNumTiles == 7, "dispatch table below lists every rung");
+    static_assert(kNumTiles == 8, "dispatch table below lists every rung");
     switch (pl.tile) {
         case 0: return launch_rung<Elt, 0>(p, pl, s);
         case 1: return launch_rung<Elt, 1>(p, pl, s);
@@ -154,7 +154,8 @@ hipError_t launch_gemm(const Plan& pl, GemmParams p, hipStream_t s) {
         case 3: return launch_rung<Elt, 3>(p, pl, s);
         case 4: return launch_rung<Elt, 4>(p, pl, s);
         case 5: return launch_rung<Elt, 5>(p, pl, s);
-        default: return launch_rung<Elt, 6>(p, pl, s);
+        case 6: return launch_rung<Elt, 6>(p, pl, s);
+        default: return launch_rung<Elt, 7>(p, pl, s);
     }
 }
 

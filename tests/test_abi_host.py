@@ -182,13 +182,13 @@ def lds_bytes(t, stages):
 
 def test_ladder_is_well_formed():
     tiles = ladder()
-    assert len(tiles) == NUM_LADDER + 2
+    assert len(tiles) == NUM_LADDER + 3
     areas = [t["bm"] * t["bn"] for t in tiles[:NUM_LADDER]]
     assert areas == sorted(areas, reverse=True), "largest tile first"
-    # the off-ladder 96 x 96 and 192 x 192 rungs: 16x16x32 MFMAs only, one
-    # k-group, no k-split
+    # the off-ladder 96 x 96, 192 x 192 and 160 x 160 rungs: 16x16x32 MFMAs
+    # only, one k-group, no k-split
     shapes = [(t["bm"], t["bn"], t["waves_m"], t["waves_n"]) for t in tiles[NUM_LADDER:]]
-    assert shapes == [(96, 96, 2, 2), (192, 192, 2, 4)]
+    assert shapes == [(96, 96, 2, 2), (192, 192, 2, 4), (160, 160, 2, 2)]
     for off in tiles[NUM_LADDER:]:
         assert off["kgroups"] == 1 and off["ksplit"] == 0 and off["long_stages"] == 0
     for t in tiles:
@@ -342,6 +342,8 @@ def test_pick_tile_properties():
     assert sdt.pick_tile(3072, 3072, 3072, 256)["id"] == 6      # 144 -> 256 workgroups
     assert sdt.pick_tile(3000, 3104, 1000, 256)["id"] == 0      # 272 > 256 of 192 x 192
     assert sdt.pick_tile(2816, 2816, 2816, 256)["id"] == 1      # 225 < 242 of 256 x 128
+    assert sdt.pick_tile(2560, 2560, 2560, 256)["id"] == 7      # 200 -> 256 workgroups
+    assert sdt.pick_tile(2048, 4096, 2048, 256)["id"] == 1      # 256 x 128 fills the CUs
     # any shape, even degenerate ones, gets a valid rung
     for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
         assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
@@ -351,7 +353,7 @@ def test_pick_tile_on_mi355x_square_sweep():
     """The rungs a sweep of every rung over square shapes measured fastest on
     MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
     want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
-            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
+            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (160, 160),
             3072: (192, 192), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
             8192: (256, 256)}
     for n, (bm, bn) in want.items():

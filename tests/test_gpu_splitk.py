@@ -171,6 +171,7 @@ def test_forced_split_needs_workspace_and_a_split_rung():
            dict(tile_id=1, splits=2, workspace=_ws(64 << 20)),
            dict(tile_id=5, splits=2, workspace=_ws(64 << 20)),
            dict(tile_id=6, splits=2, workspace=_ws(64 << 20)),
+           dict(tile_id=7, splits=2, workspace=_ws(64 << 20)),
            dict(tile_id=4, splits=17, workspace=_ws(64 << 20)),   # 16 full k-tiles
            dict(tile_id=4, splits=65, workspace=_ws(64 << 20)),
            dict(tile_id=4, splits=16, stagger=1, workspace=_ws(64 << 20))]
