@@ -125,7 +125,8 @@ typedef struct sdt_launch {
 /* C = A.B for M x N x K.
  * Requirements: M, N, K >= 0; lda >= K, ldb >= K, ldc >= N (else
  * SDT_ERR_INVALID_ARG); A, B, C 16-byte aligned and lda, ldb, ldc multiples of
- * 8 elements, lda and ldb below 2^22 (else SDT_ERR_UNSUPPORTED).  Any M, N, K
+ * 8 elements, lda and ldb below 2^22, M and N at most 2^31 - 1 (else
+ * SDT_ERR_UNSUPPORTED).  Any M, N, K
  * within those limits is computed exactly as defined (ragged edges are
  * masked).  M == 0 or N == 0 is a no-op; K == 0 writes zeros (the empty sum).
  * M == 1 runs the streaming decode kernel of gemv_f16_m1 (same result
@@ -189,7 +190,7 @@ int gemm_f16_noalloc(int64_t M, int64_t N, int64_t K,
 
 /* Bytes of workspace gemm_f16_ws's automatic plan uses for this product on a
  * device with num_cu compute units (num_cu <= 0 reads the current device);
- * 0 when it does not split.  Negative sizes: -1. */
+ * 0 when it does not split.  Negative sizes, or M, N or K past 2^31 - 1: -1. */
 int64_t sdt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int num_cu);
 
 /* Bytes of workspace a launch configuration (as gemm_f16_cfg takes it, every
@@ -343,7 +344,8 @@ int sdt_gemv_kn_num_variants(void);
  * 144 workgroups -> 256), the 192 x 192 rung in place of 256 x 256 (e.g.
  * 3072^3: 144 -> 256) and the 160 x 160 rung in place of 256 x 128 (e.g.
  * 2560^3: 200 -> 256).
- * Touches no device when num_cu > 0.  Returns SDT_OK or SDT_ERR_INVALID_ARG. */
+ * Touches no device when num_cu > 0.  Returns SDT_OK, SDT_ERR_INVALID_ARG, or
+ * SDT_ERR_UNSUPPORTED for M, N or K past 2^31 - 1. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
 
 /* Host-only: the plan gemm_f16_ws makes with a workspace of workspace_bytes
@@ -355,7 +357,9 @@ int sdt_pick_tile_ws(int64_t M, int64_t N, int64_t K, int num_cu, int64_t worksp
 /* Host-only, the mechanism of the rule above: given `rungs` thresholds in
  * units of ref_bm x ref_bn output blocks (largest tile first, non-increasing),
  * returns the first rung r with ceil(M/ref_bm)*ceil(N/ref_bn) >=
- * min_blocks[r], or rungs-1 if none qualifies; -1 on invalid input. */
+ * min_blocks[r], or rungs-1 if none qualifies; -1 on invalid input (M or N
+ * negative or past 2^31 - 1, a reference size or `rungs` not positive, NULL
+ * thresholds). */
 int sdt_pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn,
                   int rungs, const int64_t* min_blocks);
 
@@ -373,7 +377,8 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
  * the rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs) once K
  * holds at least 12 full k-tiles; the 2-stage pipeline is never planned (it
  * lost with the operands in HBM and tied with them in L2).  Stagger: as
- * gemm_f16 describes.  SDT_OK or SDT_ERR_INVALID_ARG. */
+ * gemm_f16 describes.  SDT_OK, SDT_ERR_INVALID_ARG, or SDT_ERR_UNSUPPORTED for M,
+ * N or K past 2^31 - 1. */
 int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int num_cu,
                   sdt_tile* out);
 

@@ -9,6 +9,12 @@ namespace sdt {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Every size a kernel takes is an int, and block counts are products of two
+// of them: M, N and K up to 2^31 - 1 keep those within int64_t.
+bool sizes_supported(int64_t M, int64_t N, int64_t K) {
+    return M <= INT_MAX && N <= INT_MAX && K <= INT_MAX;
+}
+
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
 sdt_tile describe(const Plan& p) {
@@ -70,6 +76,7 @@ int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     if (!d.ksplit || p.stagger) return 1;
     if (num_cu <= 0) num_cu = 256;
     const int64_t tiles = ceil_div(M, d.bm) * ceil_div(N, d.bn);
+    if (tiles <= 0) return 1;   // an empty product (M or N zero): nothing to split
     const int64_t nfull = K / kBK;
     int64_t s = num_cu / tiles;
     if (s > nfull / kSplitAutoMinKTiles) s = nfull / kSplitAutoMinKTiles;
@@ -77,8 +84,6 @@ int splits_for(const Plan& p, int64_t M, int64_t N, int64_t K, int num_cu) {
     return s >= 2 ? (int)s : 1;
 }
 
-// 2 stages while A and B (2 bytes per element) fit in one XCD's L2, else the
-// rung's deep pipeline.
 // Two k-groups on a rung built with them, when its grid is resident all at
 // once (at most one workgroup per CU) and the k-loop is long enough.
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
@@ -169,6 +174,7 @@ int check_plan(const Plan& p, int64_t K) {
 // when the caller offers ws_bytes >= 0 bytes of workspace and it fits.
 int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num_cu,
                  int64_t ws_bytes, Plan* out) {
+    if (!sizes_supported(M, N, K)) return SDT_ERR_UNSUPPORTED;
     if (cfg.tile_id < -1 || cfg.tile_id >= kNumTiles) return SDT_ERR_INVALID_ARG;
     if (cfg.stagger < -1 || cfg.stagger > 1) return SDT_ERR_INVALID_ARG;
     if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
@@ -238,7 +244,8 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
 // count reaches; the last rung is the fallback.
 int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
               const int64_t* min_blocks) {
-    if (M < 0 || N < 0 || ref_bm <= 0 || ref_bn <= 0 || rungs <= 0 || !min_blocks)
+    if (M < 0 || N < 0 || ref_bm <= 0 || ref_bn <= 0 || rungs <= 0 || !min_blocks ||
+        !sizes_supported(M, N, 0))
         return -1;
     const int64_t blocks = ceil_div(M, ref_bm) * ceil_div(N, ref_bn);
     for (int r = 0; r < rungs; ++r)
@@ -383,6 +390,7 @@ extern "C" int sdt_plan_tile(int tile_id, int64_t M, int64_t N, int64_t K, int n
                              sdt_tile* out) {
     if (tile_id < 0 || tile_id >= sdt::kNumTiles || M < 0 || N < 0 || K < 0 || !out)
         return SDT_ERR_INVALID_ARG;
+    if (!sdt::sizes_supported(M, N, K)) return SDT_ERR_UNSUPPORTED;
     if (num_cu <= 0) num_cu = 256;
     *out = sdt::describe(sdt::plan_for(tile_id, M, N, K, num_cu));
     return SDT_OK;

@@ -170,6 +170,7 @@ int check_gemv_kn_args(int64_t N, int64_t K, const void* x, const void* B, int64
                        const void* y);
 bool is_pow2(int64_t v);
 int64_t ceil_div(int64_t a, int64_t b);
+bool sizes_supported(int64_t M, int64_t N, int64_t K);
 int check_gemm_args(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda,
                     const void* B, int64_t ldb, const void* C, int64_t ldc);
 

@@ -580,7 +580,7 @@ extern "C" int gemm_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, 
 }
 
 extern "C" int64_t sdt_gemm_workspace_size(int64_t M, int64_t N, int64_t K, int num_cu) {
-    if (M < 0 || N < 0 || K < 0) return -1;
+    if (M < 0 || N < 0 || K < 0 || !sdt::sizes_supported(M, N, K)) return -1;
     if (M <= 1 || N == 0 || K == 0) return 0;   // routed to the GEMV, a no-op or a fill
     if (num_cu <= 0) {
         sdt::DeviceInfo dev;
@@ -682,6 +682,7 @@ extern "C" int sdt_gemv_kn_num_variants(void) { return sdt::kGemvKnVariants; }
 
 extern "C" int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out) {
     if (M < 0 || N < 0 || K < 0 || !out) return SDT_ERR_INVALID_ARG;
+    if (!sdt::sizes_supported(M, N, K)) return SDT_ERR_UNSUPPORTED;
     if (num_cu <= 0) {
         sdt::DeviceInfo dev;
         int st = sdt::device_info(&dev);

@@ -622,3 +622,27 @@ def test_stream_read_runs_argument_checks():
     assert L.sdt_stream_read_runs(b, 1000, 4096, 512, 64, o, None) == sdt.SDT_ERR_INVALID_ARG
     assert L.sdt_stream_read_runs(b + 8, *ok_args, o, None) == sdt.SDT_ERR_UNSUPPORTED
     assert L.sdt_stream_read_runs(b, *ok_args, o + 2, None) == sdt.SDT_ERR_UNSUPPORTED
+
+
+def test_sizes_past_int_range_refused():
+    """M, N or K past 2^31 - 1: every kernel size is an int, and the planner's
+    block counts (products of two sizes) must not overflow.  Refused before
+    any device call."""
+    big = 2 ** 40
+    for (M, N, K) in [(big, 64, 64), (64, big, 64), (64, 64, big), (big, big, 64)]:
+        with pytest.raises(sdt.SdtError) as e:
+            sdt.pick_tile(M, N, K, 256)
+        assert e.value.status == sdt.SDT_ERR_UNSUPPORTED
+        with pytest.raises(sdt.SdtError):
+            sdt.plan_tile(0, M, N, K, 256)
+        with pytest.raises(sdt.SdtError):
+            sdt.pick_tile_ws(M, N, K, 256, 1 << 30)
+        assert sdt.lib().sdt_gemm_workspace_size(M, N, K, 256) == -1
+    assert sdt.pick_rung(big, big, 1, 1, [1, 0]) == -1
+    assert sdt.pick_rung(2 ** 31 - 1, 2 ** 31 - 1, 1, 1, [1, 0]) == 0
+    L = sdt.lib()
+    # lda = ldb = K = 64 and ldc = N: the sizes alone decide
+    assert L.gemm_f16(big, 64, 64, 0x10000, 64, 0x20000, 64, 0x30000, 64, None) == \
+        sdt.SDT_ERR_UNSUPPORTED
+    assert L.gemm_f16_ws(64, big, 64, 0x10000, 64, 0x20000, 64, 0x30000, big, None, 0, None) == \
+        sdt.SDT_ERR_UNSUPPORTED
