@@ -199,31 +199,26 @@ def main():
         if n == DOMINANT:
             continue
         A, B = host[n]
-        C = ops[n][2].cpu().numpy().astype(np.float64)
-        ref = oracle.gemm(A, B)
-        gate[f"gemm_{n}_full"] = int((~(np.abs(C - ref) <= oracle.tolerance(ref))).sum())
+        gate[f"gemm_{n}_full"] = outside_tolerance(ops[n][2].cpu().numpy(), oracle.gemm(A, B))
     A, B = host[DOMINANT]
     if args.no_cpu_baseline:
         base, rows, ref = None, gate_rows(DOMINANT, 512), None
         ref = oracle.gemm(np.ascontiguousarray(A[rows]), B)
     else:
         base, rows, ref = cpu_baseline(oracle, host[DOMINANT], args.cpu_seconds)
-    C = ops[DOMINANT][2].cpu().numpy()[rows].astype(np.float64)
-    gate[f"gemm_{DOMINANT}_rows"] = int((~(np.abs(C - ref) <= oracle.tolerance(ref))).sum())
+    gate[f"gemm_{DOMINANT}_rows"] = outside_tolerance(ops[DOMINANT][2].cpu().numpy()[rows], ref)
     gate[f"gemm_{DOMINANT}_rows_checked"] = len(rows)
-    del C, ref
+    del ref
     bad_dec = 0
     for r in range(inputs.DECODE_BUFFERS):
         y.fill_(float("nan"))
         sdt.gemm_f16(x2, Ws[r], y2)
         torch.cuda.synchronize()
-        ref = oracle.gemv_m1(x_h, W_h[r])
-        got = y.cpu().numpy().astype(np.float64)
-        bad_dec += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+        bad_dec += outside_tolerance(y.cpu().numpy(), oracle.gemv_m1(x_h, W_h[r]))
     gate["gemv_8_buffers"] = bad_dec
-    if any(v for k, v in gate.items() if not k.endswith("_checked")):
-        print(json.dumps({"metric": METRIC, "value": None, "error": "parity gate failed",
-                          "gate": gate}), flush=True)
+    failed = gate_failure(gate)
+    if failed:
+        print(json.dumps(failed), flush=True)
         sys.exit(1)
     log(f"parity gate passed: {gate}")
 
@@ -274,11 +269,13 @@ def main():
                          "fp16 out) at M=N=K in {256,512,768,1024,1536,2048,4096,8192}, then "
                          "M=1 decode GEMV K=4096 N=12288 over 8 rotating weight buffers"),
             "flop_per_step": flop_step,
-            "device": props.name,
+            "device": props.name or None,
+            "arch": getattr(props, "gcnArchName", None),
             "cus": props.multi_processor_count,
             "tiles": {str(n): sdt.pick_tile(n, n, n, props.multi_processor_count)["id"]
                       for n in SIZES},
         },
+        "receipt": receipt(torch),
         "roofline": {
             "bound": "mfma",
             "kernel": f"gemm_pp_kernel (256x256 ping-pong) at {DOMINANT}^3",
@@ -319,6 +316,49 @@ def main():
         result["cpu_baseline"] = base
 
     print(json.dumps(result), flush=True)
+
+
+def receipt(torch) -> dict:
+    """What the run was made with: the build record written beside libsdt.so
+    (git commit, uncommitted changes, compiler), the ROCm release, torch and
+    its HIP runtime, the host CPU and this script's own hash."""
+    import hashlib
+    import platform
+    info = {}
+    try:
+        with open(os.path.join(ROOT, "shape_driven_tile_amd", "build_info.json")) as f:
+            info["build"] = json.load(f)
+    except (OSError, ValueError):
+        info["build"] = None
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    info["torch"] = torch.__version__
+    info["hip_runtime"] = getattr(torch.version, "hip", None)
+    info["host"] = platform.processor() or platform.machine()
+    info["bench_py_sha256_16"] = hashlib.sha256(open(__file__, "rb").read()).hexdigest()[:16]
+    return info
+
+
+def outside_tolerance(got, ref, dtype: str = "f16") -> int:
+    """Elements of `got` (values) outside the oracle's acceptance bound around
+    `ref` (fp16 output: 1e-2 + 2e-3 |ref|; bf16: the wider bf16 bound); a NaN
+    or inf where `ref` is finite counts as outside."""
+    import numpy as np
+    import oracle
+    got = np.asarray(got, dtype=np.float64)
+    return int((~(np.abs(got - ref) <= oracle.tolerance(ref, dtype))).sum())
+
+
+def gate_failure(gate: dict):
+    """The JSON record a failed parity gate prints in place of any
+    measurement (no value, no throughput), or None when every count of
+    elements outside the tolerance is zero."""
+    if any(v for k, v in gate.items() if not k.endswith("_checked")):
+        return {"metric": METRIC, "value": None, "error": "parity gate failed", "gate": gate}
+    return None
 
 
 def code_sha16(path: str) -> str:
@@ -618,9 +658,7 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
         for r in range(inputs.DECODE_BUFFERS):
             sdt.gemv_f16_m1_kn(x, Wkn[r], y, variant=v)
             torch.cuda.synchronize()
-            ref = oracle.gemv_kn(x_h, Wkn_h[r])
-            got = y.cpu().numpy().astype(np.float64)
-            bad += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+            bad += outside_tolerance(y.cpu().numpy(), oracle.gemv_kn(x_h, Wkn_h[r]))
         if bad:
             det["decode_kn_cold"]["variants"][str(v)] = {"gate": f"{bad} outside tolerance"}
             log(f"decode [K][N] variant {v}: PARITY FAILED ({bad}), not timed")
@@ -643,9 +681,7 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     for r in range(inputs.DECODE_BUFFERS):
         sdt.gemv_f16_m1_kn_ws(x, Wkn[r], y, workspace=ws_kn)
         torch.cuda.synchronize()
-        ref = oracle.gemv_kn(x_h, Wkn_h[r])
-        got = y.cpu().numpy().astype(np.float64)
-        bad += int((~(np.abs(got - ref) <= oracle.tolerance(ref))).sum())
+        bad += outside_tolerance(y.cpu().numpy(), oracle.gemv_kn(x_h, Wkn_h[r]))
     if bad:
         det["decode_kn_cold"]["split_ws"] = {"gate": f"{bad} outside tolerance"}
         log(f"decode [K][N] split over K: PARITY FAILED ({bad}), not timed")
@@ -720,8 +756,7 @@ def detail_ksplit(sdt, torch, np, inputs, oracle, dev):
         sdt.gemm_f16_ws(dA, dB, C, workspace=ws)
         torch.cuda.synchronize()
         ref = oracle.gemm(A, B)
-        bad = int((~(np.abs(C.cpu().numpy().astype(np.float64) - ref) <=
-                     oracle.tolerance(ref))).sum())
+        bad = outside_tolerance(C.cpu().numpy(), ref)
         key = f"{M}x{N}x{K}"
         if bad:
             out[key] = {"gate": f"{bad} outside tolerance"}
@@ -764,8 +799,7 @@ def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):
         r = rng.integers(0, n, 1024)
         c = rng.integers(0, n, 1024)
         ref = oracle.gemm_sample(A, B, r, c, dtype="bf16")
-        got = oracle.bf16_decode(bits(C)[r, c])
-        bad = int((~(np.abs(got - ref) <= oracle.tolerance(ref, "bf16"))).sum())
+        bad = outside_tolerance(oracle.bf16_decode(bits(C)[r, c]), ref, "bf16")
         if bad:
             out["square_graph"][str(n)] = {"gate": f"{bad} of 1024 sampled outside tolerance"}
             log(f"bf16 square {n}: PARITY FAILED ({bad}), not timed")
@@ -791,7 +825,7 @@ def detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv):
         sdt.gemv_bf16_m1(x, Ws[r], y)
         torch.cuda.synchronize()
         ref = oracle.gemv_m1(x_h, W_h[r], dtype="bf16")
-        bad += int((~(np.abs(oracle.bf16_decode(bits(y)) - ref) <= oracle.tolerance(ref, "bf16"))).sum())
+        bad += outside_tolerance(oracle.bf16_decode(bits(y)), ref, "bf16")
     if bad:
         out["decode_cold"] = {"gate": f"{bad} outside tolerance"}
         log(f"bf16 decode: PARITY FAILED ({bad}), not timed")

@@ -50,7 +50,33 @@ def build(resource_usage: bool = False, verbose: bool = False) -> str:
     if (resource_usage or verbose) and err:
         print(err)
     os.replace(tmp, LIB)
+    write_build_info()
     return LIB
+
+
+BUILD_INFO = os.path.join(HERE, "build_info.json")
+
+
+def write_build_info() -> None:
+    """Record what libsdt.so was built from (the git commit and whether the
+    tree had uncommitted changes, the compiler's version line) beside it, for
+    the benchmark's receipt; fields that cannot be read are null."""
+    import json
+
+    def run(cmd):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, cwd=ROOT, timeout=30)
+            return r.stdout.strip() if r.returncode == 0 else None
+        except (OSError, subprocess.SubprocessError):
+            return None
+    status = run(["git", "status", "--porcelain", "--untracked-files=no"])
+    hip = run([hipcc(), "--version"])
+    info = {"commit": run(["git", "rev-parse", "HEAD"]),
+            "dirty": None if status is None else bool(status),
+            "hipcc": hip.splitlines()[0] if hip else None,
+            "arch": ARCH}
+    with open(BUILD_INFO, "w") as f:
+        json.dump(info, f)
 
 
 CAPI_SRC = os.path.join(ROOT, "tests", "capi", "capi_check.cpp")
