@@ -339,8 +339,8 @@ int sdt_gemv_kn_num_variants(void);
  * sdt_pick_rung over rungs 0-4 with rung r taken from
  * (bm/64)(bn/64)(num_cu/2 + 1) 64 x 64 blocks up (the last rung below that).
  * An off-ladder rung with a smaller tile replaces the pick when its grid has
- * more workgroups than the pick's and at most num_cu (the first such rung in
- * id order): on MI355X the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3:
+ * more workgroups than the pick's, at most num_cu and at least 7/8 of num_cu
+ * (the first such rung in id order): on MI355X the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3:
  * 144 workgroups -> 256), the 192 x 192 rung in place of 256 x 256 (e.g.
  * 3072^3: 144 -> 256) and the 160 x 160 rung in place of 256 x 128 (e.g.
  * 2560^3: 200 -> 256).

@@ -287,16 +287,22 @@ int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     // 3072x3072x8192 131.9 -> 121.2, 3072x2816x4096 69.9 -> 61.3; with
     // 272 workgroups (3000x3104x1000) 41.2 against 28.1.  The 160 x 160 rung
     // in place of 256 x 128: 2560^3 36.7 -> 33.7, 2496^3 37.2 -> 33.8,
-    // 2240^3 31.3 -> 27.7, 2560x2560x1024 19.5 -> 17.1, 2560x2560x8192
-    // 101.3 -> 94.5, 1920x2560x4096 47.0 -> 45.2; it lost 2-4% where the
-    // 256 x 128 grid has no ragged edge and the 160 x 160 one does (2304^3
-    // 30.3 -> 31.5, 2176^3 28.2 -> 28.9): at the power limit the extra
-    // padded work costs clock.
+    // 2560x2560x1024 19.5 -> 17.1, 2560x2560x8192 101.3 -> 94.5,
+    // 1280x5120x4096 52.1 -> 49.9; it lost 4% at 2304^3 (30.3 -> 31.5),
+    // where the 256 x 128 grid has no ragged edge and the 160 x 160 one
+    // does: at the power limit the extra padded work costs clock.
+    //
+    // The replacement's grid must also fill at least 7/8 of the CUs: below
+    // that the measured outcomes of the 160 x 160 rung scattered by +-5% on
+    // rectangular shapes (768x6144x4096, 195 workgroups: 46.1 against 44.0;
+    // 3072x1536x4096, 200: 47.0 against 44.6; 2048x2560x4096, 208: 45.4
+    // against 48.1), while from 7/8 up every shape measured gained or tied
+    // but 2304^3 (225 workgroups: 31.5 against 30.3).
     const int64_t br = ceil_div(M, kLadder[r].bm) * ceil_div(N, kLadder[r].bn);
     for (int c = kNumLadder; c < kNumTiles; ++c) {
         const int64_t bc = ceil_div(M, kLadder[c].bm) * ceil_div(N, kLadder[c].bn);
         if (kLadder[c].bm * kLadder[c].bn < kLadder[r].bm * kLadder[r].bn && br < bc &&
-            bc <= num_cu)
+            bc <= num_cu && 8 * bc >= 7 * int64_t(num_cu))
             return c;
     }
     return r;

@@ -156,18 +156,26 @@ def blocks(t, M, N):
     return -(-M // t["bm"]) * -(-N // t["bn"])
 
 
-def expected_pick(M, N, num_cu):
-    """The header's rule, restated: the ladder's pick from the 64 x 64 block
-    count, then an off-ladder rung with a smaller tile whose grid is larger
-    than the pick's and at most num_cu."""
+def ladder_pick(M, N, num_cu):
+    """The ladder's own pick: the first rung whose 64 x 64 block count reaches
+    (bm/64)(bn/64)(num_cu/2 + 1), else the smallest."""
     tiles = ladder()
     b64 = -(-M // 64) * -(-N // 64)
     area = [(r["bm"] // 64) * (r["bn"] // 64) for r in tiles[:NUM_LADDER]]
-    r = next((i for i, a in enumerate(area[:-1]) if b64 >= a * (num_cu // 2 + 1)),
-             NUM_LADDER - 1)
+    return next((i for i, a in enumerate(area[:-1]) if b64 >= a * (num_cu // 2 + 1)),
+                NUM_LADDER - 1)
+
+
+def expected_pick(M, N, num_cu):
+    """The header's rule, restated: the ladder's pick from the 64 x 64 block
+    count, then an off-ladder rung with a smaller tile whose grid is larger
+    than the pick's, at most num_cu and at least 7/8 of it."""
+    tiles = ladder()
+    r = ladder_pick(M, N, num_cu)
     for c in tiles[NUM_LADDER:]:
         if (c["bm"] * c["bn"] < tiles[r]["bm"] * tiles[r]["bn"]
-                and blocks(tiles[r], M, N) < blocks(c, M, N) <= num_cu):
+                and blocks(tiles[r], M, N) < blocks(c, M, N) <= num_cu
+                and 8 * blocks(c, M, N) >= 7 * num_cu):
             return c["id"]
     return r
 
@@ -314,9 +322,13 @@ def test_pick_tile_properties():
             t = sdt.pick_tile(n, n, n, num_cu)
             assert 0 <= t["id"] < len(tiles)
             assert t == sdt.pick_tile(n, n, n, num_cu), "deterministic"
-            area = t["bm"] * t["bn"]
-            assert area >= prev_area, "tile grows with the square size"
+            # the ladder's pick grows with the square size; an off-ladder rung
+            # only ever stands in for it with a smaller tile
+            r = ladder_pick(n, n, num_cu)
+            area = tiles[r]["bm"] * tiles[r]["bn"]
+            assert area >= prev_area, "the ladder's tile grows with the square size"
             prev_area = area
+            assert t["id"] == r or t["bm"] * t["bn"] < area
             # never off the largest tile while its grid alone fills the machine
             big = tiles[0]
             if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
@@ -332,7 +344,7 @@ def test_pick_tile_properties():
                 wgs = (n // t["bm"]) * (n // t["bn"])
                 assert t["id"] == NUM_LADDER - 1 or wgs > num_cu // 2
             if t["id"] >= NUM_LADDER:   # more workgroups than the ladder's pick, one per CU
-                assert blocks(t, n, n) <= num_cu
+                assert 7 * num_cu <= 8 * blocks(t, n, n) <= 8 * num_cu
     for (M, N) in [(1536, 1536), (1440, 1440), (1152, 1920), (768, 3072), (1664, 1664),
                    (1536, 2048), (1280, 1280), (100, 30000), (30000, 100)]:
         for num_cu in (80, 256, 304):
@@ -344,6 +356,9 @@ def test_pick_tile_properties():
     assert sdt.pick_tile(2816, 2816, 2816, 256)["id"] == 1      # 225 < 242 of 256 x 128
     assert sdt.pick_tile(2560, 2560, 2560, 256)["id"] == 7      # 200 -> 256 workgroups
     assert sdt.pick_tile(2048, 4096, 2048, 256)["id"] == 1      # 256 x 128 fills the CUs
+    assert sdt.pick_tile(2048, 2560, 4096, 256)["id"] == 1      # 208 < 7/8 of 256 of 160 x 160
+    assert sdt.pick_tile(768, 11008, 4096, 256)["id"] == 6      # 232 of 192 x 192
+    assert sdt.pick_tile(1440, 1440, 1440, 256)["id"] == 5      # 225 of 96 x 96
     # any shape, even degenerate ones, gets a valid rung
     for (M, N) in [(1, 1), (1, 100000), (100000, 1), (0, 5), (7, 3)]:
         assert 0 <= sdt.pick_tile(M, N, 64, 256)["id"] < len(tiles)
