@@ -93,6 +93,30 @@ def test_integer_exact_8192_rows_auto():
     assert_bitexact(C[r, c], oracle.gemm_sample(A, B, r, c))
 
 
+@pytest.mark.parametrize("shape,rung", [((1536, 1536, 1536), 5), ((1440, 1440, 1000), 5),
+                                        ((3072, 3072, 1024), 6), ((768, 11008, 512), 6),
+                                        ((2560, 2560, 2560), 7), ((1280, 5120, 1024), 7)])
+def test_integer_exact_off_ladder_auto(shape, rung):
+    """Shapes whose automatic plan takes an off-ladder rung (96 x 96, 192 x 192,
+    160 x 160) at their real grids (one workgroup per CU, XCD-aware order,
+    ragged edges where the tile does not divide), every element bit for bit
+    on integer inputs, then uniform inputs within the tolerance."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    assert sdt.pick_tile(M, N, K, 256)["id"] == rung
+    A = inputs.integer_f16((M, K), 31)
+    B = inputs.integer_f16((N, K), 32)
+    say(f"integer {shape} automatic plan (rung {rung}), full C")
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_bitexact(C, oracle.gemm(A, B))
+    Au = inputs.uniform_f16((M, K), 33)
+    Bu = inputs.uniform_f16((N, K), 34)
+    say(f"uniform {shape} automatic plan (rung {rung}), full C")
+    C, _ = run_gemm(Au, Bu)
+    assert_close(C, oracle.gemm(Au, Bu))
+
+
 def test_integer_exact_pingpong_short_k_block_order():
     """The ping-pong kernel (forced, and the automatic plan) at 4096 x 4096 x
     128: two k-tiles, fewer than its stages, the 16 x 16-block tile order,
