@@ -899,7 +899,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
 // The second kernel of a k-split launch with split_algo 0: one workgroup per
 // output tile, laid out as gemm_kernel's k-group 0 (WM x WN waves), sums the
 // tile's `splits` partials in split order, ((P_0 + P_1) + P_2) + ..., and
-// stores the block with gemm_kernel's epilogue.
+// stores the block with gemm_kernel's epilogue.  The slots are loaded G at a
+// time (G * FN * FM * ACC floats per lane: 128 for every tile), all G in
+// flight before their adds: a load-then-add loop waits one memory round trip
+// per split.  A slot past the last split is loaded through an empty buffer
+// descriptor (zeros, no memory access) and not added.
 template <typename Elt, int BM, int BN, int WM, int WN, int MF>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_splitk_reduce_kernel(GemmParams p) {
     constexpr int NMN = WM * WN;
@@ -907,6 +911,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_splitk_reduce_kernel(GemmPa
     constexpr int FM = WTM / MF, FN = WTN / MF;
     constexpr int ACC = MF == 32 ? 16 : 4;
     constexpr int SLOT = FN * FM * ACC * 64;
+    constexpr int G = 128 / (FN * FM * ACC) > 8 ? 8 : 128 / (FN * FM * ACC);
+    static_assert(G >= 1, "a slot fits the registers");
     typedef std::conditional_t<MF == 32, floatx16_t, floatx4_t> acc_t;
     __shared__ int4_t smem[NMN * 256];
     const int lane = threadIdx.x & 63;
@@ -917,8 +923,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_splitk_reduce_kernel(GemmPa
     grouped_origin(p, tile, BM, BN, m0, n0);
     acc_t acc[FN][FM];
     load_partial<0, false>(acc, partial_slot(p, tile, 0, wave, NMN, SLOT), lane);
-    for (int s = 1; s < p.splits; ++s)
-        load_partial<0, true>(acc, partial_slot(p, tile, s, wave, NMN, SLOT), lane);
+    for (int s0 = 1; s0 < p.splits; s0 += G) {
+        acc_t v[G][FN][FM];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+            load_partial<0, false>(v[g],
+                                   s0 + g < p.splits ? partial_slot(p, tile, s0 + g, wave, NMN, SLOT)
+                                                     : make_rsrc(p.ws, 0),
+                                   lane);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            if (s0 + g < p.splits) {
+#pragma unroll
+                for (int i = 0; i < FN; ++i)
+#pragma unroll
+                    for (int j = 0; j < FM; ++j) acc[i][j] += v[g][i][j];
+            }
+        }
+    }
     gemm_epilogue<Elt, MF>(p, acc, m0 + wave_m * WTM, n0 + wave_n * WTN, lane, smem + wave * 256);
 }
 

@@ -395,13 +395,24 @@ __global__ __launch_bounds__(NW * 64) void gemv_kn_kernel(GemvKnParams p) {
 }
 
 // Second kernel of a split [K][N] product: y(n) = the `splits` partial sums of
-// column n added in split order, rounded once to the element type.
+// column n added in split order, rounded once to the element type.  The
+// partials are loaded eight splits at a time, all eight in flight before the
+// adds (a load-then-add loop waits one memory round trip per split).
 template <typename Elt>
 __global__ __launch_bounds__(256) void gemv_kn_reduce_kernel(GemvKnParams p, int splits) {
+    constexpr int G = 8;
     const int n = blockIdx.x * 256 + threadIdx.x;
     if (n >= p.N) return;
-    float s = p.part[n];
-    for (int q = 1; q < splits; ++q) s += p.part[(int64_t)q * p.pstride + n];
+    float s = 0.0f;
+    for (int q0 = 0; q0 < splits; q0 += G) {
+        float v[G];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            v[j] = q0 + j < splits ? p.part[(int64_t)(q0 + j) * p.pstride + n] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+            if (q0 + j < splits) s = q0 + j == 0 ? v[j] : s + v[j];
+    }
     const typename Elt::scalar h = (typename Elt::scalar)s;
     p.y[n] = __builtin_bit_cast(uint16_t, h);
 }
