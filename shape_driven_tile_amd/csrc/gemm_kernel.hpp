@@ -6,10 +6,14 @@
 // current one is consumed, an XOR swizzle, B stored transposed) and "The part
 // that actually mattered" (the tile is a compile-time parameter with its own
 // wave layout), re-designed for CDNA4:
-//   * wave64 and v_mfma_f32_32x32x16_f16 (v_mfma_f32_32x32x16_bf16 for the
-//     bf16 variant): each wave owns a (BM/WM) x (BN/WN) block of 32x32
-//     accumulator tiles (the 256 x 256 ping-pong kernel at the end of this
-//     file uses 16x16x32 MFMAs and its own schedule);
+//   * wave64, each wave owning a (BM/WM) x (BN/WN) block of accumulator
+//     tiles: MF = 32 runs v_mfma_f32_32x32x16_f16 (_bf16 for the bf16
+//     variant) on 32x32 tiles, MF = 16 v_mfma_f32_16x16x32 on 16x16 tiles,
+//     which costs less energy per FLOP where the part runs at its power
+//     limit (the one-k-group deep pipelines of the 256 x 128 and 128 x 128
+//     rungs, every pipeline of the 96, 160 and 192 rungs; the 256 x 256
+//     ping-pong kernel at the end of this file also uses 16x16x32, with its
+//     own schedule);
 //   * both operands are K-contiguous rows (A row-major, B "K-major"), staged
 //     the same way: a k-tile is BM (or BN) rows of 64 fp16 = 128 bytes, eight
 //     16-byte chunks per row; chunk c of row r is stored at chunk c ^ swz(r),
@@ -23,13 +27,15 @@
 //     landing in the others; right after the single barrier of step i the
 //     loads of tile i+NS are issued into the stage tile i just freed, so the
 //     global prefetch runs NS-1 tiles deep;
-//   * MFMA fragments are double-buffered in registers across the four 16-deep
-//     sub-steps of a k-tile, so the LDS reads of sub-step kk+1 are in flight
-//     under the MFMAs of sub-step kk, and the first reads of tile i+1 go out
-//     under the last MFMAs of tile i, past the barrier;
-//   * KS = 2 k-groups: a second set of waves takes sub-steps 1 and 3 of every
-//     k-tile while the first takes 0 and 2, halving each wave's dependent MFMA
-//     chain per k-tile and doubling the waves a small grid keeps in flight;
+//   * MFMA fragments are double-buffered in registers across the sub-steps
+//     of a k-tile (four 16 deep with MF = 32, two 32 deep with MF = 16), so
+//     the LDS reads of sub-step kk+1 are in flight under the MFMAs of
+//     sub-step kk, and the first reads of tile i+1 go out under the last
+//     MFMAs of tile i, past the barrier;
+//   * KS = 2 k-groups (MF = 32): a second set of waves takes sub-steps 1
+//     and 3 of every k-tile while the first takes 0 and 2, halving each
+//     wave's dependent MFMA chain per k-tile and doubling the waves a small
+//     grid keeps in flight;
 //     the second group's partial sums are added to the first's through LDS
 //     (a fixed order: the result is deterministic) before the epilogue;
 //   * k-loop stagger (FlyDSL PR "Speed up the RDNA3 GEMM up to 1.85x by
@@ -41,15 +47,16 @@
 //   * edges: operand rows come through buffer descriptors clipped to the
 //     valid rows, so rows past M or N read as zero; a partial last k-tile is
 //     loaded through registers with per-element masking; stores are masked;
-//     wave tiles 64 columns wide pass their output through LDS so that each
-//     lane stores 16 contiguous bytes;
+//     wave tiles 64 columns wide, and every MF = 16 wave tile, pass their
+//     output through LDS so that each lane stores 16 contiguous bytes;
 //   * MI355X deals workgroup ids round-robin over its XCDs, each with a
 //     private L2; ids are remapped so every XCD works through a contiguous,
 //     GROUP_M-grouped band of output tiles.
 //
 // The MFMA is issued as D = B_frag . A_frag^T (the instruction's first
 // operand takes rows of B), so each lane's four consecutive accumulator rows
-// are four consecutive n of one output row m and leave as one 8-byte store.
+// are four consecutive n of one output row m (one 8-byte store where a wave
+// tile 32 columns wide stores them directly).
 #pragma once
 
 #include <hip/hip_runtime.h>
