@@ -76,6 +76,37 @@ def test_bf16_integer_exact_every_tile(shape):
         assert_bitexact_bf16(C, ref)
 
 
+def _random_shapes_bf16(count, seed=4049, max_work=2 ** 33):
+    """Seeded shapes: M and N log-uniform in [1, 4096] (a quarter) or
+    [256, 4096], K log-uniform in [1, 4096], M * N * K under max_work, row
+    pitches padded by 0-40 elements and rounded up to multiples of 8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        lo = 0 if len(out) < count // 4 else 8
+        M, N = (int(round(2 ** rng.uniform(lo, 12))) for _ in range(2))
+        K = int(round(2 ** rng.uniform(0, 12)))
+        if M * N * K <= max_work:
+            out.append((M, N, K, int(rng.integers(0, 41)), int(rng.integers(0, 41))))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,pa,pb", _random_shapes_bf16(16))
+def test_bf16_integer_exact_random_shapes_auto(M, N, K, pa, pb):
+    """gemm_bf16's automatic plan on seeded random shapes with NaN-padded
+    rows: integer inputs, bit for bit against the oracle's bf16 rounding."""
+    from shape_driven_tile_amd import binding as sdt
+    say(f"bf16 random auto M={M} N={N} K={K} pads={pa},{pb} "
+        f"rung={sdt.pick_tile(M, N, K, 256)['id']}")
+    ka = -(-(K + pa) // 8) * 8
+    kb = -(-(K + pb) // 8) * 8
+    A = inputs.padded_bits(inputs.integer_bf16((M, K), 3000 + M), ka)
+    B = inputs.padded_bits(inputs.integer_bf16((N, K), 4000 + N), kb)
+    C, pad_ok = run_gemm_bf16(A, B, K=K)
+    assert pad_ok
+    assert_bitexact_bf16(C, oracle.gemm(A, B, K=K, dtype="bf16"))
+
+
 def test_bf16_two_kgroups_integer():
     from shape_driven_tile_amd import binding as sdt
     M, N, K = 257, 259, 4160

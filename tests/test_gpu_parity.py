@@ -408,6 +408,52 @@ def test_ragged_and_padded(M, N, K, pa, pb, pc):
     assert pad_ok, "kernel wrote past column N"
 
 
+def _random_shapes(count, seed=2024, max_work=2 ** 33):
+    """Seeded shapes for the automatic plan: K log-uniform in [1, 4096]; M and
+    N log-uniform in [1, 4096] for a quarter of the shapes and in [256, 4096]
+    for the rest (so the larger rungs come up too); M * N * K kept under
+    max_work so the oracle stays quick; leading dimensions padded by 0-40
+    elements, rounded up to multiples of 8."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        lo = 0 if len(out) < count // 4 else 8
+        M, N = (int(round(2 ** rng.uniform(lo, 12))) for _ in range(2))
+        K = int(round(2 ** rng.uniform(0, 12)))
+        if M * N * K > max_work:
+            continue
+        pads = [int(rng.integers(0, 41)) for _ in range(3)]
+        out.append((M, N, K, *pads))
+    return out
+
+
+@pytest.mark.parametrize("M,N,K,pa,pb,pc", _random_shapes(40))
+def test_integer_exact_random_shapes_auto(M, N, K, pa, pb, pc):
+    """Seeded random shapes through gemm_f16's automatic plan (whatever rung,
+    pipeline, k-group count and stagger it picks), integer inputs with
+    NaN-filled padding: C equals the oracle's RNE result bit for bit and
+    nothing past column N is written."""
+    from shape_driven_tile_amd import binding as sdt
+    plan = sdt.pick_tile(M, N, K, 256)
+    say(f"random auto M={M} N={N} K={K} pads={pa},{pb},{pc} rung={plan['id']} "
+        f"stages={plan['stages']} kgroups={plan['kgroups']} stagger={plan['stagger']}")
+    ka = -(-(K + pa) // 8) * 8
+    kb = -(-(K + pb) // 8) * 8
+    A = inputs.padded(inputs.integer_f16((M, K), 1000 + M), ka)
+    B = inputs.padded(inputs.integer_f16((N, K), 2000 + N), kb)
+    C, pad_ok = run_gemm(A, B, K=K, ldc_pad=pc)
+    assert_bitexact(C, oracle.gemm(A, B, K=K))
+    assert pad_ok, "kernel wrote past column N"
+
+
+def test_random_shapes_reach_every_rung():
+    """The random-shape set above reaches at least five rungs (a host-side
+    check of what it covers)."""
+    from shape_driven_tile_amd import binding as sdt
+    rungs = {sdt.pick_tile(M, N, K, 256)["id"] for M, N, K, *_ in _random_shapes(40) if M > 1}
+    assert len(rungs) >= 5, rungs
+
+
 def test_every_tile_forced_uniform():
     A, B = inputs.square_operands(520, 4)
     ref = oracle.gemm(A, B)

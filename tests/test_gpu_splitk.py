@@ -95,6 +95,50 @@ def test_integer_exact_every_split(shape):
     assert _counters_zero(ws, 65536), "arrival counters not left at zero"
 
 
+def _random_long_k(count, seed=77, max_work=2 ** 33):
+    """Seeded long-K shapes for gemm_f16_ws's automatic plan: M and N
+    log-uniform in [1, 2048], K log-uniform in [1024, 49152], M * N * K under
+    max_work (the oracle stays quick)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < count:
+        M, N = (int(round(2 ** rng.uniform(0, 11))) for _ in range(2))
+        K = int(round(2 ** rng.uniform(10, np.log2(49152))))
+        if M * N * K <= max_work:
+            out.append((M, N, K))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_long_k(24))
+def test_integer_exact_random_long_k_ws(shape):
+    """Seeded random long-K shapes through gemm_f16_ws with the workspace its
+    plan asks for (split or not, whatever the plan picks): integer inputs, C
+    equal to the oracle's RNE result bit for bit, nothing written past column
+    N, and the arrival counters left at zero."""
+    sdt = _sdt()
+    M, N, K = shape
+    plan = sdt.pick_tile_ws(M, N, K, 0, 1 << 40)
+    need = sdt.gemm_workspace_size(M, N, K)
+    assert (need > 0) == (plan["splits"] > 1)
+    say(f"random long-K ws {shape} rung={plan['id']} splits={plan['splits']} "
+        f"algo={plan['split_algo']} kgroups={plan['kgroups']} stages={plan['stages']}")
+    ld = -(-K // 8) * 8                  # rows padded (NaN) to the 8-element pitch
+    A = inputs.padded(inputs.integer_f16((M, K), 500 + M), ld)
+    B = inputs.padded(inputs.integer_f16((N, K), 600 + N), ld)
+    ws = _ws(max(need, 65536))
+    C, pad_ok = _launch(to_dev(A)[:, :K], to_dev(B)[:, :K], ws)
+    assert pad_ok
+    assert_bitexact(C, oracle.gemm(A, B, K=K))
+    assert _counters_zero(ws, 65536 if need else 0), "arrival counters not left at zero"
+
+
+def test_random_long_k_set_splits():
+    """Host-side: the random long-K set above has split and unsplit plans."""
+    sdt = _sdt()
+    splits = [sdt.pick_tile_ws(M, N, K, 256, 1 << 40)["splits"] for M, N, K in _random_long_k(24)]
+    assert sum(s > 1 for s in splits) >= 6 and sum(s == 1 for s in splits) >= 2, splits
+
+
 @pytest.mark.parametrize("shape", [(256, 256, 256), (512, 512, 512), (1024, 1024, 1024),
                                    (1536, 1536, 1536), (256, 256, 16384), (128, 128, 65536),
                                    (512, 512, 8192), (384, 384, 12288), (200, 300, 20000)])
