@@ -565,10 +565,17 @@ extern "C" int gemm_f16_noalloc(int64_t M, int64_t N, int64_t K, const void* A, 
                                 const void* B, int64_t ldb, void* C, int64_t ldc, void* stream) {
     int st = sdt::check_gemm_args(M, N, K, A, lda, B, ldb, C, ldc);
     if (st != SDT_OK) return st;
+    if (!sdt::sizes_supported(M, N, K)) return SDT_ERR_UNSUPPORTED;   // as gemm_f16
     hipStream_t s = static_cast<hipStream_t>(stream);
     // the plan gemm_f16_ws makes with a workspace as large as it asks for
-    const int64_t need = (M <= 1 || N == 0 || K == 0) ? 0 : sdt_gemm_workspace_size(M, N, K, 0);
-    if (need < 0) return SDT_ERR_INVALID_ARG;
+    int64_t need = 0;
+    if (!(M <= 1 || N == 0 || K == 0)) {
+        sdt::DeviceInfo dev;
+        st = sdt::device_info(&dev);
+        if (st != SDT_OK) return st;
+        need = sdt_gemm_workspace_size(M, N, K, dev.num_cu);
+        if (need < 0) return SDT_ERR_UNSUPPORTED;
+    }
     if (need > sdt::kScratchBytes) return SDT_ERR_UNSUPPORTED;
     void* ws = nullptr;
     if (need > 0) {

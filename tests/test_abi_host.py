@@ -661,3 +661,5 @@ def test_sizes_past_int_range_refused():
         sdt.SDT_ERR_UNSUPPORTED
     assert L.gemm_f16_ws(64, big, 64, 0x10000, 64, 0x20000, 64, 0x30000, big, None, 0, None) == \
         sdt.SDT_ERR_UNSUPPORTED
+    assert L.gemm_f16_noalloc(big, 64, 64, 0x10000, 64, 0x20000, 64, 0x30000, 64, None) == \
+        sdt.SDT_ERR_UNSUPPORTED
