@@ -312,6 +312,12 @@ def main():
             # the clock sampled in the separate under-load window
             clk["timed_region_frac_of_clock_ceiling"] = round(
                 achieved / clk["mfma_ceiling_at_clock_tflops"], 4)
+        cold = result["detail"].get("decode_cold") or {}
+        if cold.get("us"):
+            # the same GEMV alone: graph-replayed over the rotating buffers
+            # (no dispatch gap or event in the span), from detail.decode_cold
+            result["decode"]["cold_graph_us_median"] = cold["us"]["median"]
+            result["decode"]["cold_graph_hbm_frac_median"] = cold.get("hbm_frac_median")
 
     if base is not None:
         result["cpu_baseline"] = base
