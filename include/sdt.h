@@ -71,10 +71,10 @@ typedef struct sdt_tile {
                         sdt_tile_info: the rung's deep pipeline).  On rung 0
                         the deep count (3) is the ping-pong kernel: two groups
                         of 4 waves one phase apart, A in 2 stages, B in 3.
-                        On rungs 1 and 2 (256 x 128, 128 x 128) the deep count
-                        with one k-group runs v_mfma_f32_16x16x32 (two 32-deep
-                        sub-steps per k-tile), and so does every pipeline
-                        of rungs 5-7 (96 x 96 with 48 x 48 per wave,
+                        On rungs 1-4 (256 x 128 down to 64 x 64) the deep
+                        count with one k-group runs v_mfma_f32_16x16x32 (two
+                        32-deep sub-steps per k-tile), and so does every
+                        pipeline of rungs 5-7 (96 x 96 with 48 x 48 per wave,
                         192 x 192 with 96 x 48, 160 x 160 with 80 x 80);
                         every other launch runs v_mfma_f32_32x32x16.  The automatic plan takes the
                         long count (long_stages) in place of the deep one on a
@@ -371,9 +371,14 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
 
 /* Host-only: how a launch of rung tile_id on an M x N x K product on num_cu
  * CUs (num_cu <= 0: 256) is configured (stages, kgroups, threads, LDS).
- * k-groups: 2 on rungs built with them when the grid has at most num_cu
- * workgroups (on rungs 1 and 2: fewer than num_cu) and K spans at least 12 k-tiles,
- * else 1.  Stages: the rung's deep count, which with two k-groups becomes
+ * k-groups: 2 on rungs built with them by each rung's thresholds on the grid
+ * and the k-loop (K in 64-deep k-tiles, at least 12): rungs 1 and 2 with
+ * fewer workgroups than num_cu; rung 3 with fewer than 3/4 of num_cu and at
+ * least 96 k-tiles; rung 4 with fewer than num_cu and at least 24 k-tiles, or
+ * exactly num_cu and at least 40; else 1 (a k-split launch of gemm_f16_ws:
+ * 2 whenever its grid of tiles x splits fits num_cu -- on rungs 1 and 2 with
+ * fewer -- and each split runs at least 12 k-tiles).  Stages: the rung's deep
+ * count, which with two k-groups becomes
  * the rung's long count (long_stages, the 128 x 64 and 64 x 64 rungs) once K
  * holds at least 12 full k-tiles; the 2-stage pipeline is never planned (it
  * lost with the operands in HBM and tied with them in L2).  Stagger: as

@@ -97,14 +97,27 @@ int kgroups_for_grid(int id, int64_t wgs, int64_t nkt, int num_cu) {
     if (d.kgroups < 2) return 1;
     if (num_cu <= 0) num_cu = 256;
     if (nkt < kSplitMinKTiles) return 1;
-    // A rung whose one-k-group pipeline runs 16x16x32 MFMAs keeps it once the
-    // grid fills every CU: there the part runs at its power limit and that
-    // MFMA's lower energy per FLOP wins (128x128 at 2048^3: 20.0 us against
-    // 21.5 with two k-groups; 256x128 at 4096x2048x2048: 35.8 against 37.4);
-    // with CUs left idle the second k-group's shorter dependent chain wins
-    // (1536^3: 13.7 against 14.8; 256x128 at 2304^3: 31.8 against 34.6).
-    if (d.deep16) return wgs < num_cu ? 2 : 1;
-    return wgs <= num_cu ? 2 : 1;
+    // The one-k-group pipeline runs 16x16x32 MFMAs, whose lower energy per
+    // FLOP wins where the part runs at its power limit and whose shorter
+    // dependent chain per k-tile (two 32-deep MFMAs per accumulator instead
+    // of four 16-deep ones) wins on short loops; the second k-group halves
+    // the chain, which pays on long loops with CUs left idle.  The rung's
+    // thresholds (kLadder) are fitted per rung.
+    if (wgs == num_cu) return d.kg2_full_ktiles > 0 && nkt >= d.kg2_full_ktiles ? 2 : 1;
+    return 8 * wgs < int64_t(d.kg2_grid8) * num_cu && nkt >= d.kg2_min_ktiles ? 2 : 1;
+}
+
+// The k-group rule for a k-split grid, whose workgroups store partial sums
+// instead of C: two k-groups whenever the grid fits the CUs (on the 256 x 128
+// and 128 x 128 rungs, leaves some idle) and each split runs 12 k-tiles or
+// more.  On the 64 x 64 rung the one-k-group 16x16x32 pipeline that wins
+// unsplit lost here (512^2 x 8192 in 4 splits of 32 k-tiles, 256 workgroups:
+// 15.24 against 14.06 us with two k-groups).
+int kgroups_for_split(int id, int64_t wgs, int64_t nkt, int num_cu) {
+    const TileDesc& d = kLadder[id];
+    if (d.kgroups < 2 || nkt < kSplitMinKTiles) return 1;
+    if (num_cu <= 0) num_cu = 256;
+    return (d.long_stages > 0 ? wgs <= num_cu : wgs < num_cu) ? 2 : 1;
 }
 
 // The rung's long pipeline in place of its deep one when it has one, the
@@ -214,7 +227,7 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
         // the split grid decides the k-groups and stages, as for any grid
         const int64_t wgs = ceil_div(M, d.bm) * ceil_div(N, d.bn) * pl.splits;
         const int64_t nkt = (K / kBK) / pl.splits;   // full k-tiles of the shortest split
-        pl.kgroups = kgroups_for_grid(id, wgs, nkt, num_cu);
+        pl.kgroups = kgroups_for_split(id, wgs, nkt, num_cu);
         pl.stages = long_for(id, d.stages, pl.kgroups, K / pl.splits);
         pl.split_algo = cfg.split_algo >= 0 ? cfg.split_algo : kSplitAlgoAuto;
     }

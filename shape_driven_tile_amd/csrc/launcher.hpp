@@ -13,7 +13,8 @@ namespace sdt {
 constexpr int kBK = 64;
 
 // A rung of the ladder.  waves_m x waves_n wavefronts split the bm x bn block;
-// each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 MFMA tiles.
+// each wave owns a (bm/waves_m) x (bn/waves_n) sub-block of 32x32 (or, on the
+// 16x16x32 pipelines, 16x16) MFMA tiles.
 // A launch uses 2 (forced plans only), `stages` or `long_stages` LDS stages
 // of (bm + bn) x 64 elements each (see plan_for); the global prefetch runs
 // stages - 1 k-tiles deep.  A ping-pong
@@ -26,6 +27,11 @@ struct TileDesc {
     int deep16;     // 1: the deep pipeline with one k-group runs 16x16x32 MFMAs
     int long_stages;  // > 0: a deeper pipeline for long k-loops (see kLongMinKTiles)
     int ksplit;     // 1: every pipeline also built to split K across workgroups
+    // When the automatic plan runs two k-groups (kgroups == 2 only; see
+    // kgroups_for_grid): with CUs left idle, a grid below kg2_grid8 / 8 of
+    // the CUs and at least kg2_min_ktiles k-tiles; with one workgroup on
+    // every CU, at least kg2_full_ktiles k-tiles (0: never).
+    int kg2_min_ktiles, kg2_grid8, kg2_full_ktiles;
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
@@ -40,18 +46,36 @@ struct TileDesc {
 // The three smallest rungs can also split K across workgroups (the larger
 // ones are picked when the grid already fills the CUs, and the 256 x 128
 // wave tile has no registers left for the k-split sum).
+//
+// Two k-groups against one k-group of 16x16x32 MFMAs, fitted on MI355X
+// (graph-timed, us, one k-group / two): 256 x 128 and 128 x 128 take two
+// only with CUs left idle (2048^3, 256 workgroups: 20.0 / 21.5; 1536^3 on
+// 128 x 128, 144: 14.8 / 13.7).  On 64 x 64 one k-group wins on short
+// loops even with CUs idle (512^3 4.05 / 4.47, 768^3 5.00 / 5.26, 768^2 x
+// 1024 5.75 / 5.78) and two from 24 k-tiles (768^2 x 1536 7.32 / 6.92,
+// 512^2 x 1536 7.10 / 6.82), or from 40 with every CU busy (1024^2 x 2432
+// 10.32 / 10.55, 1024^2 x 2560 11.03 / 10.69).  On 128 x 64 one k-group wins
+// up to 80 k-tiles (1280^3 9.34 / 10.32, 2048 x 1024 x 2048 13.52 / 14.82,
+// 1152^2 x 5120 26.78 / 27.83) and two only on longer loops with a quarter
+// of the CUs idle (1152^2 x 6144, 162 workgroups: 31.07 / 30.49; with 200
+// workgroups one k-group still wins at 128 k-tiles, 39.68 / 40.38).
 constexpr TileDesc kLadder[] = {
-    {256, 256, 2, 4, 3, 1, 1, 0, 0, 0},  // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0},  // 4 waves, 128x64 per wave, 3 x 48 KB
-    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1},  // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 64, 2, 2, 3, 2, 0, 0, 4, 1},   // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
-    {64, 64, 2, 2, 3, 2, 0, 0, 4, 1},    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
+    // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
+    {256, 256, 2, 4, 3, 1, 1, 0, 0, 0, 0, 0, 0},
+    // 4 waves, 128x64 per wave, 3 x 48 KB
+    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0, 12, 8, 0},
+    // 4 waves, 64x64 per wave, 3 x 32 KB
+    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1, 12, 8, 0},
+    // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
+    {128, 64, 2, 2, 3, 2, 0, 1, 4, 1, 96, 6, 0},
+    // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
+    {64, 64, 2, 2, 3, 2, 0, 1, 4, 1, 24, 8, 40},
     // Off the ladder (see kNumLadder), 16x16x32 MFMAs on every pipeline (48
     // and 80 are no multiples of 32): 4 waves of 48x48, 3 x 24 KB; 8 waves of
     // 96x48, 3 x 48 KB; 4 waves of 80x80, 3 x 40 KB.
-    {96, 96, 2, 2, 3, 1, 0, 1, 0, 0},
-    {192, 192, 2, 4, 3, 1, 0, 1, 0, 0},
-    {160, 160, 2, 2, 3, 1, 0, 1, 0, 0},
+    {96, 96, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0},
+    {192, 192, 2, 4, 3, 1, 0, 1, 0, 0, 0, 0, 0},
+    {160, 160, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0},
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place
@@ -68,9 +92,10 @@ constexpr int kLongMinKTiles = 12;
 // Shortest k-loop (in 64-deep k-tiles) that a second k-group of waves pays
 // on: a grid resident all at once spends each k-tile on one chain of
 // barrier, fragment reads and dependent MFMAs; splitting every tile's four
-// sub-steps over two wave groups halves that chain (1024^3: 7.05 -> 6.21 us,
-// 1536^3: 15.8 -> 14.8 us) but costs a reduction through LDS that loops of
-// 8 k-tiles or fewer do not earn back (256^3: 3.69 -> 3.85 us).
+// sub-steps over two wave groups halves that chain (on 32x32x16 MFMAs,
+// 1024^3: 7.05 -> 6.21 us, 1536^3: 15.8 -> 14.8 us) but costs a reduction
+// through LDS that loops of 8 k-tiles or fewer do not earn back (256^3: 3.69
+// -> 3.85 us).  Each rung's own thresholds (kLadder) sit at or above it.
 constexpr int kSplitMinKTiles = 12;
 
 // Largest operand footprint, 2*K*(M+N) bytes, and fewest full k-tiles at
@@ -136,7 +161,7 @@ constexpr int64_t kMaxLd = (int64_t(1) << 22) - 64;
 // shape (K = 4096, N = 12288, weights in HBM): runs of 128 bytes per row, the
 // one-launch kernel's, read at most 5.46 TB/s however many workgroups read
 // them, runs of 512 bytes 6.29 TB/s; the split kernel alone streams in
-// 16.2 us with 768 workgroups (384: 17.9, 1536: 20.9), 19.3 us with the sum.
+// 16.2 us with 768 workgroups (384: 17.9, 1536: 20.9), 18.6 us with the sum.
 constexpr int kKnSplitSeg = 32;
 constexpr int kKnSplitWaves = 8;
 constexpr int kKnSplitTargetWgs = 768;
@@ -158,6 +183,7 @@ bool stagger_auto(int id, int64_t M, int64_t N, int64_t K);
 int long_for(int id, int stages, int kgroups, int64_t K);
 int kgroups_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);
 int kgroups_for_grid(int id, int64_t wgs, int64_t nkt, int num_cu);
+int kgroups_for_split(int id, int64_t wgs, int64_t nkt, int num_cu);
 int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num_cu,
                  int64_t ws_bytes, Plan* out);
 Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu);

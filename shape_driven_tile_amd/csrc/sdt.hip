@@ -124,7 +124,7 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
         return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
     } else {
         if constexpr (d.long_stages > 0) {
-            static_assert(!d.deep16 && d.kgroups == 2, "long pipelines: 32x32x16, both k-group forms");
+            static_assert(d.kgroups == 2, "long pipelines: 32x32x16, both k-group forms");
             if (pl.stages == d.long_stages) {
                 if (pl.kgroups == 2)
                     return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.long_stages, 2>(p, s);

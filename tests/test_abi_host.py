@@ -212,28 +212,47 @@ def test_ladder_is_well_formed():
         sdt.tile_info(len(tiles))
 
 
+# Two k-groups on the rungs built with them, per rung: (k-tiles needed with
+# CUs left idle, the grid's bound in eighths of the CUs, k-tiles needed with
+# one workgroup on every CU (0: never)).
+KG2_RULE = {1: (12, 8, 0), 2: (12, 8, 0), 3: (96, 6, 0), 4: (24, 8, 40)}
+
+
+def expected_kgroups(tile_id, wgs, nkt, num_cu):
+    if tile_id not in KG2_RULE or nkt < 12:
+        return 1
+    least, grid8, full = KG2_RULE[tile_id]
+    if wgs == num_cu:
+        return 2 if full and nkt >= full else 1
+    return 2 if 8 * wgs < grid8 * num_cu and nkt >= least else 1
+
+
 def test_launch_plan_rules():
-    """k-groups: 2 on rungs built with them when the grid has at most num_cu
-    workgroups (fewer than num_cu on the 256x128 and 128x128 rungs, whose
-    one-k-group deep pipelines run 16x16x32 MFMAs) and K spans at least 12
-    k-tiles.  Stages: the deep count, never the 2-stage pipeline; a
-    two-k-group deep pipeline becomes the rung's long one (if it has one) from
-    12 full k-tiles.  Stagger: on ladder rungs 1-4, a power-of-two count of at
-    least 16 full k-tiles and A and B within 16 MiB."""
+    """k-groups: 2 on rungs built with them by each rung's thresholds (256x128
+    and 128x128: fewer workgroups than CUs and at least 12 k-tiles; 128x64:
+    fewer than 3/4 of the CUs and at least 96; 64x64: fewer than the CUs and
+    at least 24, or one on every CU and at least 40), else the one-k-group
+    pipeline, 16x16x32 on every ladder rung below 256x256.  Stages: the deep
+    count, never the 2-stage pipeline; a two-k-group deep pipeline becomes the
+    rung's long one (if it has one) from 12 full k-tiles.  Stagger: on ladder
+    rungs 1-4, a power-of-two count of at least 16 full k-tiles and A and B
+    within 16 MiB."""
     tiles = ladder()
     shapes = [(256, 256, 256), (512, 512, 512), (768, 768, 768), (1024, 1024, 1024),
               (512, 512, 2048), (1024, 1024, 1025), (512, 512, 4096), (2048, 2048, 2048),
               (2048, 2048, 4096), (1536, 1536, 2048), (1024, 1024, 4096),
               (4096, 4096, 4096), (8192, 8192, 8192), (1, 1, 1), (100, 3000, 700),
               (512, 512, 3008), (512, 512, 3072), (1024, 1024, 8192), (64, 64, 8192),
-              (2048, 1024, 4096), (384, 384, 768), (384, 384, 704), (640, 640, 640)]
+              (2048, 1024, 4096), (384, 384, 768), (384, 384, 704), (640, 640, 640),
+              (768, 768, 1472), (768, 768, 1536), (1024, 1024, 2496), (1024, 1024, 2560),
+              (1152, 1152, 6080), (1152, 1152, 6144), (1280, 1280, 8192), (960, 960, 2560)]
     for num_cu in (80, 256):
         for t in tiles:
             for (M, N, K) in shapes:
                 p = sdt.plan_tile(t["id"], M, N, K, num_cu)
                 wgs = -(-M // t["bm"]) * -(-N // t["bn"])
-                fits = wgs < num_cu if t["id"] in (1, 2) else wgs <= num_cu
-                kg = 2 if (t["kgroups"] == 2 and fits and -(-K // 64) >= 12) else 1
+                kg = expected_kgroups(t["id"], wgs, -(-K // 64), num_cu)
+                assert kg == 1 or t["kgroups"] == 2
                 st = t["stages"]
                 if kg == 2 and t["long_stages"] and K // 64 >= 12:
                     st = t["long_stages"]
@@ -252,7 +271,12 @@ def test_launch_plan_rules():
     for (M, N, K) in shapes:
         p = sdt.pick_tile(M, N, K, 256)
         assert p == sdt.plan_tile(p["id"], M, N, K, 256)
-    assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 2
+    assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 1   # 256 x 64x64, 16 k-tiles
+    assert sdt.pick_tile(1024, 1024, 4096, 256)["kgroups"] == 2   # 64 k-tiles
+    assert sdt.pick_tile(768, 768, 768, 256)["kgroups"] == 1      # 144 workgroups, 12 k-tiles
+    assert sdt.pick_tile(768, 768, 2048, 256)["kgroups"] == 2     # 32 k-tiles
+    assert sdt.pick_tile(1280, 1280, 4096, 256)["kgroups"] == 1   # 128x64, 200 workgroups
+    assert sdt.pick_tile(1152, 1152, 8192, 256)["kgroups"] == 2   # 128x64, 162, 128 k-tiles
     assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
     assert sdt.pick_tile(1664, 1664, 1664, 256)["kgroups"] == 2   # 169 workgroups

@@ -186,9 +186,9 @@ def test_integer_exact_every_tile(shape):
 
 @pytest.mark.parametrize("shape", [(257, 259, 4160), (300, 260, 4104)])
 def test_integer_exact_every_tile_deep_pipeline(shape):
-    """The automatic plan is every rung's deep pipeline (on the rungs with
-    a long pipeline the plan takes that one at these k-loop lengths, which
-    the assertion checks; the long pipelines themselves run in
+    """The automatic plan is every rung's deep pipeline (on the rungs with a
+    long pipeline it takes that one when it runs two k-groups, which the
+    assertion checks; the long pipelines themselves run in
     test_long_pipeline_every_rung_with_one).  Here each rung's deep pipeline
     is forced: exact integer sums, bit for bit, with a ragged last k-tile in
     the second shape and ragged M/N in both; one k-group and, where built,
@@ -200,8 +200,9 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
     ref = oracle.gemm(A, B)
     for tile in range(_ntiles()):
         info = sdt.tile_info(tile)
-        want = info["long_stages"] if info["long_stages"] and K // 64 >= 12 else info["stages"]
-        assert sdt.plan_tile(tile, M, N, K, 1 << 20)["stages"] == want
+        plan = sdt.plan_tile(tile, M, N, K, 1 << 20)
+        long_ = info["long_stages"] and plan["kgroups"] == 2 and K // 64 >= 12
+        assert plan["stages"] == (info["long_stages"] if long_ else info["stages"])
         for kg in ((1, 2) if info["kgroups"] == 2 else (1,)):
             say(f"integer deep {shape} tile={tile} stages={info['stages']} kgroups={kg}")
             C, pad_ok = run_gemm(A, B, tile=tile, stagger=0, stages=info["stages"], kgroups=kg)
@@ -336,10 +337,12 @@ def test_two_kgroups_every_rung(shape):
 
 
 def test_two_kgroups_auto_plan_matches_oracle():
-    """Shapes whose automatic plan uses two k-groups (resident grid, >= 12
-    k-tiles) against the oracle, and bit-identical to the forced plan."""
+    """Shapes whose automatic plan uses two k-groups (each rung's grid and
+    k-loop thresholds) against the oracle, and bit-identical to the forced
+    plan."""
     from shape_driven_tile_amd import binding as sdt
-    for (M, N, K) in [(1024, 1024, 1024), (768, 768, 768), (1664, 1664, 1664)]:
+    for (M, N, K) in [(1024, 1024, 4096), (768, 768, 2048), (1664, 1664, 1664),
+                      (1152, 1152, 8192)]:
         p = sdt.pick_tile(M, N, K, 256)
         assert p["kgroups"] == 2, (M, N, K)
         say(f"auto two k-groups {M}x{N}x{K} tile={p['id']}")
