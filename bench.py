@@ -312,6 +312,12 @@ def main():
             # the clock sampled in the separate under-load window
             clk["timed_region_frac_of_clock_ceiling"] = round(
                 achieved / clk["mfma_ceiling_at_clock_tflops"], 4)
+        ceil = (result["detail"].get("mfma_ceiling") or {}).get("uniform") or {}
+        if ceil.get("tflops_median"):
+            # the timed region's 8192^3 rate against the register-only MFMA
+            # loop on operands of the same distribution (no memory traffic)
+            result["roofline"]["frac_of_register_only_mfma_rate"] = round(
+                achieved / ceil["tflops_median"], 4)
         cold = result["detail"].get("decode_cold") or {}
         if cold.get("us"):
             # the same GEMV alone: graph-replayed over the rotating buffers
@@ -651,6 +657,8 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
             ceil = 256 * 4096 * smi["gfx_clk_mhz_mean"] * 1e6 / 1e12
             det["clock_under_load"]["mfma_ceiling_at_clock_tflops"] = round(ceil, 1)
         log(f"under load: {smi}")
+    det["mfma_ceiling"] = mfma_ceiling(sdt, torch, np, inputs, dev_tensor,
+                                       props_cus(torch, dev))
     for n, (A, B, C) in ops.items():
         launches = 200 if n <= 2048 else (50 if n == 4096 else 20)
         f = (lambda j, A=A, B=B, C=C: sdt.gemm_f16(A, B, C))
@@ -824,6 +832,46 @@ def detail(sdt, torch, np, inputs, ops, x, Ws, y, dev, dev_tensor, flop_gemm, by
     det["bf16"] = detail_bf16(sdt, torch, np, inputs, oracle, dev, flop_gemm, bytes_gemv)
     det["ksplit"] = detail_ksplit(sdt, torch, np, inputs, oracle, dev)
     return det
+
+
+MFMA_CEILING_ITERS = 1000   # ~1.2 ms per launch on 256 CUs at the power limit
+
+
+def mfma_ceiling(sdt, torch, np, inputs, dev_tensor, cus):
+    """The matrix cores' own rate on the GEMM's operand distribution: the
+    library's register-only MFMA loop (the 256 x 256 kernel's MFMA phase, 8
+    waves per CU, no memory traffic) on uniform [-1,1] fp16 fragments and on
+    all-ones fragments, ~2 s of launches to reach the power limit's steady
+    state, then 20 launches per graph replayed 5 times; clocks sampled while
+    the random-operand loop runs."""
+    flop = float(cus) * MFMA_CEILING_ITERS * sdt.MFMA_CEILING_FLOP_PER_ITER
+    out = torch.empty((cus * 512,), dtype=torch.float32, device="cuda:0")
+    res = {"kernel": "sdt_mfma_ceiling: 64 v_mfma_f32_16x16x32_f16 per iteration per wave "
+                     "(24 fragments, 32 accumulator tiles, the 256x256 kernel's order), "
+                     f"8 waves per workgroup, {cus} workgroups, {MFMA_CEILING_ITERS} iterations",
+           "flop_per_launch": flop}
+    for name, frags_h in (("uniform", inputs.uniform_f16((24 * 64 * 8,), 5000)),
+                          ("ones", np.ones((24 * 64 * 8,), dtype=np.float16))):
+        frags = dev_tensor(frags_h.view(np.uint16))
+        f = (lambda j, frags=frags: sdt.mfma_ceiling(frags, MFMA_CEILING_ITERS, out, cus))
+        sampler = smi_sampler() if name == "uniform" else None
+        t0 = time.time()
+        while time.time() - t0 < 2.0:
+            for _ in range(100):
+                f(0)
+            torch.cuda.synchronize()
+        us, _ = graph_launches(torch, f, 20, repeats=5)
+        med = sorted(us)[len(us) // 2]
+        res[name] = {"us": _ranges(us),
+                     "tflops_median": round(flop / (med * 1e-6) / 1e12, 1),
+                     "peak_frac_median": round(flop / (med * 1e-6) / 1e12 / PEAK_FP16_TFLOPS, 4)}
+        if sampler is not None:
+            smi = smi_reading(sampler)
+            if smi:
+                res[name]["clock_under_load"] = smi
+        log(f"mfma ceiling ({name} operands): median {med:.1f} us "
+            f"{res[name]['tflops_median']} TFLOP/s")
+    return res
 
 
 def props_cus(torch, dev):

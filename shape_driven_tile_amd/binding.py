@@ -32,11 +32,11 @@ EXPORTS = (
     "gemm_f16_ws", "gemm_bf16_ws", "sdt_gemm_workspace_size", "sdt_launch_workspace_size",
     "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version", "sdt_stream_read_grid",
     "gemm_f16_noalloc", "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_gemv_kn_workspace_size",
-    "sdt_stream_read_runs",
+    "sdt_stream_read_runs", "sdt_mfma_ceiling",
 )
 
 # The include/sdt.h version these structures and signatures follow.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 class SdtTile(ctypes.Structure):
@@ -124,6 +124,7 @@ def lib():
     L.sdt_gemv_kn_workspace_size.argtypes = [_i64, _i64]
     L.sdt_gemv_kn_workspace_size.restype = _i64
     L.sdt_stream_read_runs.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp]
+    L.sdt_mfma_ceiling.argtypes = [_vp, _int, _vp, _int, _int, _vp]
     L.sdt_stagger_eligible.argtypes = [_i64]
     L.sdt_stagger_ktile.argtypes = [_i64, _i64, _i64]
     L.sdt_stagger_ktile.restype = _i64
@@ -142,7 +143,8 @@ def lib():
                  "gemm_f16_cfg", "gemm_bf16_cfg", "gemm_f16_ws", "gemm_bf16_ws",
                  "sdt_workspace_init", "sdt_pick_tile_ws", "sdt_abi_version",
                  "sdt_stream_read_grid", "gemm_f16_noalloc", "sdt_last_hip_error", "sdt_empty_kernel", "sdt_stream_read",
-                 "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_stream_read_runs"):
+                 "gemv_f16_m1_kn_ws", "gemv_bf16_m1_kn_ws", "sdt_stream_read_runs",
+                 "sdt_mfma_ceiling"):
         getattr(L, name).restype = _int
     if L.sdt_abi_version() != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH} has ABI version {L.sdt_abi_version()}, this binding "
@@ -373,6 +375,26 @@ def stream_read_grid(buf, out, workgroups: int, stream=None) -> None:
                                     _stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, "sdt_stream_read_grid")
+
+
+MFMA_CEILING_FRAGS = 24          # operand fragments per lane (one k-tile of a 128 x 64 wave tile)
+MFMA_CEILING_FLOP_PER_ITER = 8 * 64 * 2 * 16 * 16 * 32   # per workgroup: 8 waves x 64 MFMAs
+
+
+def mfma_ceiling(frags, iters: int, out, workgroups: int, bf16: bool = False,
+                 stream=None) -> None:
+    """Enqueue the library's register-only MFMA loop: `frags` is a contiguous
+    16-bit device tensor of 24 x 64 x 8 values (fragment f of lane l at
+    [(f * 64 + l) * 8, +8)), `out` a float32 tensor of at least
+    workgroups x 512 values."""
+    if frags.element_size() != 2 or frags.numel() < MFMA_CEILING_FRAGS * 64 * 8 or \
+            not frags.is_contiguous() or out.element_size() != 4 or \
+            out.numel() < 512 * int(workgroups) or not out.is_contiguous():
+        raise ValueError("mfma_ceiling: 24 x 64 x 8 16-bit fragments, workgroups x 512 floats out")
+    rc = lib().sdt_mfma_ceiling(frags.data_ptr(), int(iters), out.data_ptr(), int(workgroups),
+                                1 if bf16 else 0, _stream_handle(stream))
+    if rc != SDT_OK:
+        raise SdtError(rc, "sdt_mfma_ceiling")
 
 
 def empty_kernel(stream=None) -> None:

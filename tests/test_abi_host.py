@@ -663,6 +663,18 @@ def test_stream_read_runs_argument_checks():
     assert L.sdt_stream_read_runs(b, *ok_args, o + 2, None) == sdt.SDT_ERR_UNSUPPORTED
 
 
+def test_mfma_ceiling_argument_checks():
+    """Refusals of the register-only MFMA loop before any device call."""
+    L = sdt.lib()
+    f, o = 0x10000, 0x20000
+    assert L.sdt_mfma_ceiling(None, 10, o, 256, 0, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f, 10, None, 256, 0, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f, 0, o, 256, 0, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f, 10, o, 0, 1, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f + 8, 10, o, 256, 0, None) == sdt.SDT_ERR_UNSUPPORTED
+    assert L.sdt_mfma_ceiling(f, 10, o + 2, 256, 1, None) == sdt.SDT_ERR_UNSUPPORTED
+
+
 def test_sizes_past_int_range_refused():
     """M, N or K past 2^31 - 1: every kernel size is an int, and the planner's
     block counts (products of two sizes) must not overflow.  Refused before
