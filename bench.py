@@ -840,20 +840,27 @@ MFMA_CEILING_ITERS = 1000   # ~1.2 ms per launch on 256 CUs at the power limit
 def mfma_ceiling(sdt, torch, np, inputs, dev_tensor, cus):
     """The matrix cores' own rate on the GEMM's operand distribution: the
     library's register-only MFMA loop (the 256 x 256 kernel's MFMA phase, 8
-    waves per CU, no memory traffic) on uniform [-1,1] fp16 fragments and on
-    all-ones fragments, ~2 s of launches to reach the power limit's steady
-    state, then 20 launches per graph replayed 5 times; clocks sampled while
-    the random-operand loop runs."""
+    waves per CU, no memory traffic) on uniform [-1,1] fp16 fragments with the
+    kernel's v_mfma_f32_16x16x32_f16, the same with v_mfma_f32_32x32x16_f16,
+    on all-ones fragments, and on uniform bf16 ones; each after ~2 s of
+    launches (the power limit's steady state), then 20 launches per graph
+    replayed 5 times; clocks sampled while the first runs."""
     flop = float(cus) * MFMA_CEILING_ITERS * sdt.MFMA_CEILING_FLOP_PER_ITER
     out = torch.empty((cus * 512,), dtype=torch.float32, device="cuda:0")
-    res = {"kernel": "sdt_mfma_ceiling: 64 v_mfma_f32_16x16x32_f16 per iteration per wave "
-                     "(24 fragments, 32 accumulator tiles, the 256x256 kernel's order), "
-                     f"8 waves per workgroup, {cus} workgroups, {MFMA_CEILING_ITERS} iterations",
+    res = {"kernel": "sdt_mfma_ceiling: 8 waves per workgroup, 2^20 FLOP per wave per "
+                     "iteration (64 v_mfma_f32_16x16x32 or 32 v_mfma_f32_32x32x16 on the 24 "
+                     "fragments of one k-tile of the 256x256 kernel's wave, no memory access), "
+                     f"{cus} workgroups, {MFMA_CEILING_ITERS} iterations",
            "flop_per_launch": flop}
-    for name, frags_h in (("uniform", inputs.uniform_f16((24 * 64 * 8,), 5000)),
-                          ("ones", np.ones((24 * 64 * 8,), dtype=np.float16))):
+    n = 24 * 64 * 8
+    arms = (("uniform", inputs.uniform_f16((n,), 5000), False, False),
+            ("uniform_32x32x16", inputs.uniform_f16((n,), 5000), False, True),
+            ("ones", np.ones((n,), dtype=np.float16), False, False),
+            ("uniform_bf16", inputs.uniform_bf16((n,), 5000), True, False))
+    for name, frags_h, bf16, mfma32 in arms:
         frags = dev_tensor(frags_h.view(np.uint16))
-        f = (lambda j, frags=frags: sdt.mfma_ceiling(frags, MFMA_CEILING_ITERS, out, cus))
+        f = (lambda j, frags=frags, bf16=bf16, mfma32=mfma32:
+             sdt.mfma_ceiling(frags, MFMA_CEILING_ITERS, out, cus, bf16=bf16, mfma32=mfma32))
         sampler = smi_sampler() if name == "uniform" else None
         t0 = time.time()
         while time.time() - t0 < 2.0:
@@ -869,8 +876,7 @@ def mfma_ceiling(sdt, torch, np, inputs, dev_tensor, cus):
             smi = smi_reading(sampler)
             if smi:
                 res[name]["clock_under_load"] = smi
-        log(f"mfma ceiling ({name} operands): median {med:.1f} us "
-            f"{res[name]['tflops_median']} TFLOP/s")
+        log(f"mfma ceiling ({name}): median {med:.1f} us {res[name]['tflops_median']} TFLOP/s")
     return res
 
 

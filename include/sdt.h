@@ -467,26 +467,28 @@ int sdt_check_gemm_args(int64_t M, int64_t N, int64_t K,
 /* Measurement: enqueue a register-only MFMA loop with no memory traffic in
  * the loop: `workgroups` workgroups of 8 waves (two per SIMD, the register
  * budget of the 256 x 256 GEMM kernel), each lane holding the 24 operand
- * fragments of one k-tile of that kernel's wave tile (8 A and 4 B 16 x 32
- * fragments for each 32-deep half) and 32 fp32 accumulator tiles of 16 x 16,
- * and issuing iters x 64 v_mfma_f32_16x16x32 instructions (the GEMM kernel's
- * order: each B fragment held over 8 consecutive MFMAs).  It performs
- * workgroups x 8 x iters x 64 x 16384 floating-point operations; timed back to
- * back on the GEMM's operand distribution it gives the matrix cores' rate on
- * that data at the part's power limit, which the GEMM kernel is reported
- * against beside the nominal peak (the pages compare their kernels with a
- * power-limited ceiling measured on the part).
+ * fragments of one 64-deep k-tile of that kernel's 128 x 64 wave tile and its
+ * fp32 accumulators, and performing workgroups x 8 x iters x 2^20
+ * floating-point operations: with (flags & 2) == 0, iters x 64
+ * v_mfma_f32_16x16x32 (the GEMM kernel's instruction and order: fragments
+ * 0..7 A and 8..11 B of the first 32-deep half, 12..23 those of the second;
+ * lane l holds row l % 16, elements 8 (l / 16) .. + 7 of the half); with
+ * (flags & 2) != 0, iters x 32 v_mfma_f32_32x32x16 on the same fragments read
+ * as four 16-deep steps (fragments 6 s .. 6 s + 3 A and 6 s + 4, 6 s + 5 B of
+ * step s; lane l holds row l % 32, elements 8 (l / 32) .. + 7 of the step).
+ * (flags & 1) != 0: the values are bf16 and the bf16 MFMAs run, else fp16.
+ * Timed back to back on the GEMM's operand distribution it gives the matrix
+ * cores' rate on that data at the part's power and clock limits, which the
+ * GEMM kernel is reported against beside the nominal peak (the pages compare
+ * their kernels with a power-limited ceiling measured on the part).
  * frags (device, caller-owned): 24 x 64 x 8 16-bit values, fragment f of lane
- * l at frags[(f * 64 + l) * 8 .. + 8); f = 0..7 the A and 8..11 the B
- * fragments of the first half, 12..23 those of the second.  Lane l of a
- * 16 x 32 fragment holds row l % 16, elements 8 (l / 16) .. + 7 of the
- * 32-deep k range.  bf16 != 0: the values are bf16 and the bf16 MFMA runs,
- * else fp16.  out (device, caller-owned): workgroups x 512 floats; thread t of
- * workgroup w writes out[w * 512 + t], the sum of its 128 accumulator values
- * in a fixed order.  SDT_ERR_INVALID_ARG: a null pointer, iters <= 0 or
- * workgroups <= 0.  SDT_ERR_UNSUPPORTED: frags not 16-byte or out not 4-byte
- * aligned.  SDT_ERR_HIP: the launch failed. */
-int sdt_mfma_ceiling(const void* frags, int iters, void* out, int workgroups, int bf16,
+ * l at frags[(f * 64 + l) * 8 .. + 8).  out (device, caller-owned):
+ * workgroups x 512 floats; thread t of workgroup w writes out[w * 512 + t],
+ * the sum of its accumulator values in a fixed order.  SDT_ERR_INVALID_ARG: a
+ * null pointer, iters <= 0, workgroups <= 0 or flags outside 0..3.
+ * SDT_ERR_UNSUPPORTED: frags not 16-byte or out not 4-byte aligned.
+ * SDT_ERR_HIP: the launch failed. */
+int sdt_mfma_ceiling(const void* frags, int iters, void* out, int workgroups, int flags,
                      void* stream);
 
 /* SDT_ABI_VERSION as the library was built. */

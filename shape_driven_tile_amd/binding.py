@@ -382,17 +382,18 @@ MFMA_CEILING_FLOP_PER_ITER = 8 * 64 * 2 * 16 * 16 * 32   # per workgroup: 8 wave
 
 
 def mfma_ceiling(frags, iters: int, out, workgroups: int, bf16: bool = False,
-                 stream=None) -> None:
-    """Enqueue the library's register-only MFMA loop: `frags` is a contiguous
-    16-bit device tensor of 24 x 64 x 8 values (fragment f of lane l at
-    [(f * 64 + l) * 8, +8)), `out` a float32 tensor of at least
-    workgroups x 512 values."""
+                 mfma32: bool = False, stream=None) -> None:
+    """Enqueue the library's register-only MFMA loop (16x16x32 MFMAs, or
+    32x32x16 with mfma32): `frags` is a contiguous 16-bit device tensor of
+    24 x 64 x 8 values (fragment f of lane l at [(f * 64 + l) * 8, +8)),
+    `out` a float32 tensor of at least workgroups x 512 values."""
     if frags.element_size() != 2 or frags.numel() < MFMA_CEILING_FRAGS * 64 * 8 or \
             not frags.is_contiguous() or out.element_size() != 4 or \
             out.numel() < 512 * int(workgroups) or not out.is_contiguous():
         raise ValueError("mfma_ceiling: 24 x 64 x 8 16-bit fragments, workgroups x 512 floats out")
+    flags = (1 if bf16 else 0) | (2 if mfma32 else 0)
     rc = lib().sdt_mfma_ceiling(frags.data_ptr(), int(iters), out.data_ptr(), int(workgroups),
-                                1 if bf16 else 0, _stream_handle(stream))
+                                flags, _stream_handle(stream))
     if rc != SDT_OK:
         raise SdtError(rc, "sdt_mfma_ceiling")
 

@@ -442,48 +442,87 @@ __global__ __launch_bounds__(64) void stream_read_kernel(const int4_t* buf, uint
 }
 
 // Register-only MFMA loop: the MFMA phase of the 256 x 256 GEMM kernel's
-// wave (32 accumulator tiles of 16 x 16, the 24 fragments of one k-tile,
-// 64 v_mfma_f32_16x16x32 per iteration in the same order) repeated `iters`
-// times with no memory access, on 8 waves per workgroup (two per SIMD).
-// Each thread then writes the sum of its accumulators, so no MFMA is dead.
-template <typename Elt>
+// wave repeated `iters` times with no memory access, on 8 waves per
+// workgroup (two per SIMD).  MF = 16: 32 accumulator tiles of 16 x 16, the
+// 24 fragments of one 64-deep k-tile (two 32-deep halves of 8 A and 4 B
+// fragments), 64 v_mfma_f32_16x16x32 per iteration in the kernel's order.
+// MF = 32: the same 128 x 64 wave tile as 8 tiles of 32 x 32, the same 24
+// fragments read as four 16-deep steps of 4 A and 2 B fragments, 32
+// v_mfma_f32_32x32x16 per iteration (the same FLOPs).  Each thread then
+// writes the sum of its accumulators, so no MFMA is dead.
+template <typename Elt, int MF>
 __global__ __launch_bounds__(512) void mfma_ceiling_kernel(const int4_t* frags, int iters,
                                                            float* out) {
     typedef typename Elt::frag8 frag8;
     const int lane = threadIdx.x & 63;
-    frag8 fa[2][8], fb[2][4];
+    float sum = 0.0f;
+    if constexpr (MF == 16) {
+        frag8 fa[2][8], fb[2][4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < 2; ++h) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            fa[h][j] = __builtin_bit_cast(frag8, frags[(h * 12 + j) * 64 + lane]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fb[h][i] = __builtin_bit_cast(frag8, frags[(h * 12 + 8 + i) * 64 + lane]);
-    }
-    floatx4_t acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
-    for (int it = 0; it < iters; ++it) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
+            for (int j = 0; j < 8; ++j)
+                fa[h][j] = __builtin_bit_cast(frag8, frags[(h * 12 + j) * 64 + lane]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
+                fb[h][i] = __builtin_bit_cast(frag8, frags[(h * 12 + 8 + i) * 64 + lane]);
+        }
+        floatx4_t acc[4][8];
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = Elt::mfma16(fb[h][i], fa[h][j], acc[i][j]);
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[i][j] = Elt::mfma16(fb[h][i], fa[h][j], acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum += acc[i][j][e];
+    } else {
+        frag8 fa[4][4], fb[4][2];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fa[h][j] = __builtin_bit_cast(frag8, frags[(h * 6 + j) * 64 + lane]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fb[h][i] = __builtin_bit_cast(frag8, frags[(h * 6 + 4 + i) * 64 + lane]);
+        }
+        floatx16_t acc[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        acc[i][j] = Elt::mfma(fb[h][i], fa[h][j], acc[i][j]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sum += acc[i][j][e];
     }
-    float sum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sum += acc[i][j][e];
     out[(int64_t)blockIdx.x * 512 + threadIdx.x] = sum;
 }
 
@@ -831,15 +870,21 @@ extern "C" int sdt_stream_read_runs(const void* buf, int64_t rows, int64_t row_b
 }
 
 extern "C" int sdt_mfma_ceiling(const void* frags, int iters, void* out, int workgroups,
-                                int bf16, void* stream) {
-    if (!frags || !out || iters <= 0 || workgroups <= 0) return SDT_ERR_INVALID_ARG;
+                                int flags, void* stream) {
+    if (!frags || !out || iters <= 0 || workgroups <= 0 || (flags & ~3) != 0)
+        return SDT_ERR_INVALID_ARG;
     if ((reinterpret_cast<uintptr_t>(frags) & 15) != 0 || (reinterpret_cast<uintptr_t>(out) & 3) != 0)
         return SDT_ERR_UNSUPPORTED;
     const sdt::int4_t* f = static_cast<const sdt::int4_t*>(frags);
     float* o = static_cast<float*>(out);
     void* args[] = {&f, &iters, &o};
-    const void* k = bf16 ? reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::BF16>)
-                         : reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::F16>);
+    const void* k;
+    switch (flags) {
+        case 0: k = reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::F16, 16>); break;
+        case 1: k = reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::BF16, 16>); break;
+        case 2: k = reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::F16, 32>); break;
+        default: k = reinterpret_cast<const void*>(&sdt::mfma_ceiling_kernel<sdt::BF16, 32>); break;
+    }
     hipError_t e = hipLaunchKernel(k, dim3((unsigned)workgroups), dim3(512), args, 0,
                                    static_cast<hipStream_t>(stream));
     return e == hipSuccess ? SDT_OK : sdt::fail_hip(e);

@@ -671,6 +671,8 @@ def test_mfma_ceiling_argument_checks():
     assert L.sdt_mfma_ceiling(f, 10, None, 256, 0, None) == sdt.SDT_ERR_INVALID_ARG
     assert L.sdt_mfma_ceiling(f, 0, o, 256, 0, None) == sdt.SDT_ERR_INVALID_ARG
     assert L.sdt_mfma_ceiling(f, 10, o, 0, 1, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f, 10, o, 256, 4, None) == sdt.SDT_ERR_INVALID_ARG
+    assert L.sdt_mfma_ceiling(f, 10, o, 256, -1, None) == sdt.SDT_ERR_INVALID_ARG
     assert L.sdt_mfma_ceiling(f + 8, 10, o, 256, 0, None) == sdt.SDT_ERR_UNSUPPORTED
     assert L.sdt_mfma_ceiling(f, 10, o + 2, 256, 1, None) == sdt.SDT_ERR_UNSUPPORTED
 

@@ -137,18 +137,19 @@ def test_stream_read_runs_words_exact(run, rpw):
     assert (got[grid:] == -1).all(), "words past the grid were written"
 
 
+@pytest.mark.parametrize("mfma32", [False, True])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("iters", [1, 5])
-def test_mfma_ceiling_counts_every_product(bf16, iters):
+def test_mfma_ceiling_counts_every_product(bf16, iters, mfma32):
     """The register-only MFMA loop behind the matrix-core ceiling: with operand
     values in {-1, 0, 1} every sum is an exact integer, and the sum of a
-    wave's 64 outputs is iters x sum over both halves and every k of (the
+    wave's 64 outputs is iters x sum over every k step and every k of (the
     column sum of its B fragments) x (that of its A fragments), however the
     instruction maps rows and columns to lanes.  So every MFMA the FLOP count
     assumes was issued and accumulated."""
     import torch
     from shape_driven_tile_amd import binding as sdt
-    rng = np.random.default_rng(9100 + iters + 10 * bf16)
+    rng = np.random.default_rng(9100 + iters + 10 * bf16 + 100 * mfma32)
     vals = rng.integers(-1, 2, size=(24, 64, 8)).astype(np.float32)   # [fragment][lane][elt]
     if bf16:
         bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
@@ -157,22 +158,30 @@ def test_mfma_ceiling_counts_every_product(bf16, iters):
     frags = to_dev(np.ascontiguousarray(bits))
     wgs = 4
     out = torch.full((wgs * 512 + 16,), float("nan"), dtype=torch.float32, device=frags.device)
-    say(f"sdt_mfma_ceiling iters={iters} bf16={bf16}")
-    sdt.mfma_ceiling(frags, iters, out, wgs, bf16=bf16)
+    say(f"sdt_mfma_ceiling iters={iters} bf16={bf16} mfma32={mfma32}")
+    sdt.mfma_ceiling(frags, iters, out, wgs, bf16=bf16, mfma32=mfma32)
     torch.cuda.synchronize()
     got = out.cpu().numpy()
     assert np.isnan(got[wgs * 512:]).all(), "values past the last workgroup were written"
-    # column sums over each fragment's 16 rows: k = 8 (lane // 16) + elt
-    colsum = vals.reshape(24, 4, 16, 8).sum(axis=2).reshape(24, 32)
+    if mfma32:
+        # 32 rows per fragment, k = 8 (lane // 32) + elt of a 16-deep step;
+        # step s: fragments 6 s .. 6 s + 3 A, 6 s + 4 .. 6 s + 5 B
+        colsum = vals.reshape(24, 2, 32, 8).sum(axis=2).reshape(24, 16)
+        steps = [(range(6 * h, 6 * h + 4), range(6 * h + 4, 6 * h + 6)) for h in range(4)]
+    else:
+        # 16 rows per fragment, k = 8 (lane // 16) + elt of a 32-deep half;
+        # half h: fragments 12 h .. 12 h + 7 A, 12 h + 8 .. 12 h + 11 B
+        colsum = vals.reshape(24, 4, 16, 8).sum(axis=2).reshape(24, 32)
+        steps = [(range(12 * h, 12 * h + 8), range(12 * h + 8, 12 * h + 12)) for h in range(2)]
     expect = 0.0
-    for h in range(2):
-        a = colsum[12 * h: 12 * h + 8].sum(axis=0)
-        b = colsum[12 * h + 8: 12 * h + 12].sum(axis=0)
+    for fa, fb in steps:
+        a = colsum[list(fa)].sum(axis=0)
+        b = colsum[list(fb)].sum(axis=0)
         expect += float((a * b).sum())
     expect *= iters
     per_wave = got[:wgs * 512].astype(np.float64).reshape(wgs * 8, 64).sum(axis=1)
     np.testing.assert_array_equal(per_wave, np.full(wgs * 8, expect))
     again = torch.full_like(out, float("nan"))
-    sdt.mfma_ceiling(frags, iters, again, wgs, bf16=bf16)
+    sdt.mfma_ceiling(frags, iters, again, wgs, bf16=bf16, mfma32=mfma32)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(again.cpu().numpy()[:wgs * 512], got[:wgs * 512])
