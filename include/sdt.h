@@ -35,7 +35,8 @@
 /* Version of the structures and signatures below; bumped whenever sdt_tile,
  * sdt_launch or an entry point's arguments change, or entry points are added
  * (4: the off-ladder rungs 5-7, the [K][N] workspace entry points and
- * sdt_stream_read_runs; 5: sdt_mfma_ceiling).
+ * sdt_stream_read_runs; 5: sdt_mfma_ceiling, and loader waves: the `loaders`
+ * field of sdt_tile and sdt_launch).
  * sdt_abi_version() reports the version the library was built with: a caller
  * compiled against another header must not pass these structures to it. */
 #define SDT_ABI_VERSION 5
@@ -65,7 +66,7 @@ typedef struct sdt_tile {
                         tiles (see sdt_pick_tile) */
     int bm, bn, bk;
     int waves_m, waves_n;
-    int threads;     /* 64 * waves_m * waves_n * kgroups */
+    int threads;     /* 64 * waves_m * waves_n * kgroups, twice that with loaders */
     int stages;      /* LDS stages: the global prefetch runs stages - 1 k-tiles deep
                         (sdt_pick_tile: the count a launch of that shape uses;
                         sdt_tile_info: the rung's deep pipeline).  On rung 0
@@ -97,6 +98,12 @@ typedef struct sdt_tile {
     int persistent;  /* 0: one workgroup per tile; P > 0: P workgroups loop
                         over the tiles (ping-pong kernel only) */
     int ksplit;      /* 1: the rung is built to split K across workgroups */
+    int loaders;     /* 1: a loader wave beside each compute wave issues every
+                        global -> LDS load, so that the compute waves issue only
+                        fragment reads and MFMAs (the deep one-k-group pipeline
+                        of rungs 2 and 4, 128 x 128 and 64 x 64, without a
+                        k-split; the automatic plan from 12 full k-tiles;
+                        sdt_tile_info: 1 where the rung is built with them) */
 } sdt_tile;
 
 /* A launch configuration; -1 in a field = the automatic choice. */
@@ -118,6 +125,8 @@ typedef struct sdt_launch {
                         tiles w, w + P, w + 2P, ... (the FlyDSL PR, Changes:
                         persistent workgroups, where only 0 or the tile count
                         is accepted; any P in between is accepted here) */
+    int loaders;     /* 0 off, 1 on: loader waves issue the global loads (rungs
+                        2 and 4 with their deep count, one k-group, no k-split) */
 } sdt_launch;
 
 /* ---- main entry points ---------------------------------------------------- */

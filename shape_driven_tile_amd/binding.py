@@ -46,7 +46,8 @@ class SdtTile(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int), ("kgroups", ctypes.c_int),
                 ("stagger", ctypes.c_int), ("long_stages", ctypes.c_int),
                 ("splits", ctypes.c_int), ("split_algo", ctypes.c_int),
-                ("persistent", ctypes.c_int), ("ksplit", ctypes.c_int)]
+                ("persistent", ctypes.c_int), ("ksplit", ctypes.c_int),
+                ("loaders", ctypes.c_int)]
 
     def as_dict(self) -> dict:
         return {name: getattr(self, name) for name, _ in self._fields_}
@@ -57,7 +58,7 @@ class SdtLaunch(ctypes.Structure):
     _fields_ = [("tile_id", ctypes.c_int), ("stages", ctypes.c_int),
                 ("kgroups", ctypes.c_int), ("stagger", ctypes.c_int),
                 ("splits", ctypes.c_int), ("split_algo", ctypes.c_int),
-                ("persistent", ctypes.c_int)]
+                ("persistent", ctypes.c_int), ("loaders", ctypes.c_int)]
 
 
 class SdtError(RuntimeError):
@@ -185,9 +186,9 @@ def plan_tile(tile_id: int, M: int, N: int, K: int, num_cu: int = 256) -> dict:
 
 
 def launch_cfg(tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1, split_algo=-1,
-               persistent=-1) -> SdtLaunch:
+               persistent=-1, loaders=-1) -> SdtLaunch:
     return SdtLaunch(int(tile_id), int(stages), int(kgroups), int(stagger), int(splits),
-                     int(split_algo), int(persistent))
+                     int(split_algo), int(persistent), int(loaders))
 
 
 def pick_tile_ws(M: int, N: int, K: int, num_cu: int, workspace_bytes: int) -> dict:
@@ -474,17 +475,17 @@ def gemm_bf16_ws(A, B, C, workspace=None, stream=None) -> None:
 
 
 def gemm_f16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1,
-                 split_algo=-1, persistent=-1, workspace=None, stream=None) -> None:
+                 split_algo=-1, persistent=-1, workspace=None, stream=None, loaders=-1) -> None:
     """gemm_f16_ws with any part of the launch configuration forced (-1 = automatic)."""
     import torch
-    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent)
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent, loaders)
     _gemm_16_ws("gemm_f16_cfg", A, B, C, workspace, stream, torch.float16, (ctypes.byref(cfg),))
 
 
 def gemm_bf16_cfg(A, B, C, tile_id=-1, stages=-1, kgroups=-1, stagger=-1, splits=-1,
-                  split_algo=-1, persistent=-1, workspace=None, stream=None) -> None:
+                  split_algo=-1, persistent=-1, workspace=None, stream=None, loaders=-1) -> None:
     import torch
-    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent)
+    cfg = launch_cfg(tile_id, stages, kgroups, stagger, splits, split_algo, persistent, loaders)
     _gemm_16_ws("gemm_bf16_cfg", A, B, C, workspace, stream, torch.bfloat16, (ctypes.byref(cfg),))
 
 

@@ -593,8 +593,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, const acc_t (
     }
 }
 
-template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32, bool SK = false>
-__global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
+// HELP (one k-group, no k-split): the workgroup also holds one loader wave
+// per compute wave.  The loader waves issue every global -> LDS load, with
+// the same slabs, waits and barriers the compute waves would have used, and
+// exit after the k-loop; the compute waves then issue nothing but fragment
+// reads and MFMAs.  With one compute wave per SIMD each 1 KB direct-to-LDS
+// load otherwise takes about 17 cycles of the wave's issue (the CU's 64 B/clk)
+// between its MFMAs.
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32, bool SK = false,
+          bool HELP = false>
+__global__ __launch_bounds__(WM * WN * KS * 64 * (HELP ? 2 : 1)) void gemm_kernel(GemmParams p) {
     typedef typename Elt::frag8 frag8;
     constexpr int BK = kBK;
     constexpr int NMN = WM * WN;       // waves per k-group (one output block each)
@@ -631,7 +639,10 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
     // Wave-uniform, and said so: the per-wave LDS destinations of the
     // direct-to-LDS loads (M0) then come from scalar arithmetic instead of a
     // v_readfirstlane per load (8192^3: 909 -> 894 us).
-    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wave_id = __builtin_amdgcn_readfirstlane(t >> 6);
+    static_assert(!HELP || (KS == 1 && !SK), "loader waves: one k-group, no k-split");
+    const bool loader = HELP && wave_id >= NW;
+    const int wave = HELP ? wave_id % NW : wave_id;   // a loader wave takes its compute wave's slabs
     const int kg = wave / NMN;         // k-group: sub-steps kg, kg + KS, ... of each k-tile
     const int wmn = wave % NMN;
     const int wave_m = wmn % WM;
@@ -774,12 +785,36 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
 
     // ---- prologue: tiles 0 .. NS-1 issued, tile 0 landed ------------------------
     const int npro = min(nseq, NS);
-    for (int j = 0; j < npro; ++j) load_step(j, j);
-    if (nseq > NS)
-        wait_global_loads<(NS - 1) * L>();   // all NS prologue tiles are full ones
-    else
-        wait_global_loads<0>();
+    if (!HELP || loader) {
+        for (int j = 0; j < npro; ++j) load_step(j, j);
+        if (nseq > NS)
+            wait_global_loads<(NS - 1) * L>();   // all NS prologue tiles are full ones
+        else
+            wait_global_loads<0>();
+    }
     __syncthreads();
+    if constexpr (HELP) {
+        if (loader) {
+            // The compute waves' k-loop below without the fragment reads and
+            // MFMAs: the same waits before the same barriers, the same loads
+            // after them.
+            int sl = 0;
+            int il = 0;
+            for (; il + NS < nfull; ++il) {
+                wait_global_loads<(NS - 2) * L>();
+                __syncthreads();
+                dma_tile(il + NS, sl);
+                sl = (sl + 1 == NS) ? 0 : sl + 1;
+            }
+            for (; il < nseq; ++il) {
+                wait_global_loads<0>();
+                __syncthreads();
+                if (il + NS < nseq) load_step(il + NS, sl);
+                sl = (sl + 1 == NS) ? 0 : sl + 1;
+            }
+            return;
+        }
+    }
     read_frags(0, kg, 0);
 
     // ---- steady state: one basic block per k-tile ----------------------------------
@@ -817,12 +852,15 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
             interleave(Reads{}, None{});
             __builtin_amdgcn_sched_barrier(0);
         }
-        wait_global_loads<(NS - 2) * L>();
+        if constexpr (!HELP) wait_global_loads<(NS - 2) * L>();
         __syncthreads();
-        dma_tile(i + NS, s);
+        if constexpr (!HELP) dma_tile(i + NS, s);
         read_frags(sn, kg, 0);
         mfmas(1);
-        interleave(Reads{}, Loads{});
+        if constexpr (HELP)
+            interleave(Reads{}, None{});
+        else
+            interleave(Reads{}, Loads{});
         __builtin_amdgcn_sched_barrier(0);
         s = sn;
     }
@@ -843,9 +881,11 @@ __global__ __launch_bounds__(WM * WN * KS * 64) void gemm_kernel(GemmParams p) {
             read_frags(s, kg + 2, 1);
             mfmas(0);
         }
-        wait_global_loads<0>();
+        if constexpr (!HELP) wait_global_loads<0>();
         __syncthreads();
-        if (i + NS < nseq) load_step(i + NS, s);
+        if constexpr (!HELP) {
+            if (i + NS < nseq) load_step(i + NS, s);
+        }
         if (i + 1 < nseq) read_frags(sn, kg, 0);
         mfmas(1);
         s = sn;

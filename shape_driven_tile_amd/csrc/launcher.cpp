@@ -17,6 +17,17 @@ bool sizes_supported(int64_t M, int64_t N, int64_t K) {
 
 bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
 
+// Whether a plan's pipeline can run with loader waves: a rung built with
+// them, its deep pipeline, one k-group, no k-split.
+bool loaders_possible(const Plan& p) {
+    const TileDesc& d = kLadder[p.tile];
+    return d.helpers && p.kgroups == 1 && p.stages == d.stages && p.splits <= 1;
+}
+
+bool loaders_auto(const Plan& p, int64_t K) {
+    return loaders_possible(p) && K / kBK >= kLoaderMinKTiles;
+}
+
 sdt_tile describe(const Plan& p) {
     const TileDesc& d = kLadder[p.tile];
     sdt_tile t;
@@ -26,7 +37,7 @@ sdt_tile describe(const Plan& p) {
     t.bk = kBK;
     t.waves_m = d.waves_m;
     t.waves_n = d.waves_n;
-    t.threads = 64 * d.waves_m * d.waves_n * p.kgroups;
+    t.threads = 64 * d.waves_m * d.waves_n * p.kgroups * (p.loaders ? 2 : 1);
     t.kgroups = p.kgroups;
     t.stages = p.stages;
     t.lds_bytes = (d.pingpong && p.stages == d.stages)
@@ -38,6 +49,7 @@ sdt_tile describe(const Plan& p) {
     t.split_algo = p.splits > 1 ? p.split_algo : 0;
     t.persistent = p.persistent;
     t.ksplit = d.ksplit;
+    t.loaders = p.loaders;
     return t;
 }
 
@@ -48,7 +60,9 @@ sdt_tile describe_rung(int id) {
     p.stages = kLadder[id].stages;
     p.kgroups = kLadder[id].kgroups;
     p.stagger = 0;
-    return describe(p);
+    sdt_tile t = describe(p);
+    t.loaders = kLadder[id].helpers;
+    return t;
 }
 
 // Workspace of a k-split launch: the arrival-counter area (a fixed
@@ -149,6 +163,7 @@ Plan plan_for(int id, int64_t M, int64_t N, int64_t K, int num_cu) {
     p.kgroups = kgroups_for(id, M, N, K, num_cu);
     p.stages = long_for(id, d.stages, p.kgroups, K);
     p.stagger = stagger_auto(id, M, N, K) ? 1 : 0;
+    p.loaders = loaders_auto(p, K) ? 1 : 0;
     return p;
 }
 
@@ -179,6 +194,8 @@ int check_plan(const Plan& p, int64_t K) {
     // persistent workgroups: the ping-pong kernel only
     if (p.persistent < 0 || (p.persistent > 0 && (!d.pingpong || p.stages != d.stages)))
         return SDT_ERR_INVALID_ARG;
+    // loader waves: the pipelines built with them
+    if (p.loaders != 0 && (p.loaders != 1 || !loaders_possible(p))) return SDT_ERR_INVALID_ARG;
     return SDT_OK;
 }
 
@@ -193,6 +210,7 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
     if (cfg.stages < -1 || cfg.kgroups < -1) return SDT_ERR_INVALID_ARG;
     if (cfg.splits < -1 || cfg.splits == 0 || cfg.splits > kMaxSplits) return SDT_ERR_INVALID_ARG;
     if (cfg.split_algo < -1 || cfg.split_algo > 1 || cfg.persistent < -1) return SDT_ERR_INVALID_ARG;
+    if (cfg.loaders < -1 || cfg.loaders > 1) return SDT_ERR_INVALID_ARG;
     if (cfg.tile_id >= 0) {   // a forced rung: its forced fields must name a kernel it has
         const TileDesc& d = kLadder[cfg.tile_id];
         if (cfg.stages >= 0 && cfg.stages != 2 && cfg.stages != d.stages &&
@@ -239,6 +257,8 @@ int resolve_plan(const sdt_launch& cfg, int64_t M, int64_t N, int64_t K, int num
     if (cfg.stages >= 0) pl.stages = cfg.stages;
     if (cfg.split_algo >= 0) pl.split_algo = cfg.split_algo;
     if (cfg.persistent >= 0) pl.persistent = cfg.persistent;
+    // loader waves: forced, or the automatic rule on the plan as it now stands
+    pl.loaders = cfg.loaders >= 0 ? cfg.loaders : (loaders_auto(pl, K) ? 1 : 0);
     int st = check_plan(pl, K);
     if (st != SDT_OK) return st;
     if (pl.persistent > ceil_div(M, d.bm) * ceil_div(N, d.bn)) return SDT_ERR_INVALID_ARG;

@@ -32,6 +32,11 @@ struct TileDesc {
     // the CUs and at least kg2_min_ktiles k-tiles; with one workgroup on
     // every CU, at least kg2_full_ktiles k-tiles (0: never).
     int kg2_min_ktiles, kg2_grid8, kg2_full_ktiles;
+    // 1: the deep one-k-group 16x16x32 pipeline (the automatic plan's usual
+    // pick on the rung) runs with a loader wave beside each compute wave,
+    // which issues the global -> LDS loads (gemm_kernel's HELP); only where
+    // both waves fit on a SIMD (at most 256 registers each).
+    int helpers;
 };
 
 // Largest tile first.  The indices are the ABI's tile ids.  `stages` is the
@@ -61,21 +66,25 @@ struct TileDesc {
 // workgroups one k-group still wins at 128 k-tiles, 39.68 / 40.38).
 constexpr TileDesc kLadder[] = {
     // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
-    {256, 256, 2, 4, 3, 1, 1, 0, 0, 0, 0, 0, 0},
-    // 4 waves, 128x64 per wave, 3 x 48 KB
-    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0, 12, 8, 0},
+    {256, 256, 2, 4, 3, 1, 1, 0, 0, 0, 0, 0, 0, 0},
+    // 4 waves, 128x64 per wave, 3 x 48 KB (322 registers a wave: no loaders)
+    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0, 12, 8, 0, 0},
     // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1, 12, 8, 0},
-    // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB
-    {128, 64, 2, 2, 3, 2, 0, 1, 4, 1, 96, 6, 0},
+    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1, 12, 8, 0, 1},
+    // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB (loaders measured mixed:
+    // 4096x512x1024 7.93 / 7.49 us, 1280^3 9.30 / 9.62, 1152x1152x5120
+    // 26.80 / 27.10)
+    {128, 64, 2, 2, 3, 2, 0, 1, 4, 1, 96, 6, 0, 0},
     // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
-    {64, 64, 2, 2, 3, 2, 0, 1, 4, 1, 24, 8, 40},
+    {64, 64, 2, 2, 3, 2, 0, 1, 4, 1, 24, 8, 40, 1},
     // Off the ladder (see kNumLadder), 16x16x32 MFMAs on every pipeline (48
     // and 80 are no multiples of 32): 4 waves of 48x48, 3 x 24 KB; 8 waves of
-    // 96x48, 3 x 48 KB; 4 waves of 80x80, 3 x 40 KB.
-    {96, 96, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0},
-    {192, 192, 2, 4, 3, 1, 0, 1, 0, 0, 0, 0, 0},
-    {160, 160, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0},
+    // 96x48, 3 x 48 KB; 4 waves of 80x80, 3 x 40 KB (loaders: 96 x 96 measured
+    // even, 1536^3 11.18 / 11.18 us, 1440x1440x1000 10.64 / 10.79; the other
+    // two have too many registers for them).
+    {96, 96, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0, 0},
+    {192, 192, 2, 4, 3, 1, 0, 1, 0, 0, 0, 0, 0, 0},
+    {160, 160, 2, 2, 3, 1, 0, 1, 0, 0, 0, 0, 0, 0},
 };
 
 // Fewest full k-tiles at which a rung with a long pipeline uses it in place
@@ -141,7 +150,20 @@ constexpr int64_t kCounterBytes = 64 * 1024;
 struct Plan {
     int tile, stages, kgroups, stagger;
     int splits = 1, split_algo = 0, persistent = 0;
+    int loaders = 0;   // 1: the rung's loader-wave pipeline (gemm_kernel's HELP)
 };
+
+// Fewest full k-tiles at which the automatic plan runs a loader-wave rung's
+// deep one-k-group pipeline with its loader waves.  Fitted on MI355X
+// (graph-timed, us, without / with loaders, same bits, two boxes): from 12
+// k-tiles they win on both rungs built with them -- 128 x 128: 2048^3
+// 21.36 / 18.61, 2048x2048x1920 21.00 / 18.44, x2304 24.26 / 20.90,
+// 1024x4096x4096 38.45 / 33.09, 4096x1024x1024 11.93 / 10.83; 64 x 64:
+// 768^3 5.00 / 4.85, 1024^3 5.97 / 5.64, 384x384x768 4.84 / 4.63,
+// 256x4096x1024 5.85 / 5.49, 768x768x1280 6.48 / 5.88 -- and on shorter
+// loops the extra waves cost more than they take off the compute waves
+// (256^3 3.33 / 3.52, 512x2048x512 4.45 / 4.53).
+constexpr int kLoaderMinKTiles = 12;
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 // Rungs 0 .. kNumLadder-1 form the ladder pick_rung walks (largest first).
 // The rungs after them are off the ladder: pick_tile takes one in place of the
@@ -174,6 +196,8 @@ struct KnSplit {
 };
 KnSplit kn_split_plan(int64_t N, int64_t K);
 
+// Whether a plan runs its rung's pipeline with loader waves (the rung's
+// `helpers`, its deep pipeline, one k-group, no k-split, no long pipeline).
 sdt_tile describe(const Plan& p);
 sdt_tile describe_rung(int id);
 int64_t workspace_bytes(const Plan& p, int64_t M, int64_t N);

@@ -28,7 +28,7 @@ constexpr bool kLadderHasSplit() {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr sdt_launch kAuto = {-1, -1, -1, -1, -1, -1, -1};
+constexpr sdt_launch kAuto = {-1, -1, -1, -1, -1, -1, -1, -1};
 
 struct DeviceInfo {
     int num_cu = 0;
@@ -69,7 +69,8 @@ int device_info(DeviceInfo* out) {
 // One launch of gemm_kernel; a k-split launch (splits > 1) runs the
 // instantiation built for it, `splits` workgroups per tile, followed (with
 // split_algo 0) by the kernel that sums the partials.
-template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32>
+template <typename Elt, int BM, int BN, int WM, int WN, int NS, int KS, int MF = 32,
+          bool HELP = false>
 hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
     void* args[] = {&p};
     const int tiles = p.gm * p.gn;
@@ -85,8 +86,8 @@ hipError_t launch_gemm_tile(GemmParams p, hipStream_t stream) {
         }
     }
     return hipLaunchKernel(
-        reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS, MF>),
-        dim3(tiles), dim3(WM * WN * KS * 64), args, 0, stream);
+        reinterpret_cast<const void*>(&gemm_kernel<Elt, BM, BN, WM, WN, NS, KS, MF, false, HELP>),
+        dim3(tiles), dim3(WM * WN * KS * 64 * (HELP ? 2 : 1)), args, 0, stream);
 }
 
 // The 256 x 256 ping-pong kernel: 8 waves, 160 KB of LDS, one workgroup per
@@ -115,6 +116,11 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
                       "16x16x32-only rungs: one k-group, no long pipeline, no k-split");
         if (pl.stages == 2)
             return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1, 16>(p, s);
+        if constexpr (d.helpers != 0) {
+            if (pl.loaders)
+                return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16,
+                                        true>(p, s);
+        }
         return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16>(p, s);
     } else if constexpr (d.pingpong) {
         static_assert(d.bm == 256 && d.bn == 256 && d.waves_m == 2 && d.waves_n == 4 &&
@@ -137,6 +143,11 @@ hipError_t launch_rung(GemmParams p, const Plan& pl, hipStream_t s) {
         }
         if (pl.stages == 2)
             return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, 2, 1>(p, s);
+        if constexpr (d.deep16 && d.helpers != 0) {
+            if (pl.loaders)
+                return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16,
+                                        true>(p, s);
+        }
         if constexpr (d.deep16)
             return launch_gemm_tile<Elt, d.bm, d.bn, d.waves_m, d.waves_n, d.stages, 1, 16>(p, s);
         else
@@ -605,7 +616,7 @@ extern "C" int gemm_f16_ex(int64_t M, int64_t N, int64_t K, const void* A, int64
                            const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                            int tile_id, int stagger) {
     return sdt::gemm_impl<sdt::F16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                                    sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1}, false,
+                                    sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1, -1}, false,
                                     nullptr, 0);
 }
 
@@ -626,7 +637,7 @@ extern "C" int gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void* A, int6
                             const void* B, int64_t ldb, void* C, int64_t ldc, void* stream,
                             int tile_id, int stagger) {
     return sdt::gemm_impl<sdt::BF16>(M, N, K, A, lda, B, ldb, C, ldc, stream,
-                                     sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1}, false,
+                                     sdt_launch{tile_id, -1, -1, stagger, -1, -1, -1, -1}, false,
                                      nullptr, 0);
 }
 

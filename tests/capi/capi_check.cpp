@@ -219,7 +219,7 @@ int main() {
               SDT_ERR_UNSUPPORTED, "misaligned A");
     CHECK(gemm_f16(64, 64, 64, b, 60, b + 8192, 64, b + 65536, 64, nullptr) == SDT_ERR_INVALID_ARG,
           "lda < K");
-    sdt_launch cfg = {0, 5, -1, -1, -1, -1, -1};
+    sdt_launch cfg = {0, 5, -1, -1, -1, -1, -1, -1};
     CHECK(gemm_f16_cfg(64, 64, 64, b, 64, b + 8192, 64, b + 65536, 64, nullptr, 0, nullptr,
                        &cfg) == SDT_ERR_INVALID_ARG, "stage count without a kernel");
     CHECK(sdt_abi_version() == SDT_ABI_VERSION, "ABI version %d, header %d", sdt_abi_version(),

@@ -22,7 +22,7 @@ def to_dev(a: np.ndarray):
 
 
 def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None, stages=-1,
-             kgroups=-1):
+             kgroups=-1, loaders=-1):
     """A: (M, lda) float16, B: (N, ldb) float16 host buffers (K-contiguous rows).
     Returns the (M, N) float16 result and whether the C padding was untouched."""
     import torch
@@ -37,9 +37,9 @@ def run_gemm(A, B, K=None, tile=None, stagger=-1, ldc_pad=0, stream=None, stages
     ldc = N + ldc_pad if M == 1 else -(-(N + ldc_pad) // 8) * 8
     full = torch.full((M, ldc), float("nan"), dtype=torch.float16, device=DEV)
     dC = full[:, :N]
-    if stages != -1 or kgroups != -1:
+    if stages != -1 or kgroups != -1 or loaders != -1:
         sdt.gemm_f16_cfg(dA, dB, dC, tile_id=-1 if tile is None else tile, stages=stages,
-                         kgroups=kgroups, stagger=stagger, stream=stream)
+                         kgroups=kgroups, stagger=stagger, stream=stream, loaders=loaders)
     elif tile is None and stagger == -1:
         sdt.gemm_f16(dA, dB, dC, stream=stream)
     else:

@@ -38,7 +38,7 @@ int main() {
                 for (int cu : cus) {
                     if (!sdt::sizes_supported(M, N, K)) {   // refused before any planning
                         sdt::Plan out;
-                        sdt_launch cfg = {-1, -1, -1, -1, -1, -1, -1};
+                        sdt_launch cfg = {-1, -1, -1, -1, -1, -1, -1, -1};
                         h = mix(h, sdt::resolve_plan(cfg, M, N, K, cu, 1 << 20, &out));
                         h = mix(h, sdt_pick_rung(M, N, 64, 64, 1, &M));
                         continue;
@@ -49,7 +49,7 @@ int main() {
                     h = mix(mix(mix(h, p.stages), p.kgroups), p.stagger);
                     h = mix(h, sdt::check_plan(p, K));
                     for (int64_t ws : {int64_t(-1), int64_t(0), int64_t(1) << 20, int64_t(1) << 40}) {
-                        sdt_launch cfg = {-1, -1, -1, -1, -1, -1, -1};
+                        sdt_launch cfg = {-1, -1, -1, -1, -1, -1, -1, -1};
                         sdt::Plan out;
                         const int st = sdt::resolve_plan(cfg, M, N, K, cu, ws, &out);
                         h = mix(mix(h, st), st == SDT_OK ? out.splits : -7);
@@ -64,7 +64,7 @@ int main() {
                 for (int splits : {-1, 0, 1, 2, 16, 17, 64, 65})
                     for (int algo = -1; algo <= 2; ++algo)
                         for (int pers : {-1, 0, 1, 1000}) {
-                            sdt_launch cfg = {tile, stages, kg, -1, splits, algo, pers};
+                            sdt_launch cfg = {tile, stages, kg, -1, splits, algo, pers, -1};
                             sdt::Plan out;
                             h = mix(h, sdt::resolve_plan(cfg, 1000, 1000, 4160, 256, int64_t(1) << 30,
                                                          &out));

@@ -146,6 +146,9 @@ def test_gemv_rejects_before_launch():
 # Rungs 0-4 are the ladder pick_rung walks; the rungs after them are taken
 # only in place of the ladder's pick (the header's sdt_pick_tile rule).
 NUM_LADDER = 5
+# rungs whose deep one-k-group pipeline runs a loader wave beside each
+# compute wave (128 x 128 and 64 x 64)
+LOADER_RUNGS = (2, 4)
 
 
 def ladder():
@@ -202,6 +205,9 @@ def test_ladder_is_well_formed():
     for t in tiles:
         assert t["bk"] == 64
         assert t["kgroups"] in (1, 2)
+        # the rung as built: its deep pipeline with its most k-groups, and
+        # whether it is built with loader waves
+        assert t["loaders"] == int(t["id"] in LOADER_RUNGS)
         assert t["threads"] == 64 * t["waves_m"] * t["waves_n"] * t["kgroups"]
         mf = 32 if t["id"] < NUM_LADDER else 16
         assert t["bm"] % (mf * t["waves_m"]) == 0 and t["bn"] % (mf * t["waves_n"]) == 0
@@ -261,7 +267,9 @@ def test_launch_plan_rules():
                 stg = int(0 < t["id"] < NUM_LADDER and nkt >= 16 and nkt & (nkt - 1) == 0
                           and 2 * K * (M + N) <= 16 << 20)
                 assert p["stagger"] == stg, (num_cu, t["id"], M, N, K)
-                assert p["threads"] == 64 * t["waves_m"] * t["waves_n"] * kg
+                ld = int(t["id"] in LOADER_RUNGS and kg == 1 and st == t["stages"] and K // 64 >= 12)
+                assert p["loaders"] == ld, (num_cu, t["id"], M, N, K)
+                assert p["threads"] == 64 * t["waves_m"] * t["waves_n"] * kg * (2 if ld else 1)
                 assert p["lds_bytes"] == lds_bytes(t, st)
     with pytest.raises(sdt.SdtError):
         sdt.plan_tile(len(tiles), 1, 1, 1)
@@ -566,6 +574,45 @@ def test_ksplit_plan_rules():
             assert need == 65536 + ntile * s * t["bm"] * t["bn"] * 4
             assert sdt.pick_tile_ws(M, N, K, num_cu, need) == big
             assert sdt.pick_tile_ws(M, N, K, num_cu, need - 1)["splits"] == 1
+
+
+def test_loader_waves_plan_and_refusals():
+    """Loader waves: the automatic plan takes them on rungs 2-5's deep
+    one-k-group pipeline from 12 full k-tiles and reports twice the threads;
+    forcing them is accepted on those pipelines only (checked before any
+    device call, fake aligned pointers)."""
+    t = sdt.pick_tile(2048, 2048, 2048, 256)
+    assert (t["id"], t["kgroups"], t["loaders"], t["threads"]) == (2, 1, 1, 512)
+    t = sdt.pick_tile(256, 256, 256, 256)
+    assert (t["id"], t["loaders"], t["threads"]) == (4, 0, 256)
+    t = sdt.pick_tile(768, 768, 768, 256)
+    assert (t["id"], t["loaders"], t["threads"]) == (4, 1, 512)
+    for n in (4096, 8192):    # the ping-pong rung has none
+        assert sdt.pick_tile(n, n, n, 256)["loaders"] == 0
+    t = sdt.pick_tile_ws(512, 512, 8192, 256, 1 << 24)   # a k-split plan: none
+    assert t["splits"] > 1 and t["loaders"] == 0
+    L = sdt.lib()
+    args = (512, 512, 512, 0x10000, 512, 0x20000, 512, 0x30000, 512, None, 0, None)
+    def cfg(**kw):
+        return ctypes.byref(sdt.launch_cfg(**kw))
+    def check(expect, **kw):
+        # refused by the planner (sdt_launch_workspace_size: -1) and by
+        # gemm_f16_cfg before it touches the device
+        assert L.sdt_launch_workspace_size(512, 512, 512, cfg(**kw)) == -1, kw
+        assert L.gemm_f16_cfg(*args, cfg(**kw)) == expect, kw
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=1, loaders=1)               # rung 1: none built
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=0, loaders=1)               # the ping-pong rung
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, kgroups=2, loaders=1)    # two k-groups
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, stages=2, loaders=1)     # the 2-stage pipeline
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=6, loaders=1)               # 192 x 192: none built
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, loaders=2)
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, loaders=-2)
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=3, loaders=1)               # 128 x 64: none built
+    check(sdt.SDT_ERR_INVALID_ARG, tile_id=5, loaders=1)               # 96 x 96: none built
+    for tile in (2, 4):
+        for ld in (0, 1):
+            c = sdt.launch_cfg(tile_id=tile, kgroups=1, loaders=ld)
+            assert L.sdt_launch_workspace_size(512, 512, 512, ctypes.byref(c)) == 0
 
 
 def test_ksplit_and_persistent_cfg_refusals():

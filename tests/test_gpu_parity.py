@@ -210,6 +210,54 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
             assert_bitexact(C, ref)
 
 
+LOADER_RUNGS = (2, 4)
+
+
+@pytest.mark.parametrize("K", [8, 64, 200, 768, 1032, 2048])
+def test_loader_waves_exact_every_rung(K):
+    """Loader waves forced on and off on every rung built with them (128 x
+    128 and 64 x 64), one k-group, the deep pipeline: exact
+    integer sums bit for bit against the oracle with ragged M and N, k-loops
+    of 0 to 32 full k-tiles (a partial one after them at K = 8, 200 and
+    1032), staggered where the k-tile count allows.  The loader waves issue
+    the same loads the compute waves would, so both forms give the same bits."""
+    M, N = 300, 260
+    A = inputs.integer_f16((M, K), 60 + K)
+    B = inputs.integer_f16((N, K), 61 + K)
+    ref = oracle.gemm(A, B)
+    nfull = K // 64
+    staggers = (0, 1) if nfull >= 2 and nfull & (nfull - 1) == 0 and K % 64 == 0 else (0,)
+    for tile in LOADER_RUNGS:
+        for st in staggers:
+            for ld in (0, 1):
+                say(f"loaders={ld} K={K} tile={tile} stagger={st}")
+                C, pad_ok = run_gemm(A, B, tile=tile, stagger=st, stages=3, kgroups=1, loaders=ld)
+                assert pad_ok
+                assert_bitexact(C, ref)
+
+
+@pytest.mark.parametrize("shape", [(2048, 2048, 2048), (2048, 2048, 1920), (768, 768, 768),
+                                   (1024, 1024, 1024), (4096, 1024, 1024)])
+def test_loader_waves_same_bits_uniform(shape):
+    """On uniform inputs the automatic plan (loader waves here) and the same
+    plan without them give identical bits, and both are within tolerance of
+    the oracle on sampled rows and columns."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    A, B = inputs.square_operands(M, 70, k=K) if M == N else (inputs.uniform_f16((M, K), 71),
+                                                              inputs.uniform_f16((N, K), 72))
+    plan = sdt.pick_tile(M, N, K, 0)
+    assert plan["loaders"] == 1 and plan["threads"] == 512, plan
+    say(f"uniform {shape} automatic plan (loaders) and loaders forced off")
+    C_on, _ = run_gemm(A, B)
+    C_off, _ = run_gemm(A, B, tile=plan["id"], stagger=plan["stagger"], stages=plan["stages"],
+                        kgroups=plan["kgroups"], loaders=0)
+    assert np.array_equal(C_on.view(np.uint16), C_off.view(np.uint16))
+    rows = sorted(set([0, 1, M // 2, M - 1] + list(np.random.default_rng(M).integers(0, M, 12))))
+    ref_rows = oracle.gemm(np.ascontiguousarray(A[rows]), B)
+    assert_close(C_on[rows], ref_rows)
+
+
 @pytest.mark.parametrize("K", [8, 64, 104, 128, 192])
 def test_short_k_every_pipeline(K):
     """k-loops of 0 to 3 full k-tiles (with and without a partial one) on every
