@@ -101,8 +101,8 @@ typedef struct sdt_tile {
     int loaders;     /* 1: a loader wave beside each compute wave issues every
                         global -> LDS load, so that the compute waves issue only
                         fragment reads and MFMAs (the deep one-k-group pipeline
-                        of rungs 2 and 4, 128 x 128 and 64 x 64, without a
-                        k-split; the automatic plan from 12 full k-tiles;
+                        of rungs 1, 2 and 4, 256 x 128, 128 x 128 and 64 x 64,
+                        without a k-split; the automatic plan from 12 full k-tiles;
                         sdt_tile_info: 1 where the rung is built with them) */
 } sdt_tile;
 
@@ -126,7 +126,7 @@ typedef struct sdt_launch {
                         persistent workgroups, where only 0 or the tile count
                         is accepted; any P in between is accepted here) */
     int loaders;     /* 0 off, 1 on: loader waves issue the global loads (rungs
-                        2 and 4 with their deep count, one k-group, no k-split) */
+                        1, 2 and 4 with their deep count, one k-group, no k-split) */
 } sdt_launch;
 
 /* ---- main entry points ---------------------------------------------------- */
@@ -349,10 +349,12 @@ int sdt_gemv_kn_num_variants(void);
  * (bm/64)(bn/64)(num_cu/2 + 1) 64 x 64 blocks up (the last rung below that).
  * An off-ladder rung with a smaller tile replaces the pick when its grid has
  * more workgroups than the pick's, at most num_cu and at least 7/8 of num_cu
- * (the first such rung in id order): on MI355X the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3:
- * 144 workgroups -> 256), the 192 x 192 rung in place of 256 x 256 (e.g.
- * 3072^3: 144 -> 256) and the 160 x 160 rung in place of 256 x 128 (e.g.
- * 2560^3: 200 -> 256).
+ * (the first such rung in id order), and, where the pick runs loader waves
+ * (see sdt_tile.loaders), a tile of at most 2/3 of the pick's area: on MI355X
+ * the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3: 144 workgroups ->
+ * 256), the 192 x 192 rung in place of 256 x 256 (e.g. 3072^3: 144 -> 256)
+ * and the 160 x 160 rung in place of 256 x 128 on k-loops shorter than 12
+ * k-tiles (e.g. 2560 x 2560 x 640: 200 -> 256).
  * Touches no device when num_cu > 0.  Returns SDT_OK, SDT_ERR_INVALID_ARG, or
  * SDT_ERR_UNSUPPORTED for M, N or K past 2^31 - 1. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);
@@ -381,10 +383,10 @@ int sdt_tile_info(int tile_id, sdt_tile* out);
 /* Host-only: how a launch of rung tile_id on an M x N x K product on num_cu
  * CUs (num_cu <= 0: 256) is configured (stages, kgroups, threads, LDS).
  * k-groups: 2 on rungs built with them by each rung's thresholds on the grid
- * and the k-loop (K in 64-deep k-tiles, at least 12): rungs 1 and 2 with
- * fewer workgroups than num_cu; rung 3 with fewer than 3/4 of num_cu and at
- * least 96 k-tiles; rung 4 with fewer than num_cu and at least 24 k-tiles, or
- * exactly num_cu and at least 40; else 1 (a k-split launch of gemm_f16_ws:
+ * and the k-loop (K in 64-deep k-tiles, at least 12): never on rungs 1 and 2
+ * (their one-k-group pipeline runs loader waves); rung 3 with fewer than 3/4
+ * of num_cu and at least 96 k-tiles; rung 4 with at most num_cu workgroups
+ * and at least 40 k-tiles; else 1 (a k-split launch of gemm_f16_ws:
  * 2 whenever its grid of tiles x splits fits num_cu -- on rungs 1 and 2 with
  * fewer -- and each split runs at least 12 k-tiles).  Stages: the rung's deep
  * count, which with two k-groups becomes

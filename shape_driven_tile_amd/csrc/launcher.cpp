@@ -297,7 +297,7 @@ int pick_rung(int64_t M, int64_t N, int ref_bm, int ref_bn, int rungs,
 // rung is picked at 3072 (144 WGs of 256x256), 2560 (200 WGs of 256x128) and
 // 1536 (144 WGs of 128x128), and the smaller at 2560 / 2048 / 1024, where the
 // larger would leave half the CUs or more idle.
-int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
+int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
     if (num_cu <= 0) num_cu = 256;
     int64_t thresholds[kNumLadder];
     for (int r = 0; r < kNumLadder; ++r) {
@@ -331,11 +331,24 @@ int pick_tile(int64_t M, int64_t N, int64_t /*K*/, int num_cu) {
     // 3072x1536x4096, 200: 47.0 against 44.6; 2048x2560x4096, 208: 45.4
     // against 48.1), while from 7/8 up every shape measured gained or tied
     // but 2304^3 (225 workgroups: 31.5 against 30.3).
+    //
+    // Where the pick runs its loader-wave pipeline (K of at least
+    // kLoaderMinKTiles full k-tiles on a rung built with them), a replacement
+    // must also cut a workgroup's tile by a third: the 96 x 96 rung in place of
+    // 128 x 128 still pays (1536^3 10.66 against 13.57 us, 1456x1456x2048
+    // 13.71 against 16.16), the 160 x 160 one in place of 256 x 128 no longer
+    // does (2560^3 33.42 against 30.78, 2304^3 30.53 against 26.93, 2496^3
+    // 34.24 against 32.75, 2560x2560x1024 17.85 against 16.55, 2560x2560x8192
+    // 95.44 against 86.72, 1280x5120x4096 52.00 against 46.09), with one shape
+    // measured the other way (3000x2000x2000 35.14 against 36.51).
+    const bool loaders = kLadder[r].helpers && K / kBK >= kLoaderMinKTiles;
     const int64_t br = ceil_div(M, kLadder[r].bm) * ceil_div(N, kLadder[r].bn);
     for (int c = kNumLadder; c < kNumTiles; ++c) {
         const int64_t bc = ceil_div(M, kLadder[c].bm) * ceil_div(N, kLadder[c].bn);
-        if (kLadder[c].bm * kLadder[c].bn < kLadder[r].bm * kLadder[r].bn && br < bc &&
-            bc <= num_cu && 8 * bc >= 7 * int64_t(num_cu))
+        const int64_t ac = int64_t(kLadder[c].bm) * kLadder[c].bn;
+        const int64_t ar = int64_t(kLadder[r].bm) * kLadder[r].bn;
+        if (ac < ar && br < bc && bc <= num_cu && 8 * bc >= 7 * int64_t(num_cu) &&
+            (!loaders || 3 * ac <= 2 * ar))
             return c;
     }
     return r;

@@ -53,13 +53,18 @@ struct TileDesc {
 // wave tile has no registers left for the k-split sum).
 //
 // Two k-groups against one k-group of 16x16x32 MFMAs, fitted on MI355X
-// (graph-timed, us, one k-group / two): 256 x 128 and 128 x 128 take two
-// only with CUs left idle (2048^3, 256 workgroups: 20.0 / 21.5; 1536^3 on
-// 128 x 128, 144: 14.8 / 13.7).  On 64 x 64 one k-group wins on short
-// loops even with CUs idle (512^3 4.05 / 4.47, 768^3 5.00 / 5.26, 768^2 x
-// 1024 5.75 / 5.78) and two from 24 k-tiles (768^2 x 1536 7.32 / 6.92,
-// 512^2 x 1536 7.10 / 6.82), or from 40 with every CU busy (1024^2 x 2432
-// 10.32 / 10.55, 1024^2 x 2560 11.03 / 10.69).  On 128 x 64 one k-group wins
+// (graph-timed, us, one k-group / two).  With loader waves (the one-k-group
+// pipeline from 12 k-tiles on 256 x 128, 128 x 128 and 64 x 64) one k-group
+// wins on the two larger rungs wherever two could run, CUs idle or not
+// (2048x2560x4096 41.48 / 47.68, 3072x1536x4096 40.50 / 45.70, 2240^3
+// 27.28 / 30.62, 1536x1792x4096 26.82 / 29.31, 1920^3 16.38 / 17.64,
+// 1792^3 14.86 / 15.50, 1664^3 13.69 / 14.23, 1536x2048x1536 13.92 /
+// 14.61), so they never plan two (kg2_grid8 = 0); before them, two won
+// with CUs idle (1536^3 on 128 x 128, 144 workgroups: 14.8 / 13.7).  On
+// 64 x 64 one k-group wins up to 24 k-tiles (768^2 x 1536 6.39 / 7.13,
+// 512^2 x 1536 6.22 / 6.94) and two from 40 (1024^2 x 2560 11.44 / 10.58,
+// 512^2 x 4096 17.07 / 14.70, 768^2 x 4096 17.05 / 14.60, 1024^2 x 4096
+// 17.86 / 15.68), CUs idle or not.  On 128 x 64 one k-group wins
 // up to 80 k-tiles (1280^3 9.34 / 10.32, 2048 x 1024 x 2048 13.52 / 14.82,
 // 1152^2 x 5120 26.78 / 27.83) and two only on longer loops with a quarter
 // of the CUs idle (1152^2 x 6144, 162 workgroups: 31.07 / 30.49; with 200
@@ -67,16 +72,16 @@ struct TileDesc {
 constexpr TileDesc kLadder[] = {
     // 8 waves, 128x64 per wave; 2 x 64 KB, or ping-pong 160 KB
     {256, 256, 2, 4, 3, 1, 1, 0, 0, 0, 0, 0, 0, 0},
-    // 4 waves, 128x64 per wave, 3 x 48 KB (322 registers a wave: no loaders)
-    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0, 12, 8, 0, 0},
+    // 4 waves, 128x64 per wave, 3 x 48 KB
+    {256, 128, 2, 2, 3, 2, 0, 1, 0, 0, 12, 0, 0, 1},
     // 4 waves, 64x64 per wave, 3 x 32 KB
-    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1, 12, 8, 0, 1},
+    {128, 128, 2, 2, 3, 2, 0, 1, 0, 1, 12, 0, 0, 1},
     // 4 waves, 64x32 per wave, 3 (long: 4) x 24 KB (loaders measured mixed:
     // 4096x512x1024 7.93 / 7.49 us, 1280^3 9.30 / 9.62, 1152x1152x5120
     // 26.80 / 27.10)
     {128, 64, 2, 2, 3, 2, 0, 1, 4, 1, 96, 6, 0, 0},
     // 4 waves, 32x32 per wave, 3 (long: 4) x 16 KB
-    {64, 64, 2, 2, 3, 2, 0, 1, 4, 1, 24, 8, 40, 1},
+    {64, 64, 2, 2, 3, 2, 0, 1, 4, 1, 40, 8, 40, 1},
     // Off the ladder (see kNumLadder), 16x16x32 MFMAs on every pipeline (48
     // and 80 are no multiples of 32): 4 waves of 48x48, 3 x 24 KB; 8 waves of
     // 96x48, 3 x 48 KB; 4 waves of 80x80, 3 x 40 KB (loaders: 96 x 96 measured
@@ -155,8 +160,10 @@ struct Plan {
 
 // Fewest full k-tiles at which the automatic plan runs a loader-wave rung's
 // deep one-k-group pipeline with its loader waves.  Fitted on MI355X
-// (graph-timed, us, without / with loaders, same bits, two boxes): from 12
-// k-tiles they win on both rungs built with them -- 128 x 128: 2048^3
+// (graph-timed, us, without / with loaders, same bits, three boxes): from 12
+// k-tiles they win on the three rungs built with them -- 256 x 128:
+// 4096x2048x2048 36.88 / 32.20, 4096x2048x4096 66.70 / 57.35, 8192x1024x1024
+// 21.33 / 20.12, 2048x4096x1024 21.62 / 19.54; 128 x 128: 2048^3
 // 21.36 / 18.61, 2048x2048x1920 21.00 / 18.44, x2304 24.26 / 20.90,
 // 1024x4096x4096 38.45 / 33.09, 4096x1024x1024 11.93 / 10.83; 64 x 64:
 // 768^3 5.00 / 4.85, 1024^3 5.97 / 5.64, 384x384x768 4.84 / 4.63,

@@ -147,8 +147,8 @@ def test_gemv_rejects_before_launch():
 # only in place of the ladder's pick (the header's sdt_pick_tile rule).
 NUM_LADDER = 5
 # rungs whose deep one-k-group pipeline runs a loader wave beside each
-# compute wave (128 x 128 and 64 x 64)
-LOADER_RUNGS = (2, 4)
+# compute wave (256 x 128, 128 x 128 and 64 x 64)
+LOADER_RUNGS = (1, 2, 4)
 
 
 def ladder():
@@ -169,16 +169,19 @@ def ladder_pick(M, N, num_cu):
                 NUM_LADDER - 1)
 
 
-def expected_pick(M, N, num_cu):
+def expected_pick(M, N, num_cu, K=4096):
     """The header's rule, restated: the ladder's pick from the 64 x 64 block
     count, then an off-ladder rung with a smaller tile whose grid is larger
-    than the pick's, at most num_cu and at least 7/8 of it."""
+    than the pick's, at most num_cu and at least 7/8 of it, and at most 2/3
+    of the pick's area where the pick runs loader waves (from 12 k-tiles)."""
     tiles = ladder()
     r = ladder_pick(M, N, num_cu)
+    loaders = r in LOADER_RUNGS and K // 64 >= 12
+    ar = tiles[r]["bm"] * tiles[r]["bn"]
     for c in tiles[NUM_LADDER:]:
-        if (c["bm"] * c["bn"] < tiles[r]["bm"] * tiles[r]["bn"]
-                and blocks(tiles[r], M, N) < blocks(c, M, N) <= num_cu
-                and 8 * blocks(c, M, N) >= 7 * num_cu):
+        ac = c["bm"] * c["bn"]
+        if (ac < ar and blocks(tiles[r], M, N) < blocks(c, M, N) <= num_cu
+                and 8 * blocks(c, M, N) >= 7 * num_cu and (not loaders or 3 * ac <= 2 * ar)):
             return c["id"]
     return r
 
@@ -221,7 +224,7 @@ def test_ladder_is_well_formed():
 # Two k-groups on the rungs built with them, per rung: (k-tiles needed with
 # CUs left idle, the grid's bound in eighths of the CUs, k-tiles needed with
 # one workgroup on every CU (0: never)).
-KG2_RULE = {1: (12, 8, 0), 2: (12, 8, 0), 3: (96, 6, 0), 4: (24, 8, 40)}
+KG2_RULE = {1: (12, 0, 0), 2: (12, 0, 0), 3: (96, 6, 0), 4: (40, 8, 40)}
 
 
 def expected_kgroups(tile_id, wgs, nkt, num_cu):
@@ -235,10 +238,10 @@ def expected_kgroups(tile_id, wgs, nkt, num_cu):
 
 def test_launch_plan_rules():
     """k-groups: 2 on rungs built with them by each rung's thresholds (256x128
-    and 128x128: fewer workgroups than CUs and at least 12 k-tiles; 128x64:
-    fewer than 3/4 of the CUs and at least 96; 64x64: fewer than the CUs and
-    at least 24, or one on every CU and at least 40), else the one-k-group
-    pipeline, 16x16x32 on every ladder rung below 256x256.  Stages: the deep
+    and 128x128: never, their one-k-group pipeline runs loader waves; 128x64:
+    fewer than 3/4 of the CUs and at least 96 k-tiles; 64x64: at most one
+    workgroup per CU and at least 40), else the one-k-group pipeline, 16x16x32
+    on every ladder rung below 256x256.  Stages: the deep
     count, never the 2-stage pipeline; a two-k-group deep pipeline becomes the
     rung's long one (if it has one) from 12 full k-tiles.  Stagger: on ladder
     rungs 1-4, a power-of-two count of at least 16 full k-tiles and A and B
@@ -282,12 +285,14 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(1024, 1024, 1024, 256)["kgroups"] == 1   # 256 x 64x64, 16 k-tiles
     assert sdt.pick_tile(1024, 1024, 4096, 256)["kgroups"] == 2   # 64 k-tiles
     assert sdt.pick_tile(768, 768, 768, 256)["kgroups"] == 1      # 144 workgroups, 12 k-tiles
-    assert sdt.pick_tile(768, 768, 2048, 256)["kgroups"] == 2     # 32 k-tiles
+    assert sdt.pick_tile(768, 768, 2048, 256)["kgroups"] == 1     # 32 k-tiles: loader waves
+    assert sdt.pick_tile(768, 768, 2560, 256)["kgroups"] == 2     # 40 k-tiles
     assert sdt.pick_tile(1280, 1280, 4096, 256)["kgroups"] == 1   # 128x64, 200 workgroups
     assert sdt.pick_tile(1152, 1152, 8192, 256)["kgroups"] == 2   # 128x64, 162, 128 k-tiles
     assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
-    assert sdt.pick_tile(1664, 1664, 1664, 256)["kgroups"] == 2   # 169 workgroups
+    p = sdt.pick_tile(1664, 1664, 1664, 256)                      # 169 workgroups
+    assert (p["kgroups"], p["loaders"]) == (1, 1)
     # 1536^3: 96 x 96 in place of 128 x 128 (256 workgroups instead of 144)
     p = sdt.pick_tile(1536, 1536, 1536, 256)
     assert (p["id"], p["bm"], p["kgroups"], p["stages"], p["stagger"]) == (5, 96, 1, 3, 0)
@@ -371,7 +376,7 @@ def test_pick_tile_properties():
     for num_cu in (80, 256, 304):
         for n in [64 * i for i in range(1, 200)]:
             t = sdt.pick_tile(n, n, n, num_cu)
-            assert t["id"] == expected_pick(n, n, num_cu), (num_cu, n)
+            assert t["id"] == expected_pick(n, n, num_cu, n), (num_cu, n)
             if n % 256 == 0 and t["id"] < NUM_LADDER:
                 wgs = (n // t["bm"]) * (n // t["bn"])
                 assert t["id"] == NUM_LADDER - 1 or wgs > num_cu // 2
@@ -381,12 +386,14 @@ def test_pick_tile_properties():
                    (1536, 2048), (1280, 1280), (100, 30000), (30000, 100)]:
         for num_cu in (80, 256, 304):
             assert sdt.pick_tile(M, N, 4096, num_cu)["id"] == expected_pick(M, N, num_cu)
+            assert sdt.pick_tile(M, N, 512, num_cu)["id"] == expected_pick(M, N, num_cu, 512)
     assert sdt.pick_tile(1536, 2048, 1536, 256)["id"] == 2      # 352 > 256 workgroups of 96 x 96
     assert sdt.pick_tile(1152, 1920, 2048, 256)["id"] == 5      # 135 -> 240 workgroups
     assert sdt.pick_tile(3072, 3072, 3072, 256)["id"] == 6      # 144 -> 256 workgroups
     assert sdt.pick_tile(3000, 3104, 1000, 256)["id"] == 0      # 272 > 256 of 192 x 192
     assert sdt.pick_tile(2816, 2816, 2816, 256)["id"] == 1      # 225 < 242 of 256 x 128
-    assert sdt.pick_tile(2560, 2560, 2560, 256)["id"] == 7      # 200 -> 256 workgroups
+    assert sdt.pick_tile(2560, 2560, 2560, 256)["id"] == 1      # 256 x 128 with loader waves
+    assert sdt.pick_tile(2560, 2560, 640, 256)["id"] == 7       # 10 k-tiles: 200 -> 256 workgroups
     assert sdt.pick_tile(2048, 4096, 2048, 256)["id"] == 1      # 256 x 128 fills the CUs
     assert sdt.pick_tile(2048, 2560, 4096, 256)["id"] == 1      # 208 < 7/8 of 256 of 160 x 160
     assert sdt.pick_tile(768, 11008, 4096, 256)["id"] == 6      # 232 of 192 x 192
@@ -400,7 +407,7 @@ def test_pick_tile_on_mi355x_square_sweep():
     """The rungs a sweep of every rung over square shapes measured fastest on
     MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
     want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
-            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (160, 160),
+            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
             3072: (192, 192), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
             8192: (256, 256)}
     for n, (bm, bn) in want.items():
@@ -600,7 +607,6 @@ def test_loader_waves_plan_and_refusals():
         # gemm_f16_cfg before it touches the device
         assert L.sdt_launch_workspace_size(512, 512, 512, cfg(**kw)) == -1, kw
         assert L.gemm_f16_cfg(*args, cfg(**kw)) == expect, kw
-    check(sdt.SDT_ERR_INVALID_ARG, tile_id=1, loaders=1)               # rung 1: none built
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=0, loaders=1)               # the ping-pong rung
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, kgroups=2, loaders=1)    # two k-groups
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, stages=2, loaders=1)     # the 2-stage pipeline
@@ -609,7 +615,7 @@ def test_loader_waves_plan_and_refusals():
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=2, loaders=-2)
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=3, loaders=1)               # 128 x 64: none built
     check(sdt.SDT_ERR_INVALID_ARG, tile_id=5, loaders=1)               # 96 x 96: none built
-    for tile in (2, 4):
+    for tile in (1, 2, 4):
         for ld in (0, 1):
             c = sdt.launch_cfg(tile_id=tile, kgroups=1, loaders=ld)
             assert L.sdt_launch_workspace_size(512, 512, 512, ctypes.byref(c)) == 0

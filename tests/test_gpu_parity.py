@@ -95,7 +95,7 @@ def test_integer_exact_8192_rows_auto():
 
 @pytest.mark.parametrize("shape,rung", [((1536, 1536, 1536), 5), ((1440, 1440, 1000), 5),
                                         ((3072, 3072, 1024), 6), ((768, 11008, 512), 6),
-                                        ((2560, 2560, 2560), 7), ((1280, 5120, 1024), 7)])
+                                        ((2560, 2560, 640), 7), ((1280, 5120, 704), 7)])
 def test_integer_exact_off_ladder_auto(shape, rung):
     """Shapes whose automatic plan takes an off-ladder rung (96 x 96, 192 x 192,
     160 x 160) at their real grids (one workgroup per CU, XCD-aware order,
@@ -210,13 +210,13 @@ def test_integer_exact_every_tile_deep_pipeline(shape):
             assert_bitexact(C, ref)
 
 
-LOADER_RUNGS = (2, 4)
+LOADER_RUNGS = (1, 2, 4)
 
 
 @pytest.mark.parametrize("K", [8, 64, 200, 768, 1032, 2048])
 def test_loader_waves_exact_every_rung(K):
-    """Loader waves forced on and off on every rung built with them (128 x
-    128 and 64 x 64), one k-group, the deep pipeline: exact
+    """Loader waves forced on and off on every rung built with them (256 x
+    128, 128 x 128 and 64 x 64), one k-group, the deep pipeline: exact
     integer sums bit for bit against the oracle with ragged M and N, k-loops
     of 0 to 32 full k-tiles (a partial one after them at K = 8, 200 and
     1032), staggered where the k-tile count allows.  The loader waves issue
@@ -237,7 +237,7 @@ def test_loader_waves_exact_every_rung(K):
 
 
 @pytest.mark.parametrize("shape", [(2048, 2048, 2048), (2048, 2048, 1920), (768, 768, 768),
-                                   (1024, 1024, 1024), (4096, 1024, 1024)])
+                                   (1024, 1024, 1024), (4096, 1024, 1024), (4096, 2048, 2048)])
 def test_loader_waves_same_bits_uniform(shape):
     """On uniform inputs the automatic plan (loader waves here) and the same
     plan without them give identical bits, and both are within tolerance of
@@ -389,7 +389,7 @@ def test_two_kgroups_auto_plan_matches_oracle():
     k-loop thresholds) against the oracle, and bit-identical to the forced
     plan."""
     from shape_driven_tile_amd import binding as sdt
-    for (M, N, K) in [(1024, 1024, 4096), (768, 768, 2048), (1664, 1664, 1664),
+    for (M, N, K) in [(1024, 1024, 4096), (768, 768, 2560), (896, 896, 3072),
                       (1152, 1152, 8192)]:
         p = sdt.pick_tile(M, N, K, 256)
         assert p["kgroups"] == 2, (M, N, K)
