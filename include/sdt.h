@@ -354,7 +354,11 @@ int sdt_gemv_kn_num_variants(void);
  * the 96 x 96 rung in place of 128 x 128 (e.g. 1536^3: 144 workgroups ->
  * 256), the 192 x 192 rung in place of 256 x 256 (e.g. 3072^3: 144 -> 256)
  * and the 160 x 160 rung in place of 256 x 128 on k-loops shorter than 12
- * k-tiles (e.g. 2560 x 2560 x 640: 200 -> 256).
+ * k-tiles (e.g. 2560 x 2560 x 640: 200 -> 256).  Where the pick is rung 0 and
+ * its grid has more than num_cu and at most 3/2 num_cu workgroups, rung 1
+ * (256 x 128, with loader waves) replaces it on k-loops of at least 32
+ * k-tiles (e.g. 4608^3: 324 ping-pong workgroups, two waves, against 648 of
+ * 256 x 128 in three shorter ones).
  * Touches no device when num_cu > 0.  Returns SDT_OK, SDT_ERR_INVALID_ARG, or
  * SDT_ERR_UNSUPPORTED for M, N or K past 2^31 - 1. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);

@@ -306,6 +306,23 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
     }
     thresholds[kNumLadder - 1] = 0;
     const int r = pick_rung(M, N, 64, 64, kNumLadder, thresholds);
+    // The ping-pong grid just past one wave (more workgroups than CUs, at most
+    // one and a half times as many): its second wave leaves most CUs idle,
+    // while the 256 x 128 rung with loader waves, whose workgroup takes about
+    // 0.55 of a ping-pong workgroup's time (8192^3: 98.7 against 179.4 us per
+    // wave; 4096^3: 51.5 against 94.2), runs three waves of its twice as many
+    // workgroups in less.  Fitted on MI355X (graph-timed, us, 256 x 256 /
+    // 256 x 128 with loaders): 4352^3 (289 workgroups) 171.2 / 155.4, 4608^3
+    // (324) 184.4 / 169.0, 4096x5120x4096 (320) 163.2 / 150.9, 8192x2560x4096
+    // 162.8 / 150.3, 4096x6144x4096 (384) 169.4 / 162.6, 6144x4096x2048 93.0 /
+    // 90.9; with 16 k-tiles a tie (4096x5120x1024: 51.05 / 51.11).  Just past
+    // two waves it did not hold (6144x6144x2048, 576 workgroups: 139.2 /
+    // 142.8; 6400x6400x4096, 625: 260.9 / 264.6; only 6144^3 the other way,
+    // 376.1 / 362.9), nor closer to two (5120^3, 400: 210.3 / 242.5).
+    if (r == 0 && kLadder[1].helpers && K / kBK >= kPastOneWaveMinKTiles) {
+        const int64_t b0 = ceil_div(M, kLadder[0].bm) * ceil_div(N, kLadder[0].bn);
+        if (b0 > num_cu && 2 * b0 <= 3 * int64_t(num_cu)) return 1;
+    }
     // An off-ladder rung with a smaller tile whose grid is larger than the
     // pick's but still at most one workgroup per CU: every CU then runs one
     // smaller tile instead of some CUs idling while the others run a larger

@@ -171,6 +171,11 @@ struct Plan {
 // loops the extra waves cost more than they take off the compute waves
 // (256^3 3.33 / 3.52, 512x2048x512 4.45 / 4.53).
 constexpr int kLoaderMinKTiles = 12;
+
+// Fewest full k-tiles at which pick_tile takes the 256 x 128 rung (with loader
+// waves) in place of the ping-pong kernel when the latter's grid is between
+// one and one and a half waves of workgroups (see pick_tile).
+constexpr int kPastOneWaveMinKTiles = 32;
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 // Rungs 0 .. kNumLadder-1 form the ladder pick_rung walks (largest first).
 // The rungs after them are off the ladder: pick_tile takes one in place of the

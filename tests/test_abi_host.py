@@ -173,9 +173,13 @@ def expected_pick(M, N, num_cu, K=4096):
     """The header's rule, restated: the ladder's pick from the 64 x 64 block
     count, then an off-ladder rung with a smaller tile whose grid is larger
     than the pick's, at most num_cu and at least 7/8 of it, and at most 2/3
-    of the pick's area where the pick runs loader waves (from 12 k-tiles)."""
+    of the pick's area where the pick runs loader waves (from 12 k-tiles);
+    256 x 128 in place of a 256 x 256 grid of more than num_cu and at most
+    3/2 num_cu workgroups from 32 k-tiles."""
     tiles = ladder()
     r = ladder_pick(M, N, num_cu)
+    if r == 0 and K // 64 >= 32 and num_cu < blocks(tiles[0], M, N) <= 3 * num_cu // 2:
+        return 1
     loaders = r in LOADER_RUNGS and K // 64 >= 12
     ar = tiles[r]["bm"] * tiles[r]["bn"]
     for c in tiles[NUM_LADDER:]:
@@ -291,6 +295,12 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(1152, 1152, 8192, 256)["kgroups"] == 2   # 128x64, 162, 128 k-tiles
     assert sdt.pick_tile(256, 256, 256, 256)["kgroups"] == 1
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
+    for (M, N, K), rung in [((4608, 4608, 4608), 1), ((4352, 4352, 2048), 1),
+                            ((4096, 6144, 4096), 1), ((4096, 5120, 1984), 0),
+                            ((5120, 5120, 5120), 0), ((6144, 6144, 6144), 0),
+                            ((4096, 4096, 4096), 0), ((8192, 8192, 8192), 0)]:
+        p = sdt.pick_tile(M, N, K, 256)             # ping-pong grid past one wave
+        assert (p["id"], p["loaders"]) == (rung, rung), (M, N, K)
     p = sdt.pick_tile(1664, 1664, 1664, 256)                      # 169 workgroups
     assert (p["kgroups"], p["loaders"]) == (1, 1)
     # 1536^3: 96 x 96 in place of 128 x 128 (256 workgroups instead of 144)
@@ -366,10 +376,12 @@ def test_pick_tile_properties():
             assert area >= prev_area, "the ladder's tile grows with the square size"
             prev_area = area
             assert t["id"] == r or t["bm"] * t["bn"] < area
-            # never off the largest tile while its grid alone fills the machine
+            # never off the largest tile while its grid alone fills the
+            # machine, but for 256 x 128 just past one wave on long k-loops
             big = tiles[0]
             if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
-                assert t["id"] == 0
+                past_one_wave = num_cu < blocks(big, n, n) <= 3 * num_cu // 2 and n // 64 >= 32
+                assert t["id"] == (1 if past_one_wave else 0), (num_cu, n)
     # the largest ladder rung whose grid, counted in 64x64 blocks scaled by
     # the rung's area, exceeds half the CUs (exactly its workgroup count when
     # the tile divides the shape), or the off-ladder rung in its place

@@ -117,6 +117,24 @@ def test_integer_exact_off_ladder_auto(shape, rung):
     assert_close(C, oracle.gemm(Au, Bu))
 
 
+@pytest.mark.parametrize("shape", [(4352, 4352, 2048), (4200, 4504, 2104)])
+def test_integer_exact_past_one_wave_auto(shape):
+    """Shapes whose 256 x 256 grid is just past one wave of workgroups (289
+    and 306 on 256 CUs), where the automatic plan takes the 256 x 128 rung
+    with loader waves: every element bit for bit on integer inputs (the
+    second shape ragged in M, N and K)."""
+    from shape_driven_tile_amd import binding as sdt
+    M, N, K = shape
+    p = sdt.pick_tile(M, N, K, 256)
+    assert (p["id"], p["loaders"]) == (1, 1), p
+    A = inputs.integer_f16((M, K), 41)
+    B = inputs.integer_f16((N, K), 42)
+    say(f"integer {shape} automatic plan (256x128, loader waves), full C")
+    C, pad_ok = run_gemm(A, B)
+    assert pad_ok
+    assert_bitexact(C, oracle.gemm(A, B))
+
+
 def test_integer_exact_pingpong_short_k_block_order():
     """The ping-pong kernel (forced, and the automatic plan) at 4096 x 4096 x
     128: two k-tiles, fewer than its stages, the 16 x 16-block tile order,
