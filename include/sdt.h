@@ -358,7 +358,8 @@ int sdt_gemv_kn_num_variants(void);
  * its grid has more than num_cu and at most 3/2 num_cu workgroups, rung 1
  * (256 x 128, with loader waves) replaces it on k-loops of at least 32
  * k-tiles (e.g. 4608^3: 324 ping-pong workgroups, two waves, against 648 of
- * 256 x 128 in three shorter ones).
+ * 256 x 128 in three shorter ones), and where it has more than 2 num_cu and
+ * at most 9/4 num_cu, on k-loops of at least 64 k-tiles (e.g. 6144^3).
  * Touches no device when num_cu > 0.  Returns SDT_OK, SDT_ERR_INVALID_ARG, or
  * SDT_ERR_UNSUPPORTED for M, N or K past 2^31 - 1. */
 int sdt_pick_tile(int64_t M, int64_t N, int64_t K, int num_cu, sdt_tile* out);

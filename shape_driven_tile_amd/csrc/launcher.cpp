@@ -315,13 +315,20 @@ int pick_tile(int64_t M, int64_t N, int64_t K, int num_cu) {
     // 256 x 128 with loaders): 4352^3 (289 workgroups) 171.2 / 155.4, 4608^3
     // (324) 184.4 / 169.0, 4096x5120x4096 (320) 163.2 / 150.9, 8192x2560x4096
     // 162.8 / 150.3, 4096x6144x4096 (384) 169.4 / 162.6, 6144x4096x2048 93.0 /
-    // 90.9; with 16 k-tiles a tie (4096x5120x1024: 51.05 / 51.11).  Just past
-    // two waves it did not hold (6144x6144x2048, 576 workgroups: 139.2 /
-    // 142.8; 6400x6400x4096, 625: 260.9 / 264.6; only 6144^3 the other way,
-    // 376.1 / 362.9), nor closer to two (5120^3, 400: 210.3 / 242.5).
-    if (r == 0 && kLadder[1].helpers && K / kBK >= kPastOneWaveMinKTiles) {
+    // 90.9; with 16 k-tiles a tie (4096x5120x1024: 51.05 / 51.11).  Nearer two
+    // waves it loses (5120^3, 400: 210.3 / 242.5).  Just past two waves, up to
+    // 2.25, it pays from 64 k-tiles (5888^2 x 8192, 529: 492.3 / 470.9,
+    // 6656x5120x6144, 520: 375.7 / 360.5, 6144x5632x6144 376.4 / 363.2, 6144^3,
+    // 576: 376.1 / 362.9, 6144^2 x 4096 260.2 / 257.1, 8192x4608x6144 378.0 /
+    // 370.3) but not on 32 (6144^2 x 2048 139.2 / 142.8), and from about 2.4
+    // waves it is even (6400^2 x 6144, 625: 388.1 / 386.5; x 8192 503.3 /
+    // 505.4; x 4096 260.9 / 264.6).
+    if (r == 0 && kLadder[1].helpers) {
         const int64_t b0 = ceil_div(M, kLadder[0].bm) * ceil_div(N, kLadder[0].bn);
-        if (b0 > num_cu && 2 * b0 <= 3 * int64_t(num_cu)) return 1;
+        const int64_t nkt = K / kBK, cu = num_cu;
+        if ((b0 > cu && 2 * b0 <= 3 * cu && nkt >= kPastOneWaveMinKTiles) ||
+            (b0 > 2 * cu && 4 * b0 <= 9 * cu && nkt >= kPastTwoWavesMinKTiles))
+            return 1;
     }
     // An off-ladder rung with a smaller tile whose grid is larger than the
     // pick's but still at most one workgroup per CU: every CU then runs one

@@ -174,8 +174,10 @@ constexpr int kLoaderMinKTiles = 12;
 
 // Fewest full k-tiles at which pick_tile takes the 256 x 128 rung (with loader
 // waves) in place of the ping-pong kernel when the latter's grid is between
-// one and one and a half waves of workgroups (see pick_tile).
+// one and one and a half waves of workgroups, and between two and two and a
+// quarter (see pick_tile).
 constexpr int kPastOneWaveMinKTiles = 32;
+constexpr int kPastTwoWavesMinKTiles = 64;
 constexpr int kNumTiles = sizeof(kLadder) / sizeof(kLadder[0]);
 // Rungs 0 .. kNumLadder-1 form the ladder pick_rung walks (largest first).
 // The rungs after them are off the ladder: pick_tile takes one in place of the

@@ -169,16 +169,23 @@ def ladder_pick(M, N, num_cu):
                 NUM_LADDER - 1)
 
 
+def past_wave_band(b0, K, num_cu):
+    """A ping-pong grid of b0 workgroups just past one or two waves."""
+    return ((num_cu < b0 and 2 * b0 <= 3 * num_cu and K // 64 >= 32) or
+            (2 * num_cu < b0 and 4 * b0 <= 9 * num_cu and K // 64 >= 64))
+
+
 def expected_pick(M, N, num_cu, K=4096):
     """The header's rule, restated: the ladder's pick from the 64 x 64 block
     count, then an off-ladder rung with a smaller tile whose grid is larger
     than the pick's, at most num_cu and at least 7/8 of it, and at most 2/3
     of the pick's area where the pick runs loader waves (from 12 k-tiles);
     256 x 128 in place of a 256 x 256 grid of more than num_cu and at most
-    3/2 num_cu workgroups from 32 k-tiles."""
+    3/2 num_cu workgroups from 32 k-tiles, or of more than 2 num_cu and at
+    most 9/4 num_cu from 64."""
     tiles = ladder()
     r = ladder_pick(M, N, num_cu)
-    if r == 0 and K // 64 >= 32 and num_cu < blocks(tiles[0], M, N) <= 3 * num_cu // 2:
+    if r == 0 and past_wave_band(blocks(tiles[0], M, N), K, num_cu):
         return 1
     loaders = r in LOADER_RUNGS and K // 64 >= 12
     ar = tiles[r]["bm"] * tiles[r]["bn"]
@@ -297,7 +304,9 @@ def test_launch_plan_rules():
     assert sdt.pick_tile(8192, 8192, 8192, 256)["kgroups"] == 1
     for (M, N, K), rung in [((4608, 4608, 4608), 1), ((4352, 4352, 2048), 1),
                             ((4096, 6144, 4096), 1), ((4096, 5120, 1984), 0),
-                            ((5120, 5120, 5120), 0), ((6144, 6144, 6144), 0),
+                            ((5120, 5120, 5120), 0), ((6144, 6144, 6144), 1),
+                            ((6144, 6144, 2048), 0), ((6400, 6400, 8192), 0),
+                            ((5888, 5888, 4096), 1), ((5888, 5888, 4032), 0),
                             ((4096, 4096, 4096), 0), ((8192, 8192, 8192), 0)]:
         p = sdt.pick_tile(M, N, K, 256)             # ping-pong grid past one wave
         assert (p["id"], p["loaders"]) == (rung, rung), (M, N, K)
@@ -380,8 +389,8 @@ def test_pick_tile_properties():
             # machine, but for 256 x 128 just past one wave on long k-loops
             big = tiles[0]
             if (n // big["bm"]) * (n // big["bn"]) >= num_cu:
-                past_one_wave = num_cu < blocks(big, n, n) <= 3 * num_cu // 2 and n // 64 >= 32
-                assert t["id"] == (1 if past_one_wave else 0), (num_cu, n)
+                band = past_wave_band(blocks(big, n, n), n, num_cu)
+                assert t["id"] == (1 if band else 0), (num_cu, n)
     # the largest ladder rung whose grid, counted in 64x64 blocks scaled by
     # the rung's area, exceeds half the CUs (exactly its workgroup count when
     # the tile divides the shape), or the off-ladder rung in its place
@@ -419,8 +428,10 @@ def test_pick_tile_on_mi355x_square_sweep():
     """The rungs a sweep of every rung over square shapes measured fastest on
     MI355X (256 CUs); 1280 is a tie between 128x64 and 64x64."""
     want = {256: (64, 64), 512: (64, 64), 768: (64, 64), 1024: (64, 64), 1280: (128, 64),
-            1536: (96, 96), 1792: (128, 128), 2048: (128, 128), 2560: (256, 128),
-            3072: (192, 192), 3584: (256, 256), 4096: (256, 256), 6144: (256, 256),
+            1536: (96, 96), 1664: (128, 128), 1792: (128, 128), 1920: (128, 128),
+            2048: (128, 128), 2304: (256, 128), 2560: (256, 128), 3072: (192, 192),
+            3584: (256, 256), 4096: (256, 256), 4352: (256, 128), 4608: (256, 128),
+            5120: (256, 256), 5376: (256, 256), 5632: (256, 256), 6144: (256, 128),
             8192: (256, 256)}
     for n, (bm, bn) in want.items():
         t = sdt.pick_tile(n, n, n, 256)

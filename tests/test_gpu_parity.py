@@ -117,12 +117,12 @@ def test_integer_exact_off_ladder_auto(shape, rung):
     assert_close(C, oracle.gemm(Au, Bu))
 
 
-@pytest.mark.parametrize("shape", [(4352, 4352, 2048), (4200, 4504, 2104)])
+@pytest.mark.parametrize("shape", [(4352, 4352, 2048), (4200, 4504, 2104), (5800, 5880, 4104)])
 def test_integer_exact_past_one_wave_auto(shape):
-    """Shapes whose 256 x 256 grid is just past one wave of workgroups (289
-    and 306 on 256 CUs), where the automatic plan takes the 256 x 128 rung
-    with loader waves: every element bit for bit on integer inputs (the
-    second shape ragged in M, N and K)."""
+    """Shapes whose 256 x 256 grid is just past one or two waves of
+    workgroups (289, 306 and 529 on 256 CUs), where the automatic plan takes
+    the 256 x 128 rung with loader waves: every element bit for bit on
+    integer inputs (the last two ragged in M, N and K)."""
     from shape_driven_tile_amd import binding as sdt
     M, N, K = shape
     p = sdt.pick_tile(M, N, K, 256)
